@@ -1,0 +1,268 @@
+"""fp64 CPU oracle for ReHyAt chunk-wise hybrid attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no code with
+the HIP library and never imports it.
+
+Two independent implementations live here:
+
+* ``librehyat_oracle.so`` (``rehyat_oracle.c``): the brute-force definition plus the
+  recurrent, chunk-parallel and streaming forms, all in fp64;
+* ``numpy_bruteforce`` below: a second brute force written from the same pages with a
+  different construction (explicit N x N masks and the closed form of the polynomial
+  kernel), used to cross-check the C code.
+
+Sources: the ReHyAt blog post (maplevalley.com.cn) sections 2.1.1, 2.2.1, 2.2.2, 2.3
+and 5.2; the mind-verse.de summary sections on overlapping chunks and the recurrent
+formulation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rehyat_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "librehyat_oracle.so")
+# A test may point the loader at a deliberately mutated build of the same source, to
+# show that the pins fail on plausible mistakes.
+_OVERRIDE = os.environ.get("REHYAT_ORACLE_LIB")
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (fp64, OpenMP).  Returns the library path."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.run(
+            ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
+             "-o", tmp, _SRC, "-lm"],
+            check=True,
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int) for name in
+                ("B", "H", "D", "T", "n", "Tc", "To", "Dphi", "P", "linear_only")]
+
+
+@dataclass(frozen=True)
+class Params:
+    B: int
+    H: int
+    D: int
+    T: int
+    n: int
+    Tc: int
+    To: int
+    Dphi: int
+    P: int
+    linear_only: int = 0
+
+    @property
+    def N(self) -> int:
+        return self.T * self.n
+
+    @property
+    def F(self) -> int:
+        return self.P * self.Dphi
+
+    def with_(self, **kw) -> "Params":
+        return replace(self, **kw)
+
+    def _c(self) -> _Params:
+        return _Params(self.B, self.H, self.D, self.T, self.n, self.Tc, self.To, self.Dphi,
+                       self.P, int(self.linear_only))
+
+
+_lib = None
+_D = ctypes.POINTER(ctypes.c_double)
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = _OVERRIDE or _LIB_PATH
+        if not _OVERRIDE and not os.path.exists(_LIB_PATH):
+            build(force=False)
+        L = ctypes.CDLL(path)
+        P = ctypes.POINTER(_Params)
+        L.orc_schedule.argtypes = [P, ctypes.POINTER(ctypes.c_int)]
+        L.orc_schedule.restype = ctypes.c_int
+        L.orc_features.argtypes = [P]
+        L.orc_features.restype = ctypes.c_int
+        L.orc_phi.argtypes = [P, _D, _D, _D, _D]
+        L.orc_phi.restype = None
+        six = [P, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D]
+        for name in ("orc_bruteforce", "orc_recurrent", "orc_parallel"):
+            getattr(L, name).argtypes = six
+            getattr(L, name).restype = None
+        L.orc_parallel_rows.argtypes = [P, _D, _D, _D, _D, _D, _D, _D, ctypes.c_int64,
+                                        ctypes.POINTER(ctypes.c_int64), _D, _D, _D, _D, _D]
+        L.orc_parallel_rows.restype = None
+        L.orc_stream_state_doubles.argtypes = [P]
+        L.orc_stream_state_doubles.restype = ctypes.c_int64
+        L.orc_stream_init.argtypes = [P, _D]
+        L.orc_stream_init.restype = None
+        L.orc_stream_step.argtypes = [P, _D, _D, _D, _D, ctypes.c_int, _D, _D, _D, _D, _D]
+        L.orc_stream_step.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return ctypes.cast(None, _D)
+    return a.ctypes.data_as(_D)
+
+
+def schedule(p: Params) -> np.ndarray:
+    """[nc, 5] int table of (f0, f1, ws, we, ls) per chunk."""
+    nc = lib().orc_schedule(ctypes.byref(p._c()), None)
+    out = np.zeros((nc, 5), dtype=np.int32)
+    lib().orc_schedule(ctypes.byref(p._c()), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int)))
+    return out
+
+
+def phi(p: Params, x, w, bias=None) -> np.ndarray:
+    """Feature map over [B,H,N,D] -> [B,H,N,F] (fp64)."""
+    x, w, bias = _f64(x), _f64(w), _f64(bias)
+    feat = np.empty(x.shape[:-1] + (p.F,), dtype=np.float64)
+    lib().orc_phi(ctypes.byref(p._c()), _ptr(x), _ptr(w), _ptr(bias), _ptr(feat))
+    return feat
+
+
+def _run(name, p: Params, q, k, v, wq, wk, bq=None, bk=None, aux=False):
+    q, k, v, wq, wk, bq, bk = map(_f64, (q, k, v, wq, wk, bq, bk))
+    shape = (p.B, p.H, p.N, p.D)
+    for a in (q, k, v):
+        assert a.shape == shape, (a.shape, shape)
+    out = np.empty(shape)
+    ax = None
+    if aux:
+        ax = dict(osoft=np.empty(shape), lse=np.empty(shape[:-1]), y=np.empty(shape),
+                  z=np.empty(shape[:-1]))
+    getattr(lib(), name)(ctypes.byref(p._c()), _ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk),
+                         _ptr(bq), _ptr(bk), _ptr(out),
+                         *(_ptr(ax[key]) if ax else _ptr(None) for key in ("osoft", "lse", "y", "z")))
+    return (out, ax) if aux else out
+
+
+def bruteforce(p, q, k, v, wq, wk, bq=None, bk=None, aux=False):
+    return _run("orc_bruteforce", p, q, k, v, wq, wk, bq, bk, aux)
+
+
+def recurrent(p, q, k, v, wq, wk, bq=None, bk=None, aux=False):
+    return _run("orc_recurrent", p, q, k, v, wq, wk, bq, bk, aux)
+
+
+def parallel(p, q, k, v, wq, wk, bq=None, bk=None, aux=False):
+    return _run("orc_parallel", p, q, k, v, wq, wk, bq, bk, aux)
+
+
+def parallel_rows(p, q, k, v, wq, wk, rows, bq=None, bk=None):
+    """Outputs (and aux parts) for selected flattened rows of [B*H*N]; states in full."""
+    q, k, v, wq, wk, bq, bk = map(_f64, (q, k, v, wq, wk, bq, bk))
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    R = rows.shape[0]
+    out, osoft, y = (np.empty((R, p.D)) for _ in range(3))
+    lse, z = np.empty(R), np.empty(R)
+    lib().orc_parallel_rows(ctypes.byref(p._c()), _ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk),
+                            _ptr(bq), _ptr(bk), R,
+                            rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                            _ptr(out), _ptr(osoft), _ptr(lse), _ptr(y), _ptr(z))
+    return out, dict(osoft=osoft, lse=lse, y=y, z=z)
+
+
+class Stream:
+    """Chunk-by-chunk form with carried state (blog section 5.2 streaming loop)."""
+
+    def __init__(self, p: Params, wq, wk, bq=None, bk=None):
+        self.p = p
+        self.wq, self.wk, self.bq, self.bk = map(_f64, (wq, wk, bq, bk))
+        self.state = np.zeros(lib().orc_stream_state_doubles(ctypes.byref(p._c())))
+        lib().orc_stream_init(ctypes.byref(p._c()), _ptr(self.state))
+
+    def step(self, q, k, v, frames: int) -> np.ndarray:
+        q, k, v = map(_f64, (q, k, v))
+        out = np.empty_like(q)
+        rc = lib().orc_stream_step(ctypes.byref(self.p._c()), _ptr(self.state), _ptr(q), _ptr(k),
+                                   _ptr(v), frames, _ptr(self.wq), _ptr(self.wk), _ptr(self.bq),
+                                   _ptr(self.bk), _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle stream step rejected (frames out of range or stream closed)")
+        return out
+
+
+def stream(p, q, k, v, wq, wk, bq=None, bk=None):
+    """Run the streaming form over the whole sequence, Tc frames per call."""
+    st = Stream(p, wq, wk, bq, bk)
+    q, k, v = map(_f64, (q, k, v))
+    out = np.empty_like(q)
+    for f0 in range(0, p.T, p.Tc):
+        f1 = min(f0 + p.Tc, p.T)
+        sl = slice(f0 * p.n, f1 * p.n)
+        out[:, :, sl] = st.step(q[:, :, sl], k[:, :, sl], v[:, :, sl], f1 - f0)
+    return out
+
+
+# ---------------------------------------------------------------------------------------
+# Second, independent brute force (numpy).  Built from the same definitions but a
+# different construction: explicit frame-interval masks, dense score matrices, and the
+# polynomial kernel in its closed form kappa(q,k) = sum_j sum_{p=1..P} (u_j w_j)^p, which
+# holds because every part of phi carries every power 1..P (blog 2.2.2).
+# ---------------------------------------------------------------------------------------
+
+def _softplus(x):
+    return np.logaddexp(0.0, x)
+
+
+def numpy_masks(p: Params):
+    """Boolean [N, N] masks (softmax region, linear region) from the frame rules."""
+    frame = np.arange(p.N) // p.n
+    chunk = frame // p.Tc
+    f0 = chunk * p.Tc
+    f1 = np.minimum(f0 + p.Tc, p.T)
+    if p.linear_only:
+        lo, hi, lin_end = f1, f1, f1
+    else:
+        lo, hi = np.maximum(f0 - p.To, 0), f1
+        lin_end = lo
+    kf = frame[None, :]
+    soft = (kf >= lo[:, None]) & (kf < hi[:, None])
+    lin = kf < lin_end[:, None]
+    return soft, lin
+
+
+def numpy_bruteforce(p: Params, q, k, v, wq, wk, bq=None, bk=None):
+    q, k, v, wq, wk = map(_f64, (q, k, v, wq, wk))
+    soft, lin = numpy_masks(p)
+    out = np.empty_like(q)
+    for b in range(p.B):
+        for h in range(p.H):
+            uq = np.einsum("jd,nd->nj", wq[h], q[b, h])
+            uk = np.einsum("jd,nd->nj", wk[h], k[b, h])
+            if bq is not None:
+                uq = uq + np.asarray(bq, dtype=np.float64)[h]
+            if bk is not None:
+                uk = uk + np.asarray(bk, dtype=np.float64)[h]
+            uq, uk = _softplus(uq), _softplus(uk)
+            prod = uq[:, None, :] * uk[None, :, :]            # [N, N, Dphi]
+            kappa = sum((prod ** e).sum(-1) for e in range(1, p.P + 1))
+            s = q[b, h] @ k[b, h].T / np.sqrt(p.D)
+            smax = np.where(soft, s, -np.inf).max(axis=1, keepdims=True)
+            shift = np.maximum(np.where(np.isfinite(smax), smax, 0.0), 0.0)
+            w = np.where(soft, np.exp(s - shift), 0.0) + np.where(lin, kappa * np.exp(-shift), 0.0)
+            out[b, h] = (w @ v[b, h]) / w.sum(axis=1, keepdims=True)
+    return out
