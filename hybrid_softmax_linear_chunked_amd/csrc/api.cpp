@@ -1,0 +1,413 @@
+// api.cpp -- C ABI of the ReHyAt hybrid-attention library (declared in include/rehyat.h).
+//
+// Host responsibilities only: argument validation (always before the first HIP call),
+// the chunk schedule of the ReHyAt blog (maplevalley.com.cn) sections 2.2.1 and 2.3,
+// workspace / state sizing, and the launch sequence on the caller's stream.  Every step
+// of the computation runs in the HIP kernels of attn.hip, state.hip and phi.hip.
+#include <cmath>
+#include <cstring>
+
+#include "../../include/rehyat.h"
+#include "kernels.hpp"
+
+using namespace rehyat;
+
+namespace {
+
+constexpr int32_t kStreamMagic = 0x52485954;  // "RHYT"
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t elem_bytes(int32_t dt) { return dt == REHYAT_BF16 ? 2 : 4; }
+
+rehyat_status check_params(const rehyat_params* p, bool need_T) {
+    if (!p) return REHYAT_EINVAL;
+    if (p->B < 1 || p->H < 1 || p->frame_tokens < 1 || p->Tc < 1 || p->To < 0) return REHYAT_EINVAL;
+    if (need_T && p->T < 1) return REHYAT_EINVAL;
+    if (p->linear_only != 0 && p->linear_only != 1) return REHYAT_EINVAL;
+    if (p->in_dtype != REHYAT_FP32 && p->in_dtype != REHYAT_BF16) return REHYAT_EINVAL;
+    if (p->out_dtype != REHYAT_FP32 && p->out_dtype != REHYAT_BF16) return REHYAT_EINVAL;
+    if (p->D != 32 && p->D != 64 && p->D != 128) return REHYAT_ESHAPE;
+    if (p->Dphi < 32 || p->Dphi > 128 || p->Dphi % 32 != 0) return REHYAT_ESHAPE;
+    if (p->P < 1 || p->P > 4) return REHYAT_ESHAPE;
+    // sizes must keep every slab index inside 32-bit token counts and 64-bit offsets
+    const int64_t N = (int64_t)(need_T ? p->T : p->Tc) * p->frame_tokens;
+    if (N > (int64_t)1 << 30 || (int64_t)p->Tc * p->frame_tokens > (int64_t)1 << 28) return REHYAT_EINVAL;
+    if ((int64_t)p->B * p->H > (int64_t)1 << 24) return REHYAT_EINVAL;
+    return REHYAT_OK;
+}
+
+bool aligned16(const void* ptr) { return ptr && (reinterpret_cast<uintptr_t>(ptr) % 16 == 0); }
+bool aligned4_or_null(const void* ptr) { return !ptr || (reinterpret_cast<uintptr_t>(ptr) % 4 == 0); }
+
+int num_chunks(const rehyat_params* p) { return (p->T + p->Tc - 1) / p->Tc; }
+
+// Frames whose state enters some chunk: the last chunk's linear region [0, ls(nc-1)).
+int state_frames(const rehyat_params* p) {
+    const int nc = num_chunks(p);
+    const int f0 = (nc - 1) * p->Tc;
+    const int f1 = f0 + p->Tc < p->T ? f0 + p->Tc : p->T;
+    if (p->linear_only) return f1;
+    return f0 - p->To > 0 ? f0 - p->To : 0;
+}
+
+size_t partial_bytes(const rehyat_params* p, int frames) {
+    const size_t F = (size_t)p->P * p->Dphi;
+    const size_t BH = (size_t)p->B * p->H;
+    return align256(BH * frames * F * p->D * sizeof(float)) + align256(BH * frames * F * sizeof(float));
+}
+
+struct StateLayout {
+    size_t S, Z, ovk[2], ovv[2], total;
+};
+
+StateLayout state_layout(const rehyat_params* p) {
+    const size_t F = (size_t)p->P * p->Dphi;
+    const size_t BH = (size_t)p->B * p->H;
+    const size_t ov = BH * (size_t)p->To * p->frame_tokens * p->D * elem_bytes(p->in_dtype);
+    StateLayout L;
+    size_t off = 0;
+    L.S = off; off += align256(BH * F * p->D * sizeof(float));
+    L.Z = off; off += align256(BH * F * sizeof(float));
+    for (int i = 0; i < 2; ++i) { L.ovk[i] = off; off += align256(ov); }
+    for (int i = 0; i < 2; ++i) { L.ovv[i] = off; off += align256(ov); }
+    L.total = off;
+    return L;
+}
+
+float scale_log2(int D) { return (float)(1.4426950408889634 / std::sqrt((double)D)); }
+
+AttnArgs attn_common(const rehyat_params* p, const void* wq, const float* bq) {
+    AttnArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.wq = wq;
+    a.bq = bq;
+    a.H = p->H;
+    a.BH = p->B * p->H;
+    a.D = p->D;
+    a.n = p->frame_tokens;
+    a.T = p->T;
+    a.Tc = p->Tc;
+    a.To = p->To;
+    a.linear_only = p->linear_only;
+    a.Dphi = p->Dphi;
+    a.P = p->P;
+    a.scale_log2 = scale_log2(p->D);
+    return a;
+}
+
+StateArgs state_common(const rehyat_params* p, const void* wk, const float* bk) {
+    StateArgs s;
+    std::memset(&s, 0, sizeof(s));
+    s.wk = wk;
+    s.bk = bk;
+    s.H = p->H;
+    s.BH = p->B * p->H;
+    s.D = p->D;
+    s.n = p->frame_tokens;
+    s.Dphi = p->Dphi;
+    s.P = p->P;
+    return s;
+}
+
+rehyat_status hip_status(hipError_t e) { return e == hipSuccess ? REHYAT_OK : REHYAT_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* rehyat_status_string(rehyat_status s) {
+    switch (s) {
+        case REHYAT_OK: return "ok";
+        case REHYAT_EINVAL: return "invalid parameter value";
+        case REHYAT_ESHAPE: return "unsupported shape";
+        case REHYAT_EALIGN: return "null or misaligned pointer";
+        case REHYAT_EWORKSPACE: return "workspace missing or too small";
+        case REHYAT_ESTATE: return "invalid streaming state or call";
+        case REHYAT_EHIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+int32_t rehyat_features(const rehyat_params* p) {
+    if (check_params(p, false) != REHYAT_OK) return -1;
+    return p->P * p->Dphi;
+}
+
+rehyat_status rehyat_phi(const rehyat_params* p, const void* x, const void* w, const float* bias,
+                         void* feat, hipStream_t stream) {
+    rehyat_status st = check_params(p, true);
+    if (st != REHYAT_OK) return st;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(feat) || !aligned4_or_null(bias)) return REHYAT_EALIGN;
+    PhiArgs a;
+    a.x = x;
+    a.w = w;
+    a.bias = bias;
+    a.feat = feat;
+    a.N = (int64_t)p->T * p->frame_tokens;
+    a.H = p->H;
+    a.BH = p->B * p->H;
+    a.D = p->D;
+    a.Dphi = p->Dphi;
+    a.P = p->P;
+    return hip_status(launch_phi(a, p->in_dtype, stream));
+}
+
+size_t rehyat_workspace_bytes(const rehyat_params* p) {
+    if (check_params(p, true) != REHYAT_OK) return 0;
+    const int G = state_frames(p);
+    return G > 0 ? partial_bytes(p, G) : 0;
+}
+
+rehyat_status rehyat_forward_parallel_aux(const rehyat_params* p, const void* q, const void* k,
+                                          const void* v, const void* wq, const void* wk,
+                                          const float* bq, const float* bk, void* out,
+                                          const rehyat_aux* aux, void* ws, size_t ws_bytes,
+                                          hipStream_t stream) {
+    rehyat_status st = check_params(p, true);
+    if (st != REHYAT_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(wq) || !aligned16(wk) ||
+        !aligned16(out) || !aligned4_or_null(bq) || !aligned4_or_null(bk))
+        return REHYAT_EALIGN;
+    if (aux) {
+        if ((aux->o_soft && !aligned16(aux->o_soft)) || (aux->y && !aligned16(aux->y)) ||
+            !aligned4_or_null(aux->lse) || !aligned4_or_null(aux->z))
+            return REHYAT_EALIGN;
+    }
+    const int G = state_frames(p);
+    const size_t need = G > 0 ? partial_bytes(p, G) : 0;
+    if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0)) return REHYAT_EWORKSPACE;
+
+    const int64_t N = (int64_t)p->T * p->frame_tokens;
+    const int64_t F = (int64_t)p->P * p->Dphi;
+    const int BH = p->B * p->H;
+    float* Sp = reinterpret_cast<float*>(ws);
+    float* Zp = G > 0 ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)BH * G * F * p->D * sizeof(float))) : nullptr;
+
+    if (G > 0) {
+        StateArgs s = state_common(p, wk, bk);
+        s.k1 = k;
+        s.v1 = v;
+        s.kv1_bh_stride = N * p->D;
+        s.nf1 = p->T;
+        s.k2 = k;
+        s.v2 = v;
+        s.kv2_bh_stride = N * p->D;
+        s.g0 = 0;
+        s.G = G;
+        s.Sp = Sp;
+        s.Zp = Zp;
+        st = hip_status(launch_state(s, p->in_dtype, stream));
+        if (st != REHYAT_OK) return st;
+        ScanArgs sc;
+        sc.Sp = Sp;
+        sc.Zp = Zp;
+        sc.G = G;
+        sc.S_state = nullptr;
+        sc.Z_state = nullptr;
+        sc.BH = BH;
+        sc.F = (int)F;
+        sc.D = p->D;
+        st = hip_status(launch_scan(sc, stream));
+        if (st != REHYAT_OK) return st;
+    }
+
+    AttnArgs a = attn_common(p, wq, bq);
+    a.q = q;
+    a.out = out;
+    a.q_bh_stride = N * p->D;
+    a.k1 = k;
+    a.v1 = v;
+    a.kv1_bh_stride = N * p->D;
+    a.k2 = k;
+    a.v2 = v;
+    a.kv2_bh_stride = N * p->D;
+    a.S = Sp;
+    a.Z = Zp;
+    a.S_bh_stride = (int64_t)G * F * p->D;
+    a.S_frame_stride = F * p->D;
+    a.Z_bh_stride = (int64_t)G * F;
+    a.Z_frame_stride = F;
+    if (aux) {
+        a.aux_o_soft = aux->o_soft;
+        a.aux_lse = aux->lse;
+        a.aux_y = aux->y;
+        a.aux_z = aux->z;
+    }
+    a.aux_bh_stride = N;
+    a.stream = 0;
+    a.nchunks = num_chunks(p);
+    return hip_status(launch_attn(a, p->in_dtype, p->out_dtype, stream));
+}
+
+rehyat_status rehyat_forward_parallel(const rehyat_params* p, const void* q, const void* k,
+                                      const void* v, const void* wq, const void* wk,
+                                      const float* bq, const float* bk, void* out, void* ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+    return rehyat_forward_parallel_aux(p, q, k, v, wq, wk, bq, bk, out, nullptr, ws, ws_bytes, stream);
+}
+
+size_t rehyat_state_bytes(const rehyat_params* p) {
+    if (check_params(p, false) != REHYAT_OK) return 0;
+    return state_layout(p).total;
+}
+
+size_t rehyat_stream_workspace_bytes(const rehyat_params* p) {
+    if (check_params(p, false) != REHYAT_OK) return 0;
+    return partial_bytes(p, p->Tc);
+}
+
+rehyat_status rehyat_state_init(const rehyat_params* p, void* state, rehyat_stream* st,
+                                hipStream_t stream) {
+    rehyat_status s = check_params(p, false);
+    if (s != REHYAT_OK) return s;
+    if (!st) return REHYAT_ESTATE;
+    if (!state || reinterpret_cast<uintptr_t>(state) % 256 != 0) return REHYAT_EALIGN;
+    const StateLayout L = state_layout(p);
+    // S and Z are adjacent at the start of the state; the overlap buffers need no clearing
+    // because only the frames written by earlier steps are ever read.
+    hipError_t e = launch_zero(reinterpret_cast<float*>(state), (int64_t)(L.ovk[0] / sizeof(float)), stream);
+    if (e != hipSuccess) return REHYAT_EHIP;
+    st->frames_seen = 0;
+    st->frames_absorbed = 0;
+    st->closed = 0;
+    st->overlap_slot = 0;
+    st->magic = kStreamMagic;
+    st->reserved = 0;
+    return REHYAT_OK;
+}
+
+rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stream* st,
+                                const void* q, const void* k, const void* v, int32_t frames,
+                                const void* wq, const void* wk, const float* bq, const float* bk,
+                                void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    rehyat_status s = check_params(p, false);
+    if (s != REHYAT_OK) return s;
+    if (!st || st->magic != kStreamMagic || st->closed) return REHYAT_ESTATE;
+    if (frames < 1 || frames > p->Tc) return REHYAT_ESTATE;
+    if (st->frames_seen + frames > ((int64_t)1 << 30) / p->frame_tokens) return REHYAT_ESTATE;
+    if (!state || reinterpret_cast<uintptr_t>(state) % 256 != 0) return REHYAT_EALIGN;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(wq) || !aligned16(wk) ||
+        !aligned16(out) || !aligned4_or_null(bq) || !aligned4_or_null(bk))
+        return REHYAT_EALIGN;
+    const size_t need = partial_bytes(p, p->Tc);
+    if (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0) return REHYAT_EWORKSPACE;
+
+    const StateLayout L = state_layout(p);
+    char* base = reinterpret_cast<char*>(state);
+    float* S = reinterpret_cast<float*>(base + L.S);
+    float* Z = reinterpret_cast<float*>(base + L.Z);
+    const int slot = st->overlap_slot;
+    void* ovk = base + L.ovk[slot];
+    void* ovv = base + L.ovv[slot];
+    void* nvk = base + L.ovk[slot ^ 1];
+    void* nvv = base + L.ovv[slot ^ 1];
+
+    const int n = p->frame_tokens;
+    const int64_t f0 = st->frames_seen, f1 = f0 + frames;
+    const int64_t absorbed = st->frames_absorbed;
+    const int held = (int)(f0 - absorbed);  // overlap frames held: [absorbed, f0)
+    const int64_t ws_frame = p->linear_only ? f1 : (f0 - p->To > 0 ? f0 - p->To : 0);
+    const int64_t ls = ws_frame;  // linear region of this chunk: frames [0, ls)
+    const int64_t next_abs = p->linear_only ? f1 : (f1 - p->To > 0 ? f1 - p->To : 0);
+    const int F = p->P * p->Dphi;
+    const int BH = p->B * p->H;
+    const int64_t ov_bh = (int64_t)p->To * n * p->D;
+    const int64_t ch_bh = (int64_t)frames * n * p->D;
+    float* Sp = reinterpret_cast<float*>(ws);
+    float* Zp = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)BH * p->Tc * F * p->D * sizeof(float)));
+
+    // Fold the window frames [from, to) (global frame numbers) into S, Z: per-frame
+    // partials, then added to the state in frame order.
+    auto absorb = [&](int64_t from, int64_t to) -> rehyat_status {
+        if (to <= from) return REHYAT_OK;
+        StateArgs sa = state_common(p, wk, bk);
+        sa.k1 = ovk;
+        sa.v1 = ovv;
+        sa.kv1_bh_stride = ov_bh;
+        sa.nf1 = held;
+        sa.k2 = k;
+        sa.v2 = v;
+        sa.kv2_bh_stride = ch_bh;
+        sa.g0 = (int)(from - absorbed);
+        sa.G = (int)(to - from);
+        sa.Sp = Sp;
+        sa.Zp = Zp;
+        rehyat_status r = hip_status(launch_state(sa, p->in_dtype, stream));
+        if (r != REHYAT_OK) return r;
+        ScanArgs sc;
+        sc.Sp = Sp;
+        sc.Zp = Zp;
+        sc.G = sa.G;
+        sc.S_state = S;
+        sc.Z_state = Z;
+        sc.BH = BH;
+        sc.F = F;
+        sc.D = p->D;
+        return hip_status(launch_scan(sc, stream));
+    };
+
+    // 1. frames that belong to this chunk's linear region but are not yet in the state
+    //    (only with an empty softmax window, where the chunk itself is linear)
+    s = absorb(absorbed, ls);
+    if (s != REHYAT_OK) return s;
+
+    // 2. softmax over [held overlap | chunk], linear part from the state
+    AttnArgs a = attn_common(p, wq, bq);
+    a.q = q;
+    a.out = out;
+    a.q_bh_stride = ch_bh;
+    a.k1 = ovk;
+    a.v1 = ovv;
+    a.kv1_bh_stride = ov_bh;
+    a.k2 = k;
+    a.v2 = v;
+    a.kv2_bh_stride = ch_bh;
+    a.S = S;
+    a.Z = Z;
+    a.S_bh_stride = (int64_t)F * p->D;
+    a.Z_bh_stride = F;
+    a.aux_bh_stride = (int64_t)frames * n;
+    a.stream = 1;
+    a.s_frames = frames;
+    a.s_held = p->linear_only ? 0 : held;
+    a.s_ls = (int)ls;
+    a.nchunks = 1;
+    s = hip_status(launch_attn(a, p->in_dtype, p->out_dtype, stream));
+    if (s != REHYAT_OK) return s;
+
+    // 3. frames leaving the window before the next chunk
+    const int64_t from = ls > absorbed ? ls : absorbed;
+    s = absorb(from, next_abs);
+    if (s != REHYAT_OK) return s;
+
+    // 4. keep frames [next_abs, f1) as the next overlap (into the other buffer)
+    if (!p->linear_only && f1 > next_abs) {
+        CopyArgs c;
+        c.s1k = ovk;
+        c.s1v = ovv;
+        c.s1_bh_stride = ov_bh;
+        c.nf1 = held;
+        c.s2k = k;
+        c.s2v = v;
+        c.s2_bh_stride = ch_bh;
+        c.dk = nvk;
+        c.dv = nvv;
+        c.d_bh_stride = ov_bh;
+        c.f0 = (int)(next_abs - absorbed);
+        c.cnt = (int)(f1 - next_abs);
+        c.BH = BH;
+        c.n = n;
+        c.D = p->D;
+        c.elem_bytes = (int)elem_bytes(p->in_dtype);
+        s = hip_status(launch_copy(c, stream));
+        if (s != REHYAT_OK) return s;
+        st->overlap_slot = slot ^ 1;
+    }
+    st->frames_seen = f1;
+    st->frames_absorbed = next_abs;
+    if (frames < p->Tc) st->closed = 1;
+    return REHYAT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// kernels.hpp -- argument blocks and launchers shared by the host library and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rehyat {
+
+// Windowed softmax + fused linear part (attn.hip).
+struct AttnArgs {
+    const void* q;          // [BH, tokens_q, D] (slab stride q_bh_stride elements)
+    void* out;              // same layout as q, out dtype
+    int64_t q_bh_stride;
+    const void* k1;         // first key/value segment (whole clip in chunk-parallel mode)
+    const void* v1;
+    int64_t kv1_bh_stride;
+    const void* k2;         // second segment (the current chunk in streaming mode)
+    const void* v2;
+    int64_t kv2_bh_stride;
+    const float* S;         // linear state: prefix over frames (parallel) or running (stream)
+    const float* Z;
+    int64_t S_bh_stride, S_frame_stride;
+    int64_t Z_bh_stride, Z_frame_stride;
+    const void* wq;         // [H, Dphi, D]
+    const float* bq;        // [H, Dphi] or null
+    float* aux_o_soft;
+    float* aux_lse;
+    float* aux_y;
+    float* aux_z;
+    int64_t aux_bh_stride;  // tokens per slab of the aux arrays
+    int H, BH, D, n, T, Tc, To, linear_only, Dphi, P;
+    int stream;             // 0: all chunks of a clip; 1: one streaming chunk
+    int s_frames, s_held, s_ls;
+    int nchunks, tiles_per_chunk, total_tiles, per_xcd;  // grid bookkeeping (set by the launcher)
+    int s_lds;              // 1: stage S_c in LDS for the combine; 0: read it from memory
+    float scale_log2;       // log2(e) / sqrt(D)
+};
+
+// Per-frame partials of phi_k(K)^T V and sum phi_k(K) (state.hip).
+struct StateArgs {
+    const void* k1;         // frames [0, nf1) of the source
+    const void* v1;
+    int64_t kv1_bh_stride;
+    int nf1;
+    const void* k2;         // frames [nf1, ..) of the source
+    const void* v2;
+    int64_t kv2_bh_stride;
+    int g0, G;              // process source frames [g0, g0 + G)
+    const void* wk;
+    const float* bk;
+    float* Sp;              // [BH, G, F, D]
+    float* Zp;              // [BH, G, F]
+    int H, BH, D, n, Dphi, P;
+};
+
+// Running sum over frame partials (state.hip): prefix in place (init == null), or
+// state += partials in frame order.
+struct ScanArgs {
+    float* Sp;
+    float* Zp;
+    int G;
+    float* S_state;         // null for the in-place prefix
+    float* Z_state;
+    int BH, F, D;
+};
+
+// Copy of frames [f0, f0 + cnt) of a two-segment source into dst frames [0, cnt).
+struct CopyArgs {
+    const void* s1k;
+    const void* s1v;
+    int64_t s1_bh_stride;
+    int nf1;
+    const void* s2k;
+    const void* s2v;
+    int64_t s2_bh_stride;
+    void* dk;
+    void* dv;
+    int64_t d_bh_stride;
+    int f0, cnt, BH, n, D, elem_bytes;
+};
+
+struct PhiArgs {
+    const void* x;          // [BH, N, D]
+    const void* w;          // [H, Dphi, D]
+    const float* bias;      // [H, Dphi] or null
+    void* feat;             // [BH, N, F]
+    int64_t N;
+    int H, BH, D, Dphi, P;
+};
+
+hipError_t launch_attn(const AttnArgs& a, int in_dtype, int out_dtype, hipStream_t stream);
+hipError_t launch_state(const StateArgs& a, int in_dtype, hipStream_t stream);
+hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
+hipError_t launch_copy(const CopyArgs& a, hipStream_t stream);
+hipError_t launch_phi(const PhiArgs& a, int in_dtype, hipStream_t stream);
+hipError_t launch_zero(float* p, int64_t count, hipStream_t stream);
+
+}  // namespace rehyat

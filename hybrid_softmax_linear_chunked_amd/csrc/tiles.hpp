@@ -1,0 +1,148 @@
+// tiles.hpp -- staging of key/value tiles (64 tokens) from HBM into LDS.
+//
+// K is stored row-major (token, d) with one 16-byte chunk of padding per row, which keeps
+// the 32-lane MFMA operand reads (8 tokens x 16 bytes per LDS cycle) free of bank
+// conflicts.  V is stored transposed (d, token) because the value product contracts over
+// tokens: the tokens of each 32-block are kept in slot order (see common.hpp) so one lane
+// reads its EPL operand elements contiguously, and the 16-byte chunks of each row are
+// XOR-swizzled by a function of d so that both the transposing writes (4 token quads x
+// 4 d-chunks per 16 lanes) and the operand reads (8 consecutive d per LDS cycle) spread
+// over distinct banks.
+#pragma once
+
+#include "common.hpp"
+
+namespace rehyat {
+
+// Key/value source for a window of tokens made of two contiguous segments: tokens
+// [0, len1) come from (k1, v1), tokens [len1, ..) from (k2, v2).  Pointers are already
+// offset to the batch-head slab and the window start.
+template <class T>
+struct KeySrc {
+    const T* k1;
+    const T* v1;
+    const T* k2;
+    const T* v2;
+    int len1;
+    __device__ inline const T* krow(int g, int D) const { return g < len1 ? k1 + (int64_t)g * D : k2 + (int64_t)(g - len1) * D; }
+    __device__ inline const T* vrow(int g, int D) const { return g < len1 ? v1 + (int64_t)g * D : v2 + (int64_t)(g - len1) * D; }
+};
+
+template <class T, int D, int NT>
+struct KVTile {
+    static constexpr int BK = 64;                  // tokens per tile
+    static constexpr int VEC = 16 / sizeof(T);     // elements per 16-byte chunk
+    static constexpr int CPR = D / VEC;            // chunks per K row
+    static constexpr int KLD = D + VEC;            // padded K row, elements
+    static constexpr int VLD = BK;                 // V^T row, elements (swizzled, no padding)
+    static constexpr int VCPR = BK / VEC;          // chunks per V^T row
+    static constexpr int K_ELEMS = BK * KLD;
+    static constexpr int V_ELEMS = D * VLD;
+    static constexpr int KCH = BK * CPR;           // K chunks per tile
+    static constexpr int KPT = (KCH + NT - 1) / NT;
+    static constexpr int VUN = (BK / 4) * CPR;     // V units: 4 tokens x one 16-byte chunk
+    static constexpr int VPT = (VUN + NT - 1) / NT;
+    static_assert(CPR >= 4 && CPR % 4 == 0, "head dim too small for the V staging layout");
+
+    uint4 kr[KPT];
+    uint4 vr[VPT][4];
+
+    __device__ static inline int vswz(int d) { return ((d % 8) ^ (2 * ((d / 8) % 4))) & (VCPR - 1); }
+
+    // unit u -> (token quad a, d-chunk b): 16 consecutive units cover 4 quads x 4 chunks
+    __device__ static inline void vunit(int u, int& a, int& b) {
+        a = (u % 4) + 4 * ((u / 16) % 4);
+        b = ((u / 4) % 4) + 4 * (u / 64);
+    }
+
+    // Issue the global loads of tile tokens [t0, t0+64); tokens >= Lk read as zeros.
+    __device__ inline void load(const KeySrc<T>& src, int t0, int Lk, int tid) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int c = tid + i * NT;
+            kr[i] = make_uint4(0, 0, 0, 0);
+            if (c < KCH) {
+                const int row = c / CPR, ch = c % CPR;
+                const int g = t0 + row;
+                if (g < Lk) kr[i] = *reinterpret_cast<const uint4*>(src.krow(g, D) + ch * VEC);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int u = tid + i * NT;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) vr[i][ii] = make_uint4(0, 0, 0, 0);
+            if (u < VUN) {
+                int a, b;
+                vunit(u, a, b);
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int g = t0 + 4 * a + ii;
+                    if (g < Lk) vr[i][ii] = *reinterpret_cast<const uint4*>(src.vrow(g, D) + b * VEC);
+                }
+            }
+        }
+    }
+
+    __device__ inline void store(T* Ks, T* Vs, int tid) const {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int c = tid + i * NT;
+            if (c < KCH) {
+                const int row = c / CPR, ch = c % CPR;
+                *reinterpret_cast<uint4*>(Ks + row * KLD + ch * VEC) = kr[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int u = tid + i * NT;
+            if (u >= VUN) continue;
+            int a, b;
+            vunit(u, a, b);
+            const int kb = (4 * a) / 32, kk0 = (4 * a) % 32;
+            if constexpr (sizeof(T) == 2) {
+                // bf16: the 4 tokens of a quad stay adjacent in slot order
+                const int pos = kb * 32 + slot_pos<8>(kk0);
+                const int lc = pos / 8, half = (pos % 8) / 4;
+                const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vr[i][0]);
+                const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vr[i][1]);
+                const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vr[i][2]);
+                const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vr[i][3]);
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int d = b * 8 + jj;
+                    const int sh = (jj % 2) * 16;
+                    const uint32_t e0 = (w0[jj / 2] >> sh) & 0xFFFFu, e1 = (w1[jj / 2] >> sh) & 0xFFFFu;
+                    const uint32_t e2 = (w2[jj / 2] >> sh) & 0xFFFFu, e3 = (w3[jj / 2] >> sh) & 0xFFFFu;
+                    uint2 val = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+                    *reinterpret_cast<uint2*>(Vs + d * VLD + (lc ^ vswz(d)) * 8 + half * 4) = val;
+                }
+            } else {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int pos = kb * 32 + slot_pos<1>(kk0 + ii);
+                    const int lc = pos / VEC, e = pos % VEC;
+                    const float* src = reinterpret_cast<const float*>(&vr[i][ii]);
+#pragma unroll
+                    for (int jj = 0; jj < VEC; ++jj) {
+                        const int d = b * VEC + jj;
+                        Vs[d * VLD + (lc ^ vswz(d)) * VEC + e] = src[jj];
+                    }
+                }
+            }
+        }
+    }
+
+    // A operand of (keys x d) products: keys kb*32 + col, contraction step s over d.
+    __device__ static inline typename Mfma<T>::frag kfrag(const T* Ks, int kb, int s, int col, int h) {
+        return Mfma<T>::load(Ks + (kb * 32 + col) * KLD + s * Mfma<T>::KS + h * Mfma<T>::EPL);
+    }
+    // Operand holding V^T[d][tokens in slot order]: d = dbase + col, token block kb, step t.
+    __device__ static inline typename Mfma<T>::frag vfrag(const T* Vs, int d, int kb, int t, int h) {
+        constexpr int EPL = Mfma<T>::EPL;
+        const int pos = kb * 32 + t * 2 * EPL + h * EPL;
+        return Mfma<T>::load(Vs + d * VLD + ((pos / VEC) ^ vswz(d)) * VEC + pos % VEC);
+    }
+};
+
+}  // namespace rehyat

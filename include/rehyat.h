@@ -1,0 +1,149 @@
+/*
+ * rehyat.h -- C ABI of the MI355X (gfx950) library for ReHyAt chunk-wise recurrent
+ * hybrid attention (forward pass).
+ *
+ * The operation (ReHyAt blog, maplevalley.com.cn, sections 2.2.1, 2.2.2 and 2.3):
+ * tokens are T latent frames of `frame_tokens` (n) tokens each, token index = frame*n + s.
+ * Frames are grouped into chunks of Tc frames (the last chunk may be shorter).  A query
+ * in chunk [f0, f1) attends
+ *   - with softmax weights exp(q.k / sqrt(D)) to every key of frames [max(0, f0-To), f1)
+ *     (its own chunk plus To overlapping preceding frames; bidirectional inside), and
+ *   - with polynomial-kernel weights phi_q(q) . phi_k(k) to every key of the earlier
+ *     frames [0, max(0, f0-To)), carried as the states S = sum phi_k(k) v^T and
+ *     Z = sum phi_k(k);
+ * and the output is (softmax numerator + phi_q(q) S) / (softmax denominator + phi_q(q) Z).
+ * phi (blog section 2.2.2): u = softplus(W x + b) with one Dphi x D map per head
+ * (a grouped 1x1 linear), u split into P contiguous parts (the first Dphi mod P parts
+ * one entry longer), each part raised elementwise to the powers 1..P, all concatenated:
+ * F = P*Dphi features in the order [part0^1 | part0^2 | .. | part0^P | part1^1 | ..].
+ * Queries and keys have separate maps (W_q, W_k).  With linear_only = 1 the softmax
+ * window is empty and the linear region of chunk [f0, f1) is frames [0, f1).
+ *
+ * Conventions for every entry point:
+ *   - Layout: q, k, v, out are dense row-major [B, H, tokens, D]; weights [H, Dphi, D]
+ *     in the input dtype; biases [H, Dphi] float32 or NULL.
+ *   - Ownership: the caller allocates every device buffer (inputs, outputs, state,
+ *     workspace).  The library never allocates, frees or synchronises.
+ *   - Pointers are device pointers, 16-byte aligned (biases 4-byte aligned).
+ *   - Asynchrony: all work is enqueued on the caller's stream; the return value reports
+ *     validation (checked before any HIP call) and launch errors.  Device faults appear
+ *     at the caller's next synchronisation.
+ *   - Determinism: no atomics; repeated calls on the same inputs give identical bits.
+ *   - Thread safety: functions keep no global state; one in-flight call per stream state.
+ */
+#ifndef REHYAT_H
+#define REHYAT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    REHYAT_OK = 0,
+    REHYAT_EINVAL = 1,     /* a parameter value is out of range */
+    REHYAT_ESHAPE = 2,     /* unsupported shape: D not in {32,64,128}, Dphi not a multiple of 32, ... */
+    REHYAT_EALIGN = 3,     /* a required pointer is NULL or not 16-byte aligned */
+    REHYAT_EWORKSPACE = 4, /* workspace pointer NULL or ws_bytes below the required size */
+    REHYAT_ESTATE = 5,     /* streaming misuse: frames out of range, stream closed, bad handle */
+    REHYAT_EHIP = 6        /* a kernel launch failed */
+} rehyat_status;
+
+typedef enum { REHYAT_FP32 = 0, REHYAT_BF16 = 1 } rehyat_dtype;
+
+typedef struct {
+    int32_t B, H;          /* batch, heads */
+    int32_t D;             /* head dim (value dim = D): 32, 64 or 128 */
+    int32_t T;             /* latent frames (ignored by the streaming entry points) */
+    int32_t frame_tokens;  /* n = tokens per latent frame (H x W of the latent grid) */
+    int32_t Tc, To;        /* chunk frames (>= 1), overlap frames (>= 0) */
+    int32_t Dphi, P;       /* phi width (multiple of 32, <= 256), parts = max power (1..4) */
+    int32_t linear_only;   /* 1: empty softmax window (normalised chunk-causal linear attention) */
+    int32_t in_dtype;      /* rehyat_dtype of q, k, v, weights (and features / overlap state) */
+    int32_t out_dtype;     /* rehyat_dtype of out */
+} rehyat_params;
+
+/* Host-side handle of a streaming state; caller-owned, filled by rehyat_state_init. */
+typedef struct {
+    int64_t frames_seen;      /* frames consumed so far */
+    int64_t frames_absorbed;  /* frames already folded into S, Z */
+    int32_t closed;           /* 1 after a final chunk shorter than Tc */
+    int32_t overlap_slot;     /* which of the two overlap buffers holds the held frames */
+    int32_t magic;            /* set by rehyat_state_init */
+    int32_t reserved;
+} rehyat_stream;
+
+/* Optional per-part outputs of rehyat_forward_parallel_aux (any member may be NULL).
+ * All float32, tokens in the same [B, H, tokens] order as out. */
+typedef struct {
+    float* o_soft;  /* [B,H,N,D] softmax part normalised by its own sum (0 when the window is empty) */
+    float* lse;     /* [B,H,N] log of the softmax denominator sum_j exp(q.k_j/sqrt(D)) (-inf if empty) */
+    float* y;       /* [B,H,N,D] phi_q(q) S  (0 when the linear region is empty) */
+    float* z;       /* [B,H,N]   phi_q(q) Z  (0 when the linear region is empty) */
+} rehyat_aux;
+
+/* Human-readable name of a status code (static string). */
+const char* rehyat_status_string(rehyat_status s);
+
+/* Number of phi features F = P * Dphi, or -1 if the parameters are invalid. */
+int32_t rehyat_features(const rehyat_params* p);
+
+/* phi feature map (blog 2.2.2) of x [B,H,N,D] with w [H,Dphi,D] (+ bias [H,Dphi]) into
+ * feat [B,H,N,F] in in_dtype, N = T * frame_tokens.  Test and API entry point; the
+ * attention entry points compute phi internally and never write features to memory. */
+rehyat_status rehyat_phi(const rehyat_params* p, const void* x, const void* w, const float* bias,
+                         void* feat, hipStream_t stream);
+
+/* Workspace bytes needed by rehyat_forward_parallel(_aux): per-frame state partials and
+ * their prefix, float32 [B,H,T,F,D] + [B,H,T,F] (0 if no chunk has a linear region). */
+size_t rehyat_workspace_bytes(const rehyat_params* p);
+
+/* Chunk-parallel forward (all chunks at once): per-frame partials of phi_k(K)^T [V|1],
+ * inclusive prefix over frames, then the windowed softmax tile kernel with the linear
+ * part and the shared normalisation fused into its epilogue.  With Tc >= T this is
+ * plain softmax attention (the full-softmax comparator).
+ * q, k, v, out: [B,H,T*n,D]; wq, wk: [H,Dphi,D]; bq, bk: [H,Dphi] float32 or NULL. */
+rehyat_status rehyat_forward_parallel(const rehyat_params* p, const void* q, const void* k,
+                                      const void* v, const void* wq, const void* wk,
+                                      const float* bq, const float* bk, void* out, void* ws,
+                                      size_t ws_bytes, hipStream_t stream);
+
+/* Same as rehyat_forward_parallel, also writing the per-part outputs that are non-NULL
+ * in *aux (aux itself may be NULL). */
+rehyat_status rehyat_forward_parallel_aux(const rehyat_params* p, const void* q, const void* k,
+                                          const void* v, const void* wq, const void* wk,
+                                          const float* bq, const float* bk, void* out,
+                                          const rehyat_aux* aux, void* ws, size_t ws_bytes,
+                                          hipStream_t stream);
+
+/* Streaming (blog 5.2: states = init_states(); output, states = block(chunk, states)).
+ * Device state bytes: S float32 [B,H,F,D], Z float32 [B,H,F] and two overlap buffers of
+ * K and V [B,H,To*n,D] in in_dtype.  Independent of the clip length. */
+size_t rehyat_state_bytes(const rehyat_params* p);
+
+/* Workspace bytes for rehyat_chunk_step: per-frame partials for up to Tc frames,
+ * float32 [B,H,Tc,F,D] + [B,H,Tc,F].  Independent of the clip length. */
+size_t rehyat_stream_workspace_bytes(const rehyat_params* p);
+
+/* Zero S and Z on `stream` and reset the host handle (frames_seen = 0). */
+rehyat_status rehyat_state_init(const rehyat_params* p, void* state, rehyat_stream* st,
+                                hipStream_t stream);
+
+/* Process the next chunk of `frames` frames: q, k, v, out are [B,H,frames*n,D].
+ * frames must equal Tc except on a final, shorter call, after which the stream is closed
+ * (REHYAT_ESTATE on further calls).  Outputs equal those of rehyat_forward_parallel on
+ * the concatenated clip.  The call reads S, Z and the held overlap frames, then folds the
+ * frames that leave the softmax window into S, Z and keeps the last To frames. */
+rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stream* st,
+                                const void* q, const void* k, const void* v, int32_t frames,
+                                const void* wq, const void* wk, const float* bq, const float* bk,
+                                void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* REHYAT_H */

@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and exports every
+entry point include/rehyat.h declares, sizes follow the documented layouts, and every
+invalid call is rejected with its status code before any HIP call is made."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import hybrid_softmax_linear_chunked_amd as rh
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rehyat.h")
+
+OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, ESTATE, EHIP = range(7)
+WAN = rh.Params(1, 12, 128, 21, 1560, 3, 1, 128, 2, 0, rh.BF16, rh.BF16)
+FAKE = ctypes.c_void_p(0x10000)       # aligned, never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(rh.LIB_PATH):
+        from hybrid_softmax_linear_chunked_amd.build import build
+        build()
+    return rh.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(rehyat_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(rh.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", rh.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (rehyat_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert rh.status_string(s)
+    assert rh.status_string(0) == "ok"
+
+
+def test_sizes_follow_layouts(L):
+    a = lambda x: (x + 255) // 256 * 256
+    F = WAN.P * WAN.Dphi
+    assert rh.features(WAN) == 256
+    # chunk-parallel: per-frame partials for the 17 frames that enter some chunk's state
+    assert rh.workspace_bytes(WAN) == a(12 * 17 * F * 128 * 4) + a(12 * 17 * F * 4)
+    # streaming: S, Z and two overlap buffers of To frames of K and V, independent of T
+    ov = 12 * 1 * 1560 * 128 * 2
+    assert rh.state_bytes(WAN) == a(12 * F * 128 * 4) + a(12 * F * 4) + 4 * a(ov)
+    assert rh.state_bytes(WAN.with_(T=81)) == rh.state_bytes(WAN)
+    assert rh.stream_workspace_bytes(WAN) == a(12 * 3 * F * 128 * 4) + a(12 * 3 * F * 4)
+    # one chunk covering the clip has no linear region and needs no workspace
+    assert rh.workspace_bytes(WAN.with_(Tc=21)) == 0
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(D=48), ESHAPE), (dict(D=256), ESHAPE), (dict(Dphi=48), ESHAPE), (dict(Dphi=160), ESHAPE),
+    (dict(P=0), ESHAPE), (dict(P=5), ESHAPE), (dict(Tc=0), EINVAL), (dict(To=-1), EINVAL),
+    (dict(T=0), EINVAL), (dict(n=0), EINVAL), (dict(B=0), EINVAL), (dict(linear_only=2), EINVAL),
+    (dict(in_dtype=7), EINVAL), (dict(out_dtype=-1), EINVAL),
+])
+def test_invalid_params_rejected(L, change, status):
+    p = WAN.with_(**change).c()
+    f = L.rehyat_forward_parallel
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 1 << 40, None) == status
+    assert L.rehyat_workspace_bytes(ctypes.byref(p)) == 0
+    # features and state sizes do not depend on the clip length T
+    t_only = list(change) == ["T"]
+    assert L.rehyat_features(ctypes.byref(p)) == (256 if t_only else -1)
+
+
+def test_pointer_checks(L):
+    p = WAN.c()
+    f = L.rehyat_forward_parallel
+    args = [FAKE] * 5
+    for i in range(5):
+        bad = list(args)
+        bad[i] = None
+        assert f(ctypes.byref(p), *bad, None, None, FAKE, FAKE, 1 << 40, None) == EALIGN
+        bad[i] = MISALIGNED
+        assert f(ctypes.byref(p), *bad, None, None, FAKE, FAKE, 1 << 40, None) == EALIGN
+    assert f(ctypes.byref(p), *args, None, None, None, FAKE, 1 << 40, None) == EALIGN
+    assert f(ctypes.byref(p), *args, ctypes.c_void_p(0x10002), None, FAKE, FAKE, 1 << 40, None) == EALIGN
+    assert L.rehyat_phi(ctypes.byref(p), None, FAKE, None, FAKE, None) == EALIGN
+
+
+def test_workspace_checks(L):
+    p = WAN.c()
+    need = L.rehyat_workspace_bytes(ctypes.byref(p))
+    f = L.rehyat_forward_parallel
+    assert f(ctypes.byref(p), *[FAKE] * 5, None, None, FAKE, FAKE, need - 1, None) == EWORKSPACE
+    assert f(ctypes.byref(p), *[FAKE] * 5, None, None, FAKE, None, need, None) == EWORKSPACE
+    assert f(ctypes.byref(p), *[FAKE] * 5, None, None, FAKE, ctypes.c_void_p(0x10010), need, None) == EWORKSPACE
+
+
+def test_stream_contract(L):
+    p = WAN.c()
+    st = rh._CStream()
+    step = L.rehyat_chunk_step
+    ws = L.rehyat_stream_workspace_bytes(ctypes.byref(p))
+    call = lambda handle, frames: step(ctypes.byref(p), FAKE, ctypes.byref(handle), FAKE, FAKE, FAKE, frames,
+                                       FAKE, FAKE, None, None, FAKE, FAKE, ws, None)
+    assert call(st, 3) == ESTATE                    # never initialised
+    st.magic = 0x52485954
+    assert call(st, 4) == ESTATE                    # more than Tc frames
+    assert call(st, 0) == ESTATE
+    st.closed = 1
+    assert call(st, 2) == ESTATE                    # after a short final chunk
+    st.closed = 0
+    assert step(ctypes.byref(p), FAKE, ctypes.byref(st), FAKE, FAKE, FAKE, 3, FAKE, FAKE, None, None, FAKE,
+                FAKE, ws - 1, None) == EWORKSPACE
+    assert step(ctypes.byref(p), ctypes.c_void_p(0x10010), ctypes.byref(st), FAKE, FAKE, FAKE, 3, FAKE, FAKE,
+                None, None, FAKE, FAKE, ws, None) == EALIGN
+    assert L.rehyat_state_init(ctypes.byref(p), FAKE, None, None) == ESTATE
+    assert L.rehyat_state_init(ctypes.byref(p), ctypes.c_void_p(0x10010), ctypes.byref(st), None) == EALIGN
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(rh, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(rh, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        rh.lib()
