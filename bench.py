@@ -1,0 +1,313 @@
+#!/usr/bin/env python3
+"""Throughput of ReHyAt chunk-wise hybrid attention on one MI355X.
+
+One step = one chunk-parallel forward of the whole hot path on a Wan2.1-1.3B-shaped
+attention layer, 5 s of 480x832 video: B=1, 12 heads, D=128, 21 latent frames of 30x52 =
+1560 tokens (32,760 tokens), bf16 inputs, Tc=3, To=1, phi = per-head 128->128 map,
+2 parts, powers 1..2 (256 features).  A step runs the per-frame state kernel, the frame
+scan and the windowed softmax tile kernel with the fused linear combine, all in
+librehyat.so, on device-resident synthetic inputs.
+
+Printed as one JSON line: tokens/s (value), TFLOP/s and the fraction of the bf16 MFMA
+peak, the roofline of the dominant kernel (attention tile kernel, timed with HIP events
+on the stream it runs on), the full-softmax comparator on the same shapes, the 10 s
+streaming form with its peak memory at 21/41/81 frames, and the CPU oracle timed on a
+bounded sample of the same workload (which also serves as a parity spot check).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0
+METRIC = "hybrid-attn tokens/s & TFLOP/s (% bf16 MFMA peak), 32760-token 12-head layer"
+KERNEL_SOURCES = ["attn.hip", "tiles.hpp", "common.hpp", "kernels.hpp"]
+COUNTER_FILE = os.path.join(ROOT, "profiles", "attn_kernel_wan_5s_counters.txt")
+
+
+def schedule(T, Tc, To, linear_only=0):
+    out = []
+    for c in range((T + Tc - 1) // Tc):
+        f0 = c * Tc
+        f1 = min(f0 + Tc, T)
+        ws = f1 if linear_only else max(0, f0 - To)
+        out.append((f0, f1, ws, f1, ws))
+    return out
+
+
+def flop_model(B, H, D, T, n, Tc, To, Dphi, P, linear_only=0):
+    """Algorithmic FLOPs (2 per multiply-add, elementwise work not counted)."""
+    F = P * Dphi
+    sch = schedule(T, Tc, To, linear_only)
+    soft = sum((f1 - f0) * n * (we - ws) * n for f0, f1, ws, we, ls in sch)
+    n_s = sch[-1][4] * n                                        # tokens entering some state
+    n_c = sum((f1 - f0) * n for f0, f1, ws, we, ls in sch if ls > 0)  # queries with a linear part
+    N = T * n
+    total = B * H * (4 * D * soft + 4 * N * D * Dphi + 2 * n_s * F * D + 2 * n_c * F * (D + 1))
+    attn = B * H * (4 * D * soft + 2 * n_c * D * Dphi + 2 * n_c * F * (D + 1))
+    state = B * H * (2 * n_s * D * Dphi + 2 * n_s * F * D)
+    return dict(total=total, attn_kernel=attn, state_kernel=state)
+
+
+def sources_digest():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "hybrid_softmax_linear_chunked_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per launch of the attention kernel from the committed counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    if not os.path.exists(COUNTER_FILE):
+        return None
+    kv = {}
+    for line in open(COUNTER_FILE):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+    try:
+        if kv.get("sources_sha256") != sources_digest():
+            return None
+        return float(kv["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, x, out_gpu, budget_s=20.0):
+    """The fp64 oracle (as it stands) on a bounded sample of the same workload: head 0 with
+    its fp64 states built in full, plus a seeded sample of query rows spread over all chunks;
+    extrapolated linearly to every head and row.  Also returns the parity of the GPU output
+    on the sampled rows."""
+    import numpy as np
+    import oracle
+    p1 = oracle.Params(1, 1, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P)
+    h0 = {key: x[key][:, :1] if key in ("q", "k", "v") else x[key][:1] for key in ("q", "k", "v", "wq", "wk")}
+    h0 = {key: val.astype(np.float64) for key, val in h0.items()}
+    N = w.N
+    rng = np.random.default_rng(123)
+    t0 = time.perf_counter()
+    oracle.parallel_rows(p1, h0["q"], h0["k"], h0["v"], h0["wq"], h0["wk"], np.array([0]))
+    t_state = time.perf_counter() - t0
+    R = 256
+    rows = np.sort(rng.choice(N, size=R, replace=False))
+    t0 = time.perf_counter()
+    ref, _ = oracle.parallel_rows(p1, h0["q"], h0["k"], h0["v"], h0["wq"], h0["wk"], rows)
+    t_rows = time.perf_counter() - t0
+    per_row = max(t_rows - t_state, 1e-9) / R
+    # grow the sample while the CPU budget allows
+    extra = int(min(max((budget_s - 2 * t_state - t_rows) / per_row, 0), 8192))
+    if extra >= 256:
+        more = np.sort(rng.choice(np.setdiff1d(np.arange(N), rows), size=extra, replace=False))
+        t0 = time.perf_counter()
+        ref2, _ = oracle.parallel_rows(p1, h0["q"], h0["k"], h0["v"], h0["wq"], h0["wk"], more)
+        t_more = time.perf_counter() - t0
+        per_row = max(t_more - t_state, 1e-9) / extra
+        rows = np.concatenate([rows, more])
+        ref = np.concatenate([ref, ref2])
+        order = np.argsort(rows)
+        rows, ref = rows[order], ref[order]
+    full_s = w.B * w.H * (t_state + N * per_row)
+    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    g = out_gpu[0, 0].float().cpu().numpy()[rows]
+    err = float(np.abs(g - ref).max() / np.abs(ref).max())
+    return dict(value=round(w.B * N / full_s, 3), unit="tokens/s", cores=cores, kind="oracle",
+                sample=(f"head 0 of {w.H}: fp64 states over all {w.T} frames in full "
+                        f"({t_state:.2f} s) + {len(rows)} of {N} query rows ({per_row * 1e3:.2f} ms/row); "
+                        f"extrapolated linearly to {w.H} heads x {N} rows = {full_s:.1f} s per layer")), \
+        dict(max_rel_err=err, rows=int(len(rows)), head=0, tol=2e-2)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the comparator and streaming legs")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import hybrid_softmax_linear_chunked_amd as rh
+    from synth_inputs import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    w = WORKLOADS["wan_5s"]
+    p = rh.Params(w.B, w.H, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P, 0, rh.BF16, rh.BF16)
+    x = make_inputs(w, seed=1)
+    d = {key: torch.from_numpy(val).to(dev, torch.bfloat16).contiguous() for key, val in x.items()}
+    out = torch.empty((p.B, p.H, p.N, p.D), dtype=torch.bfloat16, device=dev)
+    ws = rh.alloc_bytes(rh.workspace_bytes(p), dev)
+
+    def step(ev_mid=None):
+        rh.parallel_states(p, d["k"], d["v"], d["wk"], None, ws)
+        if ev_mid is not None:
+            ev_mid.record()
+        rh.parallel_attend(p, d["q"], d["k"], d["v"], d["wq"], None, out, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record()
+    for i in range(args.steps):
+        starts[i].record()
+        step(mids[i])
+        ends[i].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms = t_begin.elapsed_time(t_end) / args.steps
+    attn_ms = sum(mids[i].elapsed_time(ends[i]) for i in range(args.steps)) / args.steps
+    state_ms = sum(starts[i].elapsed_time(mids[i]) for i in range(args.steps)) / args.steps
+
+    fl = flop_model(w.B, w.H, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P)
+    tokens = w.B * w.N
+    tflops = fl["total"] / (ms * 1e-3) / 1e12
+    attn_tflops = fl["attn_kernel"] / (attn_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) Q/K/V and N(0,1/D) phi weights, bf16",
+        "config": {"workload": "wan_5s", "B": w.B, "heads": w.H, "head_dim": w.D, "frames": w.T,
+                   "frame_tokens": w.n, "tokens": w.N, "Tc": w.Tc, "To": w.To, "Dphi": w.Dphi, "P": w.P,
+                   "form": "chunk-parallel"},
+        "tflops": round(tflops, 2), "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "flops_per_step": fl["total"],
+        "stages_ms": {"state_and_scan": round(state_ms, 4), "attn_kernel": round(attn_ms, 4)},
+        "roofline": {"kernel": "attn_kernel (windowed softmax + fused linear combine)", "bound": "mfma",
+                     "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic(),
+                     "algorithmic_flops_per_launch": fl["attn_kernel"]},
+    }
+
+    if not args.no_extras:
+        # full-softmax comparator: the same tile kernel with one window over all frames
+        pc = p.with_(Tc=w.T)
+        outc = torch.empty_like(out)
+        rh.forward_parallel(pc, d["q"], d["k"], d["v"], d["wq"], d["wk"], out=outc)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        e0.record()
+        for _ in range(reps):
+            rh.forward_parallel(pc, d["q"], d["k"], d["v"], d["wq"], d["wk"], out=outc)
+        e1.record()
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / reps
+        cfl = flop_model(w.B, w.H, w.D, w.T, w.n, w.T, w.To, w.Dphi, w.P)["total"]
+        res["full_softmax_comparator"] = {"ms": round(cms, 3), "tflops": round(cfl / (cms * 1e-3) / 1e12, 2),
+                                          "speedup_of_hybrid": round(cms / ms, 2)}
+        del outc
+        res["stream"] = stream_leg(rh, torch, WORKLOADS["wan_10s_stream"], dev)
+
+    if not args.no_cpu_baseline:
+        cb, parity = cpu_baseline(w, x, out)
+        res["cpu_baseline"] = cb
+        res["parity_spot_check"] = parity
+    print(json.dumps(res), flush=True)
+
+
+def stream_leg(rh, torch, w, dev):
+    """10 s clip chunk by chunk through rehyat_chunk_step: time per clip, and peak device
+    memory for 21, 41 and 81 frames with chunks generated on the fly (constant memory)."""
+    p = rh.Params(w.B, w.H, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P, 0, rh.BF16, rh.BF16)
+    g = torch.Generator(device=dev)
+    g.manual_seed(2)
+    sd = 1.0 / math.sqrt(w.D)
+    wq = (torch.randn((w.H, w.Dphi, w.D), generator=g, device=dev) * sd).to(torch.bfloat16)
+    wk = (torch.randn((w.H, w.Dphi, w.D), generator=g, device=dev) * sd).to(torch.bfloat16)
+    chunks = []
+    for f0 in range(0, w.T, w.Tc):
+        fr = min(w.Tc, w.T - f0)
+        shape = (w.B, w.H, fr * w.n, w.D)
+        chunks.append((fr, *(torch.randn(shape, generator=g, device=dev).to(torch.bfloat16) for _ in range(3))))
+    outs = [torch.empty_like(c[1]) for c in chunks]
+    st = rh.Stream(p, wq, wk)
+
+    def clip():
+        st.init()
+        for (fr, q, k, v), o in zip(chunks, outs):
+            st.step(q, k, v, fr, out=o)
+
+    clip()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        clip()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del chunks, outs, st
+    torch.cuda.empty_cache()
+
+    # one short warm-up stream first: the HIP runtime loads code objects and sizes its
+    # scratch area on the first launch of each kernel, once per process
+    full = w.B * w.H * w.Tc * w.n * w.D
+    warm = [torch.zeros(full, dtype=torch.bfloat16, device=dev) for _ in range(4)]
+    ws_ = rh.Stream(p, wq, wk)
+    for fr in (w.Tc, w.Tc, w.Tc - 1):
+        q, k, v, o = (t[:w.B * w.H * fr * w.n * w.D].view(w.B, w.H, fr * w.n, w.D) for t in warm)
+        ws_.step(q, k, v, fr, out=o)
+    torch.cuda.synchronize()
+    del warm, ws_, q, k, v, o
+    def measure(T):
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated()
+        # one chunk of q, k, v, out (a shorter final chunk uses the front of the same
+        # storage), the streaming state and its workspace: allocated once, up front
+        bufs = [torch.empty(full, dtype=torch.bfloat16, device=dev) for _ in range(4)]
+        for buf in bufs[:3]:
+            buf.normal_(generator=g)
+        s = rh.Stream(p.with_(T=T), wq, wk)
+        torch.cuda.synchronize()
+        footprint = torch.cuda.memory_allocated() - base
+        torch.cuda.reset_peak_memory_stats()
+        free0 = torch.cuda.mem_get_info()[0]
+        low = free0
+        for f0 in range(0, T, w.Tc):
+            fr = min(w.Tc, T - f0)
+            q, k, v, o = (t[:w.B * w.H * fr * w.n * w.D].view(w.B, w.H, fr * w.n, w.D) for t in bufs)
+            s.step(q, k, v, fr, out=o)
+            low = min(low, torch.cuda.mem_get_info()[0])
+        torch.cuda.synchronize()
+        return {"footprint_bytes": int(footprint),
+                "peak_allocated_bytes": int(torch.cuda.max_memory_allocated() - base),
+                "device_free_drop_during_steps": int(free0 - low)}
+
+    peak = {str(T): measure(T) for T in (21, 41, 81)}
+    return {"workload": "wan_10s_stream", "frames": w.T, "tokens": w.N, "ms_per_clip": round(ms, 3),
+            "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1),
+            "chunk_steps": (w.T + w.Tc - 1) // w.Tc, "peak_memory_by_frames": peak}
+
+
+if __name__ == "__main__":
+    main()

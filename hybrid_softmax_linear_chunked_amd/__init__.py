@@ -27,6 +27,7 @@ EXPORTS = (
     "rehyat_status_string", "rehyat_features", "rehyat_phi", "rehyat_workspace_bytes",
     "rehyat_forward_parallel", "rehyat_forward_parallel_aux", "rehyat_state_bytes",
     "rehyat_stream_workspace_bytes", "rehyat_state_init", "rehyat_chunk_step",
+    "rehyat_parallel_states", "rehyat_parallel_attend",
 )
 
 
@@ -78,6 +79,11 @@ def lib():
         L.rehyat_forward_parallel_aux.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp,
                                                   ctypes.POINTER(_CAux), vp, ctypes.c_size_t, vp]
         L.rehyat_forward_parallel_aux.restype = ctypes.c_int
+        L.rehyat_parallel_states.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.rehyat_parallel_states.restype = ctypes.c_int
+        L.rehyat_parallel_attend.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.POINTER(_CAux), vp,
+                                             ctypes.c_size_t, vp]
+        L.rehyat_parallel_attend.restype = ctypes.c_int
         L.rehyat_state_init.argtypes = [P, vp, ctypes.POINTER(_CStream), vp]
         L.rehyat_state_init.restype = ctypes.c_int
         L.rehyat_chunk_step.argtypes = [P, vp, ctypes.POINTER(_CStream), vp, vp, vp, ctypes.c_int32,
@@ -221,6 +227,21 @@ def forward_parallel(p: Params, q, k, v, wq, wk, bq=None, bk=None, out=None, ws=
                                              ws.numel() * ws.element_size(), _stream_handle()),
            "rehyat_forward_parallel_aux")
     return out, ax
+
+
+def parallel_states(p: Params, k, v, wk, bk, ws):
+    """First stage of forward_parallel: per-frame state partials and their prefix into ws."""
+    _raise(lib().rehyat_parallel_states(ctypes.byref(p.c()), _ptr(k), _ptr(v), _ptr(wk), _ptr(bk),
+                                        _ptr(ws), ws.numel() * ws.element_size(), _stream_handle()),
+           "rehyat_parallel_states")
+
+
+def parallel_attend(p: Params, q, k, v, wq, bq, out, ws):
+    """Second stage of forward_parallel: windowed softmax with the fused linear part."""
+    _raise(lib().rehyat_parallel_attend(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(wq),
+                                        _ptr(bq), _ptr(out), None, _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream_handle()),
+           "rehyat_parallel_attend")
 
 
 class Stream:

@@ -159,15 +159,56 @@ size_t rehyat_workspace_bytes(const rehyat_params* p) {
     return G > 0 ? partial_bytes(p, G) : 0;
 }
 
-rehyat_status rehyat_forward_parallel_aux(const rehyat_params* p, const void* q, const void* k,
-                                          const void* v, const void* wq, const void* wk,
-                                          const float* bq, const float* bk, void* out,
-                                          const rehyat_aux* aux, void* ws, size_t ws_bytes,
-                                          hipStream_t stream) {
+rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, const void* v,
+                                     const void* wk, const float* bk, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
     rehyat_status st = check_params(p, true);
     if (st != REHYAT_OK) return st;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(wq) || !aligned16(wk) ||
-        !aligned16(out) || !aligned4_or_null(bq) || !aligned4_or_null(bk))
+    if (!aligned16(k) || !aligned16(v) || !aligned16(wk) || !aligned4_or_null(bk)) return REHYAT_EALIGN;
+    const int G = state_frames(p);
+    const size_t need = G > 0 ? partial_bytes(p, G) : 0;
+    if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0)) return REHYAT_EWORKSPACE;
+    if (G == 0) return REHYAT_OK;
+
+    const int64_t N = (int64_t)p->T * p->frame_tokens;
+    const int64_t F = (int64_t)p->P * p->Dphi;
+    const int BH = p->B * p->H;
+    float* Sp = reinterpret_cast<float*>(ws);
+    float* Zp = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)BH * G * F * p->D * sizeof(float)));
+    StateArgs s = state_common(p, wk, bk);
+    s.k1 = k;
+    s.v1 = v;
+    s.kv1_bh_stride = N * p->D;
+    s.nf1 = p->T;
+    s.k2 = k;
+    s.v2 = v;
+    s.kv2_bh_stride = N * p->D;
+    s.g0 = 0;
+    s.G = G;
+    s.Sp = Sp;
+    s.Zp = Zp;
+    st = hip_status(launch_state(s, p->in_dtype, stream));
+    if (st != REHYAT_OK) return st;
+    ScanArgs sc;
+    sc.Sp = Sp;
+    sc.Zp = Zp;
+    sc.G = G;
+    sc.S_state = nullptr;
+    sc.Z_state = nullptr;
+    sc.BH = BH;
+    sc.F = (int)F;
+    sc.D = p->D;
+    return hip_status(launch_scan(sc, stream));
+}
+
+rehyat_status rehyat_parallel_attend(const rehyat_params* p, const void* q, const void* k,
+                                     const void* v, const void* wq, const float* bq, void* out,
+                                     const rehyat_aux* aux, const void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+    rehyat_status st = check_params(p, true);
+    if (st != REHYAT_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(wq) || !aligned16(out) ||
+        !aligned4_or_null(bq))
         return REHYAT_EALIGN;
     if (aux) {
         if ((aux->o_soft && !aligned16(aux->o_soft)) || (aux->y && !aligned16(aux->y)) ||
@@ -181,37 +222,8 @@ rehyat_status rehyat_forward_parallel_aux(const rehyat_params* p, const void* q,
     const int64_t N = (int64_t)p->T * p->frame_tokens;
     const int64_t F = (int64_t)p->P * p->Dphi;
     const int BH = p->B * p->H;
-    float* Sp = reinterpret_cast<float*>(ws);
-    float* Zp = G > 0 ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)BH * G * F * p->D * sizeof(float))) : nullptr;
-
-    if (G > 0) {
-        StateArgs s = state_common(p, wk, bk);
-        s.k1 = k;
-        s.v1 = v;
-        s.kv1_bh_stride = N * p->D;
-        s.nf1 = p->T;
-        s.k2 = k;
-        s.v2 = v;
-        s.kv2_bh_stride = N * p->D;
-        s.g0 = 0;
-        s.G = G;
-        s.Sp = Sp;
-        s.Zp = Zp;
-        st = hip_status(launch_state(s, p->in_dtype, stream));
-        if (st != REHYAT_OK) return st;
-        ScanArgs sc;
-        sc.Sp = Sp;
-        sc.Zp = Zp;
-        sc.G = G;
-        sc.S_state = nullptr;
-        sc.Z_state = nullptr;
-        sc.BH = BH;
-        sc.F = (int)F;
-        sc.D = p->D;
-        st = hip_status(launch_scan(sc, stream));
-        if (st != REHYAT_OK) return st;
-    }
-
+    const float* Sp = reinterpret_cast<const float*>(ws);
+    const float* Zp = G > 0 ? reinterpret_cast<const float*>(reinterpret_cast<const char*>(ws) + align256((size_t)BH * G * F * p->D * sizeof(float))) : nullptr;
     AttnArgs a = attn_common(p, wq, bq);
     a.q = q;
     a.out = out;
@@ -238,6 +250,30 @@ rehyat_status rehyat_forward_parallel_aux(const rehyat_params* p, const void* q,
     a.stream = 0;
     a.nchunks = num_chunks(p);
     return hip_status(launch_attn(a, p->in_dtype, p->out_dtype, stream));
+}
+
+rehyat_status rehyat_forward_parallel_aux(const rehyat_params* p, const void* q, const void* k,
+                                          const void* v, const void* wq, const void* wk,
+                                          const float* bq, const float* bk, void* out,
+                                          const rehyat_aux* aux, void* ws, size_t ws_bytes,
+                                          hipStream_t stream) {
+    // validate every argument before the first launch
+    rehyat_status st = check_params(p, true);
+    if (st != REHYAT_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(wq) || !aligned16(wk) ||
+        !aligned16(out) || !aligned4_or_null(bq) || !aligned4_or_null(bk))
+        return REHYAT_EALIGN;
+    if (aux) {
+        if ((aux->o_soft && !aligned16(aux->o_soft)) || (aux->y && !aligned16(aux->y)) ||
+            !aligned4_or_null(aux->lse) || !aligned4_or_null(aux->z))
+            return REHYAT_EALIGN;
+    }
+    const int G = state_frames(p);
+    const size_t need = G > 0 ? partial_bytes(p, G) : 0;
+    if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0)) return REHYAT_EWORKSPACE;
+    st = rehyat_parallel_states(p, k, v, wk, bk, ws, ws_bytes, stream);
+    if (st != REHYAT_OK) return st;
+    return rehyat_parallel_attend(p, q, k, v, wq, bq, out, aux, ws, ws_bytes, stream);
 }
 
 rehyat_status rehyat_forward_parallel(const rehyat_params* p, const void* q, const void* k,

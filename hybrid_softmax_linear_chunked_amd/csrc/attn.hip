@@ -397,8 +397,16 @@ static hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
     const bool s_lds = st <= lds_max;
     const size_t lds = (s_lds && st > kv) ? st : kv;
     auto fn = attn_kernel<T, OT, D, QB, NW>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+    // raise the dynamic LDS limit of this instantiation once per device (idempotent, so a
+    // race between host threads only repeats the call)
+    static size_t lds_set[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (lds > lds_set[dev]) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        lds_set[dev] = lds;
+    }
     AttnArgs b = a;
     b.s_lds = s_lds ? 1 : 0;
     constexpr int BQ = NW * QB * 32;

@@ -229,8 +229,16 @@ static hipError_t launch_state_t(const StateArgs& a, hipStream_t stream) {
     const size_t red = (size_t)(a.Dphi / 32) * 16 * 64 * sizeof(float);
     const size_t lds = kv > red ? kv : red;
     auto fn = state_kernel<T, D, P>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+    // raise the dynamic LDS limit of this instantiation once per device (idempotent, so a
+    // race between host threads only repeats the call)
+    static size_t lds_set[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (lds > lds_set[dev]) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        lds_set[dev] = lds;
+    }
     hipLaunchKernelGGL(fn, dim3(a.BH * a.G), dim3(NT), lds, stream, a);
     return hipGetLastError();
 }

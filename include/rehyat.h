@@ -29,7 +29,8 @@
  *     validation (checked before any HIP call) and launch errors.  Device faults appear
  *     at the caller's next synchronisation.
  *   - Determinism: no atomics; repeated calls on the same inputs give identical bits.
- *   - Thread safety: functions keep no global state; one in-flight call per stream state.
+ *   - Thread safety: no shared mutable state beyond a per-device cache of kernel LDS limits
+ *     (idempotent); one in-flight call per streaming state.
  */
 #ifndef REHYAT_H
 #define REHYAT_H
@@ -46,7 +47,7 @@ extern "C" {
 typedef enum {
     REHYAT_OK = 0,
     REHYAT_EINVAL = 1,     /* a parameter value is out of range */
-    REHYAT_ESHAPE = 2,     /* unsupported shape: D not in {32,64,128}, Dphi not a multiple of 32, ... */
+    REHYAT_ESHAPE = 2,     /* unsupported shape: D not in {32,64,128}, Dphi not in {32,64,96,128}, P not in 1..4 */
     REHYAT_EALIGN = 3,     /* a required pointer is NULL or not 16-byte aligned */
     REHYAT_EWORKSPACE = 4, /* workspace pointer NULL or ws_bytes below the required size */
     REHYAT_ESTATE = 5,     /* streaming misuse: frames out of range, stream closed, bad handle */
@@ -61,7 +62,7 @@ typedef struct {
     int32_t T;             /* latent frames (ignored by the streaming entry points) */
     int32_t frame_tokens;  /* n = tokens per latent frame (H x W of the latent grid) */
     int32_t Tc, To;        /* chunk frames (>= 1), overlap frames (>= 0) */
-    int32_t Dphi, P;       /* phi width (multiple of 32, <= 256), parts = max power (1..4) */
+    int32_t Dphi, P;       /* phi width (32, 64, 96 or 128), parts = max power (1..4) */
     int32_t linear_only;   /* 1: empty softmax window (normalised chunk-causal linear attention) */
     int32_t in_dtype;      /* rehyat_dtype of q, k, v, weights (and features / overlap state) */
     int32_t out_dtype;     /* rehyat_dtype of out */
@@ -119,6 +120,20 @@ rehyat_status rehyat_forward_parallel_aux(const rehyat_params* p, const void* q,
                                           const float* bq, const float* bk, void* out,
                                           const rehyat_aux* aux, void* ws, size_t ws_bytes,
                                           hipStream_t stream);
+
+/* The two stages of rehyat_forward_parallel_aux, for callers that reuse the states or time
+ * the stages separately.  rehyat_parallel_states writes the per-frame partials of
+ * phi_k(K)^T [V|1] and their inclusive prefix over frames into ws (blog 2.3 state sums);
+ * rehyat_parallel_attend runs the windowed softmax tile kernel with the fused linear part,
+ * reading the prefix from ws.  Same arguments, layouts and status codes as above; ws must
+ * hold the states of the same k, v, wk, bk when attend runs (stream order suffices). */
+rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, const void* v,
+                                     const void* wk, const float* bk, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
+rehyat_status rehyat_parallel_attend(const rehyat_params* p, const void* q, const void* k,
+                                     const void* v, const void* wq, const float* bq, void* out,
+                                     const rehyat_aux* aux, const void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
 
 /* Streaming (blog 5.2: states = init_states(); output, states = block(chunk, states)).
  * Device state bytes: S float32 [B,H,F,D], Z float32 [B,H,F] and two overlap buffers of

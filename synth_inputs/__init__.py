@@ -10,10 +10,13 @@ frame, 12 heads of dim 128), 5 s / 10 s / 20 s clips (21 / 41 / 81 latent frames
 14B-shaped layer at 720x1280 (45x80 = 3600 tokens per frame, 40 heads).  The pages use
 chunks of Tc = 3 frames with To = 1 overlap frame and a degree-2 polynomial feature map.
 
-Recipe: numpy PCG64 ``default_rng(seed)``; Q, K, V ~ N(0, 1) with shape [B, H, N, D],
-then W_q, W_k ~ N(0, 1/D) with shape [H, Dphi, D], drawn in that order as float32;
-for bf16 workloads every value is rounded to the nearest bfloat16 (ties to even) and
-kept as float32 holding that exact value.  No bias (the API accepts one).
+Recipe: numpy PCG64 with one independent stream per tensor slab, so that any (batch,
+head) slab can be regenerated on its own: Q, K, V[b, h] ~ N(0, 1) of shape [N, D] from
+``default_rng([seed, t, b, h])`` with t = 0, 1, 2; W_q[h], W_k[h] ~ N(0, 1/D) of shape
+[Dphi, D] from ``default_rng([seed, t, h])`` with t = 3, 4; all drawn as float32.  For bf16
+workloads every value is rounded to the nearest bfloat16 (ties to even) and kept as
+float32 holding that exact value.  No bias (the API accepts one).  The seed of a workload
+is its index in the list of measured workloads (tiny 0, 5 s 1, 10 s 2, 20 s 3, 14B 4).
 """
 from __future__ import annotations
 
@@ -66,25 +69,38 @@ WORKLOADS = {
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    """Round finite float32 values to the nearest bfloat16 (ties to even); returns float32."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).copy()
+    u += np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    u &= np.uint32(0xFFFF0000)
+    return u.view(np.float32)
 
 
-def make_inputs(w: Workload, seed: int):
-    """Returns dict q, k, v [B,H,N,D] and wq, wk [H,Dphi,D] as float32 arrays."""
-    rng = np.random.default_rng(seed)
-    shape = (w.B, w.H, w.N, w.D)
-    q = rng.standard_normal(shape, dtype=np.float32)
-    k = rng.standard_normal(shape, dtype=np.float32)
-    v = rng.standard_normal(shape, dtype=np.float32)
-    wshape = (w.H, w.Dphi, w.D)
-    sd = np.float32(1.0 / np.sqrt(w.D))
-    wq = rng.standard_normal(wshape, dtype=np.float32) * sd
-    wk = rng.standard_normal(wshape, dtype=np.float32) * sd
-    out = dict(q=q, k=k, v=v, wq=wq, wk=wk)
-    if w.dtype == "bf16":
-        out = {key: round_bf16(val) for key, val in out.items()}
+def _slab(seed: int, t: int, idx, shape, scale, bf16: bool) -> np.ndarray:
+    a = np.random.default_rng([seed, t, *idx]).standard_normal(shape, dtype=np.float32)
+    if scale != 1.0:
+        a *= np.float32(scale)
+    return round_bf16(a) if bf16 else a
+
+
+def make_inputs(w: Workload, seed: int, slabs=None):
+    """Returns dict q, k, v [B,H,N,D] and wq, wk [H,Dphi,D] as float32 arrays.
+
+    With ``slabs`` = list of (b, h), q/k/v hold only those slabs, stacked as
+    [len(slabs), 1, N, D], and wq/wk the matching heads as [len(slabs), Dphi, D]."""
+    bf = w.dtype == "bf16"
+    sd = 1.0 / np.sqrt(w.D)
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)] if slabs is None else list(slabs)
+    out = {}
+    for t, key in enumerate(("q", "k", "v")):
+        if slabs is None:
+            a = np.empty((w.B, w.H, w.N, w.D), dtype=np.float32)
+            for b, h in pairs:
+                a[b, h] = _slab(seed, t, (b, h), (w.N, w.D), 1.0, bf)
+        else:
+            a = np.stack([_slab(seed, t, (b, h), (w.N, w.D), 1.0, bf)[None] for b, h in pairs])
+        out[key] = a
+    heads = range(w.H) if slabs is None else [h for _, h in pairs]
+    for t, key in ((3, "wq"), (4, "wk")):
+        out[key] = np.stack([_slab(seed, t, (h,), (w.Dphi, w.D), sd, bf) for h in heads])
     return out
