@@ -57,8 +57,38 @@ size_t partial_bytes(const rehyat_params* p, int frames) {
     return align256(BH * frames * F * p->D * sizeof(float)) + align256(BH * frames * F * sizeof(float));
 }
 
+// Per-slot state image: S rows in the attention kernel's operand order (input dtype) and
+// Z reordered by power (float).
+size_t image_bytes(const rehyat_params* p, int slots) {
+    const size_t F = (size_t)p->P * p->Dphi;
+    const size_t BH = (size_t)p->B * p->H;
+    return align256(BH * slots * F * p->D * elem_bytes(p->in_dtype)) + align256(BH * slots * F * sizeof(float));
+}
+
+// Chunk-parallel workspace: per-frame partials [BH, G, F, D] + [BH, G, F], then the
+// state images of every chunk [BH, nc, ...].
+struct ParallelLayout {
+    size_t sp, zp, img, zimg, total;
+};
+
+ParallelLayout parallel_layout(const rehyat_params* p, int G) {
+    const size_t F = (size_t)p->P * p->Dphi;
+    const size_t BH = (size_t)p->B * p->H;
+    const int nc = num_chunks(p);
+    ParallelLayout L;
+    size_t off = 0;
+    L.sp = off; off += align256(BH * G * F * p->D * sizeof(float));
+    L.zp = off; off += align256(BH * G * F * sizeof(float));
+    L.img = off; off += align256(BH * nc * F * p->D * elem_bytes(p->in_dtype));
+    L.zimg = off; off += align256(BH * nc * F * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+// Streaming state: S, Z (float, carried sums), the image of the current state, and two
+// overlap buffers of To frames of K and V.
 struct StateLayout {
-    size_t S, Z, ovk[2], ovv[2], total;
+    size_t S, Z, img, zimg, ovk[2], ovv[2], total;
 };
 
 StateLayout state_layout(const rehyat_params* p) {
@@ -69,6 +99,8 @@ StateLayout state_layout(const rehyat_params* p) {
     size_t off = 0;
     L.S = off; off += align256(BH * F * p->D * sizeof(float));
     L.Z = off; off += align256(BH * F * sizeof(float));
+    L.img = off; off += align256(BH * F * p->D * elem_bytes(p->in_dtype));
+    L.zimg = off; off += align256(BH * F * sizeof(float));
     for (int i = 0; i < 2; ++i) { L.ovk[i] = off; off += align256(ov); }
     for (int i = 0; i < 2; ++i) { L.ovv[i] = off; off += align256(ov); }
     L.total = off;
@@ -156,7 +188,7 @@ rehyat_status rehyat_phi(const rehyat_params* p, const void* x, const void* w, c
 size_t rehyat_workspace_bytes(const rehyat_params* p) {
     if (check_params(p, true) != REHYAT_OK) return 0;
     const int G = state_frames(p);
-    return G > 0 ? partial_bytes(p, G) : 0;
+    return G > 0 ? parallel_layout(p, G).total : 0;
 }
 
 rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, const void* v,
@@ -166,15 +198,16 @@ rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, cons
     if (st != REHYAT_OK) return st;
     if (!aligned16(k) || !aligned16(v) || !aligned16(wk) || !aligned4_or_null(bk)) return REHYAT_EALIGN;
     const int G = state_frames(p);
-    const size_t need = G > 0 ? partial_bytes(p, G) : 0;
+    const size_t need = G > 0 ? parallel_layout(p, G).total : 0;
     if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0)) return REHYAT_EWORKSPACE;
     if (G == 0) return REHYAT_OK;
 
     const int64_t N = (int64_t)p->T * p->frame_tokens;
-    const int64_t F = (int64_t)p->P * p->Dphi;
     const int BH = p->B * p->H;
-    float* Sp = reinterpret_cast<float*>(ws);
-    float* Zp = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)BH * G * F * p->D * sizeof(float)));
+    const ParallelLayout PL = parallel_layout(p, G);
+    char* w = reinterpret_cast<char*>(ws);
+    float* Sp = reinterpret_cast<float*>(w + PL.sp);
+    float* Zp = reinterpret_cast<float*>(w + PL.zp);
     StateArgs s = state_common(p, wk, bk);
     s.k1 = k;
     s.v1 = v;
@@ -190,15 +223,22 @@ rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, cons
     st = hip_status(launch_state(s, p->in_dtype, stream));
     if (st != REHYAT_OK) return st;
     ScanArgs sc;
+    std::memset(&sc, 0, sizeof(sc));
     sc.Sp = Sp;
     sc.Zp = Zp;
     sc.G = G;
-    sc.S_state = nullptr;
-    sc.Z_state = nullptr;
+    sc.simg = w + PL.img;
+    sc.zimg = reinterpret_cast<float*>(w + PL.zimg);
+    sc.slots = num_chunks(p);
     sc.BH = BH;
-    sc.F = (int)F;
     sc.D = p->D;
-    return hip_status(launch_scan(sc, stream));
+    sc.Dphi = p->Dphi;
+    sc.P = p->P;
+    sc.T = p->T;
+    sc.Tc = p->Tc;
+    sc.To = p->To;
+    sc.linear_only = p->linear_only;
+    return hip_status(launch_scan(sc, p->in_dtype, stream));
 }
 
 rehyat_status rehyat_parallel_attend(const rehyat_params* p, const void* q, const void* k,
@@ -216,14 +256,11 @@ rehyat_status rehyat_parallel_attend(const rehyat_params* p, const void* q, cons
             return REHYAT_EALIGN;
     }
     const int G = state_frames(p);
-    const size_t need = G > 0 ? partial_bytes(p, G) : 0;
+    const size_t need = G > 0 ? parallel_layout(p, G).total : 0;
     if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0)) return REHYAT_EWORKSPACE;
 
     const int64_t N = (int64_t)p->T * p->frame_tokens;
-    const int64_t F = (int64_t)p->P * p->Dphi;
-    const int BH = p->B * p->H;
-    const float* Sp = reinterpret_cast<const float*>(ws);
-    const float* Zp = G > 0 ? reinterpret_cast<const float*>(reinterpret_cast<const char*>(ws) + align256((size_t)BH * G * F * p->D * sizeof(float))) : nullptr;
+    const char* w = reinterpret_cast<const char*>(ws);
     AttnArgs a = attn_common(p, wq, bq);
     a.q = q;
     a.out = out;
@@ -234,12 +271,12 @@ rehyat_status rehyat_parallel_attend(const rehyat_params* p, const void* q, cons
     a.k2 = k;
     a.v2 = v;
     a.kv2_bh_stride = N * p->D;
-    a.S = Sp;
-    a.Z = Zp;
-    a.S_bh_stride = (int64_t)G * F * p->D;
-    a.S_frame_stride = F * p->D;
-    a.Z_bh_stride = (int64_t)G * F;
-    a.Z_frame_stride = F;
+    if (G > 0) {
+        const ParallelLayout PL = parallel_layout(p, G);
+        a.simg = w + PL.img;
+        a.zimg = reinterpret_cast<const float*>(w + PL.zimg);
+    }
+    a.img_slots = num_chunks(p);
     if (aux) {
         a.aux_o_soft = aux->o_soft;
         a.aux_lse = aux->lse;
@@ -269,7 +306,7 @@ rehyat_status rehyat_forward_parallel_aux(const rehyat_params* p, const void* q,
             return REHYAT_EALIGN;
     }
     const int G = state_frames(p);
-    const size_t need = G > 0 ? partial_bytes(p, G) : 0;
+    const size_t need = G > 0 ? parallel_layout(p, G).total : 0;
     if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0)) return REHYAT_EWORKSPACE;
     st = rehyat_parallel_states(p, k, v, wk, bk, ws, ws_bytes, stream);
     if (st != REHYAT_OK) return st;
@@ -333,6 +370,8 @@ rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stre
     char* base = reinterpret_cast<char*>(state);
     float* S = reinterpret_cast<float*>(base + L.S);
     float* Z = reinterpret_cast<float*>(base + L.Z);
+    void* simg = base + L.img;
+    float* zimg = reinterpret_cast<float*>(base + L.zimg);
     const int slot = st->overlap_slot;
     void* ovk = base + L.ovk[slot];
     void* ovv = base + L.ovv[slot];
@@ -372,15 +411,20 @@ rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stre
         rehyat_status r = hip_status(launch_state(sa, p->in_dtype, stream));
         if (r != REHYAT_OK) return r;
         ScanArgs sc;
+        std::memset(&sc, 0, sizeof(sc));
         sc.Sp = Sp;
         sc.Zp = Zp;
         sc.G = sa.G;
         sc.S_state = S;
         sc.Z_state = Z;
+        sc.simg = simg;
+        sc.zimg = zimg;
+        sc.slots = 1;
         sc.BH = BH;
-        sc.F = F;
         sc.D = p->D;
-        return hip_status(launch_scan(sc, stream));
+        sc.Dphi = p->Dphi;
+        sc.P = p->P;
+        return hip_status(launch_scan(sc, p->in_dtype, stream));
     };
 
     // 1. frames that belong to this chunk's linear region but are not yet in the state
@@ -399,10 +443,9 @@ rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stre
     a.k2 = k;
     a.v2 = v;
     a.kv2_bh_stride = ch_bh;
-    a.S = S;
-    a.Z = Z;
-    a.S_bh_stride = (int64_t)F * p->D;
-    a.Z_bh_stride = F;
+    a.simg = simg;
+    a.zimg = zimg;
+    a.img_slots = 1;
     a.aux_bh_stride = (int64_t)frames * n;
     a.stream = 1;
     a.s_frames = frames;

@@ -1,40 +1,57 @@
 // attn.hip -- windowed softmax tile kernel with the linear part and the shared
 // normalisation fused into its epilogue (ReHyAt blog, maplevalley.com.cn, 2.2.1-2.3).
 //
-// One workgroup = NW waves = BQ = NW*QB*32 queries of one chunk of one (batch, head).
+// One workgroup = 4 waves x 32 queries of one chunk of one (batch, head); two workgroups
+// share a CU (each wave stays under 256 VGPRs), so the softmax arithmetic of one
+// workgroup overlaps the matrix-core work of the other -- they meet at no common barrier.
 // The chunk's softmax window (its own frames plus To preceding frames, bidirectional) is
 // streamed through LDS in 64-token tiles, double-buffered through registers.  Per tile
 // and wave:
 //   S^T (keys x queries) = K . Q^T  on MFMA, so every lane owns one query column and the
-//      row statistics of that query live in one lane pair (lane, lane^32);
+//      statistics of that query live in one lane pair (lane, lane^32);
 //   online softmax in the log2 domain: p = exp2(s*log2(e)/sqrt(D) - m); the running max m
 //      is only moved when a tile raises it by more than 2^8 (the accumulators are then
 //      rescaled); otherwise the stale m is kept, which is exact because the final
 //      normalisation uses the same m;
 //   O^T (d x queries) += V^T . P^T on MFMA, with P^T taken directly from the S^T
 //      registers (contraction slots follow the C layout, V^T is staged in that order).
-// Epilogue (chunks with a linear region): u = W_q q (MFMA, reusing the Q operand
-// registers), phi = per-part powers of softplus(u + b), y = phi S_c and z = phi . Z_c
-// (S_c staged in LDS), then out = (2^m O + y) / (2^m l + z), scaled by 2^-max(m,0).
+// Only the last tile of a window can be ragged; it runs a separate masked copy of the
+// tile step, so full tiles carry no bounds arithmetic.
+// Epilogue (chunks with a linear region): W_q is staged in LDS and u = W_q q computed on
+// MFMA from the Q operand registers; phi = per-part powers of softplus(u + b).  For each
+// power the chunk's state image (S_c rows for that power, written by the scan kernel in
+// the operand order used here) is staged in LDS, y += S_c^T phi on MFMA and
+// z += phi . Z_c; finally out = (2^m O + y) / (2^m l + z), scaled by 2^-max(m,0).
+#include <type_traits>
+
 #include "tiles.hpp"
 #include "kernels.hpp"
-
-#ifndef REHYAT_ATTN_QB
-#define REHYAT_ATTN_QB 2
-#endif
 
 namespace rehyat {
 
 static constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
-template <class T, class OT, int D, int QB, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
+template <class T, int D, int NT>
+struct AttnLds {
+    using Tile = KVTile<T, D, NT>;
+    static constexpr int VEC = Tile::VEC;
+    static constexpr size_t kv_bytes = 2 * (size_t)(Tile::K_ELEMS + Tile::V_ELEMS) * sizeof(T);
+    // epilogue: W_q [Dphi][D + VEC] and one power of the state image [D][Dphi + VEC]
+    static size_t epi_bytes(int Dphi) {
+        return ((size_t)Dphi * (D + VEC) + (size_t)D * (Dphi + VEC)) * sizeof(T);
+    }
+    static size_t bytes(int Dphi) { return kv_bytes > epi_bytes(Dphi) ? kv_bytes : epi_bytes(Dphi); }
+};
+
+template <class T, class OT, int D, int QB, int NW, bool STREAM>
+__global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
     using M = Mfma<T>;
-    using Tile = KVTile<T, D, NW * 64>;
+    constexpr int NT = NW * 64;
+    using Tile = KVTile<T, D, NT>;
     constexpr int KS = M::KS, EPL = M::EPL, NS = D / KS, NDB = D / 32;
     constexpr int BQ = NW * QB * 32;
-    constexpr int NT = NW * 64;
     constexpr int TPB = 16 / EPL;  // MFMA steps per 32-token block of the value product
+    constexpr int VEC = Tile::VEC;
 
     extern __shared__ __align__(16) unsigned char smem[];
     T* Ks0 = reinterpret_cast<T*>(smem);
@@ -57,8 +74,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
     KeySrc<T> src;
     const T* kb1 = reinterpret_cast<const T*>(a.k1) + (int64_t)bh * a.kv1_bh_stride;
     const T* vb1 = reinterpret_cast<const T*>(a.v1) + (int64_t)bh * a.kv1_bh_stride;
-    int64_t s_off, z_off;
-    if (!a.stream) {
+    int img_slot;
+    if constexpr (!STREAM) {
         const int f0 = c * a.Tc;
         const int f1 = min(f0 + a.Tc, a.T);
         const int ws = a.linear_only ? f1 : max(0, f0 - a.To);
@@ -70,9 +87,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
         src.v1 = vb1 + (int64_t)ws * a.n * D;
         src.k2 = src.k1;
         src.v2 = src.v1;
-        src.len1 = Lk;
-        s_off = (int64_t)bh * a.S_bh_stride + (int64_t)max(ls - 1, 0) * a.S_frame_stride;
-        z_off = (int64_t)bh * a.Z_bh_stride + (int64_t)max(ls - 1, 0) * a.Z_frame_stride;
+        src.len1 = 1 << 30;
+        img_slot = bh * a.img_slots + c;
     } else {
         q0 = 0;
         Lq = a.s_frames * a.n;
@@ -83,8 +99,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
         src.k2 = reinterpret_cast<const T*>(a.k2) + (int64_t)bh * a.kv2_bh_stride;
         src.v2 = reinterpret_cast<const T*>(a.v2) + (int64_t)bh * a.kv2_bh_stride;
         src.len1 = a.s_held * a.n;
-        s_off = (int64_t)bh * a.S_bh_stride;
-        z_off = (int64_t)bh * a.Z_bh_stride;
+        img_slot = bh;
     }
     if (qt * BQ >= Lq) return;
     const bool has_lin = ls > 0;
@@ -125,28 +140,21 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
 
     const float sc = a.scale_log2;
     const int ntiles = (Lk + Tile::BK - 1) / Tile::BK;
+    const bool ragged = Lk % Tile::BK != 0;
     Tile tile;
-    if (ntiles > 0) {
-        tile.load(src, 0, Lk, tid);
-        tile.store(Ks0, Vs0, tid);
-    }
-    __syncthreads();
 
-    for (int it = 0; it < ntiles; ++it) {
-        T* Ks = (it & 1) ? Ks1 : Ks0;
-        T* Vs = (it & 1) ? Vs1 : Vs0;
-        const int t0 = it * Tile::BK;
-        const bool more = it + 1 < ntiles;
-        if (more) tile.load(src, t0 + Tile::BK, Lk, tid);
-
-        // S^T = K Q^T for 2 key blocks x QB query blocks
+    // one 64-token tile: S^T, online softmax, O^T update
+    auto tile_step = [&](const T* Ks, const T* Vs, int t0, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         f32x16 sacc[2][QB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
+            const typename M::frag af = Tile::kfrag(Ks, kb, 0, col, h);
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = zero16();
+            for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = M::mma(af, qf[qb][0], zero16());
+        }
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
+        for (int s = 1; s < NS; ++s) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 const typename M::frag af = Tile::kfrag(Ks, kb, s, col, h);
@@ -154,7 +162,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
                 for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = M::mma(af, qf[qb][s], sacc[kb][qb]);
             }
         }
-        if (t0 + Tile::BK > Lk) {  // ragged last tile: keys beyond the window get -inf
+        if constexpr (MASK) {  // keys beyond the window get -inf
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -200,7 +208,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
             l_run[qb] += lsum;
         }
 
-        // O^T += V^T P^T
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -211,10 +218,30 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = M::mma(vf, pf[kb][t][qb], oacc[db][qb]);
                 }
+    };
 
+    // full tiles in the loop; a ragged last tile is peeled off after it
+    const int nfull = ragged ? ntiles - 1 : ntiles;
+    if (ntiles > 0) {
+        if (nfull == 0) tile.template load<true, STREAM>(src, 0, Lk, tid);
+        else tile.template load<false, STREAM>(src, 0, Lk, tid);
+        tile.store(Ks0, Vs0, tid);
+    }
+    __syncthreads();
+    for (int it = 0; it < nfull; ++it) {
+        const T* Ks = (it & 1) ? Ks1 : Ks0;
+        const T* Vs = (it & 1) ? Vs1 : Vs0;
+        const int t0 = it * Tile::BK;
+        const bool more = it + 1 < ntiles;
+        if (more) {
+            if (it + 1 == nfull) tile.template load<true, STREAM>(src, t0 + Tile::BK, Lk, tid);
+            else tile.template load<false, STREAM>(src, t0 + Tile::BK, Lk, tid);
+        }
+        tile_step(Ks, Vs, t0, std::false_type{});
         if (more) tile.store((it & 1) ? Ks0 : Ks1, (it & 1) ? Vs0 : Vs1, tid);
         __syncthreads();
     }
+    if (ragged) tile_step((nfull & 1) ? Ks1 : Ks0, (nfull & 1) ? Vs1 : Vs0, nfull * Tile::BK, std::true_type{});
 
     float l_tot[QB];
 #pragma unroll
@@ -230,99 +257,77 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
         for (int db = 0; db < NDB; ++db) yacc[db][qb] = zero16();
     }
     if (has_lin) {
-        const int Dphi = a.Dphi, P = a.P, F = Dphi * P, NJB = Dphi / 32;
-        const int SLD = F + Tile::VEC;
-        T* Ss = reinterpret_cast<T*>(smem);
-        float* Zs = reinterpret_cast<float*>(smem + (size_t)D * SLD * sizeof(T));
-        const float* Sg = a.S + s_off;
-        const float* Zg = a.Z + z_off;
-        // stage S_c^T in LDS as Ss[d][(pw-1)*Dphi + 32-block slot order of j], Z_c as Zs[(pw-1)*Dphi + j]
-        if (a.s_lds) {
-            const int items = (Dphi / 4) * P * (D / 8);
-            for (int it = tid; it < items; it += NT) {
-                const int dc = it % (D / 8);
-                const int jq = (it / (D / 8)) % (Dphi / 4);
-                const int pw = it / ((D / 8) * (Dphi / 4)) + 1;
-                const int j0 = jq * 4;
-                float v[4][8];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float* srow = Sg + (int64_t)feat_index(j0 + i, pw, Dphi, P) * D + dc * 8;
-                    const float4 lo = *reinterpret_cast<const float4*>(srow);
-                    const float4 hi = *reinterpret_cast<const float4*>(srow + 4);
-                    v[i][0] = lo.x; v[i][1] = lo.y; v[i][2] = lo.z; v[i][3] = lo.w;
-                    v[i][4] = hi.x; v[i][5] = hi.y; v[i][6] = hi.z; v[i][7] = hi.w;
-                }
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const int d = dc * 8 + jj;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int j = j0 + i;
-                        Ss[d * SLD + (pw - 1) * Dphi + (j / 32) * 32 + slot_pos<EPL>(j % 32)] = from_float<T>(v[i][jj]);
-                    }
-                }
-            }
-            for (int it = tid; it < F; it += NT) {
-                const int j = it % Dphi, pw = it / Dphi + 1;
-                Zs[it] = Zg[feat_index(j, pw, Dphi, P)];
-            }
-            __syncthreads();
-        }
-
+        const int Dphi = a.Dphi, P = a.P, NJB = Dphi / 32;
+        constexpr int WLD = D + VEC;        // W_q row stride in LDS
+        const int SLD = Dphi + VEC;         // state-image row stride in LDS
+        T* Ws = reinterpret_cast<T*>(smem);
+        T* Ss = Ws + Dphi * WLD;
         const T* wq = reinterpret_cast<const T*>(a.wq) + (int64_t)hh * Dphi * D;
+        const T* img = reinterpret_cast<const T*>(a.simg) + (int64_t)img_slot * P * D * Dphi;
+        const float* zimg = a.zimg + (int64_t)img_slot * P * Dphi;
         const float* bq = a.bq ? a.bq + (int64_t)hh * Dphi : nullptr;
+
+        __syncthreads();  // every wave is done with the K/V tiles (the peeled tile included)
+        // stage W_q [Dphi][D] (16-byte chunks)
+        for (int i = tid; i < Dphi * (D / VEC); i += NT) {
+            const int j = i / (D / VEC), ch = i % (D / VEC);
+            *reinterpret_cast<uint4*>(Ws + j * WLD + ch * VEC) = *reinterpret_cast<const uint4*>(wq + (int64_t)j * D + ch * VEC);
+        }
+        __syncthreads();
+        // u = softplus(W_q q + b) for every block of 32 phi rows (lane: one query, 16 rows)
+        constexpr int JBMAX = 4;  // Dphi <= 128
+        float uu[JBMAX][QB][16];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float zpart = 0.f;
-            for (int jb = 0; jb < NJB; ++jb) {
-                f32x16 u = zero16();
+        for (int jb = 0; jb < JBMAX; ++jb) {
+            if (jb >= NJB) break;
 #pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    const typename M::frag wf = M::load(wq + (int64_t)(jb * 32 + col) * D + s * KS + h * EPL);
-                    u = M::mma(wf, qf[qb][s], u);
-                }
-                float uu[16], ph[16];
+            for (int qb = 0; qb < QB; ++qb) {
+                f32x16 u = M::mma(M::load(Ws + (jb * 32 + col) * WLD + h * EPL), qf[qb][0], zero16());
+#pragma unroll
+                for (int s = 1; s < NS; ++s) u = M::mma(M::load(Ws + (jb * 32 + col) * WLD + s * KS + h * EPL), qf[qb][s], u);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float x = u[r] + (bq ? bq[jb * 32 + crow(r, h)] : 0.f);
-                    uu[r] = softplus(x);
-                    ph[r] = uu[r];
+                    uu[jb][qb][r] = softplus_fast<T>(x);
                 }
-                for (int pw = 1; pw <= P; ++pw) {
-                    if (pw > 1) {
+            }
+        }
+        for (int pw = 1; pw <= P; ++pw) {
+            __syncthreads();  // W_q / previous power no longer read
+            const T* ip = img + (int64_t)(pw - 1) * D * Dphi;
+            for (int i = tid; i < D * (Dphi / VEC); i += NT) {
+                const int d = i / (Dphi / VEC), ch = i % (Dphi / VEC);
+                *reinterpret_cast<uint4*>(Ss + d * SLD + ch * VEC) = *reinterpret_cast<const uint4*>(ip + (int64_t)d * Dphi + ch * VEC);
+            }
+            __syncthreads();
+            const float* zp = zimg + (pw - 1) * Dphi;
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) ph[r] *= uu[r];
-                    }
-                    const int blk = (pw - 1) * NJB + jb;
+            for (int jb = 0; jb < JBMAX; ++jb) {
+                if (jb >= NJB) break;
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    float ph[16];
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int jr = jb * 32 + crow(r, h);
-                        zpart += ph[r] * (a.s_lds ? Zs[(pw - 1) * Dphi + jr] : Zg[feat_index(jr, pw, Dphi, P)]);
+                        float v = uu[jb][qb][r];
+                        for (int e = 1; e < pw; ++e) v *= uu[jb][qb][r];
+                        ph[r] = v;
+                        zq[qb] += v * zp[jb * 32 + crow(r, h)];
                     }
 #pragma unroll
                     for (int t = 0; t < TPB; ++t) {
                         const typename M::frag bfr = M::pack(ph + t * EPL);
 #pragma unroll
                         for (int db = 0; db < NDB; ++db) {
-                            const int d = db * 32 + col;
-                            typename M::frag sf;
-                            if (a.s_lds) {
-                                sf = M::load(Ss + d * SLD + blk * 32 + t * 2 * EPL + h * EPL);
-                            } else {  // operand gathered from the fp32 state in memory
-                                float sv[EPL];
-#pragma unroll
-                                for (int e = 0; e < EPL; ++e)
-                                    sv[e] = Sg[(int64_t)feat_index(jb * 32 + crow(t * EPL + e, h), pw, Dphi, P) * D + d];
-                                sf = M::pack(sv);
-                            }
+                            const typename M::frag sf = M::load(Ss + (db * 32 + col) * SLD + jb * 32 + t * 2 * EPL + h * EPL);
                             yacc[db][qb] = M::mma(sf, bfr, yacc[db][qb]);
                         }
                     }
                 }
             }
-            zq[qb] = zpart + other_half(zpart);
         }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) zq[qb] += other_half(zq[qb]);
     }
 
     // ---- merge and write ----
@@ -388,15 +393,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
     }
 }
 
-template <class T, class OT, int D, int QB, int NW>
+template <class T, class OT, int D, bool STREAM>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
-    using Tile = KVTile<T, D, NW * 64>;
-    const size_t kv = 2 * (size_t)(Tile::K_ELEMS + Tile::V_ELEMS) * sizeof(T);
-    const size_t st = (size_t)D * (a.Dphi * a.P + Tile::VEC) * sizeof(T) + (size_t)a.Dphi * a.P * sizeof(float);
-    const size_t lds_max = 160 * 1024;
-    const bool s_lds = st <= lds_max;
-    const size_t lds = (s_lds && st > kv) ? st : kv;
-    auto fn = attn_kernel<T, OT, D, QB, NW>;
+    constexpr int QB = 1, NW = 4;
+    using LDS = AttnLds<T, D, NW * 64>;
+    const size_t lds = LDS::bytes(a.Dphi);
+    auto fn = attn_kernel<T, OT, D, QB, NW, STREAM>;
     // raise the dynamic LDS limit of this instantiation once per device (idempotent, so a
     // race between host threads only repeats the call)
     static size_t lds_set[64] = {};
@@ -408,7 +410,6 @@ static hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
         lds_set[dev] = lds;
     }
     AttnArgs b = a;
-    b.s_lds = s_lds ? 1 : 0;
     constexpr int BQ = NW * QB * 32;
     const int qlen = a.stream ? a.s_frames * a.n : a.Tc * a.n;
     b.tiles_per_chunk = (qlen + BQ - 1) / BQ;
@@ -418,15 +419,19 @@ static hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <class T, class OT>
-static hipError_t launch_dt(const AttnArgs& a, hipStream_t stream) {
-    constexpr int QB = sizeof(T) == 2 ? REHYAT_ATTN_QB : 1;
+template <class T, class OT, bool STREAM>
+static hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
     switch (a.D) {
-        case 32: return launch_one<T, OT, 32, QB, 4>(a, stream);
-        case 64: return launch_one<T, OT, 64, QB, 4>(a, stream);
-        case 128: return launch_one<T, OT, 128, QB, 4>(a, stream);
+        case 32: return launch_one<T, OT, 32, STREAM>(a, stream);
+        case 64: return launch_one<T, OT, 64, STREAM>(a, stream);
+        case 128: return launch_one<T, OT, 128, STREAM>(a, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <class T, class OT>
+static hipError_t launch_dt(const AttnArgs& a, hipStream_t stream) {
+    return a.stream ? launch_d<T, OT, true>(a, stream) : launch_d<T, OT, false>(a, stream);
 }
 
 hipError_t launch_attn(const AttnArgs& a, int in_dtype, int out_dtype, hipStream_t stream) {

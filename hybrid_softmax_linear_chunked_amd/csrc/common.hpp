@@ -96,8 +96,39 @@ __host__ __device__ inline int feat_index(int j, int pw, int Dphi, int P) {
     return P * start + (pw - 1) * len + (j - start);
 }
 
+// Inverse of feat_index: feature f -> (j, power).
+__host__ __device__ inline void feat_split(int f, int Dphi, int P, int& j, int& pw) {
+    const int q = Dphi / P, r = Dphi % P;
+    int start = 0;
+    for (int part = 0; part < P; ++part) {
+        const int len = q + (part < r ? 1 : 0);
+        if (f < P * (start + len)) {
+            const int off = f - P * start;
+            pw = off / len + 1;
+            j = start + off % len;
+            return;
+        }
+        start += len;
+    }
+    j = 0;
+    pw = 1;
+}
+
 // softplus(x) = log(1 + e^x), split so neither term overflows.
 __device__ inline float softplus(float x) { return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))); }
+
+// softplus for the bf16 path: the same split with the hardware base-2 exp and log
+// (v_exp_f32, v_log_f32).  The error of log2(1 + e) near 1 is far below the bf16 rounding
+// the features get before their product; fp32 inputs keep the log1p form.
+template <class T>
+__device__ inline float softplus_fast(float x) {
+    if constexpr (sizeof(T) == 2) {
+        const float e = __builtin_amdgcn_exp2f(-fabsf(x) * 1.4426950408889634f);
+        return fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + e) * 0.6931471805599453f;
+    } else {
+        return softplus(x);
+    }
+}
 
 // Exchange with the lane 32 positions away (the other half of the wave).
 __device__ inline float other_half(float x) { return __shfl_xor(x, 32); }

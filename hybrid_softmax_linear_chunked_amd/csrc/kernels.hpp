@@ -17,10 +17,12 @@ struct AttnArgs {
     const void* k2;         // second segment (the current chunk in streaming mode)
     const void* v2;
     int64_t kv2_bh_stride;
-    const float* S;         // linear state: prefix over frames (parallel) or running (stream)
-    const float* Z;
-    int64_t S_bh_stride, S_frame_stride;
-    int64_t Z_bh_stride, Z_frame_stride;
+    // linear state of each chunk as written by the scan kernel: per slot, the image
+    // [P][D][Dphi] (input dtype; phi index in 32-block operand slot order) and Z as
+    // float [P][Dphi]; slot = bh * img_slots + chunk (parallel) or bh (streaming)
+    const void* simg;
+    const float* zimg;
+    int img_slots;
     const void* wq;         // [H, Dphi, D]
     const float* bq;        // [H, Dphi] or null
     float* aux_o_soft;
@@ -32,7 +34,6 @@ struct AttnArgs {
     int stream;             // 0: all chunks of a clip; 1: one streaming chunk
     int s_frames, s_held, s_ls;
     int nchunks, tiles_per_chunk, total_tiles, per_xcd;  // grid bookkeeping (set by the launcher)
-    int s_lds;              // 1: stage S_c in LDS for the combine; 0: read it from memory
     float scale_log2;       // log2(e) / sqrt(D)
 };
 
@@ -53,15 +54,21 @@ struct StateArgs {
     int H, BH, D, n, Dphi, P;
 };
 
-// Running sum over frame partials (state.hip): prefix in place (init == null), or
-// state += partials in frame order.
+// Running sum over frame partials in frame order (state.hip).  Parallel form: the sums
+// start at zero and the state image of chunk c is written once frame ls(c) - 1 has been
+// added.  Streaming form: the sums start from the carried S, Z, which are written back
+// together with the image of the new state.
 struct ScanArgs {
-    float* Sp;
-    float* Zp;
+    const float* Sp;        // [BH, G, F, D]
+    const float* Zp;        // [BH, G, F]
     int G;
-    float* S_state;         // null for the in-place prefix
-    float* Z_state;
-    int BH, F, D;
+    float* S_state;         // [BH, F, D] (streaming) or null (parallel)
+    float* Z_state;         // [BH, F]
+    void* simg;             // images [BH, slots, P, D, Dphi]
+    float* zimg;            // [BH, slots, P, Dphi]
+    int slots;
+    int BH, D, Dphi, P;
+    int T, Tc, To, linear_only;  // chunk schedule (parallel form)
 };
 
 // Copy of frames [f0, f0 + cnt) of a two-segment source into dst frames [0, cnt).
@@ -90,7 +97,7 @@ struct PhiArgs {
 
 hipError_t launch_attn(const AttnArgs& a, int in_dtype, int out_dtype, hipStream_t stream);
 hipError_t launch_state(const StateArgs& a, int in_dtype, hipStream_t stream);
-hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
+hipError_t launch_scan(const ScanArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_phi(const PhiArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_zero(float* p, int64_t count, hipStream_t stream);

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(StateShape<P>::NW * 64) void state_kernel(const Sta
 
     const int ntiles = (n + Tile::BK - 1) / Tile::BK;
     Tile tile;
-    tile.load(src, 0, n, tid);
+    tile.template load<true, false>(src, 0, n, tid);
     tile.store(Ks0, Vs0, tid);
     __syncthreads();
     for (int it = 0; it < ntiles; ++it) {
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(StateShape<P>::NW * 64) void state_kernel(const Sta
         const T* Vs = (it & 1) ? Vs1 : Vs0;
         const int t0 = it * Tile::BK;
         const bool more = it + 1 < ntiles;
-        if (more) tile.load(src, t0 + Tile::BK, n, tid);
+        if (more) tile.template load<true, false>(src, t0 + Tile::BK, n, tid);
         if (active) {
 #pragma unroll
             for (int sub = ts; sub < 2; sub += TS) {
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(StateShape<P>::NW * 64) void state_kernel(const Sta
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const bool valid = t0 + sub * 32 + crow(r, h) < n;
-                    uu[r] = valid ? softplus(u[r] + bias) : 0.f;
+                    uu[r] = valid ? softplus_fast<T>(u[r] + bias) : 0.f;
                     ph[r] = uu[r];
                 }
 #pragma unroll
@@ -165,33 +165,63 @@ __global__ __launch_bounds__(StateShape<P>::NW * 64) void state_kernel(const Sta
     }
 }
 
+template <class T>
 __global__ __launch_bounds__(256) void scan_kernel(const ScanArgs a) {
-    const int64_t per = (int64_t)a.F * a.D + a.F;
+    constexpr int EPL = Mfma<T>::EPL;
+    const int Dphi = a.Dphi, P = a.P, D = a.D, F = Dphi * P;
+    const int64_t per = (int64_t)F * D + F;
     const int bh = blockIdx.y;
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= per) return;
-    float* base;
+    const bool is_s = e < (int64_t)F * D;
+    const float* base;
     int64_t stride;
-    float* state;
-    if (e < (int64_t)a.F * a.D) {
-        base = a.Sp + (int64_t)bh * a.G * a.F * a.D + e;
-        stride = (int64_t)a.F * a.D;
-        state = a.S_state ? a.S_state + (int64_t)bh * a.F * a.D + e : nullptr;
+    float* state = nullptr;
+    int64_t img_off;  // position in one slot of the image (S) or of the Z image
+    if (is_s) {
+        const int f = (int)(e / D), d = (int)(e % D);
+        int j, pw;
+        feat_split(f, Dphi, P, j, pw);
+        base = a.Sp + (int64_t)bh * a.G * F * D + e;
+        stride = (int64_t)F * D;
+        if (a.S_state) state = a.S_state + (int64_t)bh * F * D + e;
+        img_off = ((int64_t)(pw - 1) * D + d) * Dphi + (j / 32) * 32 + slot_pos<EPL>(j % 32);
     } else {
-        const int64_t z = e - (int64_t)a.F * a.D;
-        base = a.Zp + (int64_t)bh * a.G * a.F + z;
-        stride = a.F;
-        state = a.Z_state ? a.Z_state + (int64_t)bh * a.F + z : nullptr;
+        const int f = (int)(e - (int64_t)F * D);
+        int j, pw;
+        feat_split(f, Dphi, P, j, pw);
+        base = a.Zp + (int64_t)bh * a.G * F + f;
+        stride = F;
+        if (a.Z_state) state = a.Z_state + (int64_t)bh * F + f;
+        img_off = (int64_t)(pw - 1) * Dphi + j;
     }
-    if (state) {
+    T* img = reinterpret_cast<T*>(a.simg) + (int64_t)bh * a.slots * F * D;
+    float* zimg = a.zimg + (int64_t)bh * a.slots * F;
+    auto emit = [&](int slot, float v) {
+        if (is_s) img[(int64_t)slot * F * D + img_off] = from_float<T>(v);
+        else zimg[(int64_t)slot * F + img_off] = v;
+    };
+    if (state) {  // streaming: carried state + this step's frames, in frame order
         float acc = *state;
         for (int g = 0; g < a.G; ++g) acc += base[g * stride];
         *state = acc;
-    } else {
-        float acc = 0.f;
-        for (int g = 0; g < a.G; ++g) {
-            acc += base[g * stride];
-            base[g * stride] = acc;
+        emit(0, acc);
+        return;
+    }
+    // chunk-parallel: prefix over frames; chunk c reads the prefix through frame ls(c) - 1
+    const int nc = (a.T + a.Tc - 1) / a.Tc;
+    int c = 0;
+    auto ls_of = [&](int cc) {
+        const int f0 = cc * a.Tc, f1 = min(f0 + a.Tc, a.T);
+        return a.linear_only ? f1 : max(0, f0 - a.To);
+    };
+    while (c < nc && ls_of(c) == 0) ++c;
+    float acc = 0.f;
+    for (int g = 0; g < a.G && c < nc; ++g) {
+        acc += base[g * stride];
+        while (c < nc && ls_of(c) == g + 1) {
+            emit(c, acc);
+            ++c;
         }
     }
 }
@@ -272,10 +302,12 @@ hipError_t launch_state(const StateArgs& a, int in_dtype, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
+hipError_t launch_scan(const ScanArgs& a, int in_dtype, hipStream_t stream) {
     if (a.G <= 0) return hipSuccess;
-    const int64_t per = (int64_t)a.F * a.D + a.F;
-    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((per + 255) / 256), a.BH), dim3(256), 0, stream, a);
+    const int64_t per = (int64_t)a.Dphi * a.P * a.D + (int64_t)a.Dphi * a.P;
+    const dim3 grid((unsigned)((per + 255) / 256), a.BH);
+    if (in_dtype == 1) hipLaunchKernelGGL(scan_kernel<bf16>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(scan_kernel<float>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

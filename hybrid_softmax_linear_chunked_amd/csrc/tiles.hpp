@@ -1,13 +1,12 @@
 // tiles.hpp -- staging of key/value tiles (64 tokens) from HBM into LDS.
 //
-// K is stored row-major (token, d) with one 16-byte chunk of padding per row, which keeps
-// the 32-lane MFMA operand reads (8 tokens x 16 bytes per LDS cycle) free of bank
-// conflicts.  V is stored transposed (d, token) because the value product contracts over
-// tokens: the tokens of each 32-block are kept in slot order (see common.hpp) so one lane
-// reads its EPL operand elements contiguously, and the 16-byte chunks of each row are
-// XOR-swizzled by a function of d so that both the transposing writes (4 token quads x
-// 4 d-chunks per 16 lanes) and the operand reads (8 consecutive d per LDS cycle) spread
-// over distinct banks.
+// K is stored row-major (token, d) and V transposed (d, token), because the value product
+// contracts over tokens; the tokens of each 32-block of V^T are kept in slot order (see
+// common.hpp) so one lane reads its EPL operand elements contiguously.  Both get one
+// 16-byte chunk of padding per row: the MFMA operand reads (8 rows x 16 bytes per LDS
+// cycle) then hit distinct banks, and every operand address is a per-lane base plus a
+// compile-time offset.  The transposing V^T writes are arranged so that the 16 lanes of
+// one LDS cycle write the 16 token quads of one d-row: one full, conflict-free row.
 #pragma once
 
 #include "common.hpp"
@@ -34,8 +33,7 @@ struct KVTile {
     static constexpr int VEC = 16 / sizeof(T);     // elements per 16-byte chunk
     static constexpr int CPR = D / VEC;            // chunks per K row
     static constexpr int KLD = D + VEC;            // padded K row, elements
-    static constexpr int VLD = BK;                 // V^T row, elements (swizzled, no padding)
-    static constexpr int VCPR = BK / VEC;          // chunks per V^T row
+    static constexpr int VLD = BK + VEC;           // padded V^T row, elements
     static constexpr int K_ELEMS = BK * KLD;
     static constexpr int V_ELEMS = D * VLD;
     static constexpr int KCH = BK * CPR;           // K chunks per tile
@@ -47,38 +45,47 @@ struct KVTile {
     uint4 kr[KPT];
     uint4 vr[VPT][4];
 
-    __device__ static inline int vswz(int d) { return ((d % 8) ^ (2 * ((d / 8) % 4))) & (VCPR - 1); }
-
-    // unit u -> (token quad a, d-chunk b): 16 consecutive units cover 4 quads x 4 chunks
+    // unit u -> (token quad a, d-chunk b): 16 consecutive units are the 16 quads of a tile
     __device__ static inline void vunit(int u, int& a, int& b) {
-        a = (u % 4) + 4 * ((u / 16) % 4);
-        b = ((u / 4) % 4) + 4 * (u / 64);
+        a = u % 16;
+        b = u / 16;
     }
 
-    // Issue the global loads of tile tokens [t0, t0+64); tokens >= Lk read as zeros.
+    // Issue the global loads of tile tokens [t0, t0+64).  CHECK: tokens >= Lk read as zeros
+    // (only the last, ragged tile of a window needs it).  TWO: the window spans two
+    // segments (streaming: held overlap frames, then the current chunk).
+    template <bool CHECK, bool TWO>
     __device__ inline void load(const KeySrc<T>& src, int t0, int Lk, int tid) {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int c = tid + i * NT;
-            kr[i] = make_uint4(0, 0, 0, 0);
-            if (c < KCH) {
+            if (CHECK || KCH % NT != 0) kr[i] = make_uint4(0, 0, 0, 0);
+            if (KCH % NT == 0 || c < KCH) {
                 const int row = c / CPR, ch = c % CPR;
                 const int g = t0 + row;
-                if (g < Lk) kr[i] = *reinterpret_cast<const uint4*>(src.krow(g, D) + ch * VEC);
+                if (!CHECK || g < Lk) {
+                    const T* p = TWO ? src.krow(g, D) : src.k1 + (int64_t)g * D;
+                    kr[i] = *reinterpret_cast<const uint4*>(p + ch * VEC);
+                }
             }
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int u = tid + i * NT;
+            if (CHECK || VUN % NT != 0) {
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) vr[i][ii] = make_uint4(0, 0, 0, 0);
-            if (u < VUN) {
+                for (int ii = 0; ii < 4; ++ii) vr[i][ii] = make_uint4(0, 0, 0, 0);
+            }
+            if (VUN % NT == 0 || u < VUN) {
                 int a, b;
                 vunit(u, a, b);
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
                     const int g = t0 + 4 * a + ii;
-                    if (g < Lk) vr[i][ii] = *reinterpret_cast<const uint4*>(src.vrow(g, D) + b * VEC);
+                    if (!CHECK || g < Lk) {
+                        const T* p = TWO ? src.vrow(g, D) : src.v1 + (int64_t)g * D;
+                        vr[i][ii] = *reinterpret_cast<const uint4*>(p + b * VEC);
+                    }
                 }
             }
         }
@@ -115,7 +122,7 @@ struct KVTile {
                     const uint32_t e0 = (w0[jj / 2] >> sh) & 0xFFFFu, e1 = (w1[jj / 2] >> sh) & 0xFFFFu;
                     const uint32_t e2 = (w2[jj / 2] >> sh) & 0xFFFFu, e3 = (w3[jj / 2] >> sh) & 0xFFFFu;
                     uint2 val = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
-                    *reinterpret_cast<uint2*>(Vs + d * VLD + (lc ^ vswz(d)) * 8 + half * 4) = val;
+                    *reinterpret_cast<uint2*>(Vs + d * VLD + lc * 8 + half * 4) = val;
                 }
             } else {
 #pragma unroll
@@ -126,7 +133,7 @@ struct KVTile {
 #pragma unroll
                     for (int jj = 0; jj < VEC; ++jj) {
                         const int d = b * VEC + jj;
-                        Vs[d * VLD + (lc ^ vswz(d)) * VEC + e] = src[jj];
+                        Vs[d * VLD + lc * VEC + e] = src[jj];
                     }
                 }
             }
@@ -141,7 +148,7 @@ struct KVTile {
     __device__ static inline typename Mfma<T>::frag vfrag(const T* Vs, int d, int kb, int t, int h) {
         constexpr int EPL = Mfma<T>::EPL;
         const int pos = kb * 32 + t * 2 * EPL + h * EPL;
-        return Mfma<T>::load(Vs + d * VLD + ((pos / VEC) ^ vswz(d)) * VEC + pos % VEC);
+        return Mfma<T>::load(Vs + d * VLD + pos);
     }
 };
 

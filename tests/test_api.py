@@ -55,11 +55,15 @@ def test_sizes_follow_layouts(L):
     a = lambda x: (x + 255) // 256 * 256
     F = WAN.P * WAN.Dphi
     assert rh.features(WAN) == 256
-    # chunk-parallel: per-frame partials for the 17 frames that enter some chunk's state
-    assert rh.workspace_bytes(WAN) == a(12 * 17 * F * 128 * 4) + a(12 * 17 * F * 4)
-    # streaming: S, Z and two overlap buffers of To frames of K and V, independent of T
+    # chunk-parallel: per-frame partials for the 17 frames that enter some chunk's state,
+    # then one state image (S in bf16 operand order, Z in float) per chunk
+    assert rh.workspace_bytes(WAN) == (a(12 * 17 * F * 128 * 4) + a(12 * 17 * F * 4)
+                                       + a(12 * 7 * F * 128 * 2) + a(12 * 7 * F * 4))
+    # streaming: S, Z, the image of the current state and two overlap buffers of To frames
+    # of K and V, independent of T
     ov = 12 * 1 * 1560 * 128 * 2
-    assert rh.state_bytes(WAN) == a(12 * F * 128 * 4) + a(12 * F * 4) + 4 * a(ov)
+    assert rh.state_bytes(WAN) == (a(12 * F * 128 * 4) + a(12 * F * 4) + a(12 * F * 128 * 2)
+                                   + a(12 * F * 4) + 4 * a(ov))
     assert rh.state_bytes(WAN.with_(T=81)) == rh.state_bytes(WAN)
     assert rh.stream_workspace_bytes(WAN) == a(12 * 3 * F * 128 * 4) + a(12 * 3 * F * 4)
     # one chunk covering the clip has no linear region and needs no workspace
