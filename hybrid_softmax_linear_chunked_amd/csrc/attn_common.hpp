@@ -1,0 +1,248 @@
+// attn_common.hpp -- pieces shared by the attention kernels: which window a workgroup
+// works on, the linear part of the hybrid output (phi_q(q) S_c, phi_q(q) . Z_c) and the
+// shared normalisation (ReHyAt blog, maplevalley.com.cn, sections 2.2.1, 2.2.2 and 2.3).
+#pragma once
+
+#include "tiles.hpp"
+#include "kernels.hpp"
+
+namespace rehyat {
+
+// The chunk a workgroup works on: its queries, its softmax window and its linear state.
+template <class T>
+struct Window {
+    int bh, hh, c, qt;
+    int q0, Lq, Lk, ls;
+    int img_slot;
+    KeySrc<T> src;
+};
+
+// Consecutive logical ids share a chunk and are placed on one XCD: workgroups are dealt
+// round-robin over the 8 XCDs, so id L runs on XCD L / per_xcd.  Returns false for the
+// padding ids of the grid.
+template <class T, int D, bool STREAM>
+__device__ inline bool decode_window(const AttnArgs& a, Window<T>& w) {
+    const int wgid = blockIdx.x;
+    const int L = (wgid % 8) * a.per_xcd + wgid / 8;
+    if (L >= a.total_tiles) return false;
+    w.qt = L % a.tiles_per_chunk;
+    const int rest = L / a.tiles_per_chunk;
+    w.c = rest % a.nchunks;
+    w.bh = rest / a.nchunks;
+    w.hh = w.bh % a.H;
+    const T* kb1 = reinterpret_cast<const T*>(a.k1) + (int64_t)w.bh * a.kv1_bh_stride;
+    const T* vb1 = reinterpret_cast<const T*>(a.v1) + (int64_t)w.bh * a.kv1_bh_stride;
+    if constexpr (!STREAM) {
+        // chunk c = frames [f0, f1); softmax window [max(0, f0 - To), f1); linear [0, ws)
+        const int f0 = w.c * a.Tc;
+        const int f1 = min(f0 + a.Tc, a.T);
+        const int ws = a.linear_only ? f1 : max(0, f0 - a.To);
+        w.q0 = f0 * a.n;
+        w.Lq = (f1 - f0) * a.n;
+        w.Lk = (f1 - ws) * a.n;
+        w.ls = ws;
+        w.src.k1 = kb1 + (int64_t)ws * a.n * D;
+        w.src.v1 = vb1 + (int64_t)ws * a.n * D;
+        w.src.k2 = w.src.k1;
+        w.src.v2 = w.src.v1;
+        w.src.len1 = 1 << 30;
+        w.img_slot = w.bh * a.img_slots + w.c;
+    } else {
+        // one streaming chunk: window = [held overlap frames | this chunk]
+        w.q0 = 0;
+        w.Lq = a.s_frames * a.n;
+        w.Lk = a.linear_only ? 0 : (a.s_held + a.s_frames) * a.n;
+        w.ls = a.s_ls;
+        w.src.k1 = kb1;
+        w.src.v1 = vb1;
+        w.src.k2 = reinterpret_cast<const T*>(a.k2) + (int64_t)w.bh * a.kv2_bh_stride;
+        w.src.v2 = reinterpret_cast<const T*>(a.v2) + (int64_t)w.bh * a.kv2_bh_stride;
+        w.src.len1 = a.s_held * a.n;
+        w.img_slot = w.bh;
+    }
+    return true;
+}
+
+// LDS needed by the epilogue: W_q [Dphi][D + VEC] and one power of the state image
+// [D][Dphi + VEC].
+template <class T, int D>
+__host__ __device__ inline size_t epilogue_lds_bytes(int Dphi) {
+    constexpr int VEC = 16 / sizeof(T);
+    return ((size_t)Dphi * (D + VEC) + (size_t)D * (Dphi + VEC)) * sizeof(T);
+}
+
+// Linear part for the QB query blocks of this wave: u = W_q q on MFMA from the Q operand
+// registers, phi = per-part powers of softplus(u + b); per power the chunk's state image
+// is staged in LDS, y += S_c^T phi on MFMA (phi taken straight from the u registers) and
+// z += phi . Z_c.  Starts with a barrier: the caller's tiles may still be read.
+template <class T, int D, int QB, int NT>
+__device__ inline void linear_part(const AttnArgs& a, const Window<T>& w, unsigned char* smem,
+                                   const typename Mfma<T>::frag (&qf)[QB][D / Mfma<T>::KS],
+                                   f32x16 (&yacc)[D / 32][QB], float (&zq)[QB]) {
+    using M = Mfma<T>;
+    constexpr int KS = M::KS, EPL = M::EPL, NS = D / KS, NDB = D / 32, TPB = 16 / EPL;
+    constexpr int VEC = 16 / sizeof(T);
+    const int tid = threadIdx.x, lane = tid % 64, col = lane % 32, h = lane / 32;
+    const int Dphi = a.Dphi, P = a.P, NJB = Dphi / 32;
+    constexpr int WLD = D + VEC;  // W_q row stride in LDS
+    const int SLD = Dphi + VEC;   // state-image row stride in LDS
+    T* Ws = reinterpret_cast<T*>(smem);
+    T* Ss = Ws + Dphi * WLD;
+    const T* wq = reinterpret_cast<const T*>(a.wq) + (int64_t)w.hh * Dphi * D;
+    const T* img = reinterpret_cast<const T*>(a.simg) + (int64_t)w.img_slot * P * D * Dphi;
+    const float* zimg = a.zimg + (int64_t)w.img_slot * P * Dphi;
+    const float* bq = a.bq ? a.bq + (int64_t)w.hh * Dphi : nullptr;
+
+    __syncthreads();  // every wave is done with the K/V tiles
+    for (int i = tid; i < Dphi * (D / VEC); i += NT) {
+        const int j = i / (D / VEC), ch = i % (D / VEC);
+        *reinterpret_cast<uint4*>(Ws + j * WLD + ch * VEC) = *reinterpret_cast<const uint4*>(wq + (int64_t)j * D + ch * VEC);
+    }
+    __syncthreads();
+    constexpr int JBMAX = 4;  // Dphi <= 128
+    float uu[JBMAX][QB][16];
+#pragma unroll
+    for (int jb = 0; jb < JBMAX; ++jb) {
+        if (jb >= NJB) break;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            f32x16 u = M::mma(M::load(Ws + (jb * 32 + col) * WLD + h * EPL), qf[qb][0], zero16());
+#pragma unroll
+            for (int s = 1; s < NS; ++s) u = M::mma(M::load(Ws + (jb * 32 + col) * WLD + s * KS + h * EPL), qf[qb][s], u);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float x = u[r] + (bq ? bq[jb * 32 + crow(r, h)] : 0.f);
+                uu[jb][qb][r] = softplus_fast<T>(x);
+            }
+        }
+    }
+    for (int pw = 1; pw <= P; ++pw) {
+        __syncthreads();  // W_q / previous power no longer read
+        const T* ip = img + (int64_t)(pw - 1) * D * Dphi;
+        for (int i = tid; i < D * (Dphi / VEC); i += NT) {
+            const int d = i / (Dphi / VEC), ch = i % (Dphi / VEC);
+            *reinterpret_cast<uint4*>(Ss + d * SLD + ch * VEC) = *reinterpret_cast<const uint4*>(ip + (int64_t)d * Dphi + ch * VEC);
+        }
+        __syncthreads();
+        const float* zp = zimg + (pw - 1) * Dphi;
+#pragma unroll
+        for (int jb = 0; jb < JBMAX; ++jb) {
+            if (jb >= NJB) break;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                float ph[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float v = uu[jb][qb][r];
+                    for (int e = 1; e < pw; ++e) v *= uu[jb][qb][r];
+                    ph[r] = v;
+                    zq[qb] += v * zp[jb * 32 + crow(r, h)];
+                }
+#pragma unroll
+                for (int t = 0; t < TPB; ++t) {
+                    const typename M::frag bfr = M::pack(ph + t * EPL);
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const typename M::frag sf = M::load(Ss + (db * 32 + col) * SLD + jb * 32 + t * 2 * EPL + h * EPL);
+                        yacc[db][qb] = M::mma(sf, bfr, yacc[db][qb]);
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) zq[qb] += other_half(zq[qb]);
+}
+
+// out = (2^m O + y) / (2^m l + z), both scaled by 2^-max(m, 0); aux outputs if requested.
+template <class T, class OT, int D, int QB>
+__device__ inline void merge_and_store(const AttnArgs& a, const Window<T>& w, int qw, bool has_soft,
+                                       bool has_lin, const f32x16 (&oacc)[D / 32][QB],
+                                       const f32x16 (&yacc)[D / 32][QB], const float (&m_run)[QB],
+                                       const float (&l_tot)[QB], const float (&zq)[QB]) {
+    constexpr int NDB = D / 32;
+    const int lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
+    OT* outs = reinterpret_cast<OT*>(a.out) + (int64_t)w.bh * a.q_bh_stride + (int64_t)w.q0 * D;
+    const int64_t arow0 = (int64_t)w.bh * a.aux_bh_stride + w.q0;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int row = qw + qb * 32 + col;
+        if (row >= w.Lq) continue;
+        float ca, cg;
+        if (has_soft && has_lin) {
+            const float M2 = fmaxf(m_run[qb], 0.f);
+            const float ea = __builtin_amdgcn_exp2f(m_run[qb] - M2);
+            const float eg = __builtin_amdgcn_exp2f(-M2);
+            const float inv = 1.f / (ea * l_tot[qb] + eg * zq[qb]);
+            ca = ea * inv;
+            cg = eg * inv;
+        } else if (has_soft) {
+            ca = 1.f / l_tot[qb];
+            cg = 0.f;
+        } else {
+            ca = 0.f;
+            cg = 1.f / zq[qb];
+        }
+        OT* orow = outs + (int64_t)row * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = db * 32 + g * 8 + h * 4;
+                float vals[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vals[i] = ca * oacc[db][qb][g * 4 + i] + cg * yacc[db][qb][g * 4 + i];
+                if constexpr (sizeof(OT) == 4) {
+                    *reinterpret_cast<float4*>(orow + d) = make_float4(vals[0], vals[1], vals[2], vals[3]);
+                } else {
+                    bf16x4 o4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o4[i] = (bf16)vals[i];
+                    *reinterpret_cast<bf16x4*>(orow + d) = o4;
+                }
+            }
+        if (a.aux_o_soft || a.aux_y) {
+            const float il = has_soft ? 1.f / l_tot[qb] : 0.f;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int d = db * 32 + g * 8 + h * 4;
+                    float4 so, yo;
+                    so.x = oacc[db][qb][g * 4 + 0] * il; so.y = oacc[db][qb][g * 4 + 1] * il;
+                    so.z = oacc[db][qb][g * 4 + 2] * il; so.w = oacc[db][qb][g * 4 + 3] * il;
+                    yo.x = yacc[db][qb][g * 4 + 0]; yo.y = yacc[db][qb][g * 4 + 1];
+                    yo.z = yacc[db][qb][g * 4 + 2]; yo.w = yacc[db][qb][g * 4 + 3];
+                    if (a.aux_o_soft) *reinterpret_cast<float4*>(a.aux_o_soft + (arow0 + row) * D + d) = so;
+                    if (a.aux_y) *reinterpret_cast<float4*>(a.aux_y + (arow0 + row) * D + d) = yo;
+                }
+        }
+        if (h == 0) {
+            if (a.aux_lse) a.aux_lse[arow0 + row] = has_soft ? m_run[qb] * 0.6931471805599453f + logf(l_tot[qb]) : -INFINITY;
+            if (a.aux_z) a.aux_z[arow0 + row] = zq[qb];
+        }
+    }
+}
+
+// Launch bookkeeping common to the attention kernels.
+inline void attn_grid(AttnArgs& b, int BQ) {
+    const int qlen = b.stream ? b.s_frames * b.n : b.Tc * b.n;
+    b.tiles_per_chunk = (qlen + BQ - 1) / BQ;
+    b.total_tiles = b.tiles_per_chunk * b.nchunks * b.BH;
+    b.per_xcd = (b.total_tiles + 7) / 8;
+}
+
+// Raise the dynamic LDS limit of a kernel once per device (idempotent, so a race between
+// host threads only repeats the call).
+inline hipError_t ensure_lds(const void* fn, size_t lds, size_t (&done)[64]) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (lds > done[dev]) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        done[dev] = lds;
+    }
+    return hipSuccess;
+}
+
+}  // namespace rehyat

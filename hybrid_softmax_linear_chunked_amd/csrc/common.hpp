@@ -133,6 +133,15 @@ __device__ inline float softplus_fast(float x) {
 // Exchange with the lane 32 positions away (the other half of the wave).
 __device__ inline float other_half(float x) { return __shfl_xor(x, 32); }
 
+// max(x[l], x[l ^ 32]) for every lane l, on the VALU: v_permlane32_swap exchanges the upper
+// half of its first operand with the lower half of its second, so with both operands = x
+// the two results hold x[l % 32] and x[32 + l % 32].
+__device__ inline float pair_max(float x) {
+    const int xi = __float_as_int(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+
 template <class T>
 __device__ inline T from_float(float x);
 template <>

@@ -56,6 +56,12 @@ struct KVTile {
     // segments (streaming: held overlap frames, then the current chunk).
     template <bool CHECK, bool TWO>
     __device__ inline void load(const KeySrc<T>& src, int t0, int Lk, int tid) {
+        load_k<CHECK, TWO>(src, t0, Lk, tid);
+        load_v<CHECK, TWO>(src, t0, Lk, tid);
+    }
+
+    template <bool CHECK, bool TWO>
+    __device__ inline void load_k(const KeySrc<T>& src, int t0, int Lk, int tid) {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int c = tid + i * NT;
@@ -69,6 +75,9 @@ struct KVTile {
                 }
             }
         }
+    }
+    template <bool CHECK, bool TWO>
+    __device__ inline void load_v(const KeySrc<T>& src, int t0, int Lk, int tid) {
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int u = tid + i * NT;
@@ -92,6 +101,11 @@ struct KVTile {
     }
 
     __device__ inline void store(T* Ks, T* Vs, int tid) const {
+        store_k(Ks, tid);
+        store_v(Vs, tid);
+    }
+
+    __device__ inline void store_k(T* Ks, int tid) const {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int c = tid + i * NT;
@@ -100,6 +114,9 @@ struct KVTile {
                 *reinterpret_cast<uint4*>(Ks + row * KLD + ch * VEC) = kr[i];
             }
         }
+    }
+
+    __device__ inline void store_v(T* Vs, int tid) const {
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int u = tid + i * NT;
