@@ -203,16 +203,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_kernel(const AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) l_tot[qb] = l_run[qb] + other_half(l_run[qb]);
 
-    f32x16 yacc[NDB][QB];
-    float zq[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        zq[qb] = 0.f;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) yacc[db][qb] = zero16();
-    }
-    if (has_lin) linear_part<T, D, QB, NT>(a, w, smem, qf, yacc, zq);
-    merge_and_store<T, OT, D, QB>(a, w, qw, has_soft, has_lin, oacc, yacc, m_run, l_tot, zq);
+    linear_and_merge<T, OT, D, QB, NT>(a, w, smem, qw, has_soft, has_lin, qf, oacc, m_run, l_tot);
 }
 
 template <class T, class OT, int D, bool STREAM>
@@ -243,10 +234,7 @@ static hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_attn(const AttnArgs& a, int in_dtype, int out_dtype, hipStream_t stream) {
-    if (in_dtype == 1) {
-        if (out_dtype == 1) return a.stream ? launch_d<bf16, bf16, true>(a, stream) : launch_d<bf16, bf16, false>(a, stream);
-        return a.stream ? launch_d<bf16, float, true>(a, stream) : launch_d<bf16, float, false>(a, stream);
-    }
+    if (in_dtype == 1) return launch_attn_wide(a, out_dtype, stream);
     if (out_dtype == 1) return a.stream ? launch_d<float, bf16, true>(a, stream) : launch_d<float, bf16, false>(a, stream);
     return a.stream ? launch_d<float, float, true>(a, stream) : launch_d<float, float, false>(a, stream);
 }

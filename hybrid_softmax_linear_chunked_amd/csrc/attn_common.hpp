@@ -71,14 +71,21 @@ __host__ __device__ inline size_t epilogue_lds_bytes(int Dphi) {
     return ((size_t)Dphi * (D + VEC) + (size_t)D * (Dphi + VEC)) * sizeof(T);
 }
 
-// Linear part for the QB query blocks of this wave: u = W_q q on MFMA from the Q operand
-// registers, phi = per-part powers of softplus(u + b); per power the chunk's state image
-// is staged in LDS, y += S_c^T phi on MFMA (phi taken straight from the u registers) and
-// z += phi . Z_c.  Starts with a barrier: the caller's tiles may still be read.
-template <class T, int D, int QB, int NT>
-__device__ inline void linear_part(const AttnArgs& a, const Window<T>& w, unsigned char* smem,
-                                   const typename Mfma<T>::frag (&qf)[QB][D / Mfma<T>::KS],
-                                   f32x16 (&yacc)[D / 32][QB], float (&zq)[QB]) {
+// Epilogue of the attention kernels, one 32-query block of the wave at a time, so only one
+// block's linear-part registers are live next to the softmax accumulators.
+//
+// Linear part (ReHyAt blog, maplevalley.com.cn, 2.2.2): u = W_q q on MFMA from the Q
+// operand registers, phi = per-part powers of softplus(u + b); per power the chunk's state
+// image is staged in LDS, y += S_c^T phi on MFMA (phi taken straight from the u registers)
+// and z += phi . Z_c.  Merge (2.3): out = (2^m O + y) / (2^m l + z), both scaled by
+// 2^-max(m, 0); aux outputs if requested.  Starts with a barrier: the caller's K/V tiles may
+// still be read.
+template <class T, class OT, int D, int QB, int NT>
+__device__ inline void linear_and_merge(const AttnArgs& a, const Window<T>& w, unsigned char* smem, int qw,
+                                        bool has_soft, bool has_lin,
+                                        const typename Mfma<T>::frag (&qf)[QB][D / Mfma<T>::KS],
+                                        const f32x16 (&oacc)[D / 32][QB], const float (&m_run)[QB],
+                                        const float (&l_tot)[QB]) {
     using M = Mfma<T>;
     constexpr int KS = M::KS, EPL = M::EPL, NS = D / KS, NDB = D / 32, TPB = 16 / EPL;
     constexpr int VEC = 16 / sizeof(T);
@@ -93,87 +100,79 @@ __device__ inline void linear_part(const AttnArgs& a, const Window<T>& w, unsign
     const float* zimg = a.zimg + (int64_t)w.img_slot * P * Dphi;
     const float* bq = a.bq ? a.bq + (int64_t)w.hh * Dphi : nullptr;
 
-    __syncthreads();  // every wave is done with the K/V tiles
-    for (int i = tid; i < Dphi * (D / VEC); i += NT) {
-        const int j = i / (D / VEC), ch = i % (D / VEC);
-        *reinterpret_cast<uint4*>(Ws + j * WLD + ch * VEC) = *reinterpret_cast<const uint4*>(wq + (int64_t)j * D + ch * VEC);
-    }
-    __syncthreads();
-    constexpr int JBMAX = 4;  // Dphi <= 128
-    float uu[JBMAX][QB][16];
-#pragma unroll
-    for (int jb = 0; jb < JBMAX; ++jb) {
-        if (jb >= NJB) break;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            f32x16 u = M::mma(M::load(Ws + (jb * 32 + col) * WLD + h * EPL), qf[qb][0], zero16());
-#pragma unroll
-            for (int s = 1; s < NS; ++s) u = M::mma(M::load(Ws + (jb * 32 + col) * WLD + s * KS + h * EPL), qf[qb][s], u);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float x = u[r] + (bq ? bq[jb * 32 + crow(r, h)] : 0.f);
-                uu[jb][qb][r] = softplus_fast<T>(x);
-            }
+    if (has_lin) {
+        __syncthreads();  // every wave is done with the K/V tiles
+        for (int i = tid; i < Dphi * (D / VEC); i += NT) {
+            const int j = i / (D / VEC), ch = i % (D / VEC);
+            *reinterpret_cast<uint4*>(Ws + j * WLD + ch * VEC) = *reinterpret_cast<const uint4*>(wq + (int64_t)j * D + ch * VEC);
         }
     }
-    for (int pw = 1; pw <= P; ++pw) {
-        __syncthreads();  // W_q / previous power no longer read
-        const T* ip = img + (int64_t)(pw - 1) * D * Dphi;
-        for (int i = tid; i < D * (Dphi / VEC); i += NT) {
-            const int d = i / (Dphi / VEC), ch = i % (Dphi / VEC);
-            *reinterpret_cast<uint4*>(Ss + d * SLD + ch * VEC) = *reinterpret_cast<const uint4*>(ip + (int64_t)d * Dphi + ch * VEC);
-        }
-        __syncthreads();
-        const float* zp = zimg + (pw - 1) * Dphi;
 #pragma unroll
-        for (int jb = 0; jb < JBMAX; ++jb) {
-            if (jb >= NJB) break;
+    for (int qb = 0; qb < QB; ++qb) {
+        f32x16 yacc[NDB];
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                float ph[16];
+        for (int db = 0; db < NDB; ++db) yacc[db] = zero16();
+        float zq = 0.f;
+        if (has_lin) {
+            __syncthreads();  // W_q staged / previous block done with the image
+            constexpr int JBMAX = 4;  // Dphi <= 128
+            float uu[JBMAX][16];
+#pragma unroll
+            for (int jb = 0; jb < JBMAX; ++jb) {
+                if (jb >= NJB) break;
+                f32x16 u = M::mma(M::load(Ws + (jb * 32 + col) * WLD + h * EPL), qf[qb][0], zero16());
+#pragma unroll
+                for (int s = 1; s < NS; ++s) u = M::mma(M::load(Ws + (jb * 32 + col) * WLD + s * KS + h * EPL), qf[qb][s], u);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float v = uu[jb][qb][r];
-                    for (int e = 1; e < pw; ++e) v *= uu[jb][qb][r];
-                    ph[r] = v;
-                    zq[qb] += v * zp[jb * 32 + crow(r, h)];
+                    const float x = u[r] + (bq ? bq[jb * 32 + crow(r, h)] : 0.f);
+                    uu[jb][r] = softplus_fast<T>(x);
                 }
+            }
+            for (int pw = 1; pw <= P; ++pw) {
+                if (pw > 1) __syncthreads();  // previous power no longer read
+                const T* ip = img + (int64_t)(pw - 1) * D * Dphi;
+                for (int i = tid; i < D * (Dphi / VEC); i += NT) {
+                    const int d = i / (Dphi / VEC), ch = i % (Dphi / VEC);
+                    *reinterpret_cast<uint4*>(Ss + d * SLD + ch * VEC) = *reinterpret_cast<const uint4*>(ip + (int64_t)d * Dphi + ch * VEC);
+                }
+                __syncthreads();
+                const float* zp = zimg + (pw - 1) * Dphi;
 #pragma unroll
-                for (int t = 0; t < TPB; ++t) {
-                    const typename M::frag bfr = M::pack(ph + t * EPL);
+                for (int jb = 0; jb < JBMAX; ++jb) {
+                    if (jb >= NJB) break;
+                    float ph[16];
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        const typename M::frag sf = M::load(Ss + (db * 32 + col) * SLD + jb * 32 + t * 2 * EPL + h * EPL);
-                        yacc[db][qb] = M::mma(sf, bfr, yacc[db][qb]);
+                    for (int r = 0; r < 16; ++r) {
+                        float v = uu[jb][r];
+                        for (int e = 1; e < pw; ++e) v *= uu[jb][r];
+                        ph[r] = v;
+                        zq += v * zp[jb * 32 + crow(r, h)];
+                    }
+#pragma unroll
+                    for (int t = 0; t < TPB; ++t) {
+                        const typename M::frag bfr = M::pack(ph + t * EPL);
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db) {
+                            const typename M::frag sf = M::load(Ss + (db * 32 + col) * SLD + jb * 32 + t * 2 * EPL + h * EPL);
+                            yacc[db] = M::mma(sf, bfr, yacc[db]);
+                        }
                     }
                 }
             }
+            zq += other_half(zq);
         }
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) zq[qb] += other_half(zq[qb]);
-}
 
-// out = (2^m O + y) / (2^m l + z), both scaled by 2^-max(m, 0); aux outputs if requested.
-template <class T, class OT, int D, int QB>
-__device__ inline void merge_and_store(const AttnArgs& a, const Window<T>& w, int qw, bool has_soft,
-                                       bool has_lin, const f32x16 (&oacc)[D / 32][QB],
-                                       const f32x16 (&yacc)[D / 32][QB], const float (&m_run)[QB],
-                                       const float (&l_tot)[QB], const float (&zq)[QB]) {
-    constexpr int NDB = D / 32;
-    const int lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
-    OT* outs = reinterpret_cast<OT*>(a.out) + (int64_t)w.bh * a.q_bh_stride + (int64_t)w.q0 * D;
-    const int64_t arow0 = (int64_t)w.bh * a.aux_bh_stride + w.q0;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
         const int row = qw + qb * 32 + col;
         if (row >= w.Lq) continue;
+        OT* outs = reinterpret_cast<OT*>(a.out) + (int64_t)w.bh * a.q_bh_stride + (int64_t)w.q0 * D;
+        const int64_t arow0 = (int64_t)w.bh * a.aux_bh_stride + w.q0;
         float ca, cg;
         if (has_soft && has_lin) {
             const float M2 = fmaxf(m_run[qb], 0.f);
             const float ea = __builtin_amdgcn_exp2f(m_run[qb] - M2);
             const float eg = __builtin_amdgcn_exp2f(-M2);
-            const float inv = 1.f / (ea * l_tot[qb] + eg * zq[qb]);
+            const float inv = 1.f / (ea * l_tot[qb] + eg * zq);
             ca = ea * inv;
             cg = eg * inv;
         } else if (has_soft) {
@@ -181,7 +180,7 @@ __device__ inline void merge_and_store(const AttnArgs& a, const Window<T>& w, in
             cg = 0.f;
         } else {
             ca = 0.f;
-            cg = 1.f / zq[qb];
+            cg = 1.f / zq;
         }
         OT* orow = outs + (int64_t)row * D;
 #pragma unroll
@@ -191,7 +190,7 @@ __device__ inline void merge_and_store(const AttnArgs& a, const Window<T>& w, in
                 const int d = db * 32 + g * 8 + h * 4;
                 float vals[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) vals[i] = ca * oacc[db][qb][g * 4 + i] + cg * yacc[db][qb][g * 4 + i];
+                for (int i = 0; i < 4; ++i) vals[i] = ca * oacc[db][qb][g * 4 + i] + cg * yacc[db][g * 4 + i];
                 if constexpr (sizeof(OT) == 4) {
                     *reinterpret_cast<float4*>(orow + d) = make_float4(vals[0], vals[1], vals[2], vals[3]);
                 } else {
@@ -211,15 +210,15 @@ __device__ inline void merge_and_store(const AttnArgs& a, const Window<T>& w, in
                     float4 so, yo;
                     so.x = oacc[db][qb][g * 4 + 0] * il; so.y = oacc[db][qb][g * 4 + 1] * il;
                     so.z = oacc[db][qb][g * 4 + 2] * il; so.w = oacc[db][qb][g * 4 + 3] * il;
-                    yo.x = yacc[db][qb][g * 4 + 0]; yo.y = yacc[db][qb][g * 4 + 1];
-                    yo.z = yacc[db][qb][g * 4 + 2]; yo.w = yacc[db][qb][g * 4 + 3];
+                    yo.x = yacc[db][g * 4 + 0]; yo.y = yacc[db][g * 4 + 1];
+                    yo.z = yacc[db][g * 4 + 2]; yo.w = yacc[db][g * 4 + 3];
                     if (a.aux_o_soft) *reinterpret_cast<float4*>(a.aux_o_soft + (arow0 + row) * D + d) = so;
                     if (a.aux_y) *reinterpret_cast<float4*>(a.aux_y + (arow0 + row) * D + d) = yo;
                 }
         }
         if (h == 0) {
             if (a.aux_lse) a.aux_lse[arow0 + row] = has_soft ? m_run[qb] * 0.6931471805599453f + logf(l_tot[qb]) : -INFINITY;
-            if (a.aux_z) a.aux_z[arow0 + row] = zq[qb];
+            if (a.aux_z) a.aux_z[arow0 + row] = zq;
         }
     }
 }

@@ -1,0 +1,493 @@
+// attn_wide.hip -- bf16 windowed softmax tile kernel, 64 queries per wave, with the linear
+// part and the shared normalisation fused into its epilogue (ReHyAt blog,
+// maplevalley.com.cn, sections 2.2.1-2.3).
+//
+// One workgroup = 4 waves x 64 queries (two 32-query blocks per wave) of one chunk of one
+// (batch, head), one wave per SIMD with the whole register file.  Every K or V operand read
+// from LDS feeds two MFMAs (one per query block): half the LDS read traffic per product of
+// a 32-query wave, which is what bounds that layout on this part.
+//
+// The window is swept in 32-token sub-steps.  Sub-step u runs
+//   (a) S_{u+1}^T = K_{u+1} Q^T          on the matrix core (scores one sub-step ahead),
+//   (b) softmax of S_u^T -> P_u           on the vector ALU, overlapping (a),
+//   (c) O^T += V_u^T P_u^T                on the matrix core.
+// K and V are staged through LDS in 64-token tiles: K in a ring of three slots (the
+// look-ahead of (a) reaches into the next tile), V in two.  The loads of K_{t+2} and
+// V_{t+1} are issued at the top of tile t and written to LDS at its bottom.
+//
+// Softmax reference: scores are taken in the log2 domain against one fixed reference per
+// query, the maximum of its first sub-step, so p = exp2(s*log2(e)/sqrt(D) - m) and O is
+// never rescaled.  Any fixed m gives the exact result, because the final normalisation
+// uses the same m; the only risk is range.  The row sum bounds every p, so a sum above
+// 2^64 (or an infinite one) sends the workgroup through a second pass whose reference is
+// the exact row maximum, found by a score-only sweep over the window.  Row sums are taken
+// from the bf16 P actually fed to the value product (dot2 against ones), so numerator
+// and denominator see the same rounded weights.
+#include <type_traits>
+
+#include "attn_common.hpp"
+
+namespace rehyat {
+
+static constexpr float kWideSumLimit = 18446744073709551616.0f;  // 2^64
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// sum of the 8 bf16 of an operand, accumulated in fp32
+__device__ inline float sum8(bf16x8 v, float acc) {
+    const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+    return acc;
+}
+
+// Byte address within the workgroup's LDS of a pointer into it.
+__device__ inline uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One LDS-DMA instruction (global_load_lds_dwordx4): lane l copies 16 bytes from its HBM
+// address to LDS bytes [lds + 16 l, +16).  Issued from assembly so that the compiler does
+// not take every later LDS read for a possible reader of the copy (it would wait for the
+// copy in flight before the first such read and serialise the tile pipeline); completion is
+// tracked by the explicit vmcnt waits of the pipeline instead.  The instruction has no
+// register result and consumes its address operands at issue; M0 carries the LDS base and
+// needs one wait state before the copy reads it.
+__device__ inline void dma16_s(const void* gbase, uint32_t voff, uint32_t lds) {  // uniform base + lane offset
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ inline void dma16_v(const void* gaddr, uint32_t lds) {  // per-lane address
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds)
+                 : "memory", "m0");
+}
+
+// K/V tiles of 64 tokens moved HBM -> LDS by the LDS-DMA path (global_load_lds_dwordx4):
+// no registers, no LDS write instructions, and the copy of tile t+2 runs while tile t is
+// computed.  One DMA instruction fills 1 KB of LDS, lane l writing bytes [16l, 16l+16), so
+// a tile is a sequence of 16-byte chunks and each lane picks the HBM chunk for its slot.
+//   K: rows of D + 8 elements (one chunk of padding), read as MFMA A operands with one
+//      ds_read_b128 per operand at compile-time offsets, conflict-free.
+//   V: row-major rows of VLD elements, VLD chosen so that four consecutive rows start in
+//      four different 64-byte bank groups; the value product reads V^T operands with
+//      ds_read_b64_tr_b16, which hands lane i of each 16-lane group element i%4 of the
+//      chunks addressed by lanes i/4 + 4r (r = 0..3): lanes pointing at a 4-token x 16-d
+//      block receive it transposed, one d column of four tokens per lane.
+// Padding chunks are filled with a copy of the row's first chunk, so every lane of every
+// DMA instruction is active and the per-tile work is a uniform base plus fixed lane
+// offsets.  Tokens past the window (ragged last tile) are clamped to the last token: their
+// scores are masked in the softmax, so only finite values are needed there.
+template <int D, int NW>
+struct DmaTiles {
+    using T = bf16;
+    static constexpr int BK = 64;
+    static constexpr int KLD = D + 8;
+    static constexpr int VLD = D == 128 ? 160 : D == 64 ? 96 : 32;
+    static constexpr int CPK = KLD / 8, CPV = VLD / 8;  // 16-byte chunks per row
+    static constexpr int NIK = BK * CPK / 64, NIV = BK * CPV / 64;  // DMA instructions per tile
+    static constexpr int PWK = (NIK + NW - 1) / NW, PWV = (NIV + NW - 1) / NW;
+    static constexpr int K_ELEMS = BK * KLD, V_ELEMS = BK * VLD;
+    static_assert(BK * CPK % 64 == 0 && BK * CPV % 64 == 0, "tile is not a whole number of DMA instructions");
+
+    uint32_t koff[PWK], voff[PWV];  // element offset of this lane's chunk within a tile
+
+    __device__ static inline uint32_t chunk_off(int q, int cpr, int dchunks) {
+        const int row = q / cpr, c = q % cpr;
+        return (uint32_t)(row * D + (c < dchunks ? c : 0) * 8);
+    }
+    __device__ inline void init(int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < PWK; ++i) koff[i] = chunk_off((wave + i * NW) * 64 + lane, CPK, D / 8);
+#pragma unroll
+        for (int i = 0; i < PWV; ++i) voff[i] = chunk_off((wave + i * NW) * 64 + lane, CPV, D / 8);
+    }
+    // one lane's HBM chunk for tile tokens from t0; CHECK clamps to the window, TWO picks the
+    // segment of the two-segment (streaming) window
+    template <bool CHECK, bool TWO>
+    __device__ static inline const T* src_chunk(const T* b1, const T* b2, int len1, int t0, int Lk, uint32_t off) {
+        int g = t0 + (int)(off / D);
+        if (CHECK) g = min(g, Lk - 1);
+        const uint32_t col = off % D;
+        if (TWO && g >= len1) return b2 + (int64_t)(g - len1) * D + col;
+        return b1 + (int64_t)g * D + col;
+    }
+    template <bool CHECK, bool TWO, int NI, int PW>
+    __device__ static inline void issue(const T* b1, const T* b2, int len1, int t0, int Lk, T* dst, int wave,
+                                        const uint32_t (&off)[PW]) {
+#pragma unroll
+        for (int i = 0; i < PW; ++i) {
+            const int j = wave + i * NW;
+            if (NI % NW != 0 && j >= NI) break;
+            const uint32_t lds = lds_addr(dst + j * 512);
+            if (!CHECK && !TWO) dma16_s(b1 + (int64_t)t0 * D, off[i] * (uint32_t)sizeof(T), lds);
+            else dma16_v(src_chunk<CHECK, TWO>(b1, b2, len1, t0, Lk, off[i]), lds);
+        }
+    }
+    template <bool CHECK, bool TWO>
+    __device__ inline void issue_k(const KeySrc<T>& src, int t0, int Lk, T* Ks, int wave) const {
+        issue<CHECK, TWO, NIK, PWK>(src.k1, src.k2, src.len1, t0, Lk, Ks, wave, koff);
+    }
+    template <bool CHECK, bool TWO>
+    __device__ inline void issue_v(const KeySrc<T>& src, int t0, int Lk, T* Vs, int wave) const {
+        issue<CHECK, TWO, NIV, PWV>(src.v1, src.v2, src.len1, t0, Lk, Vs, wave, voff);
+    }
+
+    // A operand of (keys x d) products: keys kb*32 + col, contraction step s over d
+    __device__ static inline bf16x8 kfrag(const T* Ks, int kb, int s, int col, int h) {
+        return *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + col) * KLD + s * 16 + h * 8);
+    }
+    // per-lane part of the V^T operand address: token 4h + a/4, d 16*(g%2) + 4*(a%4) for
+    // lane = 16g + a
+    __device__ static inline int vlane(int lane) {
+        const int g = lane / 16, a = lane % 16;
+        return (4 * (g / 2) + a / 4) * VLD + 16 * (g % 2) + 4 * (a % 4);
+    }
+    // V^T operand (d = db*32 + lane%32; tokens kb*32 + 16t + {4h..4h+3} and the same + 8:
+    // the contraction slots of the C-layout P operand of step t)
+    __device__ static inline bf16x8 vfrag(const T* Vs, int vl, int db, int kb, int t) {
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+        const T* p = Vs + vl + (kb * 32 + 16 * t) * VLD + db * 32;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p + 8 * VLD));
+        const v4i16 both_lo = lo, both_hi = hi;
+        typedef short v8i16 __attribute__((ext_vector_type(8)));
+        const v8i16 all = __builtin_shufflevector(both_lo, both_hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, all);
+    }
+};
+
+template <class OT, int D, bool STREAM>
+__global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
+    using T = bf16;
+    using M = Mfma<T>;
+    constexpr int QB = 2, NW = 4, NT = NW * 64, BQ = NW * QB * 32;
+    using Tile = DmaTiles<D, NW>;
+    constexpr int KS = M::KS, EPL = M::EPL, NS = D / KS, NDB = D / 32;
+    constexpr int TPB = 32 / KS;  // value-product steps per 32-token sub-step
+    constexpr int BK = Tile::BK;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    T* const kring = reinterpret_cast<T*>(smem);
+    T* const vring = kring + 4 * Tile::K_ELEMS;
+
+    Window<T> w;
+    if (!decode_window<T, D, STREAM>(a, w)) return;
+    if (w.qt * BQ >= w.Lq) return;
+    const int Lk = w.Lk;
+    const bool has_lin = w.ls > 0;
+    const bool has_soft = Lk > 0;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform
+    const int lane = tid % 64, col = lane % 32, h = lane / 32;
+    const int qw = w.qt * BQ + wave * QB * 32;
+    const bool wave_live = qw < w.Lq;
+    const T* qs = reinterpret_cast<const T*>(a.q) + (int64_t)w.bh * a.q_bh_stride + (int64_t)w.q0 * D;
+
+    typename M::frag qf[QB][NS];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int row = qw + qb * 32 + col;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            if (row < w.Lq) {
+                qf[qb][s] = M::load(qs + (int64_t)row * D + s * KS + h * EPL);
+            } else {
+                float zz[EPL];
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) zz[e] = 0.f;
+                qf[qb][s] = M::pack(zz);
+            }
+        }
+    }
+
+    const float sc = a.scale_log2;
+    const int nt = (Lk + BK - 1) / BK;    // 64-token tiles
+    const int nsub = (Lk + 31) / 32;      // 32-token sub-steps
+    const int tail = Lk % 32;             // valid tokens of a ragged last sub-step
+    const bool ragged = Lk % BK != 0;
+    Tile tile;
+    tile.init(wave, lane);
+    const int vl = Tile::vlane(lane);
+
+    auto kslot = [&](int t) { return kring + (t & 3) * Tile::K_ELEMS; };
+    auto vslot = [&](int t) { return vring + (t % 3) * Tile::V_ELEMS; };
+    // start the DMA of K / V tile t into the given slot (completion: vmcnt + barrier)
+    auto dma_k = [&](int t, T* dst) {
+        if (ragged && t == nt - 1) tile.template issue_k<true, STREAM>(w.src, t * BK, Lk, dst, wave);
+        else tile.template issue_k<false, STREAM>(w.src, t * BK, Lk, dst, wave);
+    };
+    auto dma_v = [&](int t, T* dst) {
+        if (ragged && t == nt - 1) tile.template issue_v<true, STREAM>(w.src, t * BK, Lk, dst, wave);
+        else tile.template issue_v<false, STREAM>(w.src, t * BK, Lk, dst, wave);
+    };
+    // DMA writes of this wave complete, then every wave's are visible
+    auto dma_sync = [&]() {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+    };
+    // End of a full tile: the DMA batch issued one tile earlier is complete in every wave.
+    // Vector memory operations complete in issue order, so a wave waits until no more than
+    // the batch it issued this tile (counted for the wave with the fewest DMA instructions)
+    // is outstanding.  The barrier is a bare s_barrier: a workgroup fence would wait for
+    // this tile's batch as well.  The memory clobber keeps LDS accesses on their side.
+    auto tile_sync = [&](bool k_issued, bool v_issued) {
+        constexpr int NKMIN = Tile::NIK / NW, NVMIN = Tile::NIV / NW;
+        static_assert(NKMIN + NVMIN <= 15, "vmcnt immediate range");
+        if (k_issued && v_issued) __builtin_amdgcn_s_waitcnt(0x0070 | (NKMIN + NVMIN));  // + lgkmcnt(0)
+        else if (v_issued) __builtin_amdgcn_s_waitcnt(0x0070 | NVMIN);
+        else __builtin_amdgcn_s_waitcnt(0x0070);
+        asm volatile("s_barrier" ::: "memory");
+    };
+
+    // S^T of sub-step u (keys 32u.., both query blocks) from the K tile at Ks.  Keys past
+    // the window read as zeros here; the softmax masks them.
+    auto qk = [&](const T* Ks, int u, f32x16 (&S)[QB]) {
+        const int kb = u & 1;
+        typename M::frag ka = Tile::kfrag(Ks, kb, 0, col, h), kn;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            if (s + 1 < NS) kn = Tile::kfrag(Ks, kb, s + 1, col, h);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) S[qb] = M::mma(ka, qf[qb][s], s == 0 ? zero16() : S[qb]);
+            if (s + 1 < NS) ka = kn;
+        }
+    };
+    // row maxima of sub-step u's scores (log2 units), keys past the window excluded
+    auto rowmax = [&](int u, const f32x16 (&S)[QB], float (&mx)[QB]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (32 * u + crow(r, h) < Lk) mx[qb] = fmaxf(mx[qb], S[qb][r]);
+    };
+
+    f32x16 oacc[NDB][QB];
+    float m_ref[QB], l_run[QB];
+
+    // O^T += V_u^T P_u^T, one MFMA per fence-separated segment, the next V operand read
+    // issued one product ahead
+    auto pv_product = [&](int u, const typename M::frag (&pf)[TPB][QB]) {
+        const T* Vs = vslot(u >> 1);
+        const int kb = u & 1;
+        constexpr int NV = TPB * NDB;
+        typename M::frag va = Tile::vfrag(Vs, vl, 0, kb, 0), vn;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int db = i % NDB, t = i / NDB;
+            if (i + 1 < NV) vn = Tile::vfrag(Vs, vl, (i + 1) % NDB, kb, (i + 1) / NDB);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = M::mma(va, pf[t][qb], oacc[db][qb]);
+            if (i + 1 < NV) va = vn;
+        }
+    };
+
+    // softmax of one 8-value slice (query block qb, value-product step t) of S_u^T -> P
+    auto soft8 = [&](const f32x16 (&Sc)[QB], int qb, int t, typename M::frag (&pf)[TPB][QB], float (&lsum)[QB],
+                     auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        float pv[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[qb][t * EPL + e], sc, -m_ref[qb]));
+            if (MASK && crow(t * EPL + e, h) >= tail) pv[e] = 0.f;
+        }
+        pf[t][qb] = M::pack(pv);
+        lsum[qb] = sum8(pf[t][qb], lsum[qb]);
+    };
+
+    // K operands of the look-ahead scores, read one sub-step before their products so the
+    // LDS latency is covered by a whole sub-step of work (one wave per SIMD has no other
+    // wave to hide it behind)
+    typename M::frag kpre[NS];
+    auto read_k = [&](int u) {
+        const T* Ks = kslot(u >> 1);
+#pragma unroll
+        for (int st = 0; st < NS; ++st) kpre[st] = Tile::kfrag(Ks, u & 1, st, col, h);
+    };
+
+    // Sub-step u of a full tile (u+1 exists, kpre holds its K operands), one basic block
+    // cut by scheduling fences into
+    //   V operand reads of u | scores of u+1 with the softmax of u | K operand reads of u+2 |
+    //   value product of u.
+    // The scores and the softmax are written as 16 segments [MFMA, 1/16 of the softmax]; the
+    // compiler's MFMA/exp interleaving places the vector work between the products.  The
+    // K reads of u+2 stay inside the tile ring: u+2 lies at most in the last tile.
+    auto sub_full = [&](int u, f32x16 (&Sc)[QB], f32x16 (&Sn)[QB]) {
+        const T* Vs = vslot(u >> 1);
+        constexpr int NV = TPB * NDB;
+        typename M::frag vf[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) vf[i] = Tile::vfrag(Vs, vl, i % NDB, u & 1, i / NDB);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_iglp_opt(3);
+        typename M::frag pf[TPB][QB];
+        float lsum[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) lsum[qb] = l_run[qb];
+        float pv[QB * 16];
+        constexpr int NSEG = NS * QB;
+        constexpr int PER = QB * 16 / NSEG;  // softmax values per segment
+#pragma unroll
+        for (int i = 0; i < NSEG; ++i) {
+            const int st = i / QB, qb = i % QB;
+            Sn[qb] = M::mma(kpre[st], qf[qb][st], st == 0 ? zero16() : Sn[qb]);
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+                const int idx = i * PER + e, q2 = idx / 16, r = idx % 16;
+                pv[idx] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[q2][r], sc, -m_ref[q2]));
+                if ((idx + 1) % EPL == 0) {
+                    const int t = r / EPL;
+                    pf[t][q2] = M::pack(pv + idx + 1 - EPL);
+                    lsum[q2] = sum8(pf[t][q2], lsum[q2]);
+                }
+            }
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) l_run[qb] = lsum[qb];
+        __builtin_amdgcn_sched_barrier(0);
+        read_k(u + 2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int db = i % NDB, t = i / NDB;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = M::mma(vf[i], pf[t][qb], oacc[db][qb]);
+        }
+    };
+
+    // Sub-step u of the last tile (general form): scores of u+1 if any, softmax of u with
+    // the ragged keys masked if MASK, value product.
+    auto sub_last = [&](int u, f32x16 (&Sc)[QB], f32x16 (&Sn)[QB], auto mask_tag) {
+        if (u + 1 < nsub) qk(kslot((u + 1) >> 1), u + 1, Sn);
+        typename M::frag pf[TPB][QB];
+        float lsum[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) lsum[qb] = l_run[qb];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int t = 0; t < TPB; ++t) soft8(Sc, qb, t, pf, lsum, mask_tag);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) l_run[qb] = lsum[qb];
+        pv_product(u, pf);
+    };
+
+    f32x16 SA[QB], SB[QB];
+    // one sweep of the window with the current reference; returns the row sums
+    auto run = [&](bool first, float (&l_tot)[QB]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            l_run[qb] = 0.f;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[db][qb] = zero16();
+        }
+        if (nt > 0) {
+            // prologue: K_0, V_0, K_1 staged; scores of sub-step 0
+            // prologue: K_0, V_0, K_1 in LDS; K_2 and V_1 in flight (the batch of tile -1)
+            dma_k(0, kslot(0));
+            dma_v(0, vslot(0));
+            if (nt > 1) dma_k(1, kslot(1));
+            dma_sync();
+            if (nt > 2) dma_k(2, kslot(2));
+            if (nt > 1) dma_v(1, vslot(1));
+            if (wave_live) {
+                qk(kslot(0), 0, SA);
+                if (nsub > 1) read_k(1);
+                if (first) {
+                    float mx[QB] = {-INFINITY, -INFINITY};
+                    rowmax(0, SA, mx);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) m_ref[qb] = pair_max(mx[qb]) * sc;
+                }
+            }
+            // full tiles: tile t holds sub-steps 2t and 2t+1, neither of them ragged
+            for (int t = 0; t + 1 < nt; ++t) {
+                // batch of tile t: K_{t+3} and V_{t+2}, into the slots tile t-1 used
+                const bool kis = t + 3 < nt, vis = t + 2 < nt;
+                if (kis) dma_k(t + 3, kslot(t + 3));
+                if (vis) dma_v(t + 2, vslot(t + 2));
+                if (wave_live) {
+                    sub_full(2 * t, SA, SB);
+                    sub_full(2 * t + 1, SB, SA);
+                }
+                tile_sync(kis, vis);
+            }
+            // last tile: one or two sub-steps, the last of them possibly ragged
+            if (wave_live) {
+                const int u0 = 2 * (nt - 1);
+                if (tail != 0 && u0 == nsub - 1) sub_last(u0, SA, SB, std::true_type{});
+                else sub_last(u0, SA, SB, std::false_type{});
+                if (u0 + 1 < nsub) {
+                    if (tail != 0) sub_last(u0 + 1, SB, SA, std::true_type{});
+                    else sub_last(u0 + 1, SB, SA, std::false_type{});
+                }
+            }
+        }
+        bool over = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            l_tot[qb] = l_run[qb] + other_half(l_run[qb]);
+            over = over || (wave_live && l_tot[qb] > kWideSumLimit);
+        }
+        return __syncthreads_or(over);
+    };
+
+    float l_tot[QB];
+    if (run(true, l_tot)) {
+        // exact row maxima by a score-only sweep, as the reference of a second sweep
+        float mx[QB] = {-INFINITY, -INFINITY};
+        for (int t = 0; t < nt; ++t) {
+            dma_k(t, kslot(0));
+            dma_sync();
+            if (wave_live) {
+                for (int u = 2 * t; u < 2 * t + 2 && u < nsub; ++u) {
+                    qk(kslot(0), u, SA);
+                    rowmax(u, SA, mx);
+                }
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) m_ref[qb] = pair_max(mx[qb]) * sc;
+        run(false, l_tot);
+    }
+
+    linear_and_merge<T, OT, D, QB, NT>(a, w, smem, qw, has_soft, has_lin, qf, oacc, m_ref, l_tot);
+}
+
+template <class OT, int D, bool STREAM>
+static hipError_t launch_wide_one(const AttnArgs& a, hipStream_t stream) {
+    constexpr int NW = 4, QB = 2;
+    using Tile = DmaTiles<D, NW>;
+    const size_t kv = (4 * (size_t)Tile::K_ELEMS + 3 * (size_t)Tile::V_ELEMS) * sizeof(bf16);
+    const size_t epi = epilogue_lds_bytes<bf16, D>(a.Dphi);
+    const size_t lds = kv > epi ? kv : epi;
+    auto fn = attn_wide_kernel<OT, D, STREAM>;
+    static size_t lds_set[64] = {};
+    hipError_t e = ensure_lds(reinterpret_cast<const void*>(fn), lds, lds_set);
+    if (e != hipSuccess) return e;
+    AttnArgs b = a;
+    attn_grid(b, NW * QB * 32);
+    hipLaunchKernelGGL(fn, dim3(8 * b.per_xcd), dim3(NW * 64), lds, stream, b);
+    return hipGetLastError();
+}
+
+template <class OT, bool STREAM>
+static hipError_t launch_wide_d(const AttnArgs& a, hipStream_t stream) {
+    switch (a.D) {
+        case 32: return launch_wide_one<OT, 32, STREAM>(a, stream);
+        case 64: return launch_wide_one<OT, 64, STREAM>(a, stream);
+        case 128: return launch_wide_one<OT, 128, STREAM>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_attn_wide(const AttnArgs& a, int out_dtype, hipStream_t stream) {
+    if (out_dtype == 1) return a.stream ? launch_wide_d<bf16, true>(a, stream) : launch_wide_d<bf16, false>(a, stream);
+    return a.stream ? launch_wide_d<float, true>(a, stream) : launch_wide_d<float, false>(a, stream);
+}
+
+}  // namespace rehyat

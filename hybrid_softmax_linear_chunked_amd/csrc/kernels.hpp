@@ -96,6 +96,7 @@ struct PhiArgs {
 };
 
 hipError_t launch_attn(const AttnArgs& a, int in_dtype, int out_dtype, hipStream_t stream);
+hipError_t launch_attn_wide(const AttnArgs& a, int out_dtype, hipStream_t stream);
 hipError_t launch_state(const StateArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t stream);
