@@ -170,3 +170,62 @@ def test_stream_checkpoint_restore():
     torch.cuda.synchronize()
     for r, g in zip(ref, got):
         assert torch.equal(r, g)
+
+
+def _far_score_inputs(p, seed):
+    """Queries sharing a large positive mean and one all-3 key per frame at frame offset 45,
+    past the first 32 keys of every window: those keys score about 2^90 (log2 units) above
+    the keys at the start of their windows."""
+    from synth_inputs import round_bf16
+    x = rand_inputs(p, seed=seed)
+    q = x["q"] * np.float32(0.3) + np.float32(2.0)
+    k = x["k"].copy()
+    for f in range(p.T):
+        k[:, :, f * p.n + 45, :] = 3.0
+    if p.in_dtype == BF16:
+        q = round_bf16(q)
+    x["q"], x["k"] = q, k
+    return x
+
+
+@pytest.mark.parametrize("dt", [BF16, FP32], ids=["bf16", "f32"])
+def test_scores_far_above_window_start(dt):
+    """The bf16 kernel takes its softmax reference from the first 32 keys of a window; with
+    the planted keys every row sum overflows its range check and the window is swept again
+    against the exact row maximum.  The fp32 kernel rescales its running maximum instead.
+    Both must match the oracle, the log-sum-exp included (ReHyAt blog, maplevalley.com.cn,
+    2.2.1)."""
+    p = rh.Params(1, 2, 128, 7, 100, 3, 1, 128, 2, 0, dt, dt)
+    x = _far_score_inputs(p, seed=5)
+    q, k = x["q"], x["k"]
+    d = to_dev(x, p)
+    out, aux = run_parallel(p, d)
+    torch.cuda.synchronize()
+    op = oracle_params(p)
+    ref, rax = oracle.parallel(op, x["q"], x["k"], x["v"], x["wq"], x["wk"], None, None, aux=True)
+    # the planted keys' margin over the window start exceeds 64 log2 units
+    s = (q[0, 0, 0].astype(np.float64) @ k[0, 0, 45].astype(np.float64)) / np.sqrt(p.D) * np.log2(np.e)
+    s0 = (k[0, 0, :32].astype(np.float64) @ q[0, 0, 0].astype(np.float64)).max() / np.sqrt(p.D) * np.log2(np.e)
+    assert s - s0 > 64
+    tol = TOL[dt]
+    assert slab_err(out.float().cpu().numpy(), ref) <= tol
+    assert slab_err(aux["o_soft"].cpu().numpy(), rax["osoft"]) <= tol
+    assert np.abs(aux["lse"].cpu().numpy() - rax["lse"]).max() <= tol * np.abs(rax["lse"]).max()
+
+
+def test_stream_equals_parallel_far_scores():
+    """The streaming kernel takes the same second sweep on the same windows: bitwise equal to
+    the chunk-parallel output on the planted far-score inputs."""
+    p = rh.Params(1, 2, 128, 7, 100, 3, 1, 128, 2, 0, BF16, BF16)
+    x = _far_score_inputs(p, seed=6)
+    d = to_dev(x, p)
+    par = run_parallel(p, d, aux=False)
+    st = rh.Stream(p, d["wq"], d["wk"])
+    outs = []
+    for f0 in range(0, p.T, p.Tc):
+        f1 = min(f0 + p.Tc, p.T)
+        sl = slice(f0 * p.n, f1 * p.n)
+        outs.append(st.step(d["q"][:, :, sl].contiguous(), d["k"][:, :, sl].contiguous(),
+                            d["v"][:, :, sl].contiguous(), f1 - f0))
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(outs, dim=2), par)
