@@ -53,15 +53,22 @@ __device__ inline uint32_t lds_addr(const void* p) {
 // not take every later LDS read for a possible reader of the copy (it would wait for the
 // copy in flight before the first such read and serialise the tile pipeline); completion is
 // tracked by the explicit vmcnt waits of the pipeline instead.  The instruction has no
-// register result and consumes its address operands at issue; M0 carries the LDS base and
-// needs one wait state before the copy reads it.
+// register result and reads its address operands and M0 (the LDS base, one wait state
+// after it is written) at issue; M0 is saved and restored around it.
 __device__ inline void dma16_s(const void* gbase, uint32_t voff, uint32_t lds) {  // uniform base + lane offset
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(lds)
-                 : "memory", "m0");
+    uint32_t keep;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+        : "=&s"(keep)
+        : "v"(voff), "s"(gbase), "s"(lds)
+        : "memory");
 }
 __device__ inline void dma16_v(const void* gaddr, uint32_t lds) {  // per-lane address
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds)
-                 : "memory", "m0");
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep)
+                 : "v"(gaddr), "s"(lds)
+                 : "memory");
 }
 
 // K/V tiles of 64 tokens moved HBM -> LDS by the LDS-DMA path (global_load_lds_dwordx4):
@@ -205,22 +212,34 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
 
     const float sc = a.scale_log2;
     const int nt = (Lk + BK - 1) / BK;    // 64-token tiles
-    const int nsub = (Lk + 31) / 32;      // 32-token sub-steps
-    const int tail = Lk % 32;             // valid tokens of a ragged last sub-step
     const bool ragged = Lk % BK != 0;
+    // Tiles are processed last one first: position i of the sweep holds window tile
+    // tile_of(i), so the only ragged tile (and the masking it needs) comes before the
+    // steady-state loop, which then sees full tiles only.  The softmax sums over keys, so
+    // the order is free.
+    auto tile_of = [&](int i) { return i == 0 ? nt - 1 : i - 1; };
+    const int last_len = Lk - (nt - 1) * BK;  // valid keys of the last tile, 1..64
+    // valid keys of sweep sub-step u (two per tile): 32 except in the last tile
+    auto key_limit = [&](int u) {
+        if (u >= 2) return 32;
+        return u == 0 ? min(32, last_len) : max(0, last_len - 32);
+    };
     Tile tile;
     tile.init(wave, lane);
     const int vl = Tile::vlane(lane);
 
     auto kslot = [&](int t) { return kring + (t & 3) * Tile::K_ELEMS; };
     auto vslot = [&](int t) { return vring + (t % 3) * Tile::V_ELEMS; };
-    // start the DMA of K / V tile t into the given slot (completion: vmcnt + barrier)
-    auto dma_k = [&](int t, T* dst) {
-        if (ragged && t == nt - 1) tile.template issue_k<true, STREAM>(w.src, t * BK, Lk, dst, wave);
+    // start the DMA of the K / V tile at sweep position i into the given slot (completion:
+    // vmcnt + barrier)
+    auto dma_k = [&](int i, T* dst) {
+        const int t = tile_of(i);
+        if (ragged && i == 0) tile.template issue_k<true, STREAM>(w.src, t * BK, Lk, dst, wave);
         else tile.template issue_k<false, STREAM>(w.src, t * BK, Lk, dst, wave);
     };
-    auto dma_v = [&](int t, T* dst) {
-        if (ragged && t == nt - 1) tile.template issue_v<true, STREAM>(w.src, t * BK, Lk, dst, wave);
+    auto dma_v = [&](int i, T* dst) {
+        const int t = tile_of(i);
+        if (ragged && i == 0) tile.template issue_v<true, STREAM>(w.src, t * BK, Lk, dst, wave);
         else tile.template issue_v<false, STREAM>(w.src, t * BK, Lk, dst, wave);
     };
     // DMA writes of this wave complete, then every wave's are visible
@@ -242,8 +261,8 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
         asm volatile("s_barrier" ::: "memory");
     };
 
-    // S^T of sub-step u (keys 32u.., both query blocks) from the K tile at Ks.  Keys past
-    // the window read as zeros here; the softmax masks them.
+    // S^T of sweep sub-step u (both query blocks) from the K tile at Ks.  Keys past the
+    // window hold copies of the last key here; the softmax masks them.
     auto qk = [&](const T* Ks, int u, f32x16 (&S)[QB]) {
         const int kb = u & 1;
         typename M::frag ka = Tile::kfrag(Ks, kb, 0, col, h), kn;
@@ -255,48 +274,18 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
             if (s + 1 < NS) ka = kn;
         }
     };
-    // row maxima of sub-step u's scores (log2 units), keys past the window excluded
+    // row maxima of sweep sub-step u's scores, keys past the window excluded
     auto rowmax = [&](int u, const f32x16 (&S)[QB], float (&mx)[QB]) {
+        const int kl = key_limit(u);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                if (32 * u + crow(r, h) < Lk) mx[qb] = fmaxf(mx[qb], S[qb][r]);
+                if (crow(r, h) < kl) mx[qb] = fmaxf(mx[qb], S[qb][r]);
     };
 
     f32x16 oacc[NDB][QB];
     float m_ref[QB], l_run[QB];
-
-    // O^T += V_u^T P_u^T, one MFMA per fence-separated segment, the next V operand read
-    // issued one product ahead
-    auto pv_product = [&](int u, const typename M::frag (&pf)[TPB][QB]) {
-        const T* Vs = vslot(u >> 1);
-        const int kb = u & 1;
-        constexpr int NV = TPB * NDB;
-        typename M::frag va = Tile::vfrag(Vs, vl, 0, kb, 0), vn;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int db = i % NDB, t = i / NDB;
-            if (i + 1 < NV) vn = Tile::vfrag(Vs, vl, (i + 1) % NDB, kb, (i + 1) / NDB);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = M::mma(va, pf[t][qb], oacc[db][qb]);
-            if (i + 1 < NV) va = vn;
-        }
-    };
-
-    // softmax of one 8-value slice (query block qb, value-product step t) of S_u^T -> P
-    auto soft8 = [&](const f32x16 (&Sc)[QB], int qb, int t, typename M::frag (&pf)[TPB][QB], float (&lsum)[QB],
-                     auto mask_tag) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        float pv[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[qb][t * EPL + e], sc, -m_ref[qb]));
-            if (MASK && crow(t * EPL + e, h) >= tail) pv[e] = 0.f;
-        }
-        pf[t][qb] = M::pack(pv);
-        lsum[qb] = sum8(pf[t][qb], lsum[qb]);
-    };
 
     // K operands of the look-ahead scores, read one sub-step before their products so the
     // LDS latency is covered by a whole sub-step of work (one wave per SIMD has no other
@@ -308,14 +297,25 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
         for (int st = 0; st < NS; ++st) kpre[st] = Tile::kfrag(Ks, u & 1, st, col, h);
     };
 
-    // Sub-step u of a full tile (u+1 exists, kpre holds its K operands), one basic block
-    // cut by scheduling fences into
+    // Sub-step u (kpre holds the K operands of u+1), one basic block cut by scheduling
+    // fences into
     //   V operand reads of u | scores of u+1 with the softmax of u | K operand reads of u+2 |
     //   value product of u.
     // The scores and the softmax are written as 16 segments [MFMA, 1/16 of the softmax]; the
-    // compiler's MFMA/exp interleaving places the vector work between the products.  The
-    // K reads of u+2 stay inside the tile ring: u+2 lies at most in the last tile.
-    auto sub_full = [&](int u, f32x16 (&Sc)[QB], f32x16 (&Sn)[QB]) {
+    // compiler's MFMA/exp interleaving places the vector work between the products.  MASK
+    // (the last tile, swept first): keys of u from key_limit(u) on get a score of -inf.  At
+    // the end of the sweep the look-ahead and the K reads land in ring slots whose contents
+    // are never used; every read stays inside the ring.
+    auto sub_full = [&](int u, f32x16 (&Sc)[QB], f32x16 (&Sn)[QB], auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const int kl = MASK ? key_limit(u) : 32;
+        if (MASK && kl < 32) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (crow(r, h) >= kl)
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) Sc[qb][r] = -INFINITY;
+        }
         const T* Vs = vslot(u >> 1);
         constexpr int NV = TPB * NDB;
         typename M::frag vf[NV];
@@ -358,23 +358,6 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
         }
     };
 
-    // Sub-step u of the last tile (general form): scores of u+1 if any, softmax of u with
-    // the ragged keys masked if MASK, value product.
-    auto sub_last = [&](int u, f32x16 (&Sc)[QB], f32x16 (&Sn)[QB], auto mask_tag) {
-        if (u + 1 < nsub) qk(kslot((u + 1) >> 1), u + 1, Sn);
-        typename M::frag pf[TPB][QB];
-        float lsum[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) lsum[qb] = l_run[qb];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int t = 0; t < TPB; ++t) soft8(Sc, qb, t, pf, lsum, mask_tag);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) l_run[qb] = lsum[qb];
-        pv_product(u, pf);
-    };
-
     f32x16 SA[QB], SB[QB];
     // one sweep of the window with the current reference; returns the row sums
     auto run = [&](bool first, float (&l_tot)[QB]) {
@@ -385,8 +368,8 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
             for (int db = 0; db < NDB; ++db) oacc[db][qb] = zero16();
         }
         if (nt > 0) {
-            // prologue: K_0, V_0, K_1 staged; scores of sub-step 0
-            // prologue: K_0, V_0, K_1 in LDS; K_2 and V_1 in flight (the batch of tile -1)
+            // prologue: sweep tiles 0 and 1 (K) and 0 (V) in LDS, K of 2 and V of 1 in flight
+            // (the batch of position -1); scores of sub-step 0
             dma_k(0, kslot(0));
             dma_v(0, vslot(0));
             if (nt > 1) dma_k(1, kslot(1));
@@ -395,7 +378,7 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
             if (nt > 1) dma_v(1, vslot(1));
             if (wave_live) {
                 qk(kslot(0), 0, SA);
-                if (nsub > 1) read_k(1);
+                read_k(1);
                 if (first) {
                     float mx[QB] = {-INFINITY, -INFINITY};
                     rowmax(0, SA, mx);
@@ -403,28 +386,21 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
                     for (int qb = 0; qb < QB; ++qb) m_ref[qb] = pair_max(mx[qb]) * sc;
                 }
             }
-            // full tiles: tile t holds sub-steps 2t and 2t+1, neither of them ragged
-            for (int t = 0; t + 1 < nt; ++t) {
-                // batch of tile t: K_{t+3} and V_{t+2}, into the slots tile t-1 used
-                const bool kis = t + 3 < nt, vis = t + 2 < nt;
-                if (kis) dma_k(t + 3, kslot(t + 3));
-                if (vis) dma_v(t + 2, vslot(t + 2));
+            // sweep position i holds sub-steps 2i and 2i+1; position 0 (the last tile of the
+            // window) is the only one that can hold a ragged or an empty sub-step
+            auto position = [&](int i, auto mask_tag) {
+                // batch of position i: K of i+3 and V of i+2, into the slots position i-1 used
+                const bool kis = i + 3 < nt, vis = i + 2 < nt;
+                if (kis) dma_k(i + 3, kslot(i + 3));
+                if (vis) dma_v(i + 2, vslot(i + 2));
                 if (wave_live) {
-                    sub_full(2 * t, SA, SB);
-                    sub_full(2 * t + 1, SB, SA);
+                    sub_full(2 * i, SA, SB, mask_tag);
+                    sub_full(2 * i + 1, SB, SA, mask_tag);
                 }
                 tile_sync(kis, vis);
-            }
-            // last tile: one or two sub-steps, the last of them possibly ragged
-            if (wave_live) {
-                const int u0 = 2 * (nt - 1);
-                if (tail != 0 && u0 == nsub - 1) sub_last(u0, SA, SB, std::true_type{});
-                else sub_last(u0, SA, SB, std::false_type{});
-                if (u0 + 1 < nsub) {
-                    if (tail != 0) sub_last(u0 + 1, SB, SA, std::true_type{});
-                    else sub_last(u0 + 1, SB, SA, std::false_type{});
-                }
-            }
+            };
+            position(0, std::true_type{});
+            for (int i = 1; i < nt; ++i) position(i, std::false_type{});
         }
         bool over = false;
 #pragma unroll
@@ -439,11 +415,11 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
     if (run(true, l_tot)) {
         // exact row maxima by a score-only sweep, as the reference of a second sweep
         float mx[QB] = {-INFINITY, -INFINITY};
-        for (int t = 0; t < nt; ++t) {
-            dma_k(t, kslot(0));
+        for (int i = 0; i < nt; ++i) {
+            dma_k(i, kslot(0));
             dma_sync();
             if (wave_live) {
-                for (int u = 2 * t; u < 2 * t + 2 && u < nsub; ++u) {
+                for (int u = 2 * i; u < 2 * i + 2; ++u) {
                     qk(kslot(0), u, SA);
                     rowmax(u, SA, mx);
                 }
