@@ -71,6 +71,73 @@ __host__ __device__ inline size_t epilogue_lds_bytes(int Dphi) {
     return ((size_t)Dphi * (D + VEC) + (size_t)D * (Dphi + VEC)) * sizeof(T);
 }
 
+// Merge and store one query row of a wave's query block qb (ReHyAt blog,
+// maplevalley.com.cn, 2.3): out = (2^m O + y) / (2^m l + z), both scaled by 2^-max(m, 0);
+// aux outputs if requested.  The row's values live in lane (row % 32, h) of the C layout.
+template <class T, class OT, int D, int QB>
+__device__ inline void merge_store_block(const AttnArgs& a, const Window<T>& w, int row, bool has_soft, bool has_lin,
+                                         const f32x16 (&oacc)[D / 32][QB], int qb, const f32x16 (&yacc)[D / 32],
+                                         float m_run, float l_tot, float zq) {
+    constexpr int NDB = D / 32;
+    const int lane = threadIdx.x % 64, h = lane / 32;
+    OT* outs = reinterpret_cast<OT*>(a.out) + (int64_t)w.bh * a.q_bh_stride + (int64_t)w.q0 * D;
+    const int64_t arow0 = (int64_t)w.bh * a.aux_bh_stride + w.q0;
+    if (row >= w.Lq) return;
+    float ca, cg;
+    if (has_soft && has_lin) {
+        const float M2 = fmaxf(m_run, 0.f);
+        const float ea = __builtin_amdgcn_exp2f(m_run - M2);
+        const float eg = __builtin_amdgcn_exp2f(-M2);
+        const float inv = 1.f / (ea * l_tot + eg * zq);
+        ca = ea * inv;
+        cg = eg * inv;
+    } else if (has_soft) {
+        ca = 1.f / l_tot;
+        cg = 0.f;
+    } else {
+        ca = 0.f;
+        cg = 1.f / zq;
+    }
+    OT* orow = outs + (int64_t)row * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d = db * 32 + g * 8 + h * 4;
+            float vals[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vals[i] = ca * oacc[db][qb][g * 4 + i] + cg * yacc[db][g * 4 + i];
+            if constexpr (sizeof(OT) == 4) {
+                *reinterpret_cast<float4*>(orow + d) = make_float4(vals[0], vals[1], vals[2], vals[3]);
+            } else {
+                bf16x4 o4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o4[i] = (bf16)vals[i];
+                *reinterpret_cast<bf16x4*>(orow + d) = o4;
+            }
+        }
+    if (a.aux_o_soft || a.aux_y) {
+        const float il = has_soft ? 1.f / l_tot : 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = db * 32 + g * 8 + h * 4;
+                float4 so, yo;
+                so.x = oacc[db][qb][g * 4 + 0] * il; so.y = oacc[db][qb][g * 4 + 1] * il;
+                so.z = oacc[db][qb][g * 4 + 2] * il; so.w = oacc[db][qb][g * 4 + 3] * il;
+                yo.x = yacc[db][g * 4 + 0]; yo.y = yacc[db][g * 4 + 1];
+                yo.z = yacc[db][g * 4 + 2]; yo.w = yacc[db][g * 4 + 3];
+                if (a.aux_o_soft) *reinterpret_cast<float4*>(a.aux_o_soft + (arow0 + row) * D + d) = so;
+                if (a.aux_y) *reinterpret_cast<float4*>(a.aux_y + (arow0 + row) * D + d) = yo;
+            }
+    }
+    if (h == 0) {
+        if (a.aux_lse) a.aux_lse[arow0 + row] = has_soft ? m_run * 0.6931471805599453f + logf(l_tot) : -INFINITY;
+        if (a.aux_z) a.aux_z[arow0 + row] = zq;
+    }
+}
+
 // Epilogue of the attention kernels, one 32-query block of the wave at a time, so only one
 // block's linear-part registers are live next to the softmax accumulators.
 //
@@ -163,63 +230,8 @@ __device__ inline void linear_and_merge(const AttnArgs& a, const Window<T>& w, u
             zq += other_half(zq);
         }
 
-        const int row = qw + qb * 32 + col;
-        if (row >= w.Lq) continue;
-        OT* outs = reinterpret_cast<OT*>(a.out) + (int64_t)w.bh * a.q_bh_stride + (int64_t)w.q0 * D;
-        const int64_t arow0 = (int64_t)w.bh * a.aux_bh_stride + w.q0;
-        float ca, cg;
-        if (has_soft && has_lin) {
-            const float M2 = fmaxf(m_run[qb], 0.f);
-            const float ea = __builtin_amdgcn_exp2f(m_run[qb] - M2);
-            const float eg = __builtin_amdgcn_exp2f(-M2);
-            const float inv = 1.f / (ea * l_tot[qb] + eg * zq);
-            ca = ea * inv;
-            cg = eg * inv;
-        } else if (has_soft) {
-            ca = 1.f / l_tot[qb];
-            cg = 0.f;
-        } else {
-            ca = 0.f;
-            cg = 1.f / zq;
-        }
-        OT* orow = outs + (int64_t)row * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = db * 32 + g * 8 + h * 4;
-                float vals[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) vals[i] = ca * oacc[db][qb][g * 4 + i] + cg * yacc[db][g * 4 + i];
-                if constexpr (sizeof(OT) == 4) {
-                    *reinterpret_cast<float4*>(orow + d) = make_float4(vals[0], vals[1], vals[2], vals[3]);
-                } else {
-                    bf16x4 o4;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) o4[i] = (bf16)vals[i];
-                    *reinterpret_cast<bf16x4*>(orow + d) = o4;
-                }
-            }
-        if (a.aux_o_soft || a.aux_y) {
-            const float il = has_soft ? 1.f / l_tot[qb] : 0.f;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int d = db * 32 + g * 8 + h * 4;
-                    float4 so, yo;
-                    so.x = oacc[db][qb][g * 4 + 0] * il; so.y = oacc[db][qb][g * 4 + 1] * il;
-                    so.z = oacc[db][qb][g * 4 + 2] * il; so.w = oacc[db][qb][g * 4 + 3] * il;
-                    yo.x = yacc[db][g * 4 + 0]; yo.y = yacc[db][g * 4 + 1];
-                    yo.z = yacc[db][g * 4 + 2]; yo.w = yacc[db][g * 4 + 3];
-                    if (a.aux_o_soft) *reinterpret_cast<float4*>(a.aux_o_soft + (arow0 + row) * D + d) = so;
-                    if (a.aux_y) *reinterpret_cast<float4*>(a.aux_y + (arow0 + row) * D + d) = yo;
-                }
-        }
-        if (h == 0) {
-            if (a.aux_lse) a.aux_lse[arow0 + row] = has_soft ? m_run[qb] * 0.6931471805599453f + logf(l_tot[qb]) : -INFINITY;
-            if (a.aux_z) a.aux_z[arow0 + row] = zq;
-        }
+        merge_store_block<T, OT, D>(a, w, qw + qb * 32 + col, has_soft, has_lin, oacc, qb, yacc, m_run[qb], l_tot[qb],
+                                    zq);
     }
 }
 

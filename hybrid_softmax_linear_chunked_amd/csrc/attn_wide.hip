@@ -165,7 +165,112 @@ struct DmaTiles {
     }
 };
 
-template <class OT, int D, bool STREAM>
+// LDS bytes of the one-shot epilogue staging: W_q [Dphi][D + 8], the P powers of the state
+// image [P][D][Dphi + 8] (bf16) and Z [P][Dphi] (fp32).
+__host__ __device__ inline size_t wide_epilogue_lds_bytes(int D, int Dphi, int P) {
+    return ((size_t)Dphi * (D + 8) + (size_t)P * D * (Dphi + 8)) * 2 + (size_t)P * Dphi * 4;
+}
+
+// rows x row_bytes (rows contiguous in HBM, row_bytes a multiple of 16) into LDS at dst,
+// followed by 16 bytes of padding per row if pad, by LDS-DMA over the NW waves
+template <int NW>
+__device__ inline void dma_rows(const void* src, int rows, int row_bytes, bool pad, unsigned char* dst, int wave,
+                                int lane) {
+    const int dch = row_bytes / 16, cpr = dch + (pad ? 1 : 0), nch = rows * cpr;
+    for (int j = wave; j * 64 < nch; j += NW) {
+        const int q = j * 64 + lane;
+        if (q < nch) {
+            const int row = q / cpr, c = q % cpr;
+            dma16_v(reinterpret_cast<const unsigned char*>(src) + (int64_t)row * row_bytes + (c < dch ? c : 0) * 16,
+                    lds_addr(dst + j * 1024));
+        }
+    }
+}
+
+// Epilogue of the wide kernel when everything it reads fits in LDS at once (ReHyAt blog,
+// maplevalley.com.cn, 2.2.2-2.3): W_q, every power of the chunk's state image and Z are
+// staged by one round of LDS-DMA behind a single barrier, then each 32-query block computes
+// u = W_q q on MFMA from the Q operand registers, phi = per-part powers of softplus(u + b),
+// y = sum over powers of S_c^T phi on MFMA (phi straight from the u registers),
+// z = phi . Z_c, and merges with its softmax part.
+template <class OT, int D, int NW>
+__device__ inline void wide_linear_and_merge(const AttnArgs& a, const Window<bf16>& w, unsigned char* smem, int qw,
+                                             int wave, bool has_soft, bool has_lin,
+                                             const bf16x8 (&qf)[2][D / 16], const f32x16 (&oacc)[D / 32][2],
+                                             const float (&m_ref)[2], const float (&l_tot)[2]) {
+    using T = bf16;
+    using M = Mfma<T>;
+    constexpr int QB = 2, KS = M::KS, EPL = M::EPL, NS = D / KS, NDB = D / 32, TPB = 16 / EPL;
+    const int lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
+    const int Dphi = a.Dphi, P = a.P, NJB = Dphi / 32;
+    constexpr int WLD = D + 8;
+    const int SLD = Dphi + 8;
+    T* Ws = reinterpret_cast<T*>(smem);
+    T* Ss = Ws + Dphi * WLD;
+    float* Zs = reinterpret_cast<float*>(Ss + P * D * SLD);
+    const float* bq = a.bq ? a.bq + (int64_t)w.hh * Dphi : nullptr;
+
+    if (has_lin) {
+        __syncthreads();  // every wave is done with the K/V tiles
+        dma_rows<NW>(reinterpret_cast<const T*>(a.wq) + (int64_t)w.hh * Dphi * D, Dphi, D * 2, true,
+                     reinterpret_cast<unsigned char*>(Ws), wave, lane);
+        dma_rows<NW>(reinterpret_cast<const T*>(a.simg) + (int64_t)w.img_slot * P * D * Dphi, P * D, Dphi * 2, true,
+                     reinterpret_cast<unsigned char*>(Ss), wave, lane);
+        dma_rows<NW>(a.zimg + (int64_t)w.img_slot * P * Dphi, 1, P * Dphi * 4, false,
+                     reinterpret_cast<unsigned char*>(Zs), wave, lane);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        f32x16 yacc[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) yacc[db] = zero16();
+        float zq = 0.f;
+        if (has_lin) {
+            constexpr int JBMAX = 4;  // Dphi <= 128
+            float uu[JBMAX][16];
+#pragma unroll
+            for (int jb = 0; jb < JBMAX; ++jb) {
+                if (jb >= NJB) break;
+                f32x16 u = M::mma(M::load(Ws + (jb * 32 + col) * WLD + h * EPL), qf[qb][0], zero16());
+#pragma unroll
+                for (int st = 1; st < NS; ++st) u = M::mma(M::load(Ws + (jb * 32 + col) * WLD + st * KS + h * EPL), qf[qb][st], u);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) uu[jb][r] = softplus_fast<T>(u[r] + (bq ? bq[jb * 32 + crow(r, h)] : 0.f));
+            }
+            for (int pw = 1; pw <= P; ++pw) {
+                const T* Sp = Ss + (pw - 1) * D * SLD;
+                const float* zp = Zs + (pw - 1) * Dphi;
+#pragma unroll
+                for (int jb = 0; jb < JBMAX; ++jb) {
+                    if (jb >= NJB) break;
+                    float ph[16];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float v = uu[jb][r];
+                        for (int e = 1; e < pw; ++e) v *= uu[jb][r];
+                        ph[r] = v;
+                        zq += v * zp[jb * 32 + crow(r, h)];
+                    }
+#pragma unroll
+                    for (int t = 0; t < TPB; ++t) {
+                        const typename M::frag bfr = M::pack(ph + t * EPL);
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db) {
+                            const typename M::frag sf = M::load(Sp + (db * 32 + col) * SLD + jb * 32 + t * 2 * EPL + h * EPL);
+                            yacc[db] = M::mma(sf, bfr, yacc[db]);
+                        }
+                    }
+                }
+            }
+            zq += other_half(zq);
+        }
+        merge_store_block<T, OT, D>(a, w, qw + qb * 32 + col, has_soft, has_lin, oacc, qb, yacc, m_ref[qb], l_tot[qb], zq);
+    }
+}
+
+template <class OT, int D, bool STREAM, bool EPI_ALL>
 __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
     using T = bf16;
     using M = Mfma<T>;
@@ -431,19 +536,23 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
         run(false, l_tot);
     }
 
-    linear_and_merge<T, OT, D, QB, NT>(a, w, smem, qw, has_soft, has_lin, qf, oacc, m_ref, l_tot);
+    if constexpr (EPI_ALL) wide_linear_and_merge<OT, D, NW>(a, w, smem, qw, wave, has_soft, has_lin, qf, oacc, m_ref, l_tot);
+    else linear_and_merge<T, OT, D, QB, NT>(a, w, smem, qw, has_soft, has_lin, qf, oacc, m_ref, l_tot);
 }
 
 template <class OT, int D, bool STREAM>
 static hipError_t launch_wide_one(const AttnArgs& a, hipStream_t stream) {
     constexpr int NW = 4, QB = 2;
+    constexpr size_t kLdsMax = 160 * 1024;
     using Tile = DmaTiles<D, NW>;
     const size_t kv = (4 * (size_t)Tile::K_ELEMS + 3 * (size_t)Tile::V_ELEMS) * sizeof(bf16);
-    const size_t epi = epilogue_lds_bytes<bf16, D>(a.Dphi);
+    const size_t epi_all = wide_epilogue_lds_bytes(D, a.Dphi, a.P);
+    const bool all = epi_all <= kLdsMax;
+    const size_t epi = all ? epi_all : epilogue_lds_bytes<bf16, D>(a.Dphi);
     const size_t lds = kv > epi ? kv : epi;
-    auto fn = attn_wide_kernel<OT, D, STREAM>;
-    static size_t lds_set[64] = {};
-    hipError_t e = ensure_lds(reinterpret_cast<const void*>(fn), lds, lds_set);
+    auto fn = all ? attn_wide_kernel<OT, D, STREAM, true> : attn_wide_kernel<OT, D, STREAM, false>;
+    static size_t lds_set[2][64] = {};
+    hipError_t e = ensure_lds(reinterpret_cast<const void*>(fn), lds, lds_set[all ? 1 : 0]);
     if (e != hipSuccess) return e;
     AttnArgs b = a;
     attn_grid(b, NW * QB * 32);

@@ -48,6 +48,9 @@ CASES = [
     rh.Params(1, 2, 32, 7, 80, 3, 1, 32, 2, 0, BF16, BF16),
     rh.Params(1, 2, 128, 7, 50, 3, 1, 128, 2, 1, BF16, BF16),
     rh.Params(1, 1, 128, 10, 64, 4, 2, 96, 2, 0, BF16, BF16),
+    # bf16, P = 4 at Dphi = D = 128: W_q and all four state-image powers exceed the LDS, so the
+    # epilogue stages one power at a time
+    rh.Params(1, 1, 128, 7, 70, 3, 1, 128, 4, 0, BF16, BF16),
 ]
 
 
