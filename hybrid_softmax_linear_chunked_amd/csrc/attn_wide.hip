@@ -9,11 +9,12 @@
 //
 // The window is swept in 32-token sub-steps.  Sub-step u runs
 //   (a) S_{u+1}^T = K_{u+1} Q^T          on the matrix core (scores one sub-step ahead),
-//   (b) softmax of S_u^T -> P_u           on the vector ALU, overlapping (a),
+//   (b) softmax of S_u^T -> P_u           on the vector ALU, interleaved with (a),
 //   (c) O^T += V_u^T P_u^T                on the matrix core.
-// K and V are staged through LDS in 64-token tiles: K in a ring of three slots (the
-// look-ahead of (a) reaches into the next tile), V in two.  The loads of K_{t+2} and
-// V_{t+1} are issued at the top of tile t and written to LDS at its bottom.
+// K and V reach LDS in 64-token tiles by LDS-DMA, two tiles ahead of their use: K in a ring
+// of four slots (the look-ahead of (a) reaches into the next tile), V in three.  The tile
+// holding the ragged end of the window is swept first, so the steady-state loop sees full
+// tiles only and carries no masking.
 //
 // Softmax reference: scores are taken in the log2 domain against one fixed reference per
 // query, the maximum of its first sub-step, so p = exp2(s*log2(e)/sqrt(D) - m) and O is
@@ -427,7 +428,7 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) vf[i] = Tile::vfrag(Vs, vl, i % NDB, u & 1, i / NDB);
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_iglp_opt(3);
+        __builtin_amdgcn_iglp_opt(2);
         typename M::frag pf[TPB][QB];
         float lsum[QB];
 #pragma unroll

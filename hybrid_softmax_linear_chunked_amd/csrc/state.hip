@@ -165,63 +165,99 @@ __global__ __launch_bounds__(StateShape<P>::NW * 64) void state_kernel(const Sta
     }
 }
 
+// One workgroup per (batch-head, power, 32-feature block, 32-d block) of S, plus one per
+// batch-head for Z.  Each thread carries four running sums; partials are read along d
+// (coalesced) and every emitted image block goes through a 32 x 32 LDS tile so that it is
+// written as whole 64-byte (bf16) rows of the image, features in slot order.
 template <class T>
 __global__ __launch_bounds__(256) void scan_kernel(const ScanArgs a) {
     constexpr int EPL = Mfma<T>::EPL;
-    const int Dphi = a.Dphi, P = a.P, D = a.D, F = Dphi * P;
-    const int64_t per = (int64_t)F * D + F;
-    const int bh = blockIdx.y;
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= per) return;
-    const bool is_s = e < (int64_t)F * D;
-    const float* base;
-    int64_t stride;
-    float* state = nullptr;
-    int64_t img_off;  // position in one slot of the image (S) or of the Z image
-    if (is_s) {
-        const int f = (int)(e / D), d = (int)(e % D);
-        int j, pw;
-        feat_split(f, Dphi, P, j, pw);
-        base = a.Sp + (int64_t)bh * a.G * F * D + e;
-        stride = (int64_t)F * D;
-        if (a.S_state) state = a.S_state + (int64_t)bh * F * D + e;
-        img_off = ((int64_t)(pw - 1) * D + d) * Dphi + (j / 32) * 32 + slot_pos<EPL>(j % 32);
-    } else {
-        const int f = (int)(e - (int64_t)F * D);
-        int j, pw;
-        feat_split(f, Dphi, P, j, pw);
-        base = a.Zp + (int64_t)bh * a.G * F + f;
-        stride = F;
-        if (a.Z_state) state = a.Z_state + (int64_t)bh * F + f;
-        img_off = (int64_t)(pw - 1) * Dphi + j;
-    }
+    constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
+    constexpr int CPR = 32 * sizeof(T) / 16;  // 16-byte chunks per 32-element image row
+    const int Dphi = a.Dphi, P = a.P, D = a.D, F = Dphi * P, NJB = Dphi / 32, NDB = D / 32;
+    const int bh = blockIdx.y, tid = threadIdx.x;
     T* img = reinterpret_cast<T*>(a.simg) + (int64_t)bh * a.slots * F * D;
     float* zimg = a.zimg + (int64_t)bh * a.slots * F;
-    auto emit = [&](int slot, float v) {
-        if (is_s) img[(int64_t)slot * F * D + img_off] = from_float<T>(v);
-        else zimg[(int64_t)slot * F + img_off] = v;
-    };
-    if (state) {  // streaming: carried state + this step's frames, in frame order
-        float acc = *state;
-        for (int g = 0; g < a.G; ++g) acc += base[g * stride];
-        *state = acc;
-        emit(0, acc);
-        return;
-    }
-    // chunk-parallel: prefix over frames; chunk c reads the prefix through frame ls(c) - 1
     const int nc = (a.T + a.Tc - 1) / a.Tc;
-    int c = 0;
     auto ls_of = [&](int cc) {
         const int f0 = cc * a.Tc, f1 = min(f0 + a.Tc, a.T);
         return a.linear_only ? f1 : max(0, f0 - a.To);
     };
-    while (c < nc && ls_of(c) == 0) ++c;
-    float acc = 0.f;
-    for (int g = 0; g < a.G && c < nc; ++g) {
-        acc += base[g * stride];
-        while (c < nc && ls_of(c) == g + 1) {
-            emit(c, acc);
-            ++c;
+
+    if ((int)blockIdx.x < P * NJB * NDB) {
+        __shared__ __align__(16) T tile[32][32 + EPC];  // [d][feature, slot order]
+        const int blk = blockIdx.x;
+        const int db = blk % NDB, jb = (blk / NDB) % NJB, pw = blk / (NDB * NJB) + 1;
+        const int dl = tid % 32, jr = tid / 32;  // this thread: d = db*32 + dl, j = jb*32 + jr + 8k
+        int64_t off[4];
+        float acc[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            off[k] = (int64_t)feat_index(jb * 32 + jr + 8 * k, pw, Dphi, P) * D + db * 32 + dl;
+            acc[k] = 0.f;
+        }
+        const float* base = a.Sp + (int64_t)bh * a.G * F * D;
+        const int64_t stride = (int64_t)F * D;
+        auto emit = [&](int slot) {
+            __syncthreads();  // the previous block left the tile
+#pragma unroll
+            for (int k = 0; k < 4; ++k) tile[dl][slot_pos<EPL>(jr + 8 * k)] = from_float<T>(acc[k]);
+            __syncthreads();
+            if (tid < 32 * CPR) {
+                const int row = tid / CPR, c = tid % CPR;
+                T* dst = img + (int64_t)slot * F * D + ((int64_t)(pw - 1) * D + db * 32 + row) * Dphi + jb * 32 + c * EPC;
+                *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(&tile[row][c * EPC]);
+            }
+        };
+        if (a.S_state) {  // streaming: carried state + this step's frames, in frame order
+            float* st = a.S_state + (int64_t)bh * F * D;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[k] = st[off[k]];
+            for (int g = 0; g < a.G; ++g)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) acc[k] += base[g * stride + off[k]];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) st[off[k]] = acc[k];
+            emit(0);
+            return;
+        }
+        // chunk-parallel: prefix over frames; chunk c reads the prefix through frame ls(c) - 1
+        int c = 0;
+        while (c < nc && ls_of(c) == 0) ++c;
+        for (int g = 0; g < a.G && c < nc; ++g) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[k] += base[g * stride + off[k]];
+            while (c < nc && ls_of(c) == g + 1) {
+                emit(c);
+                ++c;
+            }
+        }
+        return;
+    }
+
+    // Z: [F] running sums per batch-head, image [P][Dphi] in plain feature order
+    const float* zb = a.Zp + (int64_t)bh * a.G * F;
+    for (int f = tid; f < F; f += 256) {
+        int j, pw;
+        feat_split(f, Dphi, P, j, pw);
+        const int zo = (pw - 1) * Dphi + j;
+        if (a.Z_state) {
+            float* st = a.Z_state + (int64_t)bh * F + f;
+            float acc = *st;
+            for (int g = 0; g < a.G; ++g) acc += zb[(int64_t)g * F + f];
+            *st = acc;
+            zimg[zo] = acc;
+            continue;
+        }
+        int c = 0;
+        while (c < nc && ls_of(c) == 0) ++c;
+        float acc = 0.f;
+        for (int g = 0; g < a.G && c < nc; ++g) {
+            acc += zb[(int64_t)g * F + f];
+            while (c < nc && ls_of(c) == g + 1) {
+                zimg[(int64_t)c * F + zo] = acc;
+                ++c;
+            }
         }
     }
 }
@@ -304,8 +340,7 @@ hipError_t launch_state(const StateArgs& a, int in_dtype, hipStream_t stream) {
 
 hipError_t launch_scan(const ScanArgs& a, int in_dtype, hipStream_t stream) {
     if (a.G <= 0) return hipSuccess;
-    const int64_t per = (int64_t)a.Dphi * a.P * a.D + (int64_t)a.Dphi * a.P;
-    const dim3 grid((unsigned)((per + 255) / 256), a.BH);
+    const dim3 grid((unsigned)(a.P * (a.Dphi / 32) * (a.D / 32) + 1), a.BH);
     if (in_dtype == 1) hipLaunchKernelGGL(scan_kernel<bf16>, grid, dim3(256), 0, stream, a);
     else hipLaunchKernelGGL(scan_kernel<float>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
