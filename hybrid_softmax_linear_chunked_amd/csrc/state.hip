@@ -13,8 +13,11 @@
 //   over the clip, chunk-parallel form) or added to a carried state (streaming form).
 //   Both forms add the same partials in the same order, so they agree bit for bit.
 // copy_kernel: keeps the last To frames of the window as the streaming overlap.
-#include "tiles.hpp"
+#include <type_traits>
+
+#include "dma.hpp"
 #include "kernels.hpp"
+#include "tiles.hpp"
 
 namespace rehyat {
 
@@ -128,6 +131,182 @@ __global__ __launch_bounds__(StateShape<P>::NW * 64) void state_kernel(const Sta
         }
         if (more) tile.store((it & 1) ? Ks0 : Ks1, (it & 1) ? Vs0 : Vs1, tid);
         __syncthreads();
+    }
+
+    // with TS = 2, the ts = 1 wave hands its tiles to ts = 0 through LDS; then store
+    float* red = reinterpret_cast<float*>(smem);  // [NJB][16 regs][64 lanes]
+    float* Sp = a.Sp + ((int64_t)bh * a.G + gi) * F * D;
+    float* Zp = a.Zp + ((int64_t)bh * a.G + gi) * F;
+#pragma unroll
+    for (int pw = 0; pw < P; ++pw) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            if (TS == 2) {
+                if (active && ts == 1) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) red[(jb * 16 + r) * 64 + lane] = acc[pw][db][r];
+                }
+                __syncthreads();
+            }
+            if (active && ts == 0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float v = acc[pw][db][r] + (TS == 2 ? red[(jb * 16 + r) * 64 + lane] : 0.f);
+                    const int f = feat_index(jb * 32 + crow(r, h), pw + 1, Dphi, P);
+                    Sp[(int64_t)f * D + db * 32 + col] = v;
+                }
+            }
+            if (TS == 2) __syncthreads();
+        }
+        const float zt = zacc[pw] + other_half(zacc[pw]);
+        if (TS == 2) {
+            if (active && ts == 1 && h == 0) red[jb * 32 + col] = zt;
+            __syncthreads();
+        }
+        if (active && ts == 0 && h == 0) Zp[feat_index(j, pw + 1, Dphi, P)] = zt + (TS == 2 ? red[jb * 32 + col] : 0.f);
+        if (TS == 2) __syncthreads();
+    }
+}
+
+// bf16 form of state_kernel (P <= 2): the same per-(batch-head, frame) partials and wave roles, with
+// the K/V tiles moved to LDS by LDS-DMA two tiles ahead (ring of three) and the V operand
+// of phi^T V read with transposing LDS reads (see dma.hpp).  The frame's ragged last tile
+// is processed first, with the padded tokens given phi = 0, so full tiles carry no bounds
+// arithmetic.  Sums run in a fixed order, so the result does not depend on timing.
+template <int D, int P>
+__global__ __launch_bounds__(StateShape<P>::NW * 64) void state_dma_kernel(const StateArgs a) {
+    using T = bf16;
+    using M = Mfma<T>;
+    constexpr int TS = StateShape<P>::TS, NW = StateShape<P>::NW;
+    using Tile = DmaTiles<D, NW>;
+    constexpr int KS = M::KS, EPL = M::EPL, NS = D / KS, NDB = D / 32, TPB = 16 / EPL, BK = Tile::BK;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    T* const kring = reinterpret_cast<T*>(smem);
+    T* const vring = kring + 3 * Tile::K_ELEMS;
+
+    const int gi = blockIdx.x % a.G;
+    const int bh = blockIdx.x / a.G;
+    const int hh = bh % a.H;
+    const int g = a.g0 + gi;
+    const int n = a.n, Dphi = a.Dphi, F = Dphi * P, NJB = Dphi / 32;
+
+    KeySrc<T> src;
+    if (g < a.nf1) {
+        src.k1 = reinterpret_cast<const T*>(a.k1) + (int64_t)bh * a.kv1_bh_stride + (int64_t)g * n * D;
+        src.v1 = reinterpret_cast<const T*>(a.v1) + (int64_t)bh * a.kv1_bh_stride + (int64_t)g * n * D;
+    } else {
+        src.k1 = reinterpret_cast<const T*>(a.k2) + (int64_t)bh * a.kv2_bh_stride + (int64_t)(g - a.nf1) * n * D;
+        src.v1 = reinterpret_cast<const T*>(a.v2) + (int64_t)bh * a.kv2_bh_stride + (int64_t)(g - a.nf1) * n * D;
+    }
+    src.k2 = src.k1;
+    src.v2 = src.v1;
+    src.len1 = n;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform
+    const int lane = tid % 64, col = lane % 32, h = lane / 32;
+    const bool active = wave < TS * NJB;
+    const int jb = wave / TS, ts = wave % TS;
+    const int j = jb * 32 + col;  // this lane's phi row
+
+    typename M::frag wf[NS];
+    float bias = 0.f;
+    if (active) {
+        const T* wk = reinterpret_cast<const T*>(a.wk) + ((int64_t)hh * Dphi + j) * D;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) wf[s] = M::load(wk + s * KS + h * EPL);
+        if (a.bk) bias = a.bk[(int64_t)hh * Dphi + j];
+    }
+
+    f32x16 acc[P][NDB];
+    float zacc[P];
+#pragma unroll
+    for (int pw = 0; pw < P; ++pw) {
+        zacc[pw] = 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[pw][db] = zero16();
+    }
+
+    Tile tile;
+    tile.init(wave, lane);
+    const int vl = Tile::vlane(lane);
+    const int nt = (n + BK - 1) / BK;
+    const int last_len = n - (nt - 1) * BK;
+    const bool ragged = last_len < BK;
+    auto tile_of = [&](int i) { return i == 0 ? nt - 1 : i - 1; };  // ragged tile first
+    auto kslot = [&](int i) { return kring + (i % 3) * Tile::K_ELEMS; };
+    auto vslot = [&](int i) { return vring + (i % 3) * Tile::V_ELEMS; };
+    auto dma = [&](int i) {
+        const int t0 = tile_of(i) * BK;
+        if (ragged && i == 0) {
+            tile.template issue_k<true, false>(src, t0, n, kslot(i), wave);
+            tile.template issue_v<true, false>(src, t0, n, vslot(i), wave);
+        } else {
+            tile.template issue_k<false, false>(src, t0, n, kslot(i), wave);
+            tile.template issue_v<false, false>(src, t0, n, vslot(i), wave);
+        }
+    };
+    // end of tile i: the batch issued at tile i-1 is complete in every wave (vector memory
+    // completes in issue order, so each wave waits until at most the batch it issued at
+    // tile i, counted for the wave with the fewest DMA instructions, is outstanding)
+    auto tile_sync = [&](bool issued) {
+        constexpr int NMIN = Tile::NIK / NW + Tile::NIV / NW;
+        static_assert(NMIN <= 15, "vmcnt immediate range");
+        if (issued) __builtin_amdgcn_s_waitcnt(0x0070 | NMIN);  // + lgkmcnt(0)
+        else __builtin_amdgcn_s_waitcnt(0x0070);
+        asm volatile("s_barrier" ::: "memory");
+    };
+
+    // phi of the 32 tokens of block sub (valid: tokens below kl) and its products
+    auto block = [&](const T* Ks, const T* Vs, int sub, int kl) {
+        f32x16 u = zero16();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) u = M::mma(Tile::kfrag(Ks, sub, s, col, h), wf[s], u);
+        float uu[16], ph[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            uu[r] = softplus_fast<T>(u[r] + bias);
+            if (kl < 32 && crow(r, h) >= kl) uu[r] = 0.f;
+            ph[r] = uu[r];
+        }
+#pragma unroll
+        for (int pw = 0; pw < P; ++pw) {
+            if (pw > 0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) ph[r] *= uu[r];
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) zacc[pw] += ph[r];
+#pragma unroll
+            for (int t = 0; t < TPB; ++t) {
+                const typename M::frag af = M::pack(ph + t * EPL);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) acc[pw][db] = M::mma(af, Tile::vfrag(Vs, vl, db, sub, t), acc[pw][db]);
+            }
+        }
+    };
+    auto process = [&](int i, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+        for (int sub = ts; sub < 2; sub += TS) {
+            const int kl = MASK ? min(32, max(0, last_len - sub * 32)) : 32;
+            block(kslot(i), vslot(i), sub, kl);
+        }
+    };
+
+    dma(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (nt > 1) dma(1);
+    for (int i = 0; i < nt; ++i) {
+        const bool issue = i + 2 < nt;
+        if (issue) dma(i + 2);  // into the slot tile i-1 used
+        if (active) {
+            if (i == 0 && ragged) process(i, std::true_type{});
+            else process(i, std::false_type{});
+        }
+        tile_sync(issue);
     }
 
     // with TS = 2, the ts = 1 wave hands its tiles to ts = 0 through LDS; then store
@@ -290,22 +469,40 @@ __global__ __launch_bounds__(256) void copy_kernel(const CopyArgs a) {
 template <class T, int D, int P>
 static hipError_t launch_state_t(const StateArgs& a, hipStream_t stream) {
     constexpr int NT = StateShape<P>::NW * 64;
-    using Tile = KVTile<T, D, NT>;
-    const size_t kv = 2 * (size_t)(Tile::K_ELEMS + Tile::V_ELEMS) * sizeof(T);
+    // bf16 with P <= 2 (two waves per 64-token tile) takes the LDS-DMA kernel; with larger P
+    // the P x D/32 accumulators leave no registers for its operand prefetch, and the
+    // register-staged kernel spills less
+    constexpr bool kUseDma = sizeof(T) == 2 && P <= 2;
     const size_t red = (size_t)(a.Dphi / 32) * 16 * 64 * sizeof(float);
+    size_t kv;
+    const void* fn;
+    if constexpr (kUseDma) {
+        using Tile = DmaTiles<D, StateShape<P>::NW>;
+        kv = 3 * (size_t)(Tile::K_ELEMS + Tile::V_ELEMS) * sizeof(T);
+        fn = reinterpret_cast<const void*>(state_dma_kernel<D, P>);
+    } else {
+        using Tile = KVTile<T, D, NT>;
+        kv = 2 * (size_t)(Tile::K_ELEMS + Tile::V_ELEMS) * sizeof(T);
+        fn = reinterpret_cast<const void*>(state_kernel<T, D, P>);
+    }
     const size_t lds = kv > red ? kv : red;
-    auto fn = state_kernel<T, D, P>;
     // raise the dynamic LDS limit of this instantiation once per device (idempotent, so a
     // race between host threads only repeats the call)
     static size_t lds_set[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
     if (lds > lds_set[dev]) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         lds_set[dev] = lds;
     }
-    hipLaunchKernelGGL(fn, dim3(a.BH * a.G), dim3(NT), lds, stream, a);
+    if constexpr (kUseDma) {
+        auto kfn = state_dma_kernel<D, P>;
+        hipLaunchKernelGGL(kfn, dim3(a.BH * a.G), dim3(NT), lds, stream, a);
+    } else {
+        auto kfn = state_kernel<T, D, P>;
+        hipLaunchKernelGGL(kfn, dim3(a.BH * a.G), dim3(NT), lds, stream, a);
+    }
     return hipGetLastError();
 }
 
