@@ -61,8 +61,7 @@ __device__ inline void dma_rows(const void* src, int rows, int row_bytes, bool p
         const int q = j * 64 + lane;
         if (q < nch) {
             const int row = q / cpr, c = q % cpr;
-            dma16_v(reinterpret_cast<const unsigned char*>(src) + (int64_t)row * row_bytes + (c < dch ? c : 0) * 16,
-                    lds_addr(dst + j * 1024));
+            dma16_s(src, (uint32_t)(row * row_bytes + (c < dch ? c : 0) * 16), lds_addr(dst + j * 1024));
         }
     }
 }

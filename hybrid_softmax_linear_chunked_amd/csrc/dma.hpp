@@ -19,20 +19,13 @@ __device__ inline uint32_t lds_addr(const void* p) {
 // tracked by the explicit vmcnt waits of the pipeline instead.  The instruction has no
 // register result and reads its address operands and M0 (the LDS base, one wait state
 // after it is written) at issue; M0 is saved and restored around it.
-__device__ inline void dma16_s(const void* gbase, uint32_t voff, uint32_t lds) {  // uniform base + lane offset
+__device__ inline void dma16_s(const void* gbase, uint32_t voff, uint32_t lds) {  // uniform base + lane byte offset
     uint32_t keep;
     asm volatile(
         "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
         : "=&s"(keep)
         : "v"(voff), "s"(gbase), "s"(lds)
         : "memory");
-}
-__device__ inline void dma16_v(const void* gaddr, uint32_t lds) {  // per-lane address
-    uint32_t keep;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(keep)
-                 : "v"(gaddr), "s"(lds)
-                 : "memory");
 }
 
 // K/V tiles of 64 tokens moved HBM -> LDS by the LDS-DMA path (global_load_lds_dwordx4):
@@ -76,14 +69,6 @@ struct DmaTiles {
     }
     // one lane's HBM chunk for tile tokens from t0; CHECK clamps to the window, TWO picks the
     // segment of the two-segment (streaming) window
-    template <bool CHECK, bool TWO>
-    __device__ static inline const T* src_chunk(const T* b1, const T* b2, int len1, int t0, int Lk, uint32_t off) {
-        int g = t0 + (int)(off / D);
-        if (CHECK) g = min(g, Lk - 1);
-        const uint32_t col = off % D;
-        if (TWO && g >= len1) return b2 + (int64_t)(g - len1) * D + col;
-        return b1 + (int64_t)g * D + col;
-    }
     template <bool CHECK, bool TWO, int NI, int PW>
     __device__ static inline void issue(const T* b1, const T* b2, int len1, int t0, int Lk, T* dst, int wave,
                                         const uint32_t (&off)[PW]) {
@@ -92,8 +77,17 @@ struct DmaTiles {
             const int j = wave + i * NW;
             if (NI % NW != 0 && j >= NI) break;
             const uint32_t lds = lds_addr(dst + j * 512);
-            if (!CHECK && !TWO) dma16_s(b1 + (int64_t)t0 * D, off[i] * (uint32_t)sizeof(T), lds);
-            else dma16_v(src_chunk<CHECK, TWO>(b1, b2, len1, t0, Lk, off[i]), lds);
+            if (!CHECK && !TWO) {
+                dma16_s(b1 + (int64_t)t0 * D, off[i] * (uint32_t)sizeof(T), lds);
+                continue;
+            }
+            // token of this lane's chunk (clamped to the window) and its segment; each
+            // segment is a uniform base, the lanes of the other one sit out (exec mask)
+            int g = t0 + (int)(off[i] / D);
+            if (CHECK) g = min(g, Lk - 1);
+            const uint32_t col = off[i] % D;
+            if (TWO && g >= len1) dma16_s(b2, ((uint32_t)(g - len1) * D + col) * (uint32_t)sizeof(T), lds);
+            else dma16_s(b1, ((uint32_t)g * D + col) * (uint32_t)sizeof(T), lds);
         }
     }
     template <bool CHECK, bool TWO>
