@@ -31,7 +31,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0
 METRIC = "hybrid-attn tokens/s & TFLOP/s (% bf16 MFMA peak), 32760-token 12-head layer"
-KERNEL_SOURCES = ["attn_wide.hip", "attn_common.hpp", "tiles.hpp", "common.hpp", "kernels.hpp"]
+KERNEL_SOURCES = ["attn_wide.hip", "attn_common.hpp", "dma.hpp", "tiles.hpp", "common.hpp", "kernels.hpp"]
 COUNTER_FILE = os.path.join(ROOT, "profiles", "attn_kernel_wan_5s_counters.txt")
 
 

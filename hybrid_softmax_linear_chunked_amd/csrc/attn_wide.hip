@@ -57,11 +57,18 @@ template <int NW>
 __device__ inline void dma_rows(const void* src, int rows, int row_bytes, bool pad, unsigned char* dst, int wave,
                                 int lane) {
     const int dch = row_bytes / 16, cpr = dch + (pad ? 1 : 0), nch = rows * cpr;
+    // chunk q = 64 j + lane of this wave's j = wave, wave + NW, ...: (row, c) = divmod(q, cpr),
+    // stepped by NW * 64 chunks without further divisions
+    int q = wave * 64 + lane, row = q / cpr, c = q % cpr;
+    const int step_r = NW * 64 / cpr, step_c = NW * 64 % cpr;
     for (int j = wave; j * 64 < nch; j += NW) {
-        const int q = j * 64 + lane;
-        if (q < nch) {
-            const int row = q / cpr, c = q % cpr;
-            dma16_s(src, (uint32_t)(row * row_bytes + (c < dch ? c : 0) * 16), lds_addr(dst + j * 1024));
+        if (q < nch) dma16_s(src, (uint32_t)(row * row_bytes + (c < dch ? c : 0) * 16), lds_addr(dst + j * 1024));
+        q += NW * 64;
+        row += step_r;
+        c += step_c;
+        if (c >= cpr) {
+            c -= cpr;
+            ++row;
         }
     }
 }
@@ -107,31 +114,40 @@ __device__ inline void wide_linear_and_merge(const AttnArgs& a, const Window<bf1
         for (int db = 0; db < NDB; ++db) yacc[db] = zero16();
         float zq = 0.f;
         if (has_lin) {
+            // one 32-feature block at a time, every power of it (all powers are staged), so
+            // only that block's u and phi are live
             constexpr int JBMAX = 4;  // Dphi <= 128
-            float uu[JBMAX][16];
 #pragma unroll
             for (int jb = 0; jb < JBMAX; ++jb) {
                 if (jb >= NJB) break;
                 f32x16 u = M::mma(M::load(Ws + (jb * 32 + col) * WLD + h * EPL), qf[qb][0], zero16());
 #pragma unroll
                 for (int st = 1; st < NS; ++st) u = M::mma(M::load(Ws + (jb * 32 + col) * WLD + st * KS + h * EPL), qf[qb][st], u);
+                float bb[16];  // rows crow(4 g + i, h) are 4 consecutive features; biases are only 4-byte aligned
 #pragma unroll
-                for (int r = 0; r < 16; ++r) uu[jb][r] = softplus_fast<T>(u[r] + (bq ? bq[jb * 32 + crow(r, h)] : 0.f));
-            }
-            for (int pw = 1; pw <= P; ++pw) {
-                const T* Sp = Ss + (pw - 1) * D * SLD;
-                const float* zp = Zs + (pw - 1) * Dphi;
+                for (int r = 0; r < 16; ++r) bb[r] = 0.f;
+                if (bq) {
 #pragma unroll
-                for (int jb = 0; jb < JBMAX; ++jb) {
-                    if (jb >= NJB) break;
-                    float ph[16];
+                    for (int r = 0; r < 16; ++r) bb[r] = bq[jb * 32 + crow(r, h)];
+                }
+                float uu[16], ph[16];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float v = uu[jb][r];
-                        for (int e = 1; e < pw; ++e) v *= uu[jb][r];
-                        ph[r] = v;
-                        zq += v * zp[jb * 32 + crow(r, h)];
+                for (int r = 0; r < 16; ++r) {
+                    uu[r] = softplus_fast<T>(u[r] + bb[r]);
+                    ph[r] = uu[r];
+                }
+                for (int pw = 1; pw <= P; ++pw) {
+                    if (pw > 1) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) ph[r] *= uu[r];
                     }
+                    const float* zp = Zs + (pw - 1) * Dphi + jb * 32 + h * 4;
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const float4 z4 = *reinterpret_cast<const float4*>(zp + g4 * 8);
+                        zq += ph[g4 * 4 + 0] * z4.x + ph[g4 * 4 + 1] * z4.y + ph[g4 * 4 + 2] * z4.z + ph[g4 * 4 + 3] * z4.w;
+                    }
+                    const T* Sp = Ss + (pw - 1) * D * SLD;
 #pragma unroll
                     for (int t = 0; t < TPB; ++t) {
                         const typename M::frag bfr = M::pack(ph + t * EPL);
@@ -158,6 +174,8 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
     constexpr int KS = M::KS, EPL = M::EPL, NS = D / KS, NDB = D / 32;
     constexpr int TPB = 32 / KS;  // value-product steps per 32-token sub-step
     constexpr int BK = Tile::BK;
+    constexpr int PWMAX = Tile::PWK > Tile::PWV ? Tile::PWK : Tile::PWV;
+    static_assert(PWMAX <= TPB * NDB, "a sub-step has fewer product pairs than copy instructions");
 
     extern __shared__ __align__(16) unsigned char smem[];
     T* const kring = reinterpret_cast<T*>(smem);
@@ -172,6 +190,7 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform
+    __builtin_assume(wave >= 0 && wave < NW);
     const int lane = tid % 64, col = lane % 32, h = lane / 32;
     const int qw = w.qt * BQ + wave * QB * 32;
     const bool wave_live = qw < w.Lq;
@@ -290,7 +309,7 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
     // (the last tile, swept first): keys of u from key_limit(u) on get a score of -inf.  At
     // the end of the sweep the look-ahead and the K reads land in ring slots whose contents
     // are never used; every read stays inside the ring.
-    auto sub_full = [&](int u, f32x16 (&Sc)[QB], f32x16 (&Sn)[QB], auto mask_tag) {
+    auto sub_full = [&](int u, f32x16 (&Sc)[QB], f32x16 (&Sn)[QB], auto mask_tag, auto&& dma_part) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int kl = MASK ? key_limit(u) : 32;
         if (MASK && kl < 32) {
@@ -339,6 +358,13 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
             const int db = i % NDB, t = i / NDB;
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = M::mma(vf[i], pf[t][qb], oacc[db][qb]);
+            // one DMA instruction of the tile copy after each pair of products, so that the
+            // copies issue in the shadow of the products instead of in a burst ahead of them
+            if (i < PWMAX) {
+                __builtin_amdgcn_sched_barrier(0);
+                dma_part(i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
 
@@ -372,19 +398,52 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
             }
             // sweep position i holds sub-steps 2i and 2i+1; position 0 (the last tile of the
             // window) is the only one that can hold a ragged or an empty sub-step
-            auto position = [&](int i, auto mask_tag) {
-                // batch of position i: K of i+3 and V of i+2, into the slots position i-1 used
+            auto none = [](int) {};
+            // Sweep position i: batch K of i+3 and V of i+2, into the slots position i-1 used
+            // (free once its barrier has passed), and sub-steps 2i and 2i+1.
+            //   UPFRONT: the batch is issued ahead of the products, by the general copy (clamped
+            //   to the window, and split between the two segments of a streaming window).  For
+            //   position 0 (with the ragged tile), streaming windows and waves without queries.
+            //   Otherwise the copy is spread over the products, K over the first sub-step and V
+            //   over the second: tiles past position 0 of a one-segment window are whole tiles
+            //   with a uniform base.  Near the end, where no tile is left to fetch, the copy is still
+            //   issued, of a whole tile into the slot just freed (nothing reads that slot again
+            //   in this sweep, and the next workgroup barrier waits for it), so the loop has no
+            //   branches and the wait one count.
+            auto position = [&](int i, auto mask_tag, auto upfront_tag) {
+                constexpr bool UPFRONT = decltype(upfront_tag)::value;
                 const bool kis = i + 3 < nt, vis = i + 2 < nt;
-                if (kis) dma_k(i + 3, kslot(i + 3));
-                if (vis) dma_v(i + 2, vslot(i + 2));
-                if (wave_live) {
-                    sub_full(2 * i, SA, SB, mask_tag);
-                    sub_full(2 * i + 1, SB, SA, mask_tag);
+                if (UPFRONT || !wave_live) {
+                    if (kis) dma_k(i + 3, kslot(i + 3));
+                    if (vis) dma_v(i + 2, vslot(i + 2));
+                    if (wave_live) {
+                        sub_full(2 * i, SA, SB, mask_tag, none);
+                        sub_full(2 * i + 1, SB, SA, mask_tag, none);
+                    }
+                    tile_sync(kis, vis);
+                    return;
                 }
-                tile_sync(kis, vis);
+                const int last = nt - 1;
+                const int tk = tile_of(min(i + 3, last)) * BK, tv = tile_of(min(i + 2, last)) * BK;
+                const T* const kb = w.src.k1 + (int64_t)tk * D;
+                const T* const vb = w.src.v1 + (int64_t)tv * D;
+                T* const kd = kslot(i + 3);
+                T* const vd = vslot(i + 2);
+                auto kpart = [&](int j) {
+                    if (j < Tile::PWK) tile.issue_k_at(j, kb, kd, wave);
+                };
+                auto vpart = [&](int j) {
+                    if (j < Tile::PWV) tile.issue_v_at(j, vb, vd, wave);
+                };
+                sub_full(2 * i, SA, SB, mask_tag, kpart);
+                sub_full(2 * i + 1, SB, SA, mask_tag, vpart);
+                tile_sync(true, true);
             };
-            position(0, std::true_type{});
-            for (int i = 1; i < nt; ++i) position(i, std::false_type{});
+            position(0, std::true_type{}, std::true_type{});
+            // A streaming window keeps the copies up front: its tiles may straddle the two
+            // segments, and a second variant of the loop body costs the allocator its
+            // registers.
+            for (int i = 1; i < nt; ++i) position(i, std::false_type{}, std::integral_constant<bool, STREAM>{});
         }
         bool over = false;
 #pragma unroll

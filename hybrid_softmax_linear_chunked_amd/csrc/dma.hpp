@@ -19,12 +19,41 @@ __device__ inline uint32_t lds_addr(const void* p) {
 // tracked by the explicit vmcnt waits of the pipeline instead.  The instruction has no
 // register result and reads its address operands and M0 (the LDS base, one wait state
 // after it is written) at issue; M0 is saved and restored around it.
+// The base and the LDS address are wave-uniform; readfirstlane states it to the compiler,
+// which may otherwise hold them in vector registers where they merge over branches.
+__device__ inline const void* uniform_ptr(const void* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ inline void dma16_s(const void* gbase, uint32_t voff, uint32_t lds) {  // uniform base + lane byte offset
+    gbase = uniform_ptr(gbase);
+    lds = __builtin_amdgcn_readfirstlane(lds);
     uint32_t keep;
     asm volatile(
         "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
         : "=&s"(keep)
         : "v"(voff), "s"(gbase), "s"(lds)
+        : "memory");
+}
+
+// The same, issued only where `issue` holds (wave-uniform) without a branch: the copy runs
+// under an EXEC mask of the current lanes or of none (an instruction with no active lane
+// moves nothing), restored before the block ends.  Keeps a basic block whole, so the
+// scheduler can interleave the products around it.
+__device__ inline void dma16_s_if(const void* gbase, uint32_t voff, uint32_t lds, bool issue) {
+    // arithmetic, not a select: a select of the EXEC value becomes a branch
+    gbase = uniform_ptr(gbase);
+    lds = __builtin_amdgcn_readfirstlane(lds);
+    const uint32_t on = __builtin_amdgcn_readfirstlane((uint32_t)issue);
+    const uint64_t mask = __builtin_amdgcn_read_exec() & (0ull - (uint64_t)on);
+    uint32_t keep;
+    uint64_t keep_exec;
+    asm volatile(
+        "s_mov_b64 %1, exec\n\ts_mov_b64 exec, %5\n\ts_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0\n\ts_mov_b64 exec, %1"
+        : "=&s"(keep), "=&s"(keep_exec)
+        : "v"(voff), "s"(gbase), "s"(lds), "s"(mask)
         : "memory");
 }
 
@@ -62,33 +91,42 @@ struct DmaTiles {
         return (uint32_t)(row * D + (c < dchunks ? c : 0) * 8);
     }
     __device__ inline void init(int wave, int lane) {
+        // a wave's missing last instruction keeps offset 0 (it moves nothing)
 #pragma unroll
-        for (int i = 0; i < PWK; ++i) koff[i] = chunk_off((wave + i * NW) * 64 + lane, CPK, D / 8);
+        for (int i = 0; i < PWK; ++i) koff[i] = wave + i * NW < NIK ? chunk_off((wave + i * NW) * 64 + lane, CPK, D / 8) : 0u;
 #pragma unroll
-        for (int i = 0; i < PWV; ++i) voff[i] = chunk_off((wave + i * NW) * 64 + lane, CPV, D / 8);
+        for (int i = 0; i < PWV; ++i) voff[i] = wave + i * NW < NIV ? chunk_off((wave + i * NW) * 64 + lane, CPV, D / 8) : 0u;
     }
-    // one lane's HBM chunk for tile tokens from t0; CHECK clamps to the window, TWO picks the
-    // segment of the two-segment (streaming) window
+    // The i-th DMA instruction of this wave for the tile of tokens from t0 (none where the
+    // wave has fewer): each lane copies its chunk; CHECK clamps tokens to the window, TWO
+    // picks the segment of the two-segment (streaming) window
+    template <bool CHECK, bool TWO, int NI, int PW>
+    __device__ static inline void issue_one(int i, const T* b1, const T* b2, int len1, int t0, int Lk, T* dst,
+                                            int wave, const uint32_t (&off)[PW]) {
+        const int j = wave + i * NW;  // only the last instruction can be missing (wave < NW)
+        const bool may_miss = NI % NW != 0 && i == PW - 1;
+        if (!CHECK && !TWO) {
+            // the missing instruction is issued under an empty EXEC mask, to a valid address
+            if (may_miss) dma16_s_if(b1 + (int64_t)t0 * D, off[i] * (uint32_t)sizeof(T), lds_addr(dst + min(j, NI - 1) * 512), j < NI);
+            else dma16_s(b1 + (int64_t)t0 * D, off[i] * (uint32_t)sizeof(T), lds_addr(dst + j * 512));
+            return;
+        }
+        if (may_miss && j >= NI) return;
+        const uint32_t lds = lds_addr(dst + j * 512);
+        // token of this lane's chunk (clamped to the window) and its segment; each
+        // segment is a uniform base, the lanes of the other one sit out (exec mask)
+        int g = t0 + (int)(off[i] / D);
+        if (CHECK) g = min(g, Lk - 1);
+        const uint32_t col = off[i] % D;
+        if (TWO && g >= len1) dma16_s(b2, ((uint32_t)(g - len1) * D + col) * (uint32_t)sizeof(T), lds);
+        else dma16_s(b1, ((uint32_t)g * D + col) * (uint32_t)sizeof(T), lds);
+    }
+    // all of this wave's DMA instructions for a tile
     template <bool CHECK, bool TWO, int NI, int PW>
     __device__ static inline void issue(const T* b1, const T* b2, int len1, int t0, int Lk, T* dst, int wave,
                                         const uint32_t (&off)[PW]) {
 #pragma unroll
-        for (int i = 0; i < PW; ++i) {
-            const int j = wave + i * NW;
-            if (NI % NW != 0 && j >= NI) break;
-            const uint32_t lds = lds_addr(dst + j * 512);
-            if (!CHECK && !TWO) {
-                dma16_s(b1 + (int64_t)t0 * D, off[i] * (uint32_t)sizeof(T), lds);
-                continue;
-            }
-            // token of this lane's chunk (clamped to the window) and its segment; each
-            // segment is a uniform base, the lanes of the other one sit out (exec mask)
-            int g = t0 + (int)(off[i] / D);
-            if (CHECK) g = min(g, Lk - 1);
-            const uint32_t col = off[i] % D;
-            if (TWO && g >= len1) dma16_s(b2, ((uint32_t)(g - len1) * D + col) * (uint32_t)sizeof(T), lds);
-            else dma16_s(b1, ((uint32_t)g * D + col) * (uint32_t)sizeof(T), lds);
-        }
+        for (int i = 0; i < PW; ++i) issue_one<CHECK, TWO, NI, PW>(i, b1, b2, len1, t0, Lk, dst, wave, off);
     }
     template <bool CHECK, bool TWO>
     __device__ inline void issue_k(const KeySrc<T>& src, int t0, int Lk, T* Ks, int wave) const {
@@ -97,6 +135,14 @@ struct DmaTiles {
     template <bool CHECK, bool TWO>
     __device__ inline void issue_v(const KeySrc<T>& src, int t0, int Lk, T* Vs, int wave) const {
         issue<CHECK, TWO, NIV, PWV>(src.v1, src.v2, src.len1, t0, Lk, Vs, wave, voff);
+    }
+    // single instructions (i < PWK, PWV) of the copy of a whole tile that starts at `tile`
+    // (64 contiguous rows), for spreading the copy over the products of a sub-step
+    __device__ inline void issue_k_at(int i, const T* tile, T* Ks, int wave) const {
+        issue_one<false, false, NIK, PWK>(i, tile, tile, 0, 0, 0, Ks, wave, koff);
+    }
+    __device__ inline void issue_v_at(int i, const T* tile, T* Vs, int wave) const {
+        issue_one<false, false, NIV, PWV>(i, tile, tile, 0, 0, 0, Vs, wave, voff);
     }
 
     // A operand of (keys x d) products: keys kb*32 + col, contraction step s over d

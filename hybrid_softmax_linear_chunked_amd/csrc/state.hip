@@ -205,6 +205,7 @@ __global__ __launch_bounds__(StateShape<P>::NW * 64) void state_dma_kernel(const
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform
+    __builtin_assume(wave >= 0 && wave < NW);
     const int lane = tid % 64, col = lane % 32, h = lane / 32;
     const bool active = wave < TS * NJB;
     const int jb = wave / TS, ts = wave % TS;
