@@ -185,10 +185,34 @@ rehyat_status rehyat_phi(const rehyat_params* p, const void* x, const void* w, c
     return hip_status(launch_phi(a, p->in_dtype, stream));
 }
 
+// Tail-split scratch of the attention stage, after the states: one arrival counter per
+// split, then the partials of both halves.
+struct SplitLayout {
+    int splits, split_per_xcd;
+    size_t cnt, part, total;
+};
+
+SplitLayout split_layout(const rehyat_params* p) {
+    SplitLayout L;
+    const int G = state_frames(p);
+    const size_t base = G > 0 ? parallel_layout(p, G).total : 0;
+    L.splits = 0;
+    L.split_per_xcd = 0;
+    if (p->in_dtype == REHYAT_BF16) {
+        AttnArgs a = attn_common(p, nullptr, nullptr);
+        a.nchunks = num_chunks(p);
+        L.splits = wide_split_plan(a);
+        L.split_per_xcd = a.split_per_xcd;
+    }
+    L.cnt = base;
+    L.part = L.cnt + (L.splits > 0 ? align256((size_t)L.splits * sizeof(unsigned)) : 0);
+    L.total = L.part + (size_t)L.splits * wide_split_part_bytes(p->D);
+    return L;
+}
+
 size_t rehyat_workspace_bytes(const rehyat_params* p) {
     if (check_params(p, true) != REHYAT_OK) return 0;
-    const int G = state_frames(p);
-    return G > 0 ? parallel_layout(p, G).total : 0;
+    return split_layout(p).total;
 }
 
 rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, const void* v,
@@ -243,7 +267,7 @@ rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, cons
 
 rehyat_status rehyat_parallel_attend(const rehyat_params* p, const void* q, const void* k,
                                      const void* v, const void* wq, const float* bq, void* out,
-                                     const rehyat_aux* aux, const void* ws, size_t ws_bytes,
+                                     const rehyat_aux* aux, void* ws, size_t ws_bytes,
                                      hipStream_t stream) {
     rehyat_status st = check_params(p, true);
     if (st != REHYAT_OK) return st;
@@ -256,11 +280,12 @@ rehyat_status rehyat_parallel_attend(const rehyat_params* p, const void* q, cons
             return REHYAT_EALIGN;
     }
     const int G = state_frames(p);
-    const size_t need = G > 0 ? parallel_layout(p, G).total : 0;
+    const SplitLayout SL = split_layout(p);
+    const size_t need = SL.total;
     if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0)) return REHYAT_EWORKSPACE;
 
     const int64_t N = (int64_t)p->T * p->frame_tokens;
-    const char* w = reinterpret_cast<const char*>(ws);
+    char* w = reinterpret_cast<char*>(ws);
     AttnArgs a = attn_common(p, wq, bq);
     a.q = q;
     a.out = out;
@@ -286,6 +311,14 @@ rehyat_status rehyat_parallel_attend(const rehyat_params* p, const void* q, cons
     a.aux_bh_stride = N;
     a.stream = 0;
     a.nchunks = num_chunks(p);
+    a.split_per_xcd = SL.split_per_xcd;
+    if (SL.splits > 0) {
+        a.split_cnt = reinterpret_cast<unsigned*>(w + SL.cnt);
+        a.split_part = reinterpret_cast<float*>(w + SL.part);
+        // arrival counters start at zero (a fill kernel: capturable, unlike a memset)
+        const hipError_t e = launch_zero(reinterpret_cast<float*>(a.split_cnt), SL.splits, stream);
+        if (e != hipSuccess) return hip_status(e);
+    }
     return hip_status(launch_attn(a, p->in_dtype, p->out_dtype, stream));
 }
 
@@ -305,8 +338,7 @@ rehyat_status rehyat_forward_parallel_aux(const rehyat_params* p, const void* q,
             !aligned4_or_null(aux->lse) || !aligned4_or_null(aux->z))
             return REHYAT_EALIGN;
     }
-    const int G = state_frames(p);
-    const size_t need = G > 0 ? parallel_layout(p, G).total : 0;
+    const size_t need = split_layout(p).total;
     if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0)) return REHYAT_EWORKSPACE;
     st = rehyat_parallel_states(p, k, v, wk, bk, ws, ws_bytes, stream);
     if (st != REHYAT_OK) return st;

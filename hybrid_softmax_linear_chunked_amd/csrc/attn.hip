@@ -218,6 +218,7 @@ static hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
     hipError_t e = ensure_lds(reinterpret_cast<const void*>(fn), lds, lds_set);
     if (e != hipSuccess) return e;
     AttnArgs b = a;
+    b.split_per_xcd = 0;  // no tail split in this kernel
     attn_grid(b, NW * QB * 32);
     hipLaunchKernelGGL(fn, dim3(8 * b.per_xcd), dim3(NW * 64), lds, stream, b);
     return hipGetLastError();

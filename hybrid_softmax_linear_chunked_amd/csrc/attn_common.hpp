@@ -15,20 +15,57 @@ struct Window {
     int q0, Lq, Lk, ls;
     int img_slot;
     KeySrc<T> src;
+    int split, half;  // tail split index (-1: whole tile) and which half of the window
 };
 
-// Consecutive logical ids share a chunk and are placed on one XCD: workgroups are dealt
-// round-robin over the 8 XCDs, so id L runs on XCD L / per_xcd.  Returns false for the
-// padding ids of the grid.
+// Share of XCD x of N items dealt as 8 contiguous runs.
+__host__ __device__ inline int xcd_share(int64_t N, int x) { return (int)(N * (x + 1) / 8 - N * x / 8); }
+// Split tiles of XCD x (the last of its chunk-0 tiles) and the splits of the XCDs before it.
+__host__ __device__ inline int xcd_splits(int64_t NS, int per, int x) {
+    const int ns = xcd_share(NS, x);
+    return ns < per ? ns : per;
+}
+
+// Workgroups are dealt round-robin over the 8 XCDs (workgroup g runs on XCD g % 8, as
+// the (g / 8)-th of that XCD), and each XCD hands its workgroups to its CUs in order.
+// The query tiles are two classes: those of chunks c >= 1, whose softmax window includes
+// the To overlap frames, and the shorter ones of chunk 0.  Every XCD takes an equal
+// contiguous share of each class, longer class first, so that its last workgroups are the
+// short ones (a shorter tail) and the tiles of one chunk share an XCD's L2.  With tail
+// splitting, the last split_per_xcd chunk-0 tiles of an XCD come as pairs of workgroups,
+// one per half of the window.  Returns false for the padding workgroups of the grid.
 template <class T, int D, bool STREAM>
 __device__ inline bool decode_window(const AttnArgs& a, Window<T>& w) {
-    const int wgid = blockIdx.x;
-    const int L = (wgid % 8) * a.per_xcd + wgid / 8;
-    if (L >= a.total_tiles) return false;
-    w.qt = L % a.tiles_per_chunk;
-    const int rest = L / a.tiles_per_chunk;
-    w.c = rest % a.nchunks;
-    w.bh = rest / a.nchunks;
+    const int x = blockIdx.x % 8, p = blockIdx.x / 8;
+    const int tpc = a.tiles_per_chunk, cl = a.nchunks - 1;  // chunks of the longer class
+    const int NL = cl * a.BH * tpc, NS = a.BH * tpc;
+    const int l0 = (int)((int64_t)NL * x / 8), nl = (int)((int64_t)NL * (x + 1) / 8) - l0;
+    const int s0 = (int)((int64_t)NS * x / 8), ns = (int)((int64_t)NS * (x + 1) / 8) - s0;
+    const int ks = STREAM ? 0 : xcd_splits(NS, a.split_per_xcd, x);
+    w.split = -1;
+    w.half = 0;
+    if (p < nl) {
+        const int idx = l0 + p, ch = idx / tpc;
+        w.qt = idx % tpc;
+        w.c = 1 + ch % cl;
+        w.bh = ch / cl;
+    } else if (p < nl + ns + ks) {
+        const int r = p - nl;  // whole chunk-0 tiles, then the split pairs
+        int idx = s0 + r;
+        if (r >= ns - ks) {
+            const int pr = r - (ns - ks);
+            int base = 0;
+            for (int y = 0; y < x; ++y) base += xcd_splits(NS, a.split_per_xcd, y);
+            idx = s0 + ns - ks + pr / 2;
+            w.half = pr % 2;
+            w.split = base + pr / 2;
+        }
+        w.qt = idx % tpc;
+        w.c = 0;
+        w.bh = idx / tpc;
+    } else {
+        return false;
+    }
     w.hh = w.bh % a.H;
     const T* kb1 = reinterpret_cast<const T*>(a.k1) + (int64_t)w.bh * a.kv1_bh_stride;
     const T* vb1 = reinterpret_cast<const T*>(a.v1) + (int64_t)w.bh * a.kv1_bh_stride;
@@ -236,11 +273,23 @@ __device__ inline void linear_and_merge(const AttnArgs& a, const Window<T>& w, u
 }
 
 // Launch bookkeeping common to the attention kernels.
-inline void attn_grid(AttnArgs& b, int BQ) {
+// Grid bookkeeping: workgroups per XCD (a share of each class plus the second halves of
+// its split tiles, see decode_window).  Returns the number of split tiles.
+inline int attn_grid(AttnArgs& b, int BQ) {
     const int qlen = b.stream ? b.s_frames * b.n : b.Tc * b.n;
     b.tiles_per_chunk = (qlen + BQ - 1) / BQ;
     b.total_tiles = b.tiles_per_chunk * b.nchunks * b.BH;
-    b.per_xcd = (b.total_tiles + 7) / 8;
+    const int64_t NL = (int64_t)(b.nchunks - 1) * b.BH * b.tiles_per_chunk, NS = (int64_t)b.BH * b.tiles_per_chunk;
+    const int per = b.stream ? 0 : b.split_per_xcd;
+    int most = 0, splits = 0;
+    for (int x = 0; x < 8; ++x) {
+        const int ks = xcd_splits(NS, per, x);
+        const int cnt = xcd_share(NL, x) + xcd_share(NS, x) + ks;
+        most = cnt > most ? cnt : most;
+        splits += ks;
+    }
+    b.per_xcd = most;
+    return splits;
 }
 
 // Raise the dynamic LDS limit of a kernel once per device (idempotent, so a race between

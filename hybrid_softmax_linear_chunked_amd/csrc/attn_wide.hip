@@ -215,6 +215,13 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
 
     const float sc = a.scale_log2;
     const int nt = (Lk + BK - 1) / BK;    // 64-token tiles
+    // sweep positions of this workgroup: all, or one half of a split tile's window
+    int p0 = 0, p1 = nt;
+    if (w.split >= 0) {
+        const int hp = (nt + 1) / 2;
+        if (w.half == 0) p1 = hp;
+        else p0 = hp;
+    }
     const bool ragged = Lk % BK != 0;
     // Tiles are processed last one first: position i of the sweep holds window tile
     // tile_of(i), so the only ragged tile (and the masking it needs) comes before the
@@ -377,21 +384,21 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) oacc[db][qb] = zero16();
         }
-        if (nt > 0) {
-            // prologue: sweep tiles 0 and 1 (K) and 0 (V) in LDS, K of 2 and V of 1 in flight
-            // (the batch of position -1); scores of sub-step 0
-            dma_k(0, kslot(0));
-            dma_v(0, vslot(0));
-            if (nt > 1) dma_k(1, kslot(1));
+        if (p1 > p0) {
+            // prologue: positions p0 and p0+1 (K) and p0 (V) in LDS, K of p0+2 and V of p0+1
+            // in flight (the batch of position p0-1); scores of the first sub-step
+            dma_k(p0, kslot(p0));
+            dma_v(p0, vslot(p0));
+            if (p0 + 1 < p1) dma_k(p0 + 1, kslot(p0 + 1));
             dma_sync();
-            if (nt > 2) dma_k(2, kslot(2));
-            if (nt > 1) dma_v(1, vslot(1));
+            if (p0 + 2 < p1) dma_k(p0 + 2, kslot(p0 + 2));
+            if (p0 + 1 < p1) dma_v(p0 + 1, vslot(p0 + 1));
             if (wave_live) {
-                qk(kslot(0), 0, SA);
-                read_k(1);
+                qk(kslot(p0), 2 * p0, SA);
+                read_k(2 * p0 + 1);
                 if (first) {
                     float mx[QB] = {-INFINITY, -INFINITY};
-                    rowmax(0, SA, mx);
+                    rowmax(2 * p0, SA, mx);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) m_ref[qb] = pair_max(mx[qb]) * sc;
                 }
@@ -412,7 +419,7 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
             //   branches and the wait one count.
             auto position = [&](int i, auto mask_tag, auto upfront_tag) {
                 constexpr bool UPFRONT = decltype(upfront_tag)::value;
-                const bool kis = i + 3 < nt, vis = i + 2 < nt;
+                const bool kis = i + 3 < p1, vis = i + 2 < p1;
                 if (UPFRONT || !wave_live) {
                     if (kis) dma_k(i + 3, kslot(i + 3));
                     if (vis) dma_v(i + 2, vslot(i + 2));
@@ -423,7 +430,7 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
                     tile_sync(kis, vis);
                     return;
                 }
-                const int last = nt - 1;
+                const int last = p1 - 1;  // >= i >= 1: a whole tile
                 const int tk = tile_of(min(i + 3, last)) * BK, tv = tile_of(min(i + 2, last)) * BK;
                 const T* const kb = w.src.k1 + (int64_t)tk * D;
                 const T* const vb = w.src.v1 + (int64_t)tv * D;
@@ -439,11 +446,12 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
                 sub_full(2 * i + 1, SB, SA, mask_tag, vpart);
                 tile_sync(true, true);
             };
-            position(0, std::true_type{}, std::true_type{});
+            if (p0 == 0) position(0, std::true_type{}, std::true_type{});
+            else position(p0, std::false_type{}, std::true_type{});
             // A streaming window keeps the copies up front: its tiles may straddle the two
             // segments, and a second variant of the loop body costs the allocator its
             // registers.
-            for (int i = 1; i < nt; ++i) position(i, std::false_type{}, std::integral_constant<bool, STREAM>{});
+            for (int i = p0 + 1; i < p1; ++i) position(i, std::false_type{}, std::integral_constant<bool, STREAM>{});
         }
         bool over = false;
 #pragma unroll
@@ -458,7 +466,7 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
     if (run(true, l_tot)) {
         // exact row maxima by a score-only sweep, as the reference of a second sweep
         float mx[QB] = {-INFINITY, -INFINITY};
-        for (int i = 0; i < nt; ++i) {
+        for (int i = p0; i < p1; ++i) {
             dma_k(i, kslot(0));
             dma_sync();
             if (wave_live) {
@@ -472,6 +480,63 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) m_ref[qb] = pair_max(mx[qb]) * sc;
         run(false, l_tot);
+    }
+
+    if (!STREAM && w.split >= 0) {
+        // Tail split: both halves store their partial (unnormalised O, reference, row sum);
+        // the second to arrive merges the other's into its own and goes on to the epilogue,
+        // the first is done.  Device-scope fences order the partials before the count.
+        constexpr int NR = NDB * QB * 16 + 2 * QB;  // values per lane
+        float* const pair = a.split_part + (size_t)64 * NR * NW * 2 * w.split;
+        float* const mine = pair + (size_t)64 * NR * (w.half * NW + wave) + lane;
+        int r = 0;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mine[64 * r++] = oacc[db][qb][e];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            mine[64 * r++] = m_ref[qb];
+            mine[64 * r++] = l_tot[qb];
+        }
+        __threadfence();
+        __syncthreads();
+        unsigned prev = 0;
+        if (tid == 0) prev = atomicAdd(a.split_cnt + w.split, 1u);
+        if (!__syncthreads_or(tid == 0 && prev != 0)) return;
+        __threadfence();
+        // the merge is written in half order (half 0's terms first) whichever half runs it,
+        // so the result does not depend on the arrival order
+        const float* const other = pair + (size_t)64 * NR * ((1 - w.half) * NW + wave) + lane;
+        const bool h0 = w.half == 0;
+        float f0q[QB], f1q[QB];
+        r = NDB * QB * 16;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float mo = other[64 * r++], lo = other[64 * r++];
+            const float m0 = h0 ? m_ref[qb] : mo, m1 = h0 ? mo : m_ref[qb];
+            const float l0 = h0 ? l_tot[qb] : lo, l1 = h0 ? lo : l_tot[qb];
+            const float mm = fmaxf(m0, m1);
+            const float f0 = __builtin_amdgcn_exp2f(m0 - mm), f1 = __builtin_amdgcn_exp2f(m1 - mm);
+            l_tot[qb] = __builtin_fmaf(l0, f0, l1 * f1);
+            m_ref[qb] = mm;
+            f0q[qb] = f0;
+            f1q[qb] = f1;
+        }
+        r = 0;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float xs = oacc[db][qb][e], xo = other[64 * r++];
+                    const float x0 = h0 ? xs : xo, x1 = h0 ? xo : xs;
+                    oacc[db][qb][e] = __builtin_fmaf(x0, f0q[qb], x1 * f1q[qb]);
+                }
+        if (tid == 0) a.split_cnt[w.split] = 0u;  // ready for the next launch
     }
 
     if constexpr (EPI_ALL) wide_linear_and_merge<OT, D, NW>(a, w, smem, qw, wave, has_soft, has_lin, qf, oacc, m_ref, l_tot);
@@ -506,6 +571,27 @@ static hipError_t launch_wide_d(const AttnArgs& a, hipStream_t stream) {
         case 128: return launch_wide_one<OT, 128, STREAM>(a, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+// Tail split plan of the bf16 chunk-parallel launch: per XCD, the last kSplitPerXcd
+// chunk-0 query tiles run as two halves.  Only where the chunk-0 window spans at least four
+// 64-token tiles and a longer class exists (otherwise the grid is a single wave of equal
+// tiles and halves do not shorten it).  Sets a.split_per_xcd; returns the split count.
+int wide_split_plan(AttnArgs& a) {
+    constexpr int kSplitPerXcd = 8, NW = 4, QB = 2;
+    a.split_per_xcd = 0;
+    if (a.stream || a.linear_only || a.nchunks < 2) return 0;
+    const int lk0 = (a.Tc < a.T ? a.Tc : a.T) * a.n;
+    if ((lk0 + 63) / 64 < 4) return 0;
+    a.split_per_xcd = kSplitPerXcd;
+    AttnArgs b = a;
+    return attn_grid(b, NW * QB * 32);
+}
+
+// Scratch bytes of one split: two halves x 4 waves x 64 lanes x (O + reference + sum).
+size_t wide_split_part_bytes(int D) {
+    const size_t nr = (size_t)(D / 32) * 2 * 16 + 4;
+    return 2 * 4 * 64 * nr * sizeof(float);
 }
 
 hipError_t launch_attn_wide(const AttnArgs& a, int out_dtype, hipStream_t stream) {

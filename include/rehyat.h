@@ -100,7 +100,10 @@ rehyat_status rehyat_phi(const rehyat_params* p, const void* x, const void* w, c
                          void* feat, hipStream_t stream);
 
 /* Workspace bytes needed by rehyat_forward_parallel(_aux): per-frame state partials and
- * their prefix, float32 [B,H,T,F,D] + [B,H,T,F] (0 if no chunk has a linear region). */
+ * their prefix, float32 [B,H,T,F,D] + [B,H,T,F] (none if no chunk has a linear region),
+ * followed by the scratch of the attention stage's tail split (bf16 inputs, several
+ * chunks: at most 64 query tiles of 256 queries, each swept as two halves of its window
+ * whose float32 partials meet there; about 135 KB per split at D = 128).  0 if neither. */
 size_t rehyat_workspace_bytes(const rehyat_params* p);
 
 /* Chunk-parallel forward (all chunks at once): per-frame partials of phi_k(K)^T [V|1],
@@ -125,14 +128,15 @@ rehyat_status rehyat_forward_parallel_aux(const rehyat_params* p, const void* q,
  * the stages separately.  rehyat_parallel_states writes the per-frame partials of
  * phi_k(K)^T [V|1] and their inclusive prefix over frames into ws (blog 2.3 state sums);
  * rehyat_parallel_attend runs the windowed softmax tile kernel with the fused linear part,
- * reading the prefix from ws.  Same arguments, layouts and status codes as above; ws must
- * hold the states of the same k, v, wk, bk when attend runs (stream order suffices). */
+ * reading the prefix from ws and writing the tail-split scratch after it (so calls on one
+ * ws must not overlap).  Same arguments, layouts and status codes as above; ws must hold
+ * the states of the same k, v, wk, bk when attend runs (stream order suffices). */
 rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, const void* v,
                                      const void* wk, const float* bk, void* ws, size_t ws_bytes,
                                      hipStream_t stream);
 rehyat_status rehyat_parallel_attend(const rehyat_params* p, const void* q, const void* k,
                                      const void* v, const void* wq, const float* bq, void* out,
-                                     const rehyat_aux* aux, const void* ws, size_t ws_bytes,
+                                     const rehyat_aux* aux, void* ws, size_t ws_bytes,
                                      hipStream_t stream);
 
 /* Streaming (blog 5.2: states = init_states(); output, states = block(chunk, states)).

@@ -91,7 +91,13 @@ def test_fullsize_stream_equals_parallel_bitwise():
         outs.append(st.step(d["q"][:, :, sl].contiguous(), d["k"][:, :, sl].contiguous(),
                             d["v"][:, :, sl].contiguous(), f1 - f0))
     torch.cuda.synchronize()
-    assert torch.equal(torch.cat(outs, dim=2), par)
+    s_out = torch.cat(outs, dim=2)
+    # bit for bit, except the chunk-0 query tiles the parallel launch splits in two halves of
+    # the window (tail split): those agree to the rounding of the merge
+    first = w.Tc * w.n
+    assert torch.equal(s_out[:, :, first:], par[:, :, first:])
+    d0 = (s_out[:, :, :first].float() - par[:, :, :first].float()).abs().max().item()
+    assert d0 <= 2 ** -6 * max(1.0, par[:, :, :first].float().abs().max().item())
 
 
 def test_stream_peak_memory_is_flat_in_clip_length():
