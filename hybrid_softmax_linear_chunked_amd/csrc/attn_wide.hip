@@ -257,17 +257,22 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
     };
-    // End of a full tile: the DMA batch issued one tile earlier is complete in every wave.
-    // Vector memory operations complete in issue order, so a wave waits until no more than
-    // the batch it issued this tile (counted for the wave with the fewest DMA instructions)
-    // is outstanding.  The barrier is a bare s_barrier: a workgroup fence would wait for
-    // this tile's batch as well.  The memory clobber keeps LDS accesses on their side.
+    // End of a sweep position: the DMA batch issued one position earlier is complete in every
+    // wave.  Vector memory operations complete in issue order, so a wave waits until no more
+    // than the batch it issued in this position (counted for the wave with the fewest DMA
+    // instructions) is outstanding.  LDS reads need no wait here: after the barrier of
+    // position i, the next batch overwrites the K slot of tile i (read in position i-1, its
+    // operands consumed by products up to position i) and the V slot of tile i (read and
+    // consumed in position i), and a read is complete once its product has issued; only the
+    // look-ahead reads of tile i+1 can still be in flight.  The barrier is a bare s_barrier:
+    // a workgroup fence would wait for this position's batch as well.  The memory clobber
+    // keeps LDS accesses on their side.
     auto tile_sync = [&](bool k_issued, bool v_issued) {
         constexpr int NKMIN = Tile::NIK / NW, NVMIN = Tile::NIV / NW;
         static_assert(NKMIN + NVMIN <= 15, "vmcnt immediate range");
-        if (k_issued && v_issued) __builtin_amdgcn_s_waitcnt(0x0070 | (NKMIN + NVMIN));  // + lgkmcnt(0)
-        else if (v_issued) __builtin_amdgcn_s_waitcnt(0x0070 | NVMIN);
-        else __builtin_amdgcn_s_waitcnt(0x0070);
+        if (k_issued && v_issued) __builtin_amdgcn_s_waitcnt(0x0F70 | (NKMIN + NVMIN));  // lgkmcnt: no wait
+        else if (v_issued) __builtin_amdgcn_s_waitcnt(0x0F70 | NVMIN);
+        else __builtin_amdgcn_s_waitcnt(0x0F70);
         asm volatile("s_barrier" ::: "memory");
     };
 
