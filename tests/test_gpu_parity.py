@@ -205,7 +205,10 @@ def test_scores_far_above_window_start(dt):
     the planted keys every row sum overflows its range check and the window is swept again
     against the exact row maximum.  The fp32 kernel rescales its running maximum instead.
     Both must match the oracle, the log-sum-exp included (ReHyAt blog, maplevalley.com.cn,
-    2.2.1)."""
+    2.2.1).  In bf16 the chunk-0 tiles run as two halves of their window (tail split): the
+    half holding frame 0's planted key after its first sub-step takes the second sweep, the
+    other starts at frame 1's planted key and does not, and the merge of the two is checked
+    here too."""
     p = rh.Params(1, 2, 128, 7, 100, 3, 1, 128, 2, 0, dt, dt)
     x = _far_score_inputs(p, seed=5)
     q, k = x["q"], x["k"]
@@ -226,7 +229,8 @@ def test_scores_far_above_window_start(dt):
 
 def test_stream_equals_parallel_far_scores():
     """The streaming kernel takes the same second sweep on the same windows: bitwise equal to
-    the chunk-parallel output on the planted far-score inputs."""
+    the chunk-parallel output on the planted far-score inputs, except the chunk-0 tiles the
+    parallel launch splits in two halves, which agree to the merge's rounding."""
     p = rh.Params(1, 2, 128, 7, 100, 3, 1, 128, 2, 0, BF16, BF16)
     x = _far_score_inputs(p, seed=6)
     d = to_dev(x, p)
@@ -239,4 +243,8 @@ def test_stream_equals_parallel_far_scores():
         outs.append(st.step(d["q"][:, :, sl].contiguous(), d["k"][:, :, sl].contiguous(),
                             d["v"][:, :, sl].contiguous(), f1 - f0))
     torch.cuda.synchronize()
-    assert torch.equal(torch.cat(outs, dim=2), par)
+    s_out = torch.cat(outs, dim=2)
+    first = p.Tc * p.n
+    assert torch.equal(s_out[:, :, first:], par[:, :, first:])
+    d0 = (s_out[:, :, :first].float() - par[:, :, :first].float()).abs().max().item()
+    assert d0 <= 2 ** -6 * max(1.0, par[:, :, :first].float().abs().max().item())
