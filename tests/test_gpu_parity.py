@@ -64,11 +64,14 @@ def test_forward_parallel_matches_oracle(p):
     x = rand_inputs(p, seed=1, bias=(p.B == 2))
     d = to_dev(x, p)
     out, aux = run_parallel(p, d)
+    # the production call, without per-part outputs
+    out_only = run_parallel(p, d, aux=False)
     torch.cuda.synchronize()
     op = oracle_params(p)
     ref, rax = oracle.parallel(op, x["q"], x["k"], x["v"], x["wq"], x["wk"], x["bq"], x["bk"], aux=True)
     tol = TOL[p.in_dtype]
     assert slab_err(out.float().cpu().numpy(), ref) <= tol
+    assert slab_err(out_only.float().cpu().numpy(), ref) <= tol
     # per-part outputs: each one is checked at the same bar where it is defined
     if not p.linear_only:
         assert slab_err(aux["o_soft"].cpu().numpy(), rax["osoft"]) <= tol
