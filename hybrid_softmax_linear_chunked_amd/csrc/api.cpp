@@ -222,9 +222,13 @@ rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, cons
     if (st != REHYAT_OK) return st;
     if (!aligned16(k) || !aligned16(v) || !aligned16(wk) || !aligned4_or_null(bk)) return REHYAT_EALIGN;
     const int G = state_frames(p);
-    const size_t need = G > 0 ? parallel_layout(p, G).total : 0;
+    const SplitLayout SL = split_layout(p);
+    const size_t need = SL.total;
     if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0)) return REHYAT_EWORKSPACE;
-    if (G == 0) return REHYAT_OK;
+    // the attention stage's tail-split counters start at zero (each split's second arrival
+    // sets its counter back, so they stay zero between attention calls)
+    unsigned* const cnt = SL.splits > 0 ? reinterpret_cast<unsigned*>(reinterpret_cast<char*>(ws) + SL.cnt) : nullptr;
+    if (G == 0) return cnt ? hip_status(launch_zero(reinterpret_cast<float*>(cnt), SL.splits, stream)) : REHYAT_OK;
 
     const int64_t N = (int64_t)p->T * p->frame_tokens;
     const int BH = p->B * p->H;
@@ -262,6 +266,8 @@ rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, cons
     sc.Tc = p->Tc;
     sc.To = p->To;
     sc.linear_only = p->linear_only;
+    sc.zero_cnt = cnt;
+    sc.nzero = SL.splits;
     return hip_status(launch_scan(sc, p->in_dtype, stream));
 }
 
@@ -313,11 +319,9 @@ rehyat_status rehyat_parallel_attend(const rehyat_params* p, const void* q, cons
     a.nchunks = num_chunks(p);
     a.split_per_xcd = SL.split_per_xcd;
     if (SL.splits > 0) {
+        // arrival counters: zeroed by rehyat_parallel_states, left zero by every call
         a.split_cnt = reinterpret_cast<unsigned*>(w + SL.cnt);
         a.split_part = reinterpret_cast<float*>(w + SL.part);
-        // arrival counters start at zero (a fill kernel: capturable, unlike a memset)
-        const hipError_t e = launch_zero(reinterpret_cast<float*>(a.split_cnt), SL.splits, stream);
-        if (e != hipSuccess) return hip_status(e);
     }
     return hip_status(launch_attn(a, p->in_dtype, p->out_dtype, stream));
 }

@@ -77,6 +77,8 @@ struct ScanArgs {
     int slots;
     int BH, D, Dphi, P;
     int T, Tc, To, linear_only;  // chunk schedule (parallel form)
+    unsigned* zero_cnt;     // counters to set to zero on the way (the attention stage's
+    int nzero;              // tail-split arrival counters), or null
 };
 
 // Copy of frames [f0, f0 + cnt) of a two-segment source into dst frames [0, cnt).

@@ -356,6 +356,8 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanArgs a) {
     constexpr int CPR = 32 * sizeof(T) / 16;  // 16-byte chunks per 32-element image row
     const int Dphi = a.Dphi, P = a.P, D = a.D, F = Dphi * P, NJB = Dphi / 32, NDB = D / 32;
     const int bh = blockIdx.y, tid = threadIdx.x;
+    if (a.zero_cnt && blockIdx.x == 0 && bh == 0)
+        for (int i = tid; i < a.nzero; i += 256) a.zero_cnt[i] = 0u;
     T* img = reinterpret_cast<T*>(a.simg) + (int64_t)bh * a.slots * F * D;
     float* zimg = a.zimg + (int64_t)bh * a.slots * F;
     const int nc = (a.T + a.Tc - 1) / a.Tc;

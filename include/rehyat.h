@@ -130,7 +130,9 @@ rehyat_status rehyat_forward_parallel_aux(const rehyat_params* p, const void* q,
  * rehyat_parallel_attend runs the windowed softmax tile kernel with the fused linear part,
  * reading the prefix from ws and writing the tail-split scratch after it (so calls on one
  * ws must not overlap).  Same arguments, layouts and status codes as above; ws must hold
- * the states of the same k, v, wk, bk when attend runs (stream order suffices). */
+ * the states of the same k, v, wk, bk when attend runs (stream order suffices).
+ * rehyat_parallel_states also sets the tail-split arrival counters to zero, and every
+ * completed attend leaves them zero, so attend may run any number of times per states. */
 rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, const void* v,
                                      const void* wk, const float* bk, void* ws, size_t ws_bytes,
                                      hipStream_t stream);

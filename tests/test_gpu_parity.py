@@ -152,6 +152,26 @@ def test_stream_rejects_calls_after_short_chunk():
     assert e.value.status == 5
 
 
+def test_attend_repeats_after_one_states_call():
+    """rehyat_parallel_states zeroes the tail-split arrival counters and every attention
+    call leaves them zero: repeated attention calls on one workspace agree bit for bit
+    (a counter left over would make a split's first half merge a stale partial)."""
+    p = CASES[16]
+    x = rand_inputs(p, seed=7)
+    d = to_dev(x, p)
+    ws = rh.alloc_bytes(rh.workspace_bytes(p))
+    rh.parallel_states(p, d["k"], d["v"], d["wk"], d["bk"], ws)
+    outs = []
+    for _ in range(3):
+        o = torch.empty_like(d["q"])
+        rh.parallel_attend(p, d["q"], d["k"], d["v"], d["wq"], d["bq"], o, ws)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    ref = oracle.parallel(oracle_params(p), x["q"], x["k"], x["v"], x["wq"], x["wk"], x["bq"], x["bk"])
+    assert slab_err(outs[2].float().cpu().numpy(), ref) <= TOL[p.in_dtype]
+
+
 @pytest.mark.parametrize("p", [CASES[1], CASES[16]], ids=_id)
 def test_deterministic(p):
     x = rand_inputs(p, seed=6)
