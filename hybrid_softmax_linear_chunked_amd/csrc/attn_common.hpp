@@ -20,7 +20,7 @@ struct Window {
 
 // Share of XCD x of N items dealt as 8 contiguous runs.
 __host__ __device__ inline int xcd_share(int64_t N, int x) { return (int)(N * (x + 1) / 8 - N * x / 8); }
-// Split tiles of XCD x (the last of its chunk-0 tiles) and the splits of the XCDs before it.
+// Number of split tiles of XCD x: the last `per` of its chunk-0 tiles (all, if it has fewer).
 __host__ __device__ inline int xcd_splits(int64_t NS, int per, int x) {
     const int ns = xcd_share(NS, x);
     return ns < per ? ns : per;
@@ -272,9 +272,9 @@ __device__ inline void linear_and_merge(const AttnArgs& a, const Window<T>& w, u
     }
 }
 
-// Launch bookkeeping common to the attention kernels.
-// Grid bookkeeping: workgroups per XCD (a share of each class plus the second halves of
-// its split tiles, see decode_window).  Returns the number of split tiles.
+// Launch bookkeeping common to the attention kernels: workgroups per XCD (a share of each
+// class plus the second halves of its split tiles, see decode_window).  Returns the number
+// of split tiles.
 inline int attn_grid(AttnArgs& b, int BQ) {
     const int qlen = b.stream ? b.s_frames * b.n : b.Tc * b.n;
     b.tiles_per_chunk = (qlen + BQ - 1) / BQ;
