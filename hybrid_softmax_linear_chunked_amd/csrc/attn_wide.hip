@@ -314,8 +314,8 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
 
     // Sub-step u (kpre holds the K operands of u+1), one basic block cut by scheduling
     // fences into
-    //   V operand reads of u | scores of u+1 with the softmax of u | K operand reads of u+2 |
-    //   value product of u.
+    //   V operand reads of u | scores of u+1 with the softmax of u | value product of u with
+    //   the K operand reads of u+2.
     // The scores and the softmax are written as 16 segments [MFMA, 1/16 of the softmax]; the
     // compiler's MFMA/exp interleaving places the vector work between the products.  MASK
     // (the last tile, swept first): keys of u from key_limit(u) on get a score of -inf.  At
@@ -362,9 +362,7 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
         }
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) l_run[qb] = lsum[qb];
-        __builtin_amdgcn_sched_barrier(0);
-        read_k(u + 2);
-        __builtin_amdgcn_sched_barrier(0);
+        read_k(u + 2);  // unfenced: the scheduler spreads these reads over the value product
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int db = i % NDB, t = i / NDB;
