@@ -5,6 +5,7 @@
 // workspace / state sizing, and the launch sequence on the caller's stream.  Every step
 // of the computation runs in the HIP kernels of attn.hip, state.hip and phi.hip.
 #include <cmath>
+#include <algorithm>
 #include <cstring>
 
 #include "../../include/rehyat.h"
@@ -86,7 +87,13 @@ ParallelLayout parallel_layout(const rehyat_params* p, int G) {
 }
 
 // Streaming state: S, Z (float, carried sums), the image of the current state, and two
-// overlap buffers of To frames of K and V.
+// overlap buffers of K and V with To frames per batch-head and 64 rows to spare: each step
+// copies the first rows of its chunk after the held frames, up to the next multiple of 64,
+// so that no 64-token key tile of the window spans both buffers.
+constexpr int kOverlapSpareRows = 64;
+
+int64_t overlap_rows(const rehyat_params* p) { return (int64_t)p->To * p->frame_tokens + kOverlapSpareRows; }
+
 struct StateLayout {
     size_t S, Z, img, zimg, ovk[2], ovv[2], total;
 };
@@ -94,7 +101,7 @@ struct StateLayout {
 StateLayout state_layout(const rehyat_params* p) {
     const size_t F = (size_t)p->P * p->Dphi;
     const size_t BH = (size_t)p->B * p->H;
-    const size_t ov = BH * (size_t)p->To * p->frame_tokens * p->D * elem_bytes(p->in_dtype);
+    const size_t ov = BH * (size_t)overlap_rows(p) * p->D * elem_bytes(p->in_dtype);
     StateLayout L;
     size_t off = 0;
     L.S = off; off += align256(BH * F * p->D * sizeof(float));
@@ -423,7 +430,7 @@ rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stre
     const int64_t next_abs = p->linear_only ? f1 : (f1 - p->To > 0 ? f1 - p->To : 0);
     const int F = p->P * p->Dphi;
     const int BH = p->B * p->H;
-    const int64_t ov_bh = (int64_t)p->To * n * p->D;
+    const int64_t ov_bh = overlap_rows(p) * p->D;
     const int64_t ch_bh = (int64_t)frames * n * p->D;
     float* Sp = reinterpret_cast<float*>(ws);
     float* Zp = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)BH * p->Tc * F * p->D * sizeof(float)));
@@ -468,7 +475,33 @@ rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stre
     s = absorb(absorbed, ls);
     if (s != REHYAT_OK) return s;
 
-    // 2. softmax over [held overlap | chunk], linear part from the state
+    // 2. softmax over [held overlap | chunk], linear part from the state.  The first rows
+    //    of the chunk are copied after the held frames, up to a multiple of 64 rows, and
+    //    read from there: every key tile but the last then lies in one buffer.
+    const int held_rows = p->linear_only ? 0 : held * n;
+    const int pad = held_rows % 64 == 0 ? 0 : std::min(64 - held_rows % 64, frames * n);
+    if (pad > 0) {
+        const int eb = (int)elem_bytes(p->in_dtype);
+        CopyArgs c;
+        c.s1k = k;  // source "frames" of one row each, all from the chunk
+        c.s1v = v;
+        c.s1_bh_stride = ch_bh;
+        c.nf1 = pad;
+        c.s2k = k;
+        c.s2v = v;
+        c.s2_bh_stride = ch_bh;
+        c.dk = reinterpret_cast<char*>(ovk) + (int64_t)held_rows * p->D * eb;
+        c.dv = reinterpret_cast<char*>(ovv) + (int64_t)held_rows * p->D * eb;
+        c.d_bh_stride = ov_bh;
+        c.f0 = 0;
+        c.cnt = pad;
+        c.BH = BH;
+        c.n = 1;
+        c.D = p->D;
+        c.elem_bytes = eb;
+        s = hip_status(launch_copy(c, stream));
+        if (s != REHYAT_OK) return s;
+    }
     AttnArgs a = attn_common(p, wq, bq);
     a.q = q;
     a.out = out;
@@ -487,6 +520,7 @@ rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stre
     a.s_frames = frames;
     a.s_held = p->linear_only ? 0 : held;
     a.s_ls = (int)ls;
+    a.s_pad = pad;
     a.nchunks = 1;
     s = hip_status(launch_attn(a, p->in_dtype, p->out_dtype, stream));
     if (s != REHYAT_OK) return s;

@@ -92,9 +92,10 @@ __device__ inline bool decode_window(const AttnArgs& a, Window<T>& w) {
         w.ls = a.s_ls;
         w.src.k1 = kb1;
         w.src.v1 = vb1;
-        w.src.k2 = reinterpret_cast<const T*>(a.k2) + (int64_t)w.bh * a.kv2_bh_stride;
-        w.src.v2 = reinterpret_cast<const T*>(a.v2) + (int64_t)w.bh * a.kv2_bh_stride;
-        w.src.len1 = a.s_held * a.n;
+        // the first s_pad chunk rows are read from their copy in the first segment
+        w.src.k2 = reinterpret_cast<const T*>(a.k2) + (int64_t)w.bh * a.kv2_bh_stride + (int64_t)a.s_pad * D;
+        w.src.v2 = reinterpret_cast<const T*>(a.v2) + (int64_t)w.bh * a.kv2_bh_stride + (int64_t)a.s_pad * D;
+        w.src.len1 = a.s_held * a.n + a.s_pad;
         w.img_slot = w.bh;
     }
     return true;

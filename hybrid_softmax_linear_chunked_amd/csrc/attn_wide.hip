@@ -413,17 +413,19 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
             // (free once its barrier has passed), and sub-steps 2i and 2i+1.
             //   UPFRONT: the batch is issued ahead of the products, by the general copy (clamped
             //   to the window, and split between the two segments of a streaming window).  For
-            //   position 0 (with the ragged tile), streaming windows and waves without queries.
+            //   position 0 (with the ragged tile), and in the chunk-parallel kernel for waves
+            //   without queries.
             //   Otherwise the copy is spread over the products, K over the first sub-step and V
-            //   over the second: tiles past position 0 of a one-segment window are whole tiles
-            //   with a uniform base.  Near the end, where no tile is left to fetch, the copy is still
-            //   issued, of a whole tile into the slot just freed (nothing reads that slot again
-            //   in this sweep, and the next workgroup barrier waits for it), so the loop has no
-            //   branches and the wait one count.
+            //   over the second (waves of a streaming window without queries issue it at once):
+            //   tiles past position 0 are whole tiles with a uniform base, in one segment.  Near
+            //   the end, where no tile is left to fetch, the copy is still issued, of a whole
+            //   tile into the slot just freed (nothing reads that slot again in this sweep, and
+            //   the next workgroup barrier waits for it), so the loop has no branches and the
+            //   wait one count.
             auto position = [&](int i, auto mask_tag, auto upfront_tag) {
                 constexpr bool UPFRONT = decltype(upfront_tag)::value;
                 const bool kis = i + 3 < p1, vis = i + 2 < p1;
-                if (UPFRONT || !wave_live) {
+                if (UPFRONT || (!STREAM && !wave_live)) {
                     if (kis) dma_k(i + 3, kslot(i + 3));
                     if (vis) dma_v(i + 2, vslot(i + 2));
                     if (wave_live) {
@@ -435,8 +437,10 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
                 }
                 const int last = p1 - 1;  // >= i >= 1: a whole tile
                 const int tk = tile_of(min(i + 3, last)) * BK, tv = tile_of(min(i + 2, last)) * BK;
-                const T* const kb = w.src.k1 + (int64_t)tk * D;
-                const T* const vb = w.src.v1 + (int64_t)tv * D;
+                // a streaming window's segment boundary is a multiple of 64 tokens (or past
+                // the last whole tile), so each of these tiles lies in one segment
+                const T* const kb = STREAM ? w.src.krow(tk, D) : w.src.k1 + (int64_t)tk * D;
+                const T* const vb = STREAM ? w.src.vrow(tv, D) : w.src.v1 + (int64_t)tv * D;
                 T* const kd = kslot(i + 3);
                 T* const vd = vslot(i + 2);
                 auto kpart = [&](int j) {
@@ -445,16 +449,20 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
                 auto vpart = [&](int j) {
                     if (j < Tile::PWV) tile.issue_v_at(j, vb, vd, wave);
                 };
-                sub_full(2 * i, SA, SB, mask_tag, kpart);
-                sub_full(2 * i + 1, SB, SA, mask_tag, vpart);
+                if (!STREAM || wave_live) {
+                    sub_full(2 * i, SA, SB, mask_tag, kpart);
+                    sub_full(2 * i + 1, SB, SA, mask_tag, vpart);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < Tile::PWK; ++j) kpart(j);
+#pragma unroll
+                    for (int j = 0; j < Tile::PWV; ++j) vpart(j);
+                }
                 tile_sync(true, true);
             };
             if (p0 == 0) position(0, std::true_type{}, std::true_type{});
             else position(p0, std::false_type{}, std::true_type{});
-            // A streaming window keeps the copies up front: its tiles may straddle the two
-            // segments, and a second variant of the loop body costs the allocator its
-            // registers.
-            for (int i = p0 + 1; i < p1; ++i) position(i, std::false_type{}, std::integral_constant<bool, STREAM>{});
+            for (int i = p0 + 1; i < p1; ++i) position(i, std::false_type{}, std::false_type{});
         }
         bool over = false;
 #pragma unroll

@@ -43,6 +43,10 @@ struct AttnArgs {
     int split_per_xcd;
     float* split_part;
     unsigned* split_cnt;
+    // streaming: rows of the chunk also copied after the held frames in the first segment,
+    // so that the segment boundary falls on a 64-token tile boundary (the second segment
+    // then starts s_pad rows into the chunk)
+    int s_pad;
 };
 
 // Per-frame partials of phi_k(K)^T V and sum phi_k(K) (state.hip).

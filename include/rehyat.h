@@ -142,8 +142,9 @@ rehyat_status rehyat_parallel_attend(const rehyat_params* p, const void* q, cons
                                      hipStream_t stream);
 
 /* Streaming (blog 5.2: states = init_states(); output, states = block(chunk, states)).
- * Device state bytes: S float32 [B,H,F,D], Z float32 [B,H,F] and two overlap buffers of
- * K and V [B,H,To*n,D] in in_dtype.  Independent of the clip length. */
+ * Device state bytes: S float32 [B,H,F,D], Z float32 [B,H,F], the image of the state and
+ * two overlap buffers of K and V [B,H,To*n+64,D] in in_dtype (the held frames, then up to
+ * 63 rows of the current chunk).  Independent of the clip length. */
 size_t rehyat_state_bytes(const rehyat_params* p);
 
 /* Workspace bytes for rehyat_chunk_step: per-frame partials for up to Tc frames,
