@@ -11,8 +11,10 @@ librehyat.so, on device-resident synthetic inputs.
 Printed as one JSON line: tokens/s (value), TFLOP/s and the fraction of the bf16 MFMA
 peak, the roofline of the dominant kernel (attention tile kernel, timed with HIP events
 on the stream it runs on), the full-softmax comparator on the same shapes, the 10 s
-streaming form with its peak memory at 21/41/81 frames, and the CPU oracle timed on a
-bounded sample of the same workload (which also serves as a parity spot check).
+streaming form with its peak memory at 21/41/81 frames, the chunking and feature-map
+variants the pages discuss (Tc/To presets and ablations, higher polynomial degree) on the
+same inputs, and the CPU oracle timed on a bounded sample of the same workload (which
+also serves as a parity spot check).
 """
 from __future__ import annotations
 
@@ -236,12 +238,50 @@ def main():
                                           "speedup_of_hybrid": round(cms / ms, 2)}
         del outc
         res["stream"] = stream_leg(rh, torch, WORKLOADS["wan_10s_stream"], dev)
+        res["variants"] = variants_leg(rh, torch, p, d, ms)
 
     if not args.no_cpu_baseline:
         cb, parity = cpu_baseline(w, x, out)
         res["cpu_baseline"] = cb
         res["parity_spot_check"] = parity
     print(json.dumps(res), flush=True)
+
+
+# chunking and feature-map variants the pages discuss (ReHyAt blog 3.2, 5.2, 5.3, 6;
+# mind-verse.de ablations), on the same Wan 5 s inputs
+VARIANTS = {"tc5_to2": dict(Tc=5, To=2), "tc1_to0": dict(Tc=1, To=0), "tc3_to0": dict(Tc=3, To=0),
+            "tc3_to2": dict(Tc=3, To=2), "tc7_to1": dict(Tc=7, To=1), "p3": dict(P=3), "p4": dict(P=4)}
+
+
+def variants_leg(rh, torch, p, d, base_ms, reps=5):
+    """Whole chunk-parallel forward (states, scan, attention) per variant: ms, tokens/s,
+    TFLOP/s of the FLOP model and its fraction of the bf16 peak."""
+    res = {}
+    for name, kw in VARIANTS.items():
+        pv = p.with_(**kw)
+        ws = rh.alloc_bytes(rh.workspace_bytes(pv), d["q"].device)
+        out = torch.empty((p.B, p.H, p.N, p.D), dtype=torch.bfloat16, device=d["q"].device)
+        call = lambda: rh.forward_parallel(pv, d["q"], d["k"], d["v"], d["wq"], d["wk"], out=out, ws=ws)
+        call()
+        call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        vms = e0.elapsed_time(e1) / reps
+        fl = flop_model(pv.B, pv.H, pv.D, pv.T, pv.n, pv.Tc, pv.To, pv.Dphi, pv.P)["total"]
+        tf = fl / (vms * 1e-3) / 1e12
+        res[name] = {"Tc": pv.Tc, "To": pv.To, "P": pv.P, "ms": round(vms, 4),
+                     "tokens_per_s": round(pv.B * pv.N / (vms * 1e-3), 1), "tflops": round(tf, 2),
+                     "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2), "flops": fl}
+        del ws, out
+    fl1 = flop_model(p.B, p.H, p.D, p.T, p.n, p.Tc, p.To, p.Dphi, p.P)["total"]
+    res["to2_vs_to1"] = {"flop_ratio": round(res["tc3_to2"]["flops"] / fl1, 4),
+                         "time_ratio": round(res["tc3_to2"]["ms"] / base_ms, 4)}
+    return res
 
 
 def stream_leg(rh, torch, w, dev):

@@ -1,0 +1,116 @@
+"""GPU parity of the chunking and feature-map variants the pages discuss, at the full
+Wan2.1-1.3B 5 s layer shape (B=1, 12 heads, D=128, 21 latent frames of 30x52 tokens,
+Dphi=128, bf16 inputs), in the launch configuration the benchmark times.
+
+Variants (ReHyAt blog, maplevalley.com.cn: 3.2 recommended values and the Tc=1 ablation,
+5.2 deployment presets and the Tc <= 7 limit, 5.3 raising the polynomial degree, 6 the
+To 1 -> 2 trade-off; mind-verse.de summary, ablations of Tc and To):
+  Tc=5 To=2 (workstation preset), Tc=1 To=0 (spatial-only softmax), Tc=3 To=0 (no
+  overlap), Tc=3 To=2 (wider overlap), Tc=7 To=1 (largest recommended chunk), P=3 and
+  P=4 (higher polynomial degree; P=3 splits Dphi=128 into 43/43/42).
+
+The oracle builds fp64 states in full for two slabs and evaluates a seeded sample of query
+rows per chunk (first and last row of every frame plus 48 random rows); the output and
+the per-part outputs are compared at the bf16 bar.  The workstation preset is also
+streamed chunk by chunk and must reproduce the chunk-parallel output bit for bit outside
+the tail-split chunk-0 tiles.
+"""
+import numpy as np
+import pytest
+import torch
+
+import hybrid_softmax_linear_chunked_amd as rh
+import oracle
+from synth_inputs import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+SEED = 5
+SLABS = [(0, 3), (0, 10)]
+VARIANTS = {
+    "tc5_to2": dict(Tc=5, To=2),
+    "tc1_to0": dict(Tc=1, To=0),
+    "tc3_to0": dict(Tc=3, To=0),
+    "tc3_to2": dict(Tc=3, To=2),
+    "tc7_to1": dict(Tc=7, To=1),
+    "p3": dict(P=3),
+    "p4": dict(P=4),
+}
+
+
+def variant_workload(name):
+    base = WORKLOADS["wan_5s"]
+    kw = {f: getattr(base, f) for f in ("B", "H", "D", "T", "n", "Tc", "To", "Dphi", "P", "dtype")}
+    kw.update(VARIANTS[name])
+    return type(base)(name=f"wan_5s_{name}", **kw)
+
+
+def sample_rows(w, per_chunk, seed):
+    rng = np.random.default_rng(seed)
+    rows = []
+    for f0 in range(0, w.T, w.Tc):
+        f1 = min(f0 + w.Tc, w.T)
+        rows += [f * w.n for f in range(f0, f1)] + [f * w.n + w.n - 1 for f in range(f0, f1)]
+        rows += rng.choice(np.arange(f0 * w.n, f1 * w.n), size=per_chunk, replace=False).tolist()
+    return np.unique(np.array(rows, dtype=np.int64))
+
+
+@pytest.fixture(scope="module")
+def inputs():
+    w = WORKLOADS["wan_5s"]
+    print("[variants] generating Wan 5 s inputs", flush=True)
+    x = make_inputs(w, SEED)
+    d = {key: torch.from_numpy(val).to("cuda", torch.bfloat16).contiguous() for key, val in x.items()}
+    del x
+    slabs = make_inputs(w, SEED, slabs=SLABS)
+    return d, slabs
+
+
+def rel(g, r):
+    return float(np.abs(g - r).max() / np.abs(r).max())
+
+
+@pytest.mark.parametrize("name", list(VARIANTS))
+def test_variant_sampled_rows_match_oracle(name, inputs):
+    d, xs = inputs
+    w = variant_workload(name)
+    p = rh.Params(w.B, w.H, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P, 0, rh.BF16, rh.BF16)
+    print(f"[{name}] forward_parallel Tc={w.Tc} To={w.To} P={w.P}", flush=True)
+    out, aux = rh.forward_parallel(p, d["q"], d["k"], d["v"], d["wq"], d["wk"], aux=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    rows = sample_rows(w, per_chunk=48, seed=SEED)
+    p1 = oracle.Params(1, 1, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P)
+    for i, (b, h) in enumerate(SLABS):
+        print(f"[{name}] oracle rows for slab b={b} h={h}: {len(rows)} rows", flush=True)
+        ref, rax = oracle.parallel_rows(p1, xs["q"][i:i + 1], xs["k"][i:i + 1], xs["v"][i:i + 1],
+                                        xs["wq"][i:i + 1], xs["wk"][i:i + 1], rows)
+        assert rel(out[b, h].float().cpu().numpy()[rows], ref) <= TOL, (name, b, h)
+        assert rel(aux["o_soft"][b, h].cpu().numpy()[rows], rax["osoft"]) <= TOL
+        assert rel(aux["lse"][b, h].cpu().numpy()[rows], rax["lse"]) <= TOL
+        lin = rax["z"] > 0
+        assert lin.any()
+        assert rel(aux["y"][b, h].cpu().numpy()[rows][lin], rax["y"][lin]) <= TOL
+        z = aux["z"][b, h].cpu().numpy()[rows][lin]
+        assert np.abs(z / rax["z"][lin] - 1).max() <= TOL
+
+
+def test_workstation_preset_stream_equals_parallel(inputs):
+    d, _ = inputs
+    w = variant_workload("tc5_to2")
+    p = rh.Params(w.B, w.H, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P, 0, rh.BF16, rh.BF16)
+    par = rh.forward_parallel(p, d["q"], d["k"], d["v"], d["wq"], d["wk"])
+    st = rh.Stream(p, d["wq"], d["wk"])
+    outs = []
+    for f0 in range(0, w.T, w.Tc):
+        f1 = min(f0 + w.Tc, w.T)
+        sl = slice(f0 * w.n, f1 * w.n)
+        outs.append(st.step(d["q"][:, :, sl].contiguous(), d["k"][:, :, sl].contiguous(),
+                            d["v"][:, :, sl].contiguous(), f1 - f0))
+    torch.cuda.synchronize()
+    s_out = torch.cat(outs, dim=2)
+    first = w.Tc * w.n
+    assert torch.equal(s_out[:, :, first:], par[:, :, first:])
+    d0 = (s_out[:, :, :first].float() - par[:, :, :first].float()).abs().max().item()
+    assert d0 <= 2 ** -6 * max(1.0, par[:, :, :first].float().abs().max().item())
