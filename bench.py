@@ -13,7 +13,8 @@ peak, the roofline of the dominant kernel (attention tile kernel, timed with HIP
 on the stream it runs on), the full-softmax comparator on the same shapes, the 10 s
 streaming form with its peak memory at 21/41/81 frames, the chunking and feature-map
 variants the pages discuss (Tc/To presets and ablations, higher polynomial degree) on the
-same inputs, and the CPU oracle timed on a bounded sample of the same workload (which
+same inputs, the distillation objective (hybrid vs full-softmax teacher, squared L2 per
+slab), and the CPU oracle timed on a bounded sample of the same workload (which
 also serves as a parity spot check).
 """
 from __future__ import annotations
@@ -239,6 +240,7 @@ def main():
         del outc
         res["stream"] = stream_leg(rh, torch, WORKLOADS["wan_10s_stream"], dev)
         res["variants"] = variants_leg(rh, torch, p, d, ms)
+        res["distill_loss"] = distill_leg(rh, torch, p, d, w)
 
     if not args.no_cpu_baseline:
         cb, parity = cpu_baseline(w, x, out)
@@ -281,6 +283,30 @@ def variants_leg(rh, torch, p, d, base_ms, reps=5):
     fl1 = flop_model(p.B, p.H, p.D, p.T, p.n, p.Tc, p.To, p.Dphi, p.P)["total"]
     res["to2_vs_to1"] = {"flop_ratio": round(res["tc3_to2"]["flops"] / fl1, 4),
                          "time_ratio": round(res["tc3_to2"]["ms"] / base_ms, 4)}
+    return res
+
+
+def distill_leg(rh, torch, p, d, w, reps=3):
+    """Distillation objective on the same inputs (student forward with float32 output,
+    full-softmax teacher, squared distance per slab): ms per call and TFLOP/s over the two
+    forwards' FLOPs."""
+    ws = rh.alloc_bytes(rh.distill_workspace_bytes(p), d["q"].device)
+    loss = torch.empty((p.B, p.H), dtype=torch.float32, device=d["q"].device)
+    call = lambda: rh.distill_loss(p, d["q"], d["k"], d["v"], d["wq"], d["wk"], loss=loss, ws=ws)
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    dms = e0.elapsed_time(e1) / reps
+    fl = (flop_model(w.B, w.H, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P)["total"]
+          + flop_model(w.B, w.H, w.D, w.T, w.n, w.T, 0, w.Dphi, w.P)["total"])
+    res = {"ms": round(dms, 3), "tflops": round(fl / (dms * 1e-3) / 1e12, 2),
+           "loss_mean_per_element": float(loss.double().sum() / (p.B * p.H * p.N * p.D))}
+    del ws
     return res
 
 

@@ -27,7 +27,8 @@ EXPORTS = (
     "rehyat_status_string", "rehyat_features", "rehyat_phi", "rehyat_workspace_bytes",
     "rehyat_forward_parallel", "rehyat_forward_parallel_aux", "rehyat_state_bytes",
     "rehyat_stream_workspace_bytes", "rehyat_state_init", "rehyat_chunk_step",
-    "rehyat_parallel_states", "rehyat_parallel_attend",
+    "rehyat_parallel_states", "rehyat_parallel_attend", "rehyat_distill_workspace_bytes",
+    "rehyat_distill_loss",
 )
 
 
@@ -89,6 +90,10 @@ def lib():
         L.rehyat_chunk_step.argtypes = [P, vp, ctypes.POINTER(_CStream), vp, vp, vp, ctypes.c_int32,
                                         vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.rehyat_chunk_step.restype = ctypes.c_int
+        L.rehyat_distill_workspace_bytes.argtypes = [P]
+        L.rehyat_distill_workspace_bytes.restype = ctypes.c_size_t
+        L.rehyat_distill_loss.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.rehyat_distill_loss.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -227,6 +232,45 @@ def forward_parallel(p: Params, q, k, v, wq, wk, bq=None, bk=None, out=None, ws=
                                              ws.numel() * ws.element_size(), _stream_handle()),
            "rehyat_forward_parallel_aux")
     return out, ax
+
+
+def distill_workspace_bytes(p: Params) -> int:
+    return int(lib().rehyat_distill_workspace_bytes(ctypes.byref(p.c())))
+
+
+def distill_loss(p: Params, q, k, v, wq, wk, bq=None, bk=None, loss=None, ws=None, outputs=False):
+    """Per-(batch, head) squared L2 distance between the hybrid output and full softmax
+    attention on the same inputs (rehyat_distill_loss).  Returns float32 [B, H]; with
+    outputs=True also the float32 student and teacher outputs it left in ws."""
+    dt = torch_dtype(p.in_dtype)
+    shape = (p.B, p.H, p.N, p.D)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, shape, dt, name)
+    for name, t in (("wq", wq), ("wk", wk)):
+        _check(t, (p.H, p.Dphi, p.D), dt, name)
+    for name, t in (("bq", bq), ("bk", bk)):
+        if t is not None:
+            _check(t, (p.H, p.Dphi), torch.float32, name)
+    if loss is None:
+        loss = torch.empty((p.B, p.H), dtype=torch.float32, device=q.device)
+    _check(loss, (p.B, p.H), torch.float32, "loss")
+    need = distill_workspace_bytes(p)
+    if need == 0:
+        raise RehyatError(1, "rehyat_distill_workspace_bytes")
+    if ws is None:
+        ws = alloc_bytes(need, q.device)
+    _raise(lib().rehyat_distill_loss(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk),
+                                     _ptr(bq), _ptr(bk), _ptr(loss), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream_handle()),
+           "rehyat_distill_loss")
+    if not outputs:
+        return loss
+    n = p.B * p.H * p.N * p.D
+    off = (n * 4 + 255) // 256 * 256
+    flat = ws.view(torch.uint8)
+    stu = flat[:n * 4].view(torch.float32).view(shape)
+    tea = flat[off:off + n * 4].view(torch.float32).view(shape)
+    return loss, stu, tea
 
 
 def parallel_states(p: Params, k, v, wk, bk, ws):

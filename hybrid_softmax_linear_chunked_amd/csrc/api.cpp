@@ -199,7 +199,7 @@ struct SplitLayout {
     size_t cnt, part, total;
 };
 
-SplitLayout split_layout(const rehyat_params* p) {
+static SplitLayout split_layout(const rehyat_params* p) {
     SplitLayout L;
     const int G = state_frames(p);
     const size_t base = G > 0 ? parallel_layout(p, G).total : 0;
@@ -557,6 +557,82 @@ rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stre
     st->frames_absorbed = next_abs;
     if (frames < p->Tc) st->closed = 1;
     return REHYAT_OK;
+}
+
+}  // extern "C"
+
+// Distillation workspace: student output, teacher output (float32 [BH, N, D] each), the
+// per-segment partial sums, then the forward workspace the two forwards share in turn.
+namespace {
+
+struct DistillLayout {
+    size_t stu, tea, part, fwd, total;
+    int nseg;
+};
+
+rehyat_params distill_student(const rehyat_params* p) {
+    rehyat_params s = *p;
+    s.out_dtype = REHYAT_FP32;
+    return s;
+}
+
+rehyat_params distill_teacher(const rehyat_params* p) {
+    rehyat_params t = *p;
+    t.Tc = p->T;
+    t.To = 0;
+    t.linear_only = 0;
+    t.out_dtype = REHYAT_FP32;
+    return t;
+}
+
+DistillLayout distill_layout(const rehyat_params* p) {
+    const rehyat_params ps = distill_student(p), pt = distill_teacher(p);
+    const int64_t len = (int64_t)p->T * p->frame_tokens * p->D;
+    const size_t out_bytes = align256((size_t)p->B * p->H * len * sizeof(float));
+    DistillLayout L;
+    L.nseg = sqdist_segments(len);
+    L.stu = 0;
+    L.tea = out_bytes;
+    L.part = 2 * out_bytes;
+    L.fwd = L.part + align256((size_t)p->B * p->H * L.nseg * sizeof(float));
+    L.total = L.fwd + std::max(split_layout(&ps).total, split_layout(&pt).total);
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rehyat_distill_workspace_bytes(const rehyat_params* p) {
+    if (check_params(p, true) != REHYAT_OK) return 0;
+    const rehyat_params pt = distill_teacher(p);
+    if (check_params(&pt, true) != REHYAT_OK) return 0;
+    return distill_layout(p).total;
+}
+
+rehyat_status rehyat_distill_loss(const rehyat_params* p, const void* q, const void* k,
+                                  const void* v, const void* wq, const void* wk,
+                                  const float* bq, const float* bk, float* loss, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+    rehyat_status st = check_params(p, true);
+    if (st != REHYAT_OK) return st;
+    const rehyat_params ps = distill_student(p), pt = distill_teacher(p);
+    st = check_params(&pt, true);
+    if (st != REHYAT_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(wq) || !aligned16(wk) ||
+        !aligned4_or_null(bq) || !aligned4_or_null(bk) || !loss || !aligned4_or_null(loss))
+        return REHYAT_EALIGN;
+    const DistillLayout L = distill_layout(p);
+    if ((int64_t)L.nseg * p->B * p->H >= ((int64_t)1 << 31)) return REHYAT_EINVAL;
+    if (!ws || ws_bytes < L.total || reinterpret_cast<uintptr_t>(ws) % 256 != 0) return REHYAT_EWORKSPACE;
+    char* w = reinterpret_cast<char*>(ws);
+    st = rehyat_forward_parallel(&ps, q, k, v, wq, wk, bq, bk, w + L.stu, w + L.fwd, ws_bytes - L.fwd, stream);
+    if (st != REHYAT_OK) return st;
+    st = rehyat_forward_parallel(&pt, q, k, v, wq, wk, bq, bk, w + L.tea, w + L.fwd, ws_bytes - L.fwd, stream);
+    if (st != REHYAT_OK) return st;
+    const int64_t len = (int64_t)p->T * p->frame_tokens * p->D;
+    return hip_status(launch_sqdist(reinterpret_cast<const float*>(w + L.stu), reinterpret_cast<const float*>(w + L.tea),
+                                    len, p->B * p->H, reinterpret_cast<float*>(w + L.part), loss, stream));
 }
 
 }  // extern "C"

@@ -118,5 +118,10 @@ hipError_t launch_scan(const ScanArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_phi(const PhiArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_zero(float* p, int64_t count, hipStream_t stream);
+// Squared distance per slab between two float tensors [BH, len] (distill.hip): partial
+// holds BH * sqdist_segments(len) floats, loss BH floats; len must be a multiple of 4.
+int sqdist_segments(int64_t len);
+hipError_t launch_sqdist(const float* a, const float* b, int64_t len, int BH, float* partial, float* loss,
+                         hipStream_t stream);
 
 }  // namespace rehyat

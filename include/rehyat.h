@@ -165,6 +165,26 @@ rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stre
                                 const void* wq, const void* wk, const float* bq, const float* bk,
                                 void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Attention-distillation objective (blog 3.1.1: with the teacher frozen, only phi_q and
+ * phi_k are trained so that the hybrid block's output approaches, in L2, the softmax
+ * teacher's output on the same inputs).  Reading taken: the squared Euclidean distance
+ * per (batch, head) slab,
+ *     loss[b*H + h] = sum_{i < N, d < D} (o_hyb[b,h,i,d] - o_soft[b,h,i,d])^2,
+ * where o_hyb is rehyat_forward_parallel with *p and float32 output, and o_soft is full
+ * softmax attention exp(q.k/sqrt(D)) over all N tokens of the clip (the same tile kernel
+ * with one window, Tc = T, no linear part).  Both outputs stay float32 in ws; the sum runs
+ * in a fixed order, so repeated calls give identical bits.  p->out_dtype is ignored.
+ * loss: device float32 [B*H] (4-byte aligned).  q, k, v, wq, wk, bq, bk as for
+ * rehyat_forward_parallel.  REHYAT_EINVAL when the teacher's single window would exceed
+ * 2^28 tokens; REHYAT_EWORKSPACE when ws is smaller than rehyat_distill_workspace_bytes or
+ * not 256-byte aligned.  The two outputs are left in ws (student first, then teacher,
+ * float32 [B,H,N,D] each, at offset 0 and at the student's size rounded up to 256 bytes). */
+size_t rehyat_distill_workspace_bytes(const rehyat_params* p);
+rehyat_status rehyat_distill_loss(const rehyat_params* p, const void* q, const void* k,
+                                  const void* v, const void* wq, const void* wk,
+                                  const float* bq, const float* bk, float* loss, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -266,3 +266,33 @@ def numpy_bruteforce(p: Params, q, k, v, wq, wk, bq=None, bk=None):
             w = np.where(soft, np.exp(s - shift), 0.0) + np.where(lin, kappa * np.exp(-shift), 0.0)
             out[b, h] = (w @ v[b, h]) / w.sum(axis=1, keepdims=True)
     return out
+
+
+# ---------------------------------------------------------------------------------------
+# Attention distillation objective (blog 3.1.1): with the softmax teacher frozen, only
+# phi_q and phi_k are trained, so that the hybrid block's output approaches the teacher's
+# in L2 on the same inputs.  Reading taken: the squared Euclidean distance per
+# (batch, head) slab, between the hybrid output and full softmax attention over the
+# whole clip.
+# ---------------------------------------------------------------------------------------
+
+def full_softmax(p: Params, q, k, v, rows=None):
+    """Teacher: softmax(q k^T / sqrt(D)) v over all N tokens of the clip (blog 2.1.1),
+    for every query, or only for the given token indices of each slab."""
+    q, k, v = map(_f64, (q, k, v))
+    if rows is not None:
+        q = q[:, :, np.asarray(rows)]
+    out = np.empty(q.shape)
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            s = q[b, h] @ k[b, h].T / np.sqrt(p.D)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            out[b, h] = (e @ v[b, h]) / e.sum(axis=1, keepdims=True)
+    return out
+
+
+def distill_loss(p: Params, q, k, v, wq, wk, bq=None, bk=None):
+    """[B, H]: sum over tokens and channels of (hybrid - full softmax)^2, fp64."""
+    hyb = parallel(p, q, k, v, wq, wk, bq, bk)
+    soft = full_softmax(p, q, k, v)
+    return ((hyb - soft) ** 2).sum(axis=(2, 3))

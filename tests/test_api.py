@@ -147,3 +147,28 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(rh, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         rh.lib()
+
+
+def test_distill_sizes_and_checks(L):
+    """Distillation workspace: student and teacher outputs (float32), per-segment partial
+    sums (16,384 floats per segment), then the larger of the two forwards' workspaces."""
+    a = lambda x: (x + 255) // 256 * 256
+    p = WAN.c()
+    out = a(12 * 32760 * 128 * 4)
+    nseg = -(-32760 * 128 // 16384)
+    student = rh.workspace_bytes(WAN.with_(out_dtype=rh.FP32))
+    teacher = rh.workspace_bytes(WAN.with_(Tc=21, To=0, out_dtype=rh.FP32))
+    need = L.rehyat_distill_workspace_bytes(ctypes.byref(p))
+    assert need == 2 * out + a(12 * nseg * 4) + max(student, teacher)
+    f = L.rehyat_distill_loss
+    assert f(ctypes.byref(p), *[FAKE] * 5, None, None, FAKE, FAKE, need - 1, None) == EWORKSPACE
+    assert f(ctypes.byref(p), *[FAKE] * 5, None, None, FAKE, ctypes.c_void_p(0x10010), need, None) == EWORKSPACE
+    assert f(ctypes.byref(p), *[FAKE] * 5, None, None, None, FAKE, need, None) == EALIGN
+    assert f(ctypes.byref(p), *[FAKE] * 5, None, None, ctypes.c_void_p(0x10002), FAKE, need, None) == EALIGN
+    assert f(ctypes.byref(p), FAKE, MISALIGNED, *[FAKE] * 3, None, None, FAKE, FAKE, need, None) == EALIGN
+    # the teacher's one window must stay within 2^28 tokens
+    big = WAN.with_(T=2 ** 28 // 1560 + 1, Tc=3).c()
+    assert L.rehyat_distill_workspace_bytes(ctypes.byref(big)) == 0
+    assert f(ctypes.byref(big), *[FAKE] * 5, None, None, FAKE, FAKE, 1 << 50, None) == EINVAL
+    bad = WAN.with_(D=48).c()
+    assert f(ctypes.byref(bad), *[FAKE] * 5, None, None, FAKE, FAKE, 1 << 40, None) == ESHAPE
