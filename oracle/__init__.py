@@ -296,3 +296,150 @@ def distill_loss(p: Params, q, k, v, wq, wk, bq=None, bk=None):
     hyb = parallel(p, q, k, v, wq, wk, bq, bk)
     soft = full_softmax(p, q, k, v)
     return ((hyb - soft) ** 2).sum(axis=(2, 3))
+
+
+# ---------------------------------------------------------------------------------------
+# Gradients of the distillation objective with respect to the feature-map parameters
+# (blog 3.1.1: only phi_q and phi_k are trained; the teacher does not depend on them).
+# With L = sum over slabs of distill_loss, g_i = dL/do_i = 2 (o_i - t_i), and the hybrid
+# output o_i = num_i / den_i of blog 2.2.1:
+#   dL/dkappa_ij = a_i . v_j - h_i   for j in the linear region of i, where
+#   a_i = g_i / den_i and h_i = (g_i . o_i) / den_i;
+#   kappa_ij = phi_q(q_i) . phi_k(k_j), so dL/dphi_q(q_i) = sum_j dL/dkappa_ij phi_k(k_j)
+#   and dL/dphi_k(k_j) = sum_i dL/dkappa_ij phi_q(q_i);
+#   phi = per-part powers u^p of u = softplus(pre), pre = W x + b (blog 2.2.2), so
+#   dL/du_j = sum_p p u_j^(p-1) dL/dphi_(j,p), dL/dpre = dL/du * sigmoid(pre),
+#   dL/dW = sum over tokens of dL/dpre x^T, dL/db = sum over tokens of dL/dpre.
+# ---------------------------------------------------------------------------------------
+
+def feature_map(p: Params):
+    """(element, power) of every feature in phi's layout: parts are contiguous ranges of
+    the Dphi elements (the first Dphi mod P parts one longer) and each part lists all its
+    elements at power 1, then at power 2, ..., then P (blog 2.2.2)."""
+    q, r = divmod(p.Dphi, p.P)
+    elem, power = [], []
+    start = 0
+    for part in range(p.P):
+        ln = q + (1 if part < r else 0)
+        for pw in range(1, p.P + 1):
+            elem += list(range(start, start + ln))
+            power += [pw] * ln
+        start += ln
+    return np.array(elem), np.array(power)
+
+
+def _phi_parts(p, x, w, b):
+    """pre = W x + b, u = softplus(pre), phi [N, F] for one slab."""
+    pre = x @ w.T
+    if b is not None:
+        pre = pre + b
+    u = _softplus(pre)
+    elem, power = feature_map(p)
+    return pre, u, u[:, elem] ** power
+
+
+def _phi_backward(p, pre, u, x, dphi):
+    """dL/dW and dL/db of one slab from dL/dphi [N, F]."""
+    elem, power = feature_map(p)
+    du = np.zeros_like(u)
+    for f in range(elem.size):
+        du[:, elem[f]] += power[f] * u[:, elem[f]] ** (power[f] - 1) * dphi[:, f]
+    dpre = du / (1.0 + np.exp(-pre))
+    return dpre.T @ x, dpre.sum(axis=0)
+
+
+def distill_phi_grads(p: Params, q, k, v, wq, wk, bq=None, bk=None):
+    """Brute force: explicit masks and the N x N matrix dL/dkappa.  Returns dict with
+    loss [B,H], dwq, dwk [H,Dphi,D], dbq, dbk [H,Dphi] of the summed loss."""
+    q, k, v, wq, wk = map(_f64, (q, k, v, wq, wk))
+    bq = None if bq is None else np.asarray(bq, dtype=np.float64)
+    bk = None if bk is None else np.asarray(bk, dtype=np.float64)
+    soft, lin = numpy_masks(p)
+    t = full_softmax(p, q, k, v)
+    res = dict(loss=np.zeros((p.B, p.H)), dwq=np.zeros(wq.shape), dwk=np.zeros(wk.shape),
+               dbq=np.zeros(wq.shape[:2]), dbk=np.zeros(wk.shape[:2]))
+    for b in range(p.B):
+        for h in range(p.H):
+            prq, uq, fq = _phi_parts(p, q[b, h], wq[h], None if bq is None else bq[h])
+            prk, uk, fk = _phi_parts(p, k[b, h], wk[h], None if bk is None else bk[h])
+            s = q[b, h] @ k[b, h].T / np.sqrt(p.D)
+            smax = np.where(soft, s, -np.inf).max(axis=1, keepdims=True)
+            shift = np.maximum(np.where(np.isfinite(smax), smax, 0.0), 0.0)
+            kap = fq @ fk.T
+            wgt = np.where(soft, np.exp(s - shift), 0.0) + np.where(lin, kap * np.exp(-shift), 0.0)
+            den = wgt.sum(axis=1, keepdims=True)             # true denominator times e^-shift
+            o = (wgt @ v[b, h]) / den
+            g = 2.0 * (o - t[b, h])
+            res["loss"][b, h] = ((o - t[b, h]) ** 2).sum()
+            scale = np.exp(-shift) / den                      # 1 / true denominator
+            a = g * scale
+            hv = (g * o).sum(axis=1, keepdims=True) * scale
+            dkap = np.where(lin, a @ v[b, h].T - hv, 0.0)
+            dwq, dbq = _phi_backward(p, prq, uq, q[b, h], dkap @ fk)
+            dwk, dbk = _phi_backward(p, prk, uk, k[b, h], dkap.T @ fq)
+            res["dwq"][h] += dwq
+            res["dbq"][h] += dbq
+            res["dwk"][h] += dwk
+            res["dbk"][h] += dbk
+    return res
+
+
+def distill_phi_grads_chunked(p: Params, q, k, v, wq, wk, bq=None, bk=None, heads=None):
+    """The same gradients through the recurrent states (blog 2.3): per chunk c the state
+    S_c = sum phi_k(k_j) v_j^T and Z_c = sum phi_k(k_j) over the frames [0, ls(c)), so
+    dL/dphi_q(q_i) = S_c a_i - h_i Z_c; per chunk R_c = sum_i phi_q(q_i) a_i^T and
+    r_c = sum_i phi_q(q_i) h_i over its queries, and key frame f receives the sum of R_c,
+    r_c over the chunks whose linear region holds it, dL/dphi_k(k_j) = R v_j - r.  The
+    outputs come from the chunk-parallel oracle (with its per-part outputs, so the
+    denominator is exp(lse) + z), the teacher from full_softmax.  Memory O(N F) per slab,
+    so whole Wan-sized slabs fit.  heads: restrict to these heads (others left zero)."""
+    q, k, v, wq, wk = map(_f64, (q, k, v, wq, wk))
+    bq = None if bq is None else np.asarray(bq, dtype=np.float64)
+    bk = None if bk is None else np.asarray(bk, dtype=np.float64)
+    sch = schedule(p)
+    n = p.n
+    res = dict(loss=np.zeros((p.B, p.H)), dwq=np.zeros(wq.shape), dwk=np.zeros(wk.shape),
+               dbq=np.zeros(wq.shape[:2]), dbk=np.zeros(wk.shape[:2]))
+    p1 = replace(p, B=1, H=1)
+    for b in range(p.B):
+        for h in (range(p.H) if heads is None else heads):
+            sl = lambda a: a[b:b + 1, h:h + 1]
+            o, ax = parallel_rows(p1, sl(q), sl(k), sl(v), wq[h:h + 1], wk[h:h + 1], np.arange(p.N),
+                                  None if bq is None else bq[h:h + 1], None if bk is None else bk[h:h + 1])
+            t = np.empty_like(o)
+            for r0 in range(0, p.N, 4096):
+                rows = np.arange(r0, min(r0 + 4096, p.N))
+                t[rows] = full_softmax(p1, sl(q), sl(k), sl(v), rows=rows)[0, 0]
+            den = np.exp(ax["lse"]) + ax["z"]
+            g = 2.0 * (o - t)
+            res["loss"][b, h] = ((o - t) ** 2).sum()
+            a = g / den[:, None]
+            hv = (g * o).sum(axis=1) / den
+            prq, uq, fq = _phi_parts(p, q[b, h], wq[h], None if bq is None else bq[h])
+            prk, uk, fk = _phi_parts(p, k[b, h], wk[h], None if bk is None else bk[h])
+            dfq = np.zeros_like(fq)
+            dfk = np.zeros_like(fk)
+            R = np.zeros((fq.shape[1], p.D))
+            r = np.zeros(fq.shape[1])
+            # chunks from the last: R, r accumulate the chunks whose region reaches further
+            for c in range(len(sch) - 1, -1, -1):
+                f0, f1, ws, we, ls = sch[c]
+                lo, hi = f0 * n, f1 * n
+                if ls > 0:
+                    keys = slice(0, ls * n)
+                    S = fk[keys].T @ v[b, h][keys]
+                    Z = fk[keys].sum(axis=0)
+                    dfq[lo:hi] = a[lo:hi] @ S.T - hv[lo:hi, None] * Z[None, :]
+                R += fq[lo:hi].T @ a[lo:hi]
+                r += fq[lo:hi].T @ hv[lo:hi]
+                # key frames whose earliest linear reader is chunk c: [ls(c-1), ls(c))
+                lprev = sch[c - 1][4] if c > 0 else 0
+                ks = slice(lprev * n, ls * n)
+                dfk[ks] = v[b, h][ks] @ R.T - r[None, :]
+            dwq, dbq = _phi_backward(p, prq, uq, q[b, h], dfq)
+            dwk, dbk = _phi_backward(p, prk, uk, k[b, h], dfk)
+            res["dwq"][h] += dwq
+            res["dbq"][h] += dbq
+            res["dwk"][h] += dwk
+            res["dbk"][h] += dbk
+    return res
