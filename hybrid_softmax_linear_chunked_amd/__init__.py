@@ -28,7 +28,7 @@ EXPORTS = (
     "rehyat_forward_parallel", "rehyat_forward_parallel_aux", "rehyat_state_bytes",
     "rehyat_stream_workspace_bytes", "rehyat_state_init", "rehyat_chunk_step",
     "rehyat_parallel_states", "rehyat_parallel_attend", "rehyat_distill_workspace_bytes",
-    "rehyat_distill_loss",
+    "rehyat_distill_loss", "rehyat_distill_grad_workspace_bytes", "rehyat_distill_grad",
 )
 
 
@@ -94,6 +94,10 @@ def lib():
         L.rehyat_distill_workspace_bytes.restype = ctypes.c_size_t
         L.rehyat_distill_loss.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.rehyat_distill_loss.restype = ctypes.c_int
+        L.rehyat_distill_grad_workspace_bytes.argtypes = [P]
+        L.rehyat_distill_grad_workspace_bytes.restype = ctypes.c_size_t
+        L.rehyat_distill_grad.argtypes = [P] + [vp] * 13 + [ctypes.c_size_t, vp]
+        L.rehyat_distill_grad.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -271,6 +275,43 @@ def distill_loss(p: Params, q, k, v, wq, wk, bq=None, bk=None, loss=None, ws=Non
     stu = flat[:n * 4].view(torch.float32).view(shape)
     tea = flat[off:off + n * 4].view(torch.float32).view(shape)
     return loss, stu, tea
+
+
+def distill_grad_workspace_bytes(p: Params) -> int:
+    return int(lib().rehyat_distill_grad_workspace_bytes(ctypes.byref(p.c())))
+
+
+def distill_grad(p: Params, q, k, v, wq, wk, bq=None, bk=None, ws=None, biases=True):
+    """Distillation loss and its gradients with respect to W_q, W_k (and b_q, b_k) through
+    rehyat_distill_grad.  Returns a dict of float32 tensors: loss [B,H], dwq, dwk
+    [H,Dphi,D], and dbq, dbk [H,Dphi] when biases=True."""
+    dt = torch_dtype(p.in_dtype)
+    shape = (p.B, p.H, p.N, p.D)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, shape, dt, name)
+    for name, t in (("wq", wq), ("wk", wk)):
+        _check(t, (p.H, p.Dphi, p.D), dt, name)
+    for name, t in (("bq", bq), ("bk", bk)):
+        if t is not None:
+            _check(t, (p.H, p.Dphi), torch.float32, name)
+    dev = q.device
+    out = dict(loss=torch.empty((p.B, p.H), dtype=torch.float32, device=dev),
+               dwq=torch.empty((p.H, p.Dphi, p.D), dtype=torch.float32, device=dev),
+               dwk=torch.empty((p.H, p.Dphi, p.D), dtype=torch.float32, device=dev))
+    if biases:
+        out["dbq"] = torch.empty((p.H, p.Dphi), dtype=torch.float32, device=dev)
+        out["dbk"] = torch.empty((p.H, p.Dphi), dtype=torch.float32, device=dev)
+    need = distill_grad_workspace_bytes(p)
+    if need == 0:
+        raise RehyatError(1, "rehyat_distill_grad_workspace_bytes")
+    if ws is None:
+        ws = alloc_bytes(need, dev)
+    _raise(lib().rehyat_distill_grad(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk),
+                                     _ptr(bq), _ptr(bk), _ptr(out["loss"]), _ptr(out["dwq"]), _ptr(out["dwk"]),
+                                     _ptr(out.get("dbq")), _ptr(out.get("dbk")), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream_handle()),
+           "rehyat_distill_grad")
+    return out
 
 
 def parallel_states(p: Params, k, v, wk, bk, ws):

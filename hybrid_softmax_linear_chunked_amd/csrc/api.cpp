@@ -636,3 +636,277 @@ rehyat_status rehyat_distill_loss(const rehyat_params* p, const void* q, const v
 }
 
 }  // extern "C"
+
+// Distillation-gradient workspace: the two outputs, the student's per-part outputs lse and
+// z, the loss partials, separate forward workspaces for the student (whose per-frame state
+// partials the gradient reads) and the teacher, then the gradient buffers.
+namespace {
+
+constexpr int kGradSegRows = 2048;  // token rows per dW partial
+
+struct GradLayout {
+    size_t stu, tea, lse, z, sqd, fwd_s, fwd_t, ah, u, phi, dphi, sz, rp, r, wp, bp, total;
+    int nseg_sq, nseg_w;
+};
+
+GradArgs grad_args(const rehyat_params* p) {
+    GradArgs s;
+    s.H = p->H;
+    s.BH = p->B * p->H;
+    s.n = p->frame_tokens;
+    s.N = p->T * p->frame_tokens;
+    s.D = p->D;
+    s.Dphi = p->Dphi;
+    s.P = p->P;
+    s.F = p->P * p->Dphi;
+    s.T = p->T;
+    s.Tc = p->Tc;
+    s.To = p->To;
+    s.linear_only = p->linear_only;
+    s.nc = num_chunks(p);
+    s.G = state_frames(p);
+    return s;
+}
+
+GradLayout grad_layout(const rehyat_params* p) {
+    const rehyat_params ps = distill_student(p), pt = distill_teacher(p);
+    const GradArgs s = grad_args(p);
+    const size_t BH = s.BH, N = s.N, f4 = sizeof(float), LD = s.D + 32;
+    GradLayout L;
+    L.nseg_sq = sqdist_segments((int64_t)N * s.D);
+    L.nseg_w = (int)((N + kGradSegRows - 1) / kGradSegRows);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align256(bytes);
+        return at;
+    };
+    L.stu = take(BH * N * s.D * f4);
+    L.tea = take(BH * N * s.D * f4);
+    L.lse = take(BH * N * f4);
+    L.z = take(BH * N * f4);
+    L.sqd = take(BH * L.nseg_sq * f4);
+    L.fwd_s = take(split_layout(&ps).total);
+    L.fwd_t = take(split_layout(&pt).total);
+    L.ah = take(BH * N * LD * f4);
+    L.u = take(BH * N * s.Dphi * f4);
+    L.phi = take(BH * N * s.F * f4);
+    L.dphi = take(BH * N * s.F * f4);
+    L.sz = take(BH * s.nc * s.F * LD * f4);
+    L.rp = take(BH * s.nc * s.Tc * s.F * LD * f4);
+    L.r = take(BH * s.nc * s.F * LD * f4);
+    L.wp = take(BH * L.nseg_w * s.Dphi * s.D * f4);
+    L.bp = take(BH * L.nseg_w * s.Dphi * f4);
+    L.total = off;
+    return L;
+}
+
+int tiles32(int rows) { return (rows + 31) / 32; }
+
+}  // namespace
+
+extern "C" {
+
+size_t rehyat_distill_grad_workspace_bytes(const rehyat_params* p) {
+    if (check_params(p, true) != REHYAT_OK) return 0;
+    const rehyat_params pt = distill_teacher(p);
+    if (check_params(&pt, true) != REHYAT_OK) return 0;
+    return grad_layout(p).total;
+}
+
+rehyat_status rehyat_distill_grad(const rehyat_params* p, const void* q, const void* k, const void* v,
+                                  const void* wq, const void* wk, const float* bq, const float* bk, float* loss,
+                                  float* dwq, float* dwk, float* dbq, float* dbk, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+    rehyat_status st = check_params(p, true);
+    if (st != REHYAT_OK) return st;
+    const rehyat_params ps = distill_student(p), pt = distill_teacher(p);
+    st = check_params(&pt, true);
+    if (st != REHYAT_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(wq) || !aligned16(wk) ||
+        !aligned4_or_null(bq) || !aligned4_or_null(bk) || !loss || !aligned4_or_null(loss) || !dwq ||
+        !aligned4_or_null(dwq) || !dwk || !aligned4_or_null(dwk) || !aligned4_or_null(dbq) || !aligned4_or_null(dbk))
+        return REHYAT_EALIGN;
+    const GradArgs s = grad_args(p);
+    const GradLayout L = grad_layout(p);
+    if ((int64_t)L.nseg_sq * s.BH >= ((int64_t)1 << 31) || (int64_t)s.N * (s.D + 32) >= ((int64_t)1 << 31) ||
+        (int64_t)s.N * s.F >= ((int64_t)1 << 31))
+        return REHYAT_EINVAL;
+    // grid y / z extents of the gradient launches
+    if (s.BH > 65535 || tiles32(s.N) > 65535 || (int64_t)s.T * tiles32(s.n) > 65535 ||
+        (int64_t)s.nc * tiles32(s.Tc * s.n) > 65535 || (int64_t)s.BH * s.nc > 65535 || (int64_t)s.nc * s.Tc > 65535)
+        return REHYAT_EINVAL;
+    if (!ws || ws_bytes < L.total || reinterpret_cast<uintptr_t>(ws) % 256 != 0) return REHYAT_EWORKSPACE;
+    char* w = reinterpret_cast<char*>(ws);
+    auto F32 = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+    const bool bf = p->in_dtype == REHYAT_BF16;
+
+    // forward: student (float output and per-part outputs), teacher, loss
+    rehyat_aux aux;
+    std::memset(&aux, 0, sizeof(aux));
+    aux.lse = F32(L.lse);
+    aux.z = F32(L.z);
+    st = rehyat_forward_parallel_aux(&ps, q, k, v, wq, wk, bq, bk, w + L.stu, &aux, w + L.fwd_s, L.fwd_t - L.fwd_s,
+                                     stream);
+    if (st != REHYAT_OK) return st;
+    st = rehyat_forward_parallel(&pt, q, k, v, wq, wk, bq, bk, w + L.tea, w + L.fwd_t, L.ah - L.fwd_t, stream);
+    if (st != REHYAT_OK) return st;
+    const int64_t len = (int64_t)s.N * s.D;
+    st = hip_status(launch_sqdist(F32(L.stu), F32(L.tea), len, s.BH, F32(L.sqd), loss, stream));
+    if (st != REHYAT_OK) return st;
+    const int64_t HW = (int64_t)p->H * s.Dphi * s.D;
+    if (s.G == 0) {  // no linear region: the loss does not depend on phi
+        st = hip_status(launch_zero(dwq, HW, stream));
+        if (st == REHYAT_OK) st = hip_status(launch_zero(dwk, HW, stream));
+        if (st == REHYAT_OK && dbq) st = hip_status(launch_zero(dbq, (int64_t)p->H * s.Dphi, stream));
+        if (st == REHYAT_OK && dbk) st = hip_status(launch_zero(dbk, (int64_t)p->H * s.Dphi, stream));
+        return st;
+    }
+    const int LD = s.D + 32;
+    const int64_t N = s.N;
+#define GRAD_TRY(expr)                              \
+    do {                                            \
+        st = hip_status(expr);                      \
+        if (st != REHYAT_OK) return st;             \
+    } while (0)
+    // a_i, h_i per query; [S_c | -Z_c] per chunk from the student's per-frame partials
+    GRAD_TRY(launch_grad_rows(s, F32(L.stu), F32(L.tea), F32(L.lse), F32(L.z), F32(L.ah), stream));
+    const ParallelLayout PL = parallel_layout(&ps, s.G);
+    GRAD_TRY(launch_grad_state_sz(s, F32(L.fwd_s + PL.sp), F32(L.fwd_s + PL.zp), F32(L.sz), stream));
+
+    auto pre = [&](const void* x, const void* wmat, const float* bias) {
+        NtArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.x = x;
+        a.x_bt_stride = N * s.D;
+        a.ldx = s.D;
+        a.y = wmat;
+        a.y_mat_stride = (int64_t)s.Dphi * s.D;
+        a.ldy = s.D;
+        a.nmat = p->H;
+        a.mode = 0;
+        a.K = s.D;
+        a.ncols = s.Dphi;
+        a.sub_col = -1;
+        a.colbias = bias;
+        a.colbias_head_stride = s.Dphi;
+        a.c = F32(L.u);
+        a.c_bt_stride = N * s.Dphi;
+        a.ldc = s.Dphi;
+        a.rows = s.N;
+        a.group_rows = s.N;
+        a.ngroups = 1;
+        a.tiles_per_group = tiles32(s.N);
+        return launch_nt(a, s, bf, bf, stream);
+    };
+    auto dw = [&](const void* x, float* dwout, float* dbout) -> hipError_t {
+        TnArgs t;
+        std::memset(&t, 0, sizeof(t));
+        t.x = F32(L.u);
+        t.x_bt_stride = N * s.Dphi;
+        t.ldx = s.Dphi;
+        t.y = x;
+        t.y_bt_stride = N * s.D;
+        t.ldy = s.D;
+        t.mrows = s.Dphi;
+        t.ncols = s.D;
+        t.part = F32(L.wp);
+        t.rows = s.N;
+        t.group_rows = s.N;
+        t.ngroups = 1;
+        t.seg_rows = kGradSegRows;
+        t.nseg = L.nseg_w;
+        hipError_t e = launch_tn(t, s.BH, bf, stream);
+        if (e == hipSuccess) e = launch_grad_reduce(F32(L.wp), dwout, p->B, p->H, L.nseg_w, (int64_t)s.Dphi * s.D, stream);
+        if (e == hipSuccess && dbout) {
+            e = launch_grad_colsum(F32(L.u), s.BH, N, s.Dphi, kGradSegRows, F32(L.bp), stream);
+            if (e == hipSuccess) e = launch_grad_reduce(F32(L.bp), dbout, p->B, p->H, L.nseg_w, s.Dphi, stream);
+        }
+        return e;
+    };
+
+    // query side: phi_q, dphi_q = [S_c | -Z_c] [a | h], dpre_q, dW_q, db_q
+    GRAD_TRY(pre(q, wq, bq));
+    GRAD_TRY(launch_grad_phi_fwd(s, F32(L.u), F32(L.phi), stream));
+    {
+        NtArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.x = F32(L.ah);
+        a.x_bt_stride = N * LD;
+        a.ldx = LD;
+        a.y = F32(L.sz);
+        a.y_mat_stride = (int64_t)s.F * LD;
+        a.ldy = LD;
+        a.nmat = s.nc;
+        a.mode = 1;
+        a.K = LD;
+        a.ncols = s.F;
+        a.sub_col = -1;
+        a.c = F32(L.dphi);
+        a.c_bt_stride = N * s.F;
+        a.ldc = s.F;
+        a.rows = s.N;
+        a.group_rows = s.Tc * s.n;
+        a.ngroups = s.nc;
+        a.tiles_per_group = tiles32(s.Tc * s.n);
+        GRAD_TRY(launch_nt(a, s, false, false, stream));
+    }
+    // per-chunk R = phi_q^T [a | h] over the chunk's queries (partials per frame), suffix
+    {
+        TnArgs t;
+        std::memset(&t, 0, sizeof(t));
+        t.x = F32(L.phi);
+        t.x_bt_stride = N * s.F;
+        t.ldx = s.F;
+        t.y = F32(L.ah);
+        t.y_bt_stride = N * LD;
+        t.ldy = LD;
+        t.mrows = s.F;
+        t.ncols = LD;
+        t.part = F32(L.rp);
+        t.rows = s.N;
+        t.group_rows = s.Tc * s.n;
+        t.ngroups = s.nc;
+        t.seg_rows = s.n;
+        t.nseg = s.Tc;
+        GRAD_TRY(launch_tn(t, s.BH, false, stream));
+        const int64_t E = (int64_t)s.F * LD;
+        GRAD_TRY(launch_grad_reduce(F32(L.rp), F32(L.r), 1, s.BH * s.nc, s.Tc, E, stream));
+        GRAD_TRY(launch_grad_suffix(F32(L.r), s.BH, s.nc, E, stream));
+    }
+    GRAD_TRY(launch_grad_phi_bwd(s, F32(L.u), F32(L.dphi), stream));
+    GRAD_TRY(dw(q, dwq, dbq));
+
+    // key side: phi_k, dphi_k = R v - r per key frame, dpre_k, dW_k, db_k
+    GRAD_TRY(pre(k, wk, bk));
+    GRAD_TRY(launch_grad_phi_fwd(s, F32(L.u), F32(L.phi), stream));
+    {
+        NtArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.x = v;
+        a.x_bt_stride = N * s.D;
+        a.ldx = s.D;
+        a.y = F32(L.r);
+        a.y_mat_stride = (int64_t)s.F * LD;
+        a.ldy = LD;
+        a.nmat = s.nc;
+        a.mode = 2;
+        a.K = s.D;
+        a.ncols = s.F;
+        a.sub_col = s.D;
+        a.c = F32(L.dphi);
+        a.c_bt_stride = N * s.F;
+        a.ldc = s.F;
+        a.rows = s.N;
+        a.group_rows = s.n;
+        a.ngroups = s.T;
+        a.tiles_per_group = tiles32(s.n);
+        GRAD_TRY(launch_nt(a, s, bf, false, stream));
+    }
+    GRAD_TRY(launch_grad_phi_bwd(s, F32(L.u), F32(L.dphi), stream));
+    GRAD_TRY(dw(k, dwk, dbk));
+#undef GRAD_TRY
+    return REHYAT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,375 @@
+// grad.hip -- gradients of the attention-distillation objective with respect to the
+// feature-map parameters W_q, W_k, b_q, b_k (ReHyAt blog, maplevalley.com.cn, 3.1.1: only
+// phi_q and phi_k are trained, towards the frozen softmax teacher's output).
+//
+// With g_i = 2 (o_i - t_i) and the hybrid output o_i = num_i / den_i (blog 2.2.1), the
+// derivative with respect to a linear weight kappa_ij = phi_q(q_i) . phi_k(k_j) is
+// a_i . v_j - h_i, a_i = g_i / den_i, h_i = (g_i . o_i) / den_i.  Through the recurrent
+// states of blog 2.3 this gives
+//   dphi_q(q_i) = S_c a_i - h_i Z_c                      (state of the query's chunk),
+//   dphi_k(k_j) = R v_j - r,  R = sum phi_q a^T, r = sum phi_q h over the queries of
+//                 every chunk whose linear region holds k_j (a suffix over chunks),
+// and the feature map (blog 2.2.2: u = softplus(W x + b), per-part powers u^p) gives
+// dpre = sigmoid(pre) sum_p p u^(p-1) dphi_(j,p), dW = sum dpre x^T, db = sum dpre.
+//
+// The dense products run on the fp32 matrix core (v_mfma_f32_32x32x2f32) so that fp32
+// and bf16 inputs share one exact-product path:
+//   nt_kernel: C[i][f] = sum_d X[i][d] Y_m[f][d] for row groups that each read one matrix
+//              Y_m (a head's W, a chunk's [S | -Z], a key frame's suffix R), contraction
+//              slots (h, s) <-> d = h K/2 + s so each lane reads contiguous half-rows;
+//   tn_kernel: per token segment, C[m][n] = sum_k X[k][m] Y[k][n] (dW and R partials),
+//              lanes reading consecutive columns of a row;
+// and every sum over segments, frames, chunks or batches runs in a fixed order, so the
+// gradients are bitwise reproducible.
+#include "kernels.hpp"
+#include "common.hpp"
+
+namespace rehyat {
+
+namespace {
+
+template <class T>
+__device__ inline void load16(const T* p, float (&o)[16]) {
+    if constexpr (sizeof(T) == 2) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(p + 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            o[e] = (float)a[e];
+            o[8 + e] = (float)b[e];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float4 v = reinterpret_cast<const float4*>(p)[e];
+            o[4 * e] = v.x;
+            o[4 * e + 1] = v.y;
+            o[4 * e + 2] = v.z;
+            o[4 * e + 3] = v.w;
+        }
+    }
+}
+
+template <class T>
+__device__ inline float load1(const T* p) {
+    return (float)*p;
+}
+
+__device__ inline f32x16 mma32(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ inline int ls_of(const GradArgs& a, int c) {
+    const int f0 = c * a.Tc, f1 = min(f0 + a.Tc, a.T);
+    return a.linear_only ? f1 : max(0, f0 - a.To);
+}
+
+// One wave per 32x32 output block; four waves per workgroup cover 32 rows x 128 columns.
+template <class TX, class TY>
+__global__ __launch_bounds__(256) void nt_kernel(const NtArgs a, const GradArgs s) {
+    const int bt = blockIdx.z;
+    const int grp = blockIdx.y / a.tiles_per_group, t = blockIdx.y % a.tiles_per_group;
+    const int row0 = grp * a.group_rows + t * 32;
+    const int rend = min((grp + 1) * a.group_rows, a.rows);
+    if (row0 >= rend) return;
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
+    const int cb = blockIdx.x * 4 + wave;
+    if (cb * 32 >= a.ncols) return;
+
+    int m;
+    if (a.mode == 0) {
+        m = bt % s.H;
+    } else if (a.mode == 1) {
+        m = bt * a.nmat + grp;
+    } else {
+        // earliest chunk whose linear region holds key frame grp
+        int c = 0;
+        while (c < a.nmat && ls_of(s, c) <= grp) ++c;
+        m = c < a.nmat ? bt * a.nmat + c : -1;
+    }
+    const int r = row0 + col;
+    const bool rv = r < rend;
+    const int f = cb * 32 + col;
+    float* crow_base = a.c + (int64_t)bt * a.c_bt_stride;
+    if (m < 0) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int rr = row0 + crow(q, h);
+            if (rr < rend) crow_base[(int64_t)rr * a.ldc + f] = 0.f;
+        }
+        return;
+    }
+    const TX* xr = reinterpret_cast<const TX*>(a.x) + (int64_t)bt * a.x_bt_stride + (int64_t)(rv ? r : row0) * a.ldx;
+    const TY* yr = reinterpret_cast<const TY*>(a.y) + (int64_t)m * a.y_mat_stride + (int64_t)f * a.ldy;
+    const int half = a.K / 2;
+    f32x16 acc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+    for (int kc = 0; kc < half; kc += 16) {
+        float xa[16], yb[16];
+        load16<TX>(xr + h * half + kc, xa);
+        load16<TY>(yr + h * half + kc, yb);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc = mma32(rv ? xa[q] : 0.f, yb[q], acc);
+    }
+    float add = 0.f;
+    if (a.colbias) add += a.colbias[(int64_t)(bt % s.H) * a.colbias_head_stride + f];
+    if (a.sub_col >= 0) add -= load1<TY>(yr + a.sub_col);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int rr = row0 + crow(q, h);
+        if (rr < rend) crow_base[(int64_t)rr * a.ldc + f] = acc[q] + add;
+    }
+}
+
+// Partial C[m][n] = sum over the rows k of one segment of X[k][m] Y[k][n]; one wave per
+// 32x32 block, four blocks per workgroup; empty segments store zeros.
+template <class TX, class TY>
+__global__ __launch_bounds__(256) void tn_kernel(const TnArgs a) {
+    const int bt = blockIdx.z;
+    const int grp = blockIdx.y / a.nseg, sg = blockIdx.y % a.nseg;
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
+    const int nbn = a.ncols / 32;
+    const int bi = blockIdx.x * 4 + wave;
+    if (bi >= (a.mrows / 32) * nbn) return;
+    const int mb = bi / nbn, nb = bi % nbn;
+    const int gend = min((grp + 1) * a.group_rows, a.rows);
+    const int k0 = grp * a.group_rows + sg * a.seg_rows;
+    const int k1 = min(k0 + a.seg_rows, gend);
+    const TX* xb = reinterpret_cast<const TX*>(a.x) + (int64_t)bt * a.x_bt_stride + mb * 32 + col;
+    const TY* yb = reinterpret_cast<const TY*>(a.y) + (int64_t)bt * a.y_bt_stride + nb * 32 + col;
+    f32x16 acc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+    for (int k = k0; k < k1; k += 32) {
+        float xa[16], ya[16];
+#pragma unroll
+        for (int st = 0; st < 16; ++st) {
+            const int row = k + 2 * st + h;
+            const bool ok = row < k1;
+            xa[st] = ok ? load1<TX>(xb + (int64_t)row * a.ldx) : 0.f;
+            ya[st] = ok ? load1<TY>(yb + (int64_t)row * a.ldy) : 0.f;
+        }
+#pragma unroll
+        for (int st = 0; st < 16; ++st) acc = mma32(xa[st], ya[st], acc);
+    }
+    float* out = a.part + (((int64_t)bt * a.ngroups + grp) * a.nseg + sg) * a.mrows * a.ncols;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) out[(int64_t)(mb * 32 + crow(q, h)) * a.ncols + nb * 32 + col] = acc[q];
+}
+
+// out[o][e] = sum_{b < nb} sum_{s < ns} part[((b * no + o) * ns + s) * E + e], in that order
+__global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ part, float* __restrict__ out, int nb,
+                                                     int no, int ns, int64_t E) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int o = blockIdx.y;
+    if (e >= E) return;
+    float acc = 0.f;
+    for (int b = 0; b < nb; ++b)
+        for (int s = 0; s < ns; ++s) acc += part[(((int64_t)b * no + o) * ns + s) * E + e];
+    out[(int64_t)o * E + e] = acc;
+}
+
+// R[bt][c] <- sum over c' >= c of R[bt][c'] (from the last chunk), in place
+__global__ __launch_bounds__(256) void suffix_kernel(float* __restrict__ R, int nc, int64_t E) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= E) return;
+    float* base = R + (int64_t)blockIdx.y * nc * E + e;
+    float acc = 0.f;
+    for (int c = nc - 1; c >= 0; --c) {
+        acc += base[(int64_t)c * E];
+        base[(int64_t)c * E] = acc;
+    }
+}
+
+// SZ[bt][c][f][d] = [S_c | -Z_c | 0] with S_c, Z_c the sums of the per-frame partials over
+// frames [0, ls(c)) in frame order; chunks without a linear region get zeros.
+__global__ __launch_bounds__(256) void state_sz_kernel(const GradArgs s, const float* __restrict__ Sp,
+                                                       const float* __restrict__ Zp, float* __restrict__ SZ) {
+    const int LD = s.D + 32, F = s.F;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)F * LD) return;
+    const int bt = blockIdx.y, f = (int)(e / LD), d = (int)(e % LD);
+    const int nc = s.nc;
+    float* out = SZ + (int64_t)bt * nc * F * LD + e;
+    const float* src = nullptr;
+    int64_t stride = 0;
+    float sign = 1.f;
+    if (d < s.D) {
+        src = Sp + ((int64_t)bt * s.G * F + f) * s.D + d;
+        stride = (int64_t)F * s.D;
+    } else if (d == s.D) {
+        src = Zp + (int64_t)bt * s.G * F + f;
+        stride = F;
+        sign = -1.f;
+    }
+    float acc = 0.f;
+    int g = 0;
+    for (int c = 0; c < nc; ++c) {
+        const int l = ls_of(s, c);
+        for (; g < l && g < s.G; ++g)
+            if (src) acc += src[(int64_t)g * stride];
+        out[(int64_t)c * F * LD] = sign * acc;
+    }
+}
+
+// Per query row (one wave per row): g = 2 (o - t), 1/den from lse and z, then
+// AH[i] = [g / den | (g . o) / den | 0 ...] (D + 32 columns)
+__global__ __launch_bounds__(256) void rows_kernel(const GradArgs s, const float* __restrict__ o,
+                                                   const float* __restrict__ t, const float* __restrict__ lse,
+                                                   const float* __restrict__ z, float* __restrict__ AH) {
+    const int bt = blockIdx.y, wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int64_t i = (int64_t)blockIdx.x * 4 + wave;
+    if (i >= s.N) return;
+    const int D = s.D, LD = D + 32;
+    const int64_t row = (int64_t)bt * s.N + i;
+    float gv[2], dot = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int d = lane + 64 * u;
+        gv[u] = 0.f;
+        if (d < D) {
+            const float ov = o[row * D + d];
+            gv[u] = 2.f * (ov - t[row * D + d]);
+            dot += gv[u] * ov;
+        }
+    }
+#pragma unroll
+    for (int msk = 32; msk >= 1; msk >>= 1) dot += __shfl_xor(dot, msk, 64);
+    const float L = lse[row], zz = z[row];
+    float inv;
+    if (L == -INFINITY) {
+        inv = 1.f / zz;
+    } else if (zz <= 0.f || L > logf(zz)) {
+        const float e = expf(-L);
+        inv = e / (1.f + zz * e);
+    } else {
+        inv = 1.f / (zz + expf(L));
+    }
+    float* ah = AH + row * LD;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int d = lane + 64 * u;
+        if (d < D) ah[d] = gv[u] * inv;
+    }
+    if (lane < 32) ah[D + lane] = lane == 0 ? dot * inv : 0.f;
+}
+
+// u = softplus(pre) in place of pre, and phi[i][feat(j, p)] = u^p
+__global__ __launch_bounds__(256) void phi_fwd_kernel(const GradArgs s, float* __restrict__ U, float* __restrict__ phi) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)s.BH * s.N * s.Dphi) return;
+    const int64_t row = e / s.Dphi;
+    const int j = (int)(e % s.Dphi);
+    const float x = U[e];
+    const float u = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+    U[e] = u;
+    float pw = u;
+    float* out = phi + row * s.F;
+    for (int p = 1; p <= s.P; ++p) {
+        out[feat_index(j, p, s.Dphi, s.P)] = pw;
+        pw *= u;
+    }
+}
+
+// dpre = sigmoid(pre) sum_p p u^(p-1) dphi[feat(j, p)], with sigmoid(pre) = 1 - exp(-u),
+// in place of u
+__global__ __launch_bounds__(256) void phi_bwd_kernel(const GradArgs s, float* __restrict__ U,
+                                                      const float* __restrict__ dphi) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)s.BH * s.N * s.Dphi) return;
+    const int64_t row = e / s.Dphi;
+    const int j = (int)(e % s.Dphi);
+    const float u = U[e];
+    const float* dp = dphi + row * s.F;
+    float du = 0.f, upow = 1.f;
+    for (int p = 1; p <= s.P; ++p) {
+        du += (float)p * upow * dp[feat_index(j, p, s.Dphi, s.P)];
+        upow *= u;
+    }
+    U[e] = du * -expm1f(-u);
+}
+
+// part[bt][sg][j] = sum over the rows of segment sg of X[row][j], in row order
+__global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ X, int64_t rows, int cols, int seg_rows,
+                                                     float* __restrict__ part) {
+    const int bt = blockIdx.y, sg = blockIdx.x;
+    const int64_t r0 = (int64_t)sg * seg_rows, r1 = min(r0 + seg_rows, rows);
+    for (int j = threadIdx.x; j < cols; j += 256) {
+        float acc = 0.f;
+        for (int64_t r = r0; r < r1; ++r) acc += X[((int64_t)bt * rows + r) * cols + j];
+        part[((int64_t)bt * gridDim.x + sg) * cols + j] = acc;
+    }
+}
+
+template <class TX, class TY>
+hipError_t launch_nt_t(const NtArgs& a, const GradArgs& s, hipStream_t stream) {
+    const dim3 grid((a.ncols + 127) / 128, a.ngroups * a.tiles_per_group, s.BH);
+    hipLaunchKernelGGL((nt_kernel<TX, TY>), grid, dim3(256), 0, stream, a, s);
+    return hipGetLastError();
+}
+
+template <class TX, class TY>
+hipError_t launch_tn_t(const TnArgs& a, int BH, hipStream_t stream) {
+    const int blocks = (a.mrows / 32) * (a.ncols / 32);
+    const dim3 grid((blocks + 3) / 4, a.ngroups * a.nseg, BH);
+    hipLaunchKernelGGL((tn_kernel<TX, TY>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_nt(const NtArgs& a, const GradArgs& s, bool x_bf16, bool y_bf16, hipStream_t stream) {
+    if (x_bf16 && y_bf16) return launch_nt_t<bf16, bf16>(a, s, stream);
+    if (x_bf16) return launch_nt_t<bf16, float>(a, s, stream);
+    if (y_bf16) return launch_nt_t<float, bf16>(a, s, stream);
+    return launch_nt_t<float, float>(a, s, stream);
+}
+
+hipError_t launch_tn(const TnArgs& a, int BH, bool y_bf16, hipStream_t stream) {
+    return y_bf16 ? launch_tn_t<float, bf16>(a, BH, stream) : launch_tn_t<float, float>(a, BH, stream);
+}
+
+hipError_t launch_grad_reduce(const float* part, float* out, int nb, int no, int ns, int64_t E, hipStream_t stream) {
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((E + 255) / 256), no), dim3(256), 0, stream, part, out, nb, no,
+                       ns, E);
+    return hipGetLastError();
+}
+
+hipError_t launch_grad_suffix(float* R, int BH, int nc, int64_t E, hipStream_t stream) {
+    hipLaunchKernelGGL(suffix_kernel, dim3((unsigned)((E + 255) / 256), BH), dim3(256), 0, stream, R, nc, E);
+    return hipGetLastError();
+}
+
+hipError_t launch_grad_state_sz(const GradArgs& s, const float* Sp, const float* Zp, float* SZ, hipStream_t stream) {
+    const int64_t E = (int64_t)s.F * (s.D + 32);
+    hipLaunchKernelGGL(state_sz_kernel, dim3((unsigned)((E + 255) / 256), s.BH), dim3(256), 0, stream, s, Sp, Zp, SZ);
+    return hipGetLastError();
+}
+
+hipError_t launch_grad_rows(const GradArgs& s, const float* o, const float* t, const float* lse, const float* z,
+                            float* AH, hipStream_t stream) {
+    hipLaunchKernelGGL(rows_kernel, dim3((unsigned)((s.N + 3) / 4), s.BH), dim3(256), 0, stream, s, o, t, lse, z, AH);
+    return hipGetLastError();
+}
+
+hipError_t launch_grad_phi_fwd(const GradArgs& s, float* U, float* phi, hipStream_t stream) {
+    const int64_t E = (int64_t)s.BH * s.N * s.Dphi;
+    hipLaunchKernelGGL(phi_fwd_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, stream, s, U, phi);
+    return hipGetLastError();
+}
+
+hipError_t launch_grad_phi_bwd(const GradArgs& s, float* U, const float* dphi, hipStream_t stream) {
+    const int64_t E = (int64_t)s.BH * s.N * s.Dphi;
+    hipLaunchKernelGGL(phi_bwd_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, stream, s, U, dphi);
+    return hipGetLastError();
+}
+
+hipError_t launch_grad_colsum(const float* X, int BH, int64_t rows, int cols, int seg_rows, float* part,
+                              hipStream_t stream) {
+    const int nseg = (int)((rows + seg_rows - 1) / seg_rows);
+    hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)nseg, BH), dim3(256), 0, stream, X, rows, cols, seg_rows, part);
+    return hipGetLastError();
+}
+
+}  // namespace rehyat

@@ -118,6 +118,56 @@ hipError_t launch_scan(const ScanArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_phi(const PhiArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_zero(float* p, int64_t count, hipStream_t stream);
+// Distillation gradients (grad.hip).  Shapes and the chunk schedule of one call.
+struct GradArgs {
+    int H, BH, N, n, D, Dphi, P, F, T, Tc, To, linear_only, nc, G;
+};
+
+// C[bt][i][f] = sum_{d < K} X[bt][i][d] Y_m[f][d] (+ colbias[h][f]) (- Y_m[f][sub_col]) over
+// row groups of group_rows rows (tiles of 32 rows never cross a group); the matrix m of a
+// group: mode 0 the head of bt, mode 1 chunk = group, mode 2 the earliest chunk whose linear
+// region holds key frame = group (none: the rows get zeros).
+struct NtArgs {
+    const void* x;
+    int64_t x_bt_stride;
+    int ldx;
+    const void* y;
+    int64_t y_mat_stride;
+    int ldy;
+    int nmat, mode, K, ncols, sub_col;
+    const float* colbias;
+    int64_t colbias_head_stride;
+    float* c;
+    int64_t c_bt_stride;
+    int ldc;
+    int rows, group_rows, ngroups, tiles_per_group;
+};
+
+// part[bt][group][seg][m][n] = sum over the rows k of segment seg of group of X[k][m] Y[k][n]
+struct TnArgs {
+    const void* x;
+    int64_t x_bt_stride;
+    int ldx;
+    const void* y;
+    int64_t y_bt_stride;
+    int ldy;
+    int mrows, ncols;
+    float* part;
+    int rows, group_rows, ngroups, seg_rows, nseg;
+};
+
+hipError_t launch_nt(const NtArgs& a, const GradArgs& s, bool x_bf16, bool y_bf16, hipStream_t stream);
+hipError_t launch_tn(const TnArgs& a, int BH, bool y_bf16, hipStream_t stream);
+hipError_t launch_grad_reduce(const float* part, float* out, int nb, int no, int ns, int64_t E, hipStream_t stream);
+hipError_t launch_grad_suffix(float* R, int BH, int nc, int64_t E, hipStream_t stream);
+hipError_t launch_grad_state_sz(const GradArgs& s, const float* Sp, const float* Zp, float* SZ, hipStream_t stream);
+hipError_t launch_grad_rows(const GradArgs& s, const float* o, const float* t, const float* lse, const float* z,
+                            float* AH, hipStream_t stream);
+hipError_t launch_grad_phi_fwd(const GradArgs& s, float* U, float* phi, hipStream_t stream);
+hipError_t launch_grad_phi_bwd(const GradArgs& s, float* U, const float* dphi, hipStream_t stream);
+hipError_t launch_grad_colsum(const float* X, int BH, int64_t rows, int cols, int seg_rows, float* part,
+                              hipStream_t stream);
+
 // Squared distance per slab between two float tensors [BH, len] (distill.hip): partial
 // holds BH * sqdist_segments(len) floats, loss BH floats; len must be a multiple of 4.
 int sqdist_segments(int64_t len);

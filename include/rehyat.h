@@ -185,6 +185,30 @@ rehyat_status rehyat_distill_loss(const rehyat_params* p, const void* q, const v
                                   const float* bq, const float* bk, float* loss, void* ws,
                                   size_t ws_bytes, hipStream_t stream);
 
+/* Gradients of the summed distillation objective L = sum_{b,h} loss[b*H + h] (as
+ * rehyat_distill_loss) with respect to the feature-map parameters, the only parameters the
+ * distillation stage trains (blog 3.1.1).  By the chain rule through the joint
+ * normalisation (blog 2.2.1), the recurrent states (blog 2.3) and the feature map (blog
+ * 2.2.2): with g_i = 2 (o_i - t_i), a_i = g_i / den_i and h_i = (g_i . o_i) / den_i,
+ *   dL/dphi_q(q_i) = S_c a_i - h_i Z_c for the state S_c, Z_c of the query's chunk,
+ *   dL/dphi_k(k_j) = R v_j - r with R, r the sums of phi_q a^T and phi_q h over the
+ *                    queries of every chunk whose linear region holds k_j,
+ *   dL/dpre = sigmoid(pre) sum_p p u^(p-1) dL/dphi_(j,p) with u = softplus(pre), and
+ *   dL/dW = sum over tokens (and batches) of dL/dpre x^T, dL/db = sum of dL/dpre.
+ * Outputs (device float32, 4-byte aligned): loss [B*H] as rehyat_distill_loss, dwq and dwk
+ * [H,Dphi,D], dbq and dbk [H,Dphi] (each of the two may be NULL).  All sums run in a fixed
+ * order (bitwise reproducible).  Inputs as for rehyat_forward_parallel; p->out_dtype is
+ * ignored.  Status: as rehyat_distill_loss, plus REHYAT_EINVAL when a launch grid would
+ * exceed 65,535 row tiles (about 2M tokens) or B*H*chunks exceeds 65,535.  The workspace
+ * holds the student and teacher outputs and float32 [B,H,N,*] gradient buffers (about
+ * 1.9 GB for a 12-head, 32,760-token layer). */
+size_t rehyat_distill_grad_workspace_bytes(const rehyat_params* p);
+rehyat_status rehyat_distill_grad(const rehyat_params* p, const void* q, const void* k,
+                                  const void* v, const void* wq, const void* wk,
+                                  const float* bq, const float* bk, float* loss, float* dwq,
+                                  float* dwk, float* dbq, float* dbk, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

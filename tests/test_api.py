@@ -172,3 +172,22 @@ def test_distill_sizes_and_checks(L):
     assert f(ctypes.byref(big), *[FAKE] * 5, None, None, FAKE, FAKE, 1 << 50, None) == EINVAL
     bad = WAN.with_(D=48).c()
     assert f(ctypes.byref(bad), *[FAKE] * 5, None, None, FAKE, FAKE, 1 << 40, None) == ESHAPE
+
+
+def test_distill_grad_checks(L):
+    p = WAN.c()
+    need = L.rehyat_distill_grad_workspace_bytes(ctypes.byref(p))
+    assert need > L.rehyat_distill_workspace_bytes(ctypes.byref(p))
+    f = L.rehyat_distill_grad
+    outs = [FAKE, FAKE, FAKE, None, None]            # loss, dwq, dwk, dbq, dbk
+    assert f(ctypes.byref(p), *[FAKE] * 5, None, None, *outs, FAKE, need - 1, None) == EWORKSPACE
+    assert f(ctypes.byref(p), *[FAKE] * 5, None, None, *outs, ctypes.c_void_p(0x10010), need, None) == EWORKSPACE
+    for i in range(3):
+        bad = list(outs)
+        bad[i] = None
+        assert f(ctypes.byref(p), *[FAKE] * 5, None, None, *bad, FAKE, need, None) == EALIGN
+    assert f(ctypes.byref(p), *[FAKE] * 5, None, None, FAKE, FAKE, FAKE, ctypes.c_void_p(0x10002), None, FAKE,
+             need, None) == EALIGN
+    big = WAN.with_(T=2 ** 28 // 1560 + 1).c()
+    assert L.rehyat_distill_grad_workspace_bytes(ctypes.byref(big)) == 0
+    assert f(ctypes.byref(big), *[FAKE] * 5, None, None, *outs, FAKE, 1 << 50, None) == EINVAL
