@@ -14,7 +14,7 @@ on the stream it runs on), the full-softmax comparator on the same shapes, the 1
 streaming form with its peak memory at 21/41/81 frames, the chunking and feature-map
 variants the pages discuss (Tc/To presets and ablations, higher polynomial degree) on the
 same inputs, the distillation objective (hybrid vs full-softmax teacher, squared L2 per
-slab), and the CPU oracle timed on a bounded sample of the same workload (which
+slab) and its gradients with respect to the feature-map weights, and the CPU oracle timed on a bounded sample of the same workload (which
 also serves as a parity spot check).
 """
 from __future__ import annotations
@@ -241,6 +241,7 @@ def main():
         res["stream"] = stream_leg(rh, torch, WORKLOADS["wan_10s_stream"], dev)
         res["variants"] = variants_leg(rh, torch, p, d, ms)
         res["distill_loss"] = distill_leg(rh, torch, p, d, w)
+        res["distill_grad"] = distill_grad_leg(rh, torch, p, d, w, res["distill_loss"]["ms"])
 
     if not args.no_cpu_baseline:
         cb, parity = cpu_baseline(w, x, out)
@@ -306,6 +307,43 @@ def distill_leg(rh, torch, p, d, w, reps=3):
           + flop_model(w.B, w.H, w.D, w.T, w.n, w.T, 0, w.Dphi, w.P)["total"])
     res = {"ms": round(dms, 3), "tflops": round(fl / (dms * 1e-3) / 1e12, 2),
            "loss_mean_per_element": float(loss.double().sum() / (p.B * p.H * p.N * p.D))}
+    del ws
+    return res
+
+
+def grad_flops(B, H, D, T, n, Tc, To, Dphi, P, linear_only=0):
+    """Algorithmic FLOPs of the feature-map gradients after the two forwards: phi of every
+    query and key, dphi_q over the queries with a linear region, the per-chunk sums
+    R = phi_q^T [a|h], dphi_k over the keys that enter a state, dW_q over all queries and
+    dW_k over those keys (2 per multiply-add)."""
+    F = P * Dphi
+    sch = schedule(T, Tc, To, linear_only)
+    N = T * n
+    n_s = sch[-1][4] * n
+    n_c = sum((f1 - f0) * n for f0, f1, ws, we, ls in sch if ls > 0)
+    return B * H * (4 * N * D * Dphi + 4 * n_c * F * (D + 1) + 2 * n_s * F * (D + 1)
+                    + 2 * N * Dphi * D + 2 * n_s * Dphi * D)
+
+
+def distill_grad_leg(rh, torch, p, d, w, loss_ms, reps=3):
+    """Distillation loss and its gradients with respect to W_q, W_k, b_q, b_k: ms per call,
+    the gradient stages' share (call minus the loss-only call) and their TFLOP/s."""
+    ws = rh.alloc_bytes(rh.distill_grad_workspace_bytes(p), d["q"].device)
+    call = lambda: rh.distill_grad(p, d["q"], d["k"], d["v"], d["wq"], d["wk"], ws=ws)
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    gms = e0.elapsed_time(e1) / reps
+    gfl = grad_flops(w.B, w.H, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P)
+    bw = max(gms - loss_ms, 1e-6)
+    res = {"ms": round(gms, 3), "gradient_stages_ms": round(bw, 3), "gradient_flops": gfl,
+           "gradient_tflops": round(gfl / (bw * 1e-3) / 1e12, 2), "peak_fp32_matrix_tflops": 157.3,
+           "workspace_bytes": int(ws.numel())}
     del ws
     return res
 

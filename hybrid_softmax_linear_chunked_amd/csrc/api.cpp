@@ -642,11 +642,12 @@ rehyat_status rehyat_distill_loss(const rehyat_params* p, const void* q, const v
 // partials the gradient reads) and the teacher, then the gradient buffers.
 namespace {
 
-constexpr int kGradSegRows = 2048;  // token rows per dW partial
+constexpr int kGradSegRows = 2048;    // token rows per dW partial
+constexpr int kColsumSegRows = 256;   // token rows per bias-gradient partial
 
 struct GradLayout {
     size_t stu, tea, lse, z, sqd, fwd_s, fwd_t, ah, u, phi, dphi, sz, rp, r, wp, bp, total;
-    int nseg_sq, nseg_w;
+    int nseg_sq, nseg_w, nseg_b;
 };
 
 GradArgs grad_args(const rehyat_params* p) {
@@ -675,6 +676,7 @@ GradLayout grad_layout(const rehyat_params* p) {
     GradLayout L;
     L.nseg_sq = sqdist_segments((int64_t)N * s.D);
     L.nseg_w = (int)((N + kGradSegRows - 1) / kGradSegRows);
+    L.nseg_b = (int)((N + kColsumSegRows - 1) / kColsumSegRows);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -696,7 +698,7 @@ GradLayout grad_layout(const rehyat_params* p) {
     L.rp = take(BH * s.nc * s.Tc * s.F * LD * f4);
     L.r = take(BH * s.nc * s.F * LD * f4);
     L.wp = take(BH * L.nseg_w * s.Dphi * s.D * f4);
-    L.bp = take(BH * L.nseg_w * s.Dphi * f4);
+    L.bp = take(BH * L.nseg_b * s.Dphi * f4);
     L.total = off;
     return L;
 }
@@ -796,7 +798,6 @@ rehyat_status rehyat_distill_grad(const rehyat_params* p, const void* q, const v
         a.rows = s.N;
         a.group_rows = s.N;
         a.ngroups = 1;
-        a.tiles_per_group = tiles32(s.N);
         return launch_nt(a, s, bf, bf, stream);
     };
     auto dw = [&](const void* x, float* dwout, float* dbout) -> hipError_t {
@@ -819,8 +820,8 @@ rehyat_status rehyat_distill_grad(const rehyat_params* p, const void* q, const v
         hipError_t e = launch_tn(t, s.BH, bf, stream);
         if (e == hipSuccess) e = launch_grad_reduce(F32(L.wp), dwout, p->B, p->H, L.nseg_w, (int64_t)s.Dphi * s.D, stream);
         if (e == hipSuccess && dbout) {
-            e = launch_grad_colsum(F32(L.u), s.BH, N, s.Dphi, kGradSegRows, F32(L.bp), stream);
-            if (e == hipSuccess) e = launch_grad_reduce(F32(L.bp), dbout, p->B, p->H, L.nseg_w, s.Dphi, stream);
+            e = launch_grad_colsum(F32(L.u), s.BH, N, s.Dphi, kColsumSegRows, F32(L.bp), stream);
+            if (e == hipSuccess) e = launch_grad_reduce(F32(L.bp), dbout, p->B, p->H, L.nseg_b, s.Dphi, stream);
         }
         return e;
     };
@@ -848,7 +849,6 @@ rehyat_status rehyat_distill_grad(const rehyat_params* p, const void* q, const v
         a.rows = s.N;
         a.group_rows = s.Tc * s.n;
         a.ngroups = s.nc;
-        a.tiles_per_group = tiles32(s.Tc * s.n);
         GRAD_TRY(launch_nt(a, s, false, false, stream));
     }
     // per-chunk R = phi_q^T [a | h] over the chunk's queries (partials per frame), suffix
@@ -900,7 +900,6 @@ rehyat_status rehyat_distill_grad(const rehyat_params* p, const void* q, const v
         a.rows = s.N;
         a.group_rows = s.n;
         a.ngroups = s.T;
-        a.tiles_per_group = tiles32(s.n);
         GRAD_TRY(launch_nt(a, s, bf, false, stream));
     }
     GRAD_TRY(launch_grad_phi_bwd(s, F32(L.u), F32(L.dphi), stream));

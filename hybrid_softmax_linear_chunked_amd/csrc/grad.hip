@@ -15,10 +15,10 @@
 // The dense products run on the fp32 matrix core (v_mfma_f32_32x32x2f32) so that fp32
 // and bf16 inputs share one exact-product path:
 //   nt_kernel: C[i][f] = sum_d X[i][d] Y_m[f][d] for row groups that each read one matrix
-//              Y_m (a head's W, a chunk's [S | -Z], a key frame's suffix R), contraction
-//              slots (h, s) <-> d = h K/2 + s so each lane reads contiguous half-rows;
-//   tn_kernel: per token segment, C[m][n] = sum_k X[k][m] Y[k][n] (dW and R partials),
-//              lanes reading consecutive columns of a row;
+//              Y_m (a head's W, a chunk's [S | -Z], a key frame's suffix R);
+//   tn_kernel: per token segment, C[m][n] = sum_k X[k][m] Y[k][n] (dW and R partials);
+// both stage 64 x 32 slices of their operands through LDS with 16-byte loads along rows,
+// and each wave reads its MFMA operands from there (one 32x32 output block per wave);
 // and every sum over segments, frames, chunks or batches runs in a fixed order, so the
 // gradients are bitwise reproducible.
 #include "kernels.hpp"
@@ -27,28 +27,6 @@
 namespace rehyat {
 
 namespace {
-
-template <class T>
-__device__ inline void load16(const T* p, float (&o)[16]) {
-    if constexpr (sizeof(T) == 2) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(p + 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            o[e] = (float)a[e];
-            o[8 + e] = (float)b[e];
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float4 v = reinterpret_cast<const float4*>(p)[e];
-            o[4 * e] = v.x;
-            o[4 * e + 1] = v.y;
-            o[4 * e + 2] = v.z;
-            o[4 * e + 3] = v.w;
-        }
-    }
-}
 
 template <class T>
 __device__ inline float load1(const T* p) {
@@ -64,17 +42,54 @@ __device__ inline int ls_of(const GradArgs& a, int c) {
     return a.linear_only ? f1 : max(0, f0 - a.To);
 }
 
-// One wave per 32x32 output block; four waves per workgroup cover 32 rows x 128 columns.
+// Rows [r0, r0 + 64) x columns [c0, c0 + 32) of a row-major source into LDS as float,
+// dst[r][c] with row stride 33 (conflict-free column reads); rows at or past rlim and
+// columns at or past clim (a multiple of 4, or of 8 for bf16) read as zero.
+template <class T>
+__device__ inline void stage_rows(const T* src, int64_t ld, int r0, int rlim, int c0, int clim, float* dst) {
+    const int t = threadIdx.x;
+    if constexpr (sizeof(T) == 2) {
+        const int r = t / 4, c = (t % 4) * 8;  // 64 rows x 4 chunks of 8
+        float v[8];
+        const bool ok = r0 + r < rlim && c0 + c < clim;
+        if (ok) {
+            const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + (int64_t)(r0 + r) * ld + c0 + c);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[r * 33 + c + e] = v[e];
+    } else {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int q = t + 256 * u, r = q / 8, c = (q % 8) * 4;  // 64 rows x 8 chunks of 4
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (r0 + r < rlim && c0 + c < clim)
+                x = *reinterpret_cast<const float4*>(src + (int64_t)(r0 + r) * ld + c0 + c);
+            dst[r * 33 + c] = x.x;
+            dst[r * 33 + c + 1] = x.y;
+            dst[r * 33 + c + 2] = x.z;
+            dst[r * 33 + c + 3] = x.w;
+        }
+    }
+}
+
+// 64 rows x 64 columns per workgroup, one 32x32 block per wave; X and Y slices of 32
+// contraction elements staged through LDS with coalesced 16-byte loads.
 template <class TX, class TY>
 __global__ __launch_bounds__(256) void nt_kernel(const NtArgs a, const GradArgs s) {
+    __shared__ float xs[64 * 33], ys[64 * 33];
     const int bt = blockIdx.z;
     const int grp = blockIdx.y / a.tiles_per_group, t = blockIdx.y % a.tiles_per_group;
-    const int row0 = grp * a.group_rows + t * 32;
+    const int row0 = grp * a.group_rows + t * 64;
     const int rend = min((grp + 1) * a.group_rows, a.rows);
     if (row0 >= rend) return;
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
-    const int cb = blockIdx.x * 4 + wave;
-    if (cb * 32 >= a.ncols) return;
+    const int wr = wave / 2, wc = wave % 2;
+    const int c0 = blockIdx.x * 64;
 
     int m;
     if (a.mode == 0) {
@@ -87,75 +102,109 @@ __global__ __launch_bounds__(256) void nt_kernel(const NtArgs a, const GradArgs 
         while (c < a.nmat && ls_of(s, c) <= grp) ++c;
         m = c < a.nmat ? bt * a.nmat + c : -1;
     }
-    const int r = row0 + col;
-    const bool rv = r < rend;
-    const int f = cb * 32 + col;
-    float* crow_base = a.c + (int64_t)bt * a.c_bt_stride;
+    float* cb = a.c + (int64_t)bt * a.c_bt_stride;
+    const int f = c0 + wc * 32 + col;
+    const bool fv = f < a.ncols;
     if (m < 0) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-            const int rr = row0 + crow(q, h);
-            if (rr < rend) crow_base[(int64_t)rr * a.ldc + f] = 0.f;
+            const int rr = row0 + wr * 32 + crow(q, h);
+            if (rr < rend && fv) cb[(int64_t)rr * a.ldc + f] = 0.f;
         }
         return;
     }
-    const TX* xr = reinterpret_cast<const TX*>(a.x) + (int64_t)bt * a.x_bt_stride + (int64_t)(rv ? r : row0) * a.ldx;
-    const TY* yr = reinterpret_cast<const TY*>(a.y) + (int64_t)m * a.y_mat_stride + (int64_t)f * a.ldy;
-    const int half = a.K / 2;
+    const TX* xb = reinterpret_cast<const TX*>(a.x) + (int64_t)bt * a.x_bt_stride;
+    const TY* yb = reinterpret_cast<const TY*>(a.y) + (int64_t)m * a.y_mat_stride;
     f32x16 acc;
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = 0.f;
-    for (int kc = 0; kc < half; kc += 16) {
-        float xa[16], yb[16];
-        load16<TX>(xr + h * half + kc, xa);
-        load16<TY>(yr + h * half + kc, yb);
+    for (int d0 = 0; d0 < a.K; d0 += 32) {
+        __syncthreads();  // the previous slice has been read
+        stage_rows<TX>(xb, a.ldx, row0, rend, d0, a.K, xs);
+        stage_rows<TY>(yb, a.ldy, c0, a.ncols, d0, a.K, ys);
+        __syncthreads();
+        const float* xr = xs + (wr * 32 + col) * 33 + h;
+        const float* yr = ys + (wc * 32 + col) * 33 + h;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) acc = mma32(rv ? xa[q] : 0.f, yb[q], acc);
+        for (int st = 0; st < 16; ++st) acc = mma32(xr[2 * st], yr[2 * st], acc);
     }
+    if (!fv) return;
+    const TY* yrow = yb + (int64_t)f * a.ldy;
     float add = 0.f;
     if (a.colbias) add += a.colbias[(int64_t)(bt % s.H) * a.colbias_head_stride + f];
-    if (a.sub_col >= 0) add -= load1<TY>(yr + a.sub_col);
+    if (a.sub_col >= 0) add -= load1<TY>(yrow + a.sub_col);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-        const int rr = row0 + crow(q, h);
-        if (rr < rend) crow_base[(int64_t)rr * a.ldc + f] = acc[q] + add;
+        const int rr = row0 + wr * 32 + crow(q, h);
+        if (rr < rend) cb[(int64_t)rr * a.ldc + f] = acc[q] + add;
     }
 }
 
-// Partial C[m][n] = sum over the rows k of one segment of X[k][m] Y[k][n]; one wave per
-// 32x32 block, four blocks per workgroup; empty segments store zeros.
+// Slice [k0, k0 + 32) x [c0, c0 + 64) of a row-major source into LDS as float, dst[k][c]
+// with row stride 68; rows at or past klim and columns at or past clim read as zero.
+template <class T>
+__device__ inline void stage_cols(const T* src, int64_t ld, int k0, int klim, int c0, int clim, float* dst) {
+    const int t = threadIdx.x;
+    if constexpr (sizeof(T) == 2) {
+        const int k = t / 8, c = (t % 8) * 8;  // 32 rows x 8 chunks of 8
+        float v[8];
+        if (k0 + k < klim && c0 + c < clim) {
+            const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + (int64_t)(k0 + k) * ld + c0 + c);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[k * 68 + c + e] = v[e];
+    } else {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int q = t + 256 * u, k = q / 16, c = (q % 16) * 4;  // 32 rows x 16 chunks of 4
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (k0 + k < klim && c0 + c < clim)
+                x = *reinterpret_cast<const float4*>(src + (int64_t)(k0 + k) * ld + c0 + c);
+            *reinterpret_cast<float4*>(dst + k * 68 + c) = x;
+        }
+    }
+}
+
+// Partial C[m][n] = sum over the rows k of one segment of X[k][m] Y[k][n]: 64 x 64 outputs
+// per workgroup (one 32x32 block per wave), rows staged 32 at a time through LDS; empty
+// segments store zeros.
 template <class TX, class TY>
 __global__ __launch_bounds__(256) void tn_kernel(const TnArgs a) {
+    __shared__ __align__(16) float xs[32 * 68], ys[32 * 68];
     const int bt = blockIdx.z;
     const int grp = blockIdx.y / a.nseg, sg = blockIdx.y % a.nseg;
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
-    const int nbn = a.ncols / 32;
-    const int bi = blockIdx.x * 4 + wave;
-    if (bi >= (a.mrows / 32) * nbn) return;
-    const int mb = bi / nbn, nb = bi % nbn;
+    const int wm = wave / 2, wn = wave % 2;
+    const int ntn = (a.ncols + 63) / 64;
+    const int m0 = (blockIdx.x / ntn) * 64, n0 = (blockIdx.x % ntn) * 64;
     const int gend = min((grp + 1) * a.group_rows, a.rows);
     const int k0 = grp * a.group_rows + sg * a.seg_rows;
     const int k1 = min(k0 + a.seg_rows, gend);
-    const TX* xb = reinterpret_cast<const TX*>(a.x) + (int64_t)bt * a.x_bt_stride + mb * 32 + col;
-    const TY* yb = reinterpret_cast<const TY*>(a.y) + (int64_t)bt * a.y_bt_stride + nb * 32 + col;
+    const TX* xb = reinterpret_cast<const TX*>(a.x) + (int64_t)bt * a.x_bt_stride;
+    const TY* yb = reinterpret_cast<const TY*>(a.y) + (int64_t)bt * a.y_bt_stride;
     f32x16 acc;
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = 0.f;
     for (int k = k0; k < k1; k += 32) {
-        float xa[16], ya[16];
+        __syncthreads();
+        stage_cols<TX>(xb, a.ldx, k, k1, m0, a.mrows, xs);
+        stage_cols<TY>(yb, a.ldy, k, k1, n0, a.ncols, ys);
+        __syncthreads();
+        const float* xr = xs + h * 68 + wm * 32 + col;
+        const float* yr = ys + h * 68 + wn * 32 + col;
 #pragma unroll
-        for (int st = 0; st < 16; ++st) {
-            const int row = k + 2 * st + h;
-            const bool ok = row < k1;
-            xa[st] = ok ? load1<TX>(xb + (int64_t)row * a.ldx) : 0.f;
-            ya[st] = ok ? load1<TY>(yb + (int64_t)row * a.ldy) : 0.f;
-        }
-#pragma unroll
-        for (int st = 0; st < 16; ++st) acc = mma32(xa[st], ya[st], acc);
+        for (int st = 0; st < 16; ++st) acc = mma32(xr[2 * st * 68], yr[2 * st * 68], acc);
     }
+    const int mm = m0 + wm * 32, nn = n0 + wn * 32;
+    if (mm >= a.mrows || nn >= a.ncols) return;
     float* out = a.part + (((int64_t)bt * a.ngroups + grp) * a.nseg + sg) * a.mrows * a.ncols;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) out[(int64_t)(mb * 32 + crow(q, h)) * a.ncols + nb * 32 + col] = acc[q];
+    for (int q = 0; q < 16; ++q) out[(int64_t)(mm + crow(q, h)) * a.ncols + nn + col] = acc[q];
 }
 
 // out[o][e] = sum_{b < nb} sum_{s < ns} part[((b * no + o) * ns + s) * E + e], in that order
@@ -255,20 +304,38 @@ __global__ __launch_bounds__(256) void rows_kernel(const GradArgs s, const float
     if (lane < 32) ah[D + lane] = lane == 0 ? dot * inv : 0.f;
 }
 
+// Elementwise feature-map kernels: thread t of a workgroup owns element j = t % Dphi of
+// rows t / Dphi, t / Dphi + per, ... (per = 256 / Dphi rows at a time, threads past
+// per * Dphi idle) of the workgroup's kPhiRows rows; feature (j, p) of a row sits at
+// feat(j, 1) + (p - 1) * len(part of j).
+constexpr int kPhiRows = 32;
+
+__device__ inline int part_len(int j, int Dphi, int P) {
+    const int q = Dphi / P, r = Dphi % P;
+    return j < r * (q + 1) ? q + 1 : q;
+}
+
 // u = softplus(pre) in place of pre, and phi[i][feat(j, p)] = u^p
 __global__ __launch_bounds__(256) void phi_fwd_kernel(const GradArgs s, float* __restrict__ U, float* __restrict__ phi) {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= (int64_t)s.BH * s.N * s.Dphi) return;
-    const int64_t row = e / s.Dphi;
-    const int j = (int)(e % s.Dphi);
-    const float x = U[e];
-    const float u = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
-    U[e] = u;
-    float pw = u;
-    float* out = phi + row * s.F;
-    for (int p = 1; p <= s.P; ++p) {
-        out[feat_index(j, p, s.Dphi, s.P)] = pw;
-        pw *= u;
+    const int per = 256 / s.Dphi, t = threadIdx.x;
+    if (t >= per * s.Dphi) return;
+    const int j = t % s.Dphi, r_off = t / s.Dphi;
+    const int f1 = feat_index(j, 1, s.Dphi, s.P), step = part_len(j, s.Dphi, s.P);
+    const int64_t rows = (int64_t)s.BH * s.N;
+    const int64_t r0 = (int64_t)blockIdx.x * kPhiRows;
+    for (int rr = r_off; rr < kPhiRows; rr += per) {
+        const int64_t row = r0 + rr;
+        if (row >= rows) break;
+        float* up = U + row * s.Dphi + j;
+        const float x = *up;
+        const float u = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+        *up = u;
+        float pw = u;
+        float* out = phi + row * s.F + f1;
+        for (int p = 0; p < s.P; ++p) {
+            out[p * step] = pw;
+            pw *= u;
+        }
     }
 }
 
@@ -276,43 +343,61 @@ __global__ __launch_bounds__(256) void phi_fwd_kernel(const GradArgs s, float* _
 // in place of u
 __global__ __launch_bounds__(256) void phi_bwd_kernel(const GradArgs s, float* __restrict__ U,
                                                       const float* __restrict__ dphi) {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= (int64_t)s.BH * s.N * s.Dphi) return;
-    const int64_t row = e / s.Dphi;
-    const int j = (int)(e % s.Dphi);
-    const float u = U[e];
-    const float* dp = dphi + row * s.F;
-    float du = 0.f, upow = 1.f;
-    for (int p = 1; p <= s.P; ++p) {
-        du += (float)p * upow * dp[feat_index(j, p, s.Dphi, s.P)];
-        upow *= u;
+    const int per = 256 / s.Dphi, t = threadIdx.x;
+    if (t >= per * s.Dphi) return;
+    const int j = t % s.Dphi, r_off = t / s.Dphi;
+    const int f1 = feat_index(j, 1, s.Dphi, s.P), step = part_len(j, s.Dphi, s.P);
+    const int64_t rows = (int64_t)s.BH * s.N;
+    const int64_t r0 = (int64_t)blockIdx.x * kPhiRows;
+    for (int rr = r_off; rr < kPhiRows; rr += per) {
+        const int64_t row = r0 + rr;
+        if (row >= rows) break;
+        float* up = U + row * s.Dphi + j;
+        const float u = *up;
+        const float* dp = dphi + row * s.F + f1;
+        float du = 0.f, upow = 1.f;
+        for (int p = 0; p < s.P; ++p) {
+            du += (float)(p + 1) * upow * dp[p * step];
+            upow *= u;
+        }
+        *up = du * -expm1f(-u);
     }
-    U[e] = du * -expm1f(-u);
 }
 
-// part[bt][sg][j] = sum over the rows of segment sg of X[row][j], in row order
+// part[bt][sg][j] = sum over the rows of segment sg of X[row][j]: with per = 256 / cols
+// (threads from per * cols on idle), thread t sums column t % cols over rows t / cols,
+// t / cols + per, ... in order, and the per partial sums of a column are added in index
+// order
 __global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ X, int64_t rows, int cols, int seg_rows,
                                                      float* __restrict__ part) {
-    const int bt = blockIdx.y, sg = blockIdx.x;
+    __shared__ float red[256];
+    const int bt = blockIdx.y, sg = blockIdx.x, t = threadIdx.x;
+    const int per = 256 / cols, j = t % cols, r_off = t / cols;
     const int64_t r0 = (int64_t)sg * seg_rows, r1 = min(r0 + seg_rows, rows);
-    for (int j = threadIdx.x; j < cols; j += 256) {
-        float acc = 0.f;
-        for (int64_t r = r0; r < r1; ++r) acc += X[((int64_t)bt * rows + r) * cols + j];
-        part[((int64_t)bt * gridDim.x + sg) * cols + j] = acc;
+    float acc = 0.f;
+    if (r_off < per)
+        for (int64_t r = r0 + r_off; r < r1; r += per) acc += X[((int64_t)bt * rows + r) * cols + j];
+    red[t] = acc;
+    __syncthreads();
+    if (t < cols) {
+        float tot = 0.f;
+        for (int i = 0; i < per; ++i) tot += red[i * cols + t];
+        part[((int64_t)bt * gridDim.x + sg) * cols + t] = tot;
     }
 }
 
 template <class TX, class TY>
-hipError_t launch_nt_t(const NtArgs& a, const GradArgs& s, hipStream_t stream) {
-    const dim3 grid((a.ncols + 127) / 128, a.ngroups * a.tiles_per_group, s.BH);
+hipError_t launch_nt_t(NtArgs a, const GradArgs& s, hipStream_t stream) {
+    a.tiles_per_group = (a.group_rows + 63) / 64;
+    const dim3 grid((a.ncols + 63) / 64, a.ngroups * a.tiles_per_group, s.BH);
     hipLaunchKernelGGL((nt_kernel<TX, TY>), grid, dim3(256), 0, stream, a, s);
     return hipGetLastError();
 }
 
 template <class TX, class TY>
 hipError_t launch_tn_t(const TnArgs& a, int BH, hipStream_t stream) {
-    const int blocks = (a.mrows / 32) * (a.ncols / 32);
-    const dim3 grid((blocks + 3) / 4, a.ngroups * a.nseg, BH);
+    const int blocks = ((a.mrows + 63) / 64) * ((a.ncols + 63) / 64);
+    const dim3 grid(blocks, a.ngroups * a.nseg, BH);
     hipLaunchKernelGGL((tn_kernel<TX, TY>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
@@ -354,14 +439,16 @@ hipError_t launch_grad_rows(const GradArgs& s, const float* o, const float* t, c
 }
 
 hipError_t launch_grad_phi_fwd(const GradArgs& s, float* U, float* phi, hipStream_t stream) {
-    const int64_t E = (int64_t)s.BH * s.N * s.Dphi;
-    hipLaunchKernelGGL(phi_fwd_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, stream, s, U, phi);
+    const int64_t rows = (int64_t)s.BH * s.N;
+    hipLaunchKernelGGL(phi_fwd_kernel, dim3((unsigned)((rows + kPhiRows - 1) / kPhiRows)), dim3(256), 0, stream, s, U,
+                       phi);
     return hipGetLastError();
 }
 
 hipError_t launch_grad_phi_bwd(const GradArgs& s, float* U, const float* dphi, hipStream_t stream) {
-    const int64_t E = (int64_t)s.BH * s.N * s.Dphi;
-    hipLaunchKernelGGL(phi_bwd_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, stream, s, U, dphi);
+    const int64_t rows = (int64_t)s.BH * s.N;
+    hipLaunchKernelGGL(phi_bwd_kernel, dim3((unsigned)((rows + kPhiRows - 1) / kPhiRows)), dim3(256), 0, stream, s, U,
+                       dphi);
     return hipGetLastError();
 }
 
