@@ -443,3 +443,64 @@ def distill_phi_grads_chunked(p: Params, q, k, v, wq, wk, bq=None, bk=None, head
             res["dwk"][h] += dwk
             res["dbk"][h] += dbk
     return res
+
+
+# ---------------------------------------------------------------------------------------
+# Backward of the hybrid attention for an upstream gradient G = dL/do (blog 2.2.1-2.3 with
+# the chain rule): for a weight w_ij of key j in query i (exp(s_ij) in the softmax region,
+# kappa_ij in the linear region), dL/dw_ij = a_i . v_j - h_i with a_i = G_i / den_i and
+# h_i = (G_i . o_i) / den_i, and dL/dv_j = sum_i (w_ij / den_i) G_i.  Softmax weights give
+# dL/ds_ij = exp(s_ij) (a_i . v_j - h_i) on the scaled score s_ij = q_i . k_j / sqrt(D), so
+# dq_i += sum_j dL/ds_ij k_j / sqrt(D) and dk_j += sum_i dL/ds_ij q_i / sqrt(D); linear
+# weights reach q and k through phi: dq += W_q^T dpre_q, dk += W_k^T dpre_k.
+# ---------------------------------------------------------------------------------------
+
+def backward(p: Params, q, k, v, wq, wk, dout, bq=None, bk=None):
+    """Brute force with explicit masks.  Returns dict dq, dk, dv [B,H,N,D], dwq, dwk
+    [H,Dphi,D], dbq, dbk [H,Dphi]."""
+    q, k, v, wq, wk, G = map(_f64, (q, k, v, wq, wk, dout))
+    bq = None if bq is None else np.asarray(bq, dtype=np.float64)
+    bk = None if bk is None else np.asarray(bk, dtype=np.float64)
+    soft, lin = numpy_masks(p)
+    res = dict(dq=np.zeros(q.shape), dk=np.zeros(k.shape), dv=np.zeros(v.shape), dwq=np.zeros(wq.shape),
+               dwk=np.zeros(wk.shape), dbq=np.zeros(wq.shape[:2]), dbk=np.zeros(wk.shape[:2]))
+    rs = 1.0 / np.sqrt(p.D)
+    for b in range(p.B):
+        for h in range(p.H):
+            prq, uq, fq = _phi_parts(p, q[b, h], wq[h], None if bq is None else bq[h])
+            prk, uk, fk = _phi_parts(p, k[b, h], wk[h], None if bk is None else bk[h])
+            s = q[b, h] @ k[b, h].T * rs
+            smax = np.where(soft, s, -np.inf).max(axis=1, keepdims=True)
+            shift = np.maximum(np.where(np.isfinite(smax), smax, 0.0), 0.0)
+            ws_ = np.where(soft, np.exp(s - shift), 0.0)
+            wl = np.where(lin, (fq @ fk.T) * np.exp(-shift), 0.0)
+            den = (ws_ + wl).sum(axis=1, keepdims=True)
+            o = ((ws_ + wl) @ v[b, h]) / den
+            g = G[b, h]
+            a = g / den                                       # G_i / den_i (shifted units)
+            hv = (g * o).sum(axis=1, keepdims=True) / den
+            dw = a @ v[b, h].T - hv                           # dL/dw_ij in shifted units
+            ds = ws_ * dw                                     # dL/ds_ij
+            res["dq"][b, h] += ds @ k[b, h] * rs
+            res["dk"][b, h] += ds.T @ q[b, h] * rs
+            res["dv"][b, h] += (ws_ + wl).T @ a
+            dkap = np.where(lin, dw * np.exp(-shift), 0.0)
+            dwq, dbq, dxq = _phi_backward_x(p, prq, uq, q[b, h], wq[h], dkap @ fk)
+            dwk, dbk, dxk = _phi_backward_x(p, prk, uk, k[b, h], wk[h], dkap.T @ fq)
+            res["dq"][b, h] += dxq
+            res["dk"][b, h] += dxk
+            res["dwq"][h] += dwq
+            res["dbq"][h] += dbq
+            res["dwk"][h] += dwk
+            res["dbk"][h] += dbk
+    return res
+
+
+def _phi_backward_x(p, pre, u, x, w, dphi):
+    """dL/dW, dL/db and dL/dx of one slab from dL/dphi (pre = x W^T + b)."""
+    elem, power = feature_map(p)
+    du = np.zeros_like(u)
+    for f in range(elem.size):
+        du[:, elem[f]] += power[f] * u[:, elem[f]] ** (power[f] - 1) * dphi[:, f]
+    dpre = du / (1.0 + np.exp(-pre))
+    return dpre.T @ x, dpre.sum(axis=0), dpre @ w
