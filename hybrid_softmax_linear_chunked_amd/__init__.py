@@ -29,6 +29,7 @@ EXPORTS = (
     "rehyat_stream_workspace_bytes", "rehyat_state_init", "rehyat_chunk_step",
     "rehyat_parallel_states", "rehyat_parallel_attend", "rehyat_distill_workspace_bytes",
     "rehyat_distill_loss", "rehyat_distill_grad_workspace_bytes", "rehyat_distill_grad",
+    "rehyat_backward_workspace_bytes", "rehyat_backward",
 )
 
 
@@ -98,6 +99,10 @@ def lib():
         L.rehyat_distill_grad_workspace_bytes.restype = ctypes.c_size_t
         L.rehyat_distill_grad.argtypes = [P] + [vp] * 13 + [ctypes.c_size_t, vp]
         L.rehyat_distill_grad.restype = ctypes.c_int
+        L.rehyat_backward_workspace_bytes.argtypes = [P]
+        L.rehyat_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.rehyat_backward.argtypes = [P] + [vp] * 16 + [ctypes.c_size_t, vp]
+        L.rehyat_backward.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -311,6 +316,44 @@ def distill_grad(p: Params, q, k, v, wq, wk, bq=None, bk=None, ws=None, biases=T
                                      _ptr(out.get("dbq")), _ptr(out.get("dbk")), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream_handle()),
            "rehyat_distill_grad")
+    return out
+
+
+def backward_workspace_bytes(p: Params) -> int:
+    return int(lib().rehyat_backward_workspace_bytes(ctypes.byref(p.c())))
+
+
+def backward(p: Params, q, k, v, wq, wk, dout, bq=None, bk=None, ws=None, biases=True):
+    """Gradients of the chunk-parallel forward for the upstream gradient dout (float32
+    [B,H,N,D]) through rehyat_backward.  Returns a dict of float32 tensors dq, dk, dv
+    [B,H,N,D], dwq, dwk [H,Dphi,D], and dbq, dbk [H,Dphi] when biases=True."""
+    dt = torch_dtype(p.in_dtype)
+    shape = (p.B, p.H, p.N, p.D)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, shape, dt, name)
+    _check(dout, shape, torch.float32, "dout")
+    for name, t in (("wq", wq), ("wk", wk)):
+        _check(t, (p.H, p.Dphi, p.D), dt, name)
+    for name, t in (("bq", bq), ("bk", bk)):
+        if t is not None:
+            _check(t, (p.H, p.Dphi), torch.float32, name)
+    dev = q.device
+    out = {key: torch.empty(shape, dtype=torch.float32, device=dev) for key in ("dq", "dk", "dv")}
+    out["dwq"] = torch.empty((p.H, p.Dphi, p.D), dtype=torch.float32, device=dev)
+    out["dwk"] = torch.empty((p.H, p.Dphi, p.D), dtype=torch.float32, device=dev)
+    if biases:
+        out["dbq"] = torch.empty((p.H, p.Dphi), dtype=torch.float32, device=dev)
+        out["dbk"] = torch.empty((p.H, p.Dphi), dtype=torch.float32, device=dev)
+    need = backward_workspace_bytes(p)
+    if need == 0:
+        raise RehyatError(1, "rehyat_backward_workspace_bytes")
+    if ws is None:
+        ws = alloc_bytes(need, dev)
+    _raise(lib().rehyat_backward(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), _ptr(bq),
+                                 _ptr(bk), _ptr(dout), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                 _ptr(out["dwq"]), _ptr(out["dwk"]), _ptr(out.get("dbq")), _ptr(out.get("dbk")),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream_handle()),
+           "rehyat_backward")
     return out
 
 

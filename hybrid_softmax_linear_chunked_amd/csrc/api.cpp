@@ -637,17 +637,22 @@ rehyat_status rehyat_distill_loss(const rehyat_params* p, const void* q, const v
 
 }  // extern "C"
 
-// Distillation-gradient workspace: the two outputs, the student's per-part outputs lse and
+// Gradient workspace.  Distillation: the two outputs, the student's per-part outputs lse and
 // z, the loss partials, separate forward workspaces for the student (whose per-frame state
-// partials the gradient reads) and the teacher, then the gradient buffers.
+// partials the gradient reads) and the teacher, then the linear-branch buffers.  Backward
+// (upstream gradient given): no teacher; adds delta and log den per query, transposed
+// weights and chunk sums, and the per-chunk softmax-branch buffers (P and dS of one chunk
+// window for every slab, the transposed window keys, partial sums over query segments).
 namespace {
 
 constexpr int kGradSegRows = 2048;    // token rows per dW partial
 constexpr int kColsumSegRows = 256;   // token rows per bias-gradient partial
+constexpr int kSoftSegRows = 1024;    // query rows per dK / dV partial of a window
 
 struct GradLayout {
-    size_t stu, tea, lse, z, sqd, fwd_s, fwd_t, ah, u, phi, dphi, sz, rp, r, wp, bp, total;
-    int nseg_sq, nseg_w, nseg_b;
+    size_t stu, tea, lse, z, sqd, fwd_s, fwd_t, ah, u, phi, dphi, sz, rp, r, wp, bp;
+    size_t delta, lden, wt, rt, sbuf, dpbuf, kt, pp, total;
+    int nseg_sq, nseg_w, nseg_b, lq_max, lk_max, ldp, nseg_s;
 };
 
 GradArgs grad_args(const rehyat_params* p) {
@@ -669,7 +674,18 @@ GradArgs grad_args(const rehyat_params* p) {
     return s;
 }
 
-GradLayout grad_layout(const rehyat_params* p) {
+// chunk c: query rows [r0, r1), window key rows [k0, k1)
+void chunk_rows(const rehyat_params* p, int c, int& r0, int& r1, int& k0, int& k1) {
+    const int n = p->frame_tokens;
+    const int f0 = c * p->Tc, f1 = std::min(f0 + p->Tc, p->T);
+    const int ws = p->linear_only ? f1 : std::max(0, f0 - p->To);
+    r0 = f0 * n;
+    r1 = f1 * n;
+    k0 = ws * n;
+    k1 = f1 * n;
+}
+
+GradLayout grad_layout(const rehyat_params* p, bool backward) {
     const rehyat_params ps = distill_student(p), pt = distill_teacher(p);
     const GradArgs s = grad_args(p);
     const size_t BH = s.BH, N = s.N, f4 = sizeof(float), LD = s.D + 32;
@@ -677,6 +693,15 @@ GradLayout grad_layout(const rehyat_params* p) {
     L.nseg_sq = sqdist_segments((int64_t)N * s.D);
     L.nseg_w = (int)((N + kGradSegRows - 1) / kGradSegRows);
     L.nseg_b = (int)((N + kColsumSegRows - 1) / kColsumSegRows);
+    L.lq_max = L.lk_max = 0;
+    for (int c = 0; c < s.nc; ++c) {
+        int r0, r1, k0, k1;
+        chunk_rows(p, c, r0, r1, k0, k1);
+        L.lq_max = std::max(L.lq_max, r1 - r0);
+        L.lk_max = std::max(L.lk_max, k1 - k0);
+    }
+    L.ldp = (L.lk_max + 31) / 32 * 32;
+    L.nseg_s = (L.lq_max + kSoftSegRows - 1) / kSoftSegRows;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -684,12 +709,12 @@ GradLayout grad_layout(const rehyat_params* p) {
         return at;
     };
     L.stu = take(BH * N * s.D * f4);
-    L.tea = take(BH * N * s.D * f4);
+    L.tea = take(backward ? 0 : BH * N * s.D * f4);
     L.lse = take(BH * N * f4);
     L.z = take(BH * N * f4);
-    L.sqd = take(BH * L.nseg_sq * f4);
+    L.sqd = take(backward ? 0 : BH * L.nseg_sq * f4);
     L.fwd_s = take(split_layout(&ps).total);
-    L.fwd_t = take(split_layout(&pt).total);
+    L.fwd_t = take(backward ? 0 : split_layout(&pt).total);
     L.ah = take(BH * N * LD * f4);
     L.u = take(BH * N * s.Dphi * f4);
     L.phi = take(BH * N * s.F * f4);
@@ -699,86 +724,58 @@ GradLayout grad_layout(const rehyat_params* p) {
     L.r = take(BH * s.nc * s.F * LD * f4);
     L.wp = take(BH * L.nseg_w * s.Dphi * s.D * f4);
     L.bp = take(BH * L.nseg_b * s.Dphi * f4);
+    const size_t bw = backward ? 1 : 0;
+    L.delta = take(bw * BH * N * f4);
+    L.lden = take(bw * BH * N * f4);
+    L.wt = take(bw * p->H * s.D * s.Dphi * f4);
+    L.rt = take(bw * BH * s.nc * s.D * s.F * f4);
+    L.sbuf = take(bw * BH * L.lq_max * L.ldp * f4);
+    L.dpbuf = take(bw * BH * L.lq_max * L.ldp * f4);
+    L.kt = take(bw * BH * s.D * L.ldp * f4);
+    L.pp = take(bw * BH * L.nseg_s * (size_t)L.lk_max * s.D * f4);
     L.total = off;
     return L;
 }
 
 int tiles32(int rows) { return (rows + 31) / 32; }
 
-}  // namespace
-
-extern "C" {
-
-size_t rehyat_distill_grad_workspace_bytes(const rehyat_params* p) {
-    if (check_params(p, true) != REHYAT_OK) return 0;
-    const rehyat_params pt = distill_teacher(p);
-    if (check_params(&pt, true) != REHYAT_OK) return 0;
-    return grad_layout(p).total;
+// grid y / z extents of the gradient launches
+bool grad_grid_ok(const GradArgs& s, const GradLayout& L) {
+    return s.BH <= 65535 && tiles32(s.N) <= 65535 && (int64_t)s.T * tiles32(s.n) <= 65535 &&
+           (int64_t)s.nc * tiles32(s.Tc * s.n) <= 65535 && (int64_t)s.BH * s.nc <= 65535 &&
+           (int64_t)s.nc * s.Tc <= 65535 && L.lq_max <= 65535 && (int64_t)L.nseg_s <= 65535;
 }
 
-rehyat_status rehyat_distill_grad(const rehyat_params* p, const void* q, const void* k, const void* v,
-                                  const void* wq, const void* wk, const float* bq, const float* bk, float* loss,
-                                  float* dwq, float* dwk, float* dbq, float* dbk, void* ws, size_t ws_bytes,
-                                  hipStream_t stream) {
-    rehyat_status st = check_params(p, true);
-    if (st != REHYAT_OK) return st;
-    const rehyat_params ps = distill_student(p), pt = distill_teacher(p);
-    st = check_params(&pt, true);
-    if (st != REHYAT_OK) return st;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(wq) || !aligned16(wk) ||
-        !aligned4_or_null(bq) || !aligned4_or_null(bk) || !loss || !aligned4_or_null(loss) || !dwq ||
-        !aligned4_or_null(dwq) || !dwk || !aligned4_or_null(dwk) || !aligned4_or_null(dbq) || !aligned4_or_null(dbk))
-        return REHYAT_EALIGN;
-    const GradArgs s = grad_args(p);
-    const GradLayout L = grad_layout(p);
-    if ((int64_t)L.nseg_sq * s.BH >= ((int64_t)1 << 31) || (int64_t)s.N * (s.D + 32) >= ((int64_t)1 << 31) ||
-        (int64_t)s.N * s.F >= ((int64_t)1 << 31))
-        return REHYAT_EINVAL;
-    // grid y / z extents of the gradient launches
-    if (s.BH > 65535 || tiles32(s.N) > 65535 || (int64_t)s.T * tiles32(s.n) > 65535 ||
-        (int64_t)s.nc * tiles32(s.Tc * s.n) > 65535 || (int64_t)s.BH * s.nc > 65535 || (int64_t)s.nc * s.Tc > 65535)
-        return REHYAT_EINVAL;
-    if (!ws || ws_bytes < L.total || reinterpret_cast<uintptr_t>(ws) % 256 != 0) return REHYAT_EWORKSPACE;
-    char* w = reinterpret_cast<char*>(ws);
-    auto F32 = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
-    const bool bf = p->in_dtype == REHYAT_BF16;
-
-    // forward: student (float output and per-part outputs), teacher, loss
-    rehyat_aux aux;
-    std::memset(&aux, 0, sizeof(aux));
-    aux.lse = F32(L.lse);
-    aux.z = F32(L.z);
-    st = rehyat_forward_parallel_aux(&ps, q, k, v, wq, wk, bq, bk, w + L.stu, &aux, w + L.fwd_s, L.fwd_t - L.fwd_s,
-                                     stream);
-    if (st != REHYAT_OK) return st;
-    st = rehyat_forward_parallel(&pt, q, k, v, wq, wk, bq, bk, w + L.tea, w + L.fwd_t, L.ah - L.fwd_t, stream);
-    if (st != REHYAT_OK) return st;
-    const int64_t len = (int64_t)s.N * s.D;
-    st = hip_status(launch_sqdist(F32(L.stu), F32(L.tea), len, s.BH, F32(L.sqd), loss, stream));
-    if (st != REHYAT_OK) return st;
-    const int64_t HW = (int64_t)p->H * s.Dphi * s.D;
-    if (s.G == 0) {  // no linear region: the loss does not depend on phi
-        st = hip_status(launch_zero(dwq, HW, stream));
-        if (st == REHYAT_OK) st = hip_status(launch_zero(dwk, HW, stream));
-        if (st == REHYAT_OK && dbq) st = hip_status(launch_zero(dbq, (int64_t)p->H * s.Dphi, stream));
-        if (st == REHYAT_OK && dbk) st = hip_status(launch_zero(dbk, (int64_t)p->H * s.Dphi, stream));
-        return st;
-    }
-    const int LD = s.D + 32;
-    const int64_t N = s.N;
 #define GRAD_TRY(expr)                              \
     do {                                            \
-        st = hip_status(expr);                      \
-        if (st != REHYAT_OK) return st;             \
+        rehyat_status st_ = hip_status(expr);       \
+        if (st_ != REHYAT_OK) return st_;           \
     } while (0)
-    // a_i, h_i per query; [S_c | -Z_c] per chunk from the student's per-frame partials
-    GRAD_TRY(launch_grad_rows(s, F32(L.stu), F32(L.tea), F32(L.lse), F32(L.z), F32(L.ah), stream));
+
+// Linear branch of the backward (chunk states of blog 2.3, feature map of blog 2.2.2): with
+// AH = [a | h | 0] per query in place, the gradients of W_q, W_k (b_q, b_k when non-null)
+// and, when dq is non-null, the linear branch's share of dq, dk, dv added to them.
+rehyat_status linear_branch(const rehyat_params* p, const GradArgs& s, const GradLayout& L, char* w,
+                            const void* q, const void* k, const void* v, const void* wq, const void* wk,
+                            const float* bq, const float* bk, float* dwq, float* dwk, float* dbq, float* dbk,
+                            float* dq, float* dk, float* dv, hipStream_t stream) {
+    auto F32 = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+    const bool bf = p->in_dtype == REHYAT_BF16;
+    const int LD = s.D + 32;
+    const int64_t N = s.N;
+    const rehyat_params ps = distill_student(p);
     const ParallelLayout PL = parallel_layout(&ps, s.G);
     GRAD_TRY(launch_grad_state_sz(s, F32(L.fwd_s + PL.sp), F32(L.fwd_s + PL.zp), F32(L.sz), stream));
 
-    auto pre = [&](const void* x, const void* wmat, const float* bias) {
+    auto nt_base = [&]() {
         NtArgs a;
         std::memset(&a, 0, sizeof(a));
+        a.sub_col = -1;
+        a.rows = s.N;
+        return a;
+    };
+    auto pre = [&](const void* x, const void* wmat, const float* bias) {
+        NtArgs a = nt_base();
         a.x = x;
         a.x_bt_stride = N * s.D;
         a.ldx = s.D;
@@ -789,13 +786,11 @@ rehyat_status rehyat_distill_grad(const rehyat_params* p, const void* q, const v
         a.mode = 0;
         a.K = s.D;
         a.ncols = s.Dphi;
-        a.sub_col = -1;
         a.colbias = bias;
         a.colbias_head_stride = s.Dphi;
         a.c = F32(L.u);
         a.c_bt_stride = N * s.Dphi;
         a.ldc = s.Dphi;
-        a.rows = s.N;
         a.group_rows = s.N;
         a.ngroups = 1;
         return launch_nt(a, s, bf, bf, stream);
@@ -825,13 +820,36 @@ rehyat_status rehyat_distill_grad(const rehyat_params* p, const void* q, const v
         }
         return e;
     };
+    // dx += dpre W (contraction over Dphi) with W transposed into L.wt
+    auto dx = [&](const void* wmat, float* dxout) -> hipError_t {
+        hipError_t e = launch_transpose(wmat, bf, (int64_t)s.Dphi * s.D, s.D, F32(L.wt), (int64_t)s.D * s.Dphi, s.Dphi,
+                                        s.Dphi, s.D, p->H, stream);
+        if (e != hipSuccess) return e;
+        NtArgs a = nt_base();
+        a.x = F32(L.u);
+        a.x_bt_stride = N * s.Dphi;
+        a.ldx = s.Dphi;
+        a.y = F32(L.wt);
+        a.y_mat_stride = (int64_t)s.D * s.Dphi;
+        a.ldy = s.Dphi;
+        a.nmat = p->H;
+        a.mode = 0;
+        a.K = s.Dphi;
+        a.ncols = s.D;
+        a.c = dxout;
+        a.c_bt_stride = N * s.D;
+        a.ldc = s.D;
+        a.group_rows = s.N;
+        a.ngroups = 1;
+        a.accumulate = 1;
+        return launch_nt(a, s, false, false, stream);
+    };
 
-    // query side: phi_q, dphi_q = [S_c | -Z_c] [a | h], dpre_q, dW_q, db_q
+    // query side: phi_q, dphi_q = [S_c | -Z_c] [a | h], R per chunk, dpre_q, dW_q, db_q
     GRAD_TRY(pre(q, wq, bq));
     GRAD_TRY(launch_grad_phi_fwd(s, F32(L.u), F32(L.phi), stream));
     {
-        NtArgs a;
-        std::memset(&a, 0, sizeof(a));
+        NtArgs a = nt_base();
         a.x = F32(L.ah);
         a.x_bt_stride = N * LD;
         a.ldx = LD;
@@ -842,16 +860,13 @@ rehyat_status rehyat_distill_grad(const rehyat_params* p, const void* q, const v
         a.mode = 1;
         a.K = LD;
         a.ncols = s.F;
-        a.sub_col = -1;
         a.c = F32(L.dphi);
         a.c_bt_stride = N * s.F;
         a.ldc = s.F;
-        a.rows = s.N;
         a.group_rows = s.Tc * s.n;
         a.ngroups = s.nc;
         GRAD_TRY(launch_nt(a, s, false, false, stream));
     }
-    // per-chunk R = phi_q^T [a | h] over the chunk's queries (partials per frame), suffix
     {
         TnArgs t;
         std::memset(&t, 0, sizeof(t));
@@ -876,13 +891,35 @@ rehyat_status rehyat_distill_grad(const rehyat_params* p, const void* q, const v
     }
     GRAD_TRY(launch_grad_phi_bwd(s, F32(L.u), F32(L.dphi), stream));
     GRAD_TRY(dw(q, dwq, dbq));
+    if (dq) GRAD_TRY(dx(wq, dq));
 
-    // key side: phi_k, dphi_k = R v - r per key frame, dpre_k, dW_k, db_k
+    // key side: phi_k, (dv += R^T phi_k), dphi_k = R v - r per key frame, dpre_k, dW_k, db_k
     GRAD_TRY(pre(k, wk, bk));
     GRAD_TRY(launch_grad_phi_fwd(s, F32(L.u), F32(L.phi), stream));
+    if (dv) {
+        GRAD_TRY(launch_transpose(F32(L.r), false, (int64_t)s.F * LD, LD, F32(L.rt), (int64_t)s.D * s.F, s.F, s.F, s.D,
+                                  s.BH * s.nc, stream));
+        NtArgs a = nt_base();
+        a.x = F32(L.phi);
+        a.x_bt_stride = N * s.F;
+        a.ldx = s.F;
+        a.y = F32(L.rt);
+        a.y_mat_stride = (int64_t)s.D * s.F;
+        a.ldy = s.F;
+        a.nmat = s.nc;
+        a.mode = 2;
+        a.K = s.F;
+        a.ncols = s.D;
+        a.c = dv;
+        a.c_bt_stride = N * s.D;
+        a.ldc = s.D;
+        a.group_rows = s.n;
+        a.ngroups = s.T;
+        a.accumulate = 1;
+        GRAD_TRY(launch_nt(a, s, false, false, stream));
+    }
     {
-        NtArgs a;
-        std::memset(&a, 0, sizeof(a));
+        NtArgs a = nt_base();
         a.x = v;
         a.x_bt_stride = N * s.D;
         a.ldx = s.D;
@@ -897,14 +934,201 @@ rehyat_status rehyat_distill_grad(const rehyat_params* p, const void* q, const v
         a.c = F32(L.dphi);
         a.c_bt_stride = N * s.F;
         a.ldc = s.F;
-        a.rows = s.N;
         a.group_rows = s.n;
         a.ngroups = s.T;
         GRAD_TRY(launch_nt(a, s, bf, false, stream));
     }
     GRAD_TRY(launch_grad_phi_bwd(s, F32(L.u), F32(L.dphi), stream));
     GRAD_TRY(dw(k, dwk, dbk));
-#undef GRAD_TRY
+    if (dk) GRAD_TRY(dx(wk, dk));
+    return REHYAT_OK;
+}
+
+rehyat_status zero_param_grads(const rehyat_params* p, const GradArgs& s, float* dwq, float* dwk, float* dbq,
+                               float* dbk, hipStream_t stream) {
+    const int64_t HW = (int64_t)p->H * s.Dphi * s.D;
+    GRAD_TRY(launch_zero(dwq, HW, stream));
+    GRAD_TRY(launch_zero(dwk, HW, stream));
+    if (dbq) GRAD_TRY(launch_zero(dbq, (int64_t)p->H * s.Dphi, stream));
+    if (dbk) GRAD_TRY(launch_zero(dbk, (int64_t)p->H * s.Dphi, stream));
+    return REHYAT_OK;
+}
+
+bool grad_ptrs_ok(const void* q, const void* k, const void* v, const void* wq, const void* wk, const float* bq,
+                  const float* bk, const float* dwq, const float* dwk, const float* dbq, const float* dbk) {
+    return aligned16(q) && aligned16(k) && aligned16(v) && aligned16(wq) && aligned16(wk) && aligned4_or_null(bq) &&
+           aligned4_or_null(bk) && dwq && aligned4_or_null(dwq) && dwk && aligned4_or_null(dwk) &&
+           aligned4_or_null(dbq) && aligned4_or_null(dbk);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rehyat_distill_grad_workspace_bytes(const rehyat_params* p) {
+    if (check_params(p, true) != REHYAT_OK) return 0;
+    const rehyat_params pt = distill_teacher(p);
+    if (check_params(&pt, true) != REHYAT_OK) return 0;
+    return grad_layout(p, false).total;
+}
+
+rehyat_status rehyat_distill_grad(const rehyat_params* p, const void* q, const void* k, const void* v,
+                                  const void* wq, const void* wk, const float* bq, const float* bk, float* loss,
+                                  float* dwq, float* dwk, float* dbq, float* dbk, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+    rehyat_status st = check_params(p, true);
+    if (st != REHYAT_OK) return st;
+    const rehyat_params ps = distill_student(p), pt = distill_teacher(p);
+    st = check_params(&pt, true);
+    if (st != REHYAT_OK) return st;
+    if (!grad_ptrs_ok(q, k, v, wq, wk, bq, bk, dwq, dwk, dbq, dbk) || !loss || !aligned4_or_null(loss))
+        return REHYAT_EALIGN;
+    const GradArgs s = grad_args(p);
+    const GradLayout L = grad_layout(p, false);
+    if ((int64_t)L.nseg_sq * s.BH >= ((int64_t)1 << 31) || (int64_t)s.N * (s.D + 32) >= ((int64_t)1 << 31) ||
+        (int64_t)s.N * s.F >= ((int64_t)1 << 31) || !grad_grid_ok(s, L))
+        return REHYAT_EINVAL;
+    if (!ws || ws_bytes < L.total || reinterpret_cast<uintptr_t>(ws) % 256 != 0) return REHYAT_EWORKSPACE;
+    char* w = reinterpret_cast<char*>(ws);
+    auto F32 = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+
+    // forward: student (float output and per-part outputs), teacher, loss
+    rehyat_aux aux;
+    std::memset(&aux, 0, sizeof(aux));
+    aux.lse = F32(L.lse);
+    aux.z = F32(L.z);
+    st = rehyat_forward_parallel_aux(&ps, q, k, v, wq, wk, bq, bk, w + L.stu, &aux, w + L.fwd_s, L.fwd_t - L.fwd_s,
+                                     stream);
+    if (st != REHYAT_OK) return st;
+    st = rehyat_forward_parallel(&pt, q, k, v, wq, wk, bq, bk, w + L.tea, w + L.fwd_t, L.ah - L.fwd_t, stream);
+    if (st != REHYAT_OK) return st;
+    const int64_t len = (int64_t)s.N * s.D;
+    GRAD_TRY(launch_sqdist(F32(L.stu), F32(L.tea), len, s.BH, F32(L.sqd), loss, stream));
+    if (s.G == 0) return zero_param_grads(p, s, dwq, dwk, dbq, dbk, stream);  // the loss does not depend on phi
+    GRAD_TRY(launch_grad_rows(s, F32(L.stu), F32(L.tea), nullptr, F32(L.lse), F32(L.z), F32(L.ah), nullptr, nullptr,
+                              stream));
+    return linear_branch(p, s, L, w, q, k, v, wq, wk, bq, bk, dwq, dwk, dbq, dbk, nullptr, nullptr, nullptr, stream);
+}
+
+size_t rehyat_backward_workspace_bytes(const rehyat_params* p) {
+    if (check_params(p, true) != REHYAT_OK) return 0;
+    return grad_layout(p, true).total;
+}
+
+rehyat_status rehyat_backward(const rehyat_params* p, const void* q, const void* k, const void* v, const void* wq,
+                              const void* wk, const float* bq, const float* bk, const float* dout, float* dq,
+                              float* dk, float* dv, float* dwq, float* dwk, float* dbq, float* dbk, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+    rehyat_status st = check_params(p, true);
+    if (st != REHYAT_OK) return st;
+    if (!grad_ptrs_ok(q, k, v, wq, wk, bq, bk, dwq, dwk, dbq, dbk) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv))
+        return REHYAT_EALIGN;
+    const rehyat_params ps = distill_student(p);
+    const GradArgs s = grad_args(p);
+    const GradLayout L = grad_layout(p, true);
+    if ((int64_t)s.N * (s.D + 32) >= ((int64_t)1 << 31) || (int64_t)s.N * s.F >= ((int64_t)1 << 31) ||
+        (int64_t)L.lq_max * L.ldp >= ((int64_t)1 << 31) || !grad_grid_ok(s, L))
+        return REHYAT_EINVAL;
+    if (!ws || ws_bytes < L.total || reinterpret_cast<uintptr_t>(ws) % 256 != 0) return REHYAT_EWORKSPACE;
+    char* w = reinterpret_cast<char*>(ws);
+    auto F32 = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+    const bool bf = p->in_dtype == REHYAT_BF16;
+    const int64_t N = s.N, ND = N * s.D;
+
+    // recompute the forward with float output and the per-part outputs lse, z
+    rehyat_aux aux;
+    std::memset(&aux, 0, sizeof(aux));
+    aux.lse = F32(L.lse);
+    aux.z = F32(L.z);
+    st = rehyat_forward_parallel_aux(&ps, q, k, v, wq, wk, bq, bk, w + L.stu, &aux, w + L.fwd_s, L.fwd_t - L.fwd_s,
+                                     stream);
+    if (st != REHYAT_OK) return st;
+    GRAD_TRY(launch_zero(dq, (int64_t)s.BH * ND, stream));
+    GRAD_TRY(launch_zero(dk, (int64_t)s.BH * ND, stream));
+    GRAD_TRY(launch_zero(dv, (int64_t)s.BH * ND, stream));
+    GRAD_TRY(launch_grad_rows(s, F32(L.stu), nullptr, dout, F32(L.lse), F32(L.z), F32(L.ah), F32(L.delta),
+                              F32(L.lden), stream));
+    if (s.G > 0) {
+        st = linear_branch(p, s, L, w, q, k, v, wq, wk, bq, bk, dwq, dwk, dbq, dbk, dq, dk, dv, stream);
+        if (st != REHYAT_OK) return st;
+    } else {
+        st = zero_param_grads(p, s, dwq, dwk, dbq, dbk, stream);
+        if (st != REHYAT_OK) return st;
+    }
+
+    // softmax branch, one chunk window at a time (blog 2.2.1 window, scores q.k / sqrt(D))
+    const float scale = (float)(1.0 / std::sqrt((double)s.D));
+    const int64_t pbt = (int64_t)L.lq_max * L.ldp;
+    for (int c = 0; c < s.nc; ++c) {
+        int r0, r1, k0, k1;
+        chunk_rows(p, c, r0, r1, k0, k1);
+        const int Lq = r1 - r0, Lk = k1 - k0;
+        if (Lk == 0) continue;
+        const size_t es = bf ? 2 : 4;
+        const char* qc = reinterpret_cast<const char*>(q) + (size_t)r0 * s.D * es;
+        const char* kw = reinterpret_cast<const char*>(k) + (size_t)k0 * s.D * es;
+        const char* vw = reinterpret_cast<const char*>(v) + (size_t)k0 * s.D * es;
+        auto nt = [&](const void* x, bool xbf, int64_t xbs, int ldx, const void* y, bool ybf, int64_t ybs, int ldy,
+                      int K, int ncols, float* c_, int64_t cbs, int ldc, int acc) {
+            NtArgs a;
+            std::memset(&a, 0, sizeof(a));
+            a.x = x;
+            a.x_bt_stride = xbs;
+            a.ldx = ldx;
+            a.y = y;
+            a.y_mat_stride = ybs;
+            a.ldy = ldy;
+            a.nmat = s.BH;
+            a.mode = 3;
+            a.K = K;
+            a.ncols = ncols;
+            a.sub_col = -1;
+            a.c = c_;
+            a.c_bt_stride = cbs;
+            a.ldc = ldc;
+            a.rows = Lq;
+            a.group_rows = Lq;
+            a.ngroups = 1;
+            a.accumulate = acc;
+            return launch_nt(a, s, xbf, ybf, stream);
+        };
+        // S = Q_c K_w^T and dP = G_c V_w^T, then P and dS in place
+        GRAD_TRY(nt(qc, bf, ND, s.D, kw, bf, ND, s.D, s.D, Lk, F32(L.sbuf), pbt, L.ldp, 0));
+        GRAD_TRY(nt(dout + (size_t)r0 * s.D, false, ND, s.D, vw, bf, ND, s.D, s.D, Lk, F32(L.dpbuf), pbt, L.ldp, 0));
+        GRAD_TRY(launch_softmax_bwd(F32(L.sbuf), F32(L.dpbuf), F32(L.lden) + r0, F32(L.delta) + r0, N, s.BH, Lq, Lk,
+                                    L.ldp, pbt, scale, stream));
+        // dV_w += P^T G_c and dK_w += dS^T Q_c: partial sums over query segments, then added
+        auto tn_add = [&](const float* X, const void* Y, bool ybf, float* out) -> hipError_t {
+            TnArgs t;
+            std::memset(&t, 0, sizeof(t));
+            t.x = X;
+            t.x_bt_stride = pbt;
+            t.ldx = L.ldp;
+            t.y = Y;
+            t.y_bt_stride = ND;
+            t.ldy = s.D;
+            t.mrows = Lk;
+            t.ncols = s.D;
+            t.part = F32(L.pp);
+            t.rows = Lq;
+            t.group_rows = Lq;
+            t.ngroups = 1;
+            t.seg_rows = kSoftSegRows;
+            t.nseg = (Lq + kSoftSegRows - 1) / kSoftSegRows;
+            hipError_t e = launch_tn(t, s.BH, ybf, stream);
+            if (e == hipSuccess)
+                e = launch_grad_reduce(F32(L.pp), out + (size_t)k0 * s.D, 1, s.BH, t.nseg, (int64_t)Lk * s.D, stream,
+                                       ND, true);
+            return e;
+        };
+        GRAD_TRY(tn_add(F32(L.sbuf), dout + (size_t)r0 * s.D, false, dv));
+        GRAD_TRY(tn_add(F32(L.dpbuf), qc, bf, dk));
+        // dQ_c += dS K_w with K_w transposed (zero past Lk)
+        GRAD_TRY(launch_transpose(kw, bf, ND, s.D, F32(L.kt), (int64_t)s.D * L.ldp, L.ldp, Lk, s.D, s.BH, stream));
+        GRAD_TRY(nt(F32(L.dpbuf), false, pbt, L.ldp, F32(L.kt), false, (int64_t)s.D * L.ldp, L.ldp, Lk, s.D,
+                    dq + (size_t)r0 * s.D, ND, s.D, 1));
+    }
     return REHYAT_OK;
 }
 

@@ -96,6 +96,8 @@ __global__ __launch_bounds__(256) void nt_kernel(const NtArgs a, const GradArgs 
         m = bt % s.H;
     } else if (a.mode == 1) {
         m = bt * a.nmat + grp;
+    } else if (a.mode == 3) {
+        m = bt;
     } else {
         // earliest chunk whose linear region holds key frame grp
         int c = 0;
@@ -106,6 +108,7 @@ __global__ __launch_bounds__(256) void nt_kernel(const NtArgs a, const GradArgs 
     const int f = c0 + wc * 32 + col;
     const bool fv = f < a.ncols;
     if (m < 0) {
+        if (a.accumulate) return;
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             const int rr = row0 + wr * 32 + crow(q, h);
@@ -136,7 +139,10 @@ __global__ __launch_bounds__(256) void nt_kernel(const NtArgs a, const GradArgs 
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         const int rr = row0 + wr * 32 + crow(q, h);
-        if (rr < rend) cb[(int64_t)rr * a.ldc + f] = acc[q] + add;
+        if (rr < rend) {
+            float* dst = cb + (int64_t)rr * a.ldc + f;
+            *dst = a.accumulate ? *dst + (acc[q] + add) : acc[q] + add;
+        }
     }
 }
 
@@ -203,20 +209,26 @@ __global__ __launch_bounds__(256) void tn_kernel(const TnArgs a) {
     const int mm = m0 + wm * 32, nn = n0 + wn * 32;
     if (mm >= a.mrows || nn >= a.ncols) return;
     float* out = a.part + (((int64_t)bt * a.ngroups + grp) * a.nseg + sg) * a.mrows * a.ncols;
+    if (nn + col >= a.ncols) return;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) out[(int64_t)(mm + crow(q, h)) * a.ncols + nn + col] = acc[q];
+    for (int q = 0; q < 16; ++q) {
+        const int r = mm + crow(q, h);
+        if (r < a.mrows) out[(int64_t)r * a.ncols + nn + col] = acc[q];
+    }
 }
 
-// out[o][e] = sum_{b < nb} sum_{s < ns} part[((b * no + o) * ns + s) * E + e], in that order
+// out[o * ostride + e] (+)= sum_{b < nb} sum_{s < ns} part[((b * no + o) * ns + s) * E + e],
+// summed in that order (and then added to out when accumulating)
 __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ part, float* __restrict__ out, int nb,
-                                                     int no, int ns, int64_t E) {
+                                                     int no, int ns, int64_t E, int64_t ostride, int accumulate) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int o = blockIdx.y;
     if (e >= E) return;
     float acc = 0.f;
     for (int b = 0; b < nb; ++b)
         for (int s = 0; s < ns; ++s) acc += part[(((int64_t)b * no + o) * ns + s) * E + e];
-    out[(int64_t)o * E + e] = acc;
+    float* dst = out + (int64_t)o * ostride + e;
+    *dst = accumulate ? *dst + acc : acc;
 }
 
 // R[bt][c] <- sum over c' >= c of R[bt][c'] (from the last chunk), in place
@@ -262,11 +274,14 @@ __global__ __launch_bounds__(256) void state_sz_kernel(const GradArgs s, const f
     }
 }
 
-// Per query row (one wave per row): g = 2 (o - t), 1/den from lse and z, then
-// AH[i] = [g / den | (g . o) / den | 0 ...] (D + 32 columns)
+// Per query row (one wave per row): g = dout, or 2 (o - t) for the distillation objective;
+// 1/den from lse and z; AH[i] = [g / den | (g . o) / den | 0 ...] (D + 32 columns), and
+// when asked, delta_i = g . o and log den_i
 __global__ __launch_bounds__(256) void rows_kernel(const GradArgs s, const float* __restrict__ o,
-                                                   const float* __restrict__ t, const float* __restrict__ lse,
-                                                   const float* __restrict__ z, float* __restrict__ AH) {
+                                                   const float* __restrict__ t, const float* __restrict__ dout,
+                                                   const float* __restrict__ lse, const float* __restrict__ z,
+                                                   float* __restrict__ AH, float* __restrict__ delta,
+                                                   float* __restrict__ lden) {
     const int bt = blockIdx.y, wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int64_t i = (int64_t)blockIdx.x * 4 + wave;
     if (i >= s.N) return;
@@ -279,7 +294,7 @@ __global__ __launch_bounds__(256) void rows_kernel(const GradArgs s, const float
         gv[u] = 0.f;
         if (d < D) {
             const float ov = o[row * D + d];
-            gv[u] = 2.f * (ov - t[row * D + d]);
+            gv[u] = dout ? dout[row * D + d] : 2.f * (ov - t[row * D + d]);
             dot += gv[u] * ov;
         }
     }
@@ -302,6 +317,51 @@ __global__ __launch_bounds__(256) void rows_kernel(const GradArgs s, const float
         if (d < D) ah[d] = gv[u] * inv;
     }
     if (lane < 32) ah[D + lane] = lane == 0 ? dot * inv : 0.f;
+    if (lane == 0 && delta) {
+        delta[row] = dot;
+        // log(exp(L) + z), stable for either term dominating
+        const float lz = zz > 0.f ? logf(zz) : -INFINITY;
+        const float hi = fmaxf(L, lz), lo = fminf(L, lz);
+        lden[row] = lo == -INFINITY ? hi : hi + log1pf(expf(lo - hi));
+    }
+}
+
+__global__ __launch_bounds__(256) void softmax_bwd_kernel(float* __restrict__ S, float* __restrict__ dP,
+                                                          const float* __restrict__ lden,
+                                                          const float* __restrict__ delta, int64_t stat_bt_stride,
+                                                          int Lq, int Lk, int ldp, int64_t bt_stride, float scale) {
+    const int bt = blockIdx.z, i = blockIdx.y;
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= ldp) return;
+    const int64_t off = (int64_t)bt * bt_stride + (int64_t)i * ldp + j;
+    if (j >= Lk) {
+        S[off] = 0.f;
+        dP[off] = 0.f;
+        return;
+    }
+    const float L = lden[(int64_t)bt * stat_bt_stride + i], dl = delta[(int64_t)bt * stat_bt_stride + i];
+    const float pr = expf(S[off] * scale - L);
+    S[off] = pr;
+    dP[off] = pr * (dP[off] - dl) * scale;
+}
+
+// 32 x 32 tiles through LDS
+template <class T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, int64_t in_bt_stride, int ldi,
+                                                        float* __restrict__ out, int64_t out_bt_stride, int ldo,
+                                                        int rows, int cols) {
+    __shared__ float tile[32][33];
+    const int bt = blockIdx.z, r0 = blockIdx.x * 32, c0 = blockIdx.y * 32;
+    const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;  // 8 rows of threads
+    for (int k = ty; k < 32; k += 8) {
+        const int r = r0 + k, c = c0 + tx;
+        tile[k][tx] = (r < rows && c < cols) ? (float)in[(int64_t)bt * in_bt_stride + (int64_t)r * ldi + c] : 0.f;
+    }
+    __syncthreads();
+    for (int k = ty; k < 32; k += 8) {
+        const int c = c0 + k, r = r0 + tx;
+        if (c < cols && r < ldo) out[(int64_t)bt * out_bt_stride + (int64_t)c * ldo + r] = tile[tx][k];
+    }
 }
 
 // Elementwise feature-map kernels: thread t of a workgroup owns element j = t % Dphi of
@@ -415,9 +475,29 @@ hipError_t launch_tn(const TnArgs& a, int BH, bool y_bf16, hipStream_t stream) {
     return y_bf16 ? launch_tn_t<float, bf16>(a, BH, stream) : launch_tn_t<float, float>(a, BH, stream);
 }
 
-hipError_t launch_grad_reduce(const float* part, float* out, int nb, int no, int ns, int64_t E, hipStream_t stream) {
+hipError_t launch_grad_reduce(const float* part, float* out, int nb, int no, int ns, int64_t E, hipStream_t stream,
+                              int64_t out_stride, bool accumulate) {
     hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((E + 255) / 256), no), dim3(256), 0, stream, part, out, nb, no,
-                       ns, E);
+                       ns, E, out_stride < 0 ? E : out_stride, accumulate ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_softmax_bwd(float* S, float* dP, const float* lden, const float* delta, int64_t stat_bt_stride,
+                              int BH, int Lq, int Lk, int ldp, int64_t bt_stride, float scale, hipStream_t stream) {
+    hipLaunchKernelGGL(softmax_bwd_kernel, dim3((unsigned)((ldp + 255) / 256), Lq, BH), dim3(256), 0, stream, S, dP,
+                       lden, delta, stat_bt_stride, Lq, Lk, ldp, bt_stride, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose(const void* in, bool in_bf16, int64_t in_bt_stride, int ldi, float* out,
+                            int64_t out_bt_stride, int ldo, int rows, int cols, int nbt, hipStream_t stream) {
+    const dim3 grid((unsigned)((ldo + 31) / 32), (unsigned)((cols + 31) / 32), nbt);
+    if (in_bf16)
+        hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(256), 0, stream, reinterpret_cast<const bf16*>(in),
+                           in_bt_stride, ldi, out, out_bt_stride, ldo, rows, cols);
+    else
+        hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, stream, reinterpret_cast<const float*>(in),
+                           in_bt_stride, ldi, out, out_bt_stride, ldo, rows, cols);
     return hipGetLastError();
 }
 
@@ -432,9 +512,10 @@ hipError_t launch_grad_state_sz(const GradArgs& s, const float* Sp, const float*
     return hipGetLastError();
 }
 
-hipError_t launch_grad_rows(const GradArgs& s, const float* o, const float* t, const float* lse, const float* z,
-                            float* AH, hipStream_t stream) {
-    hipLaunchKernelGGL(rows_kernel, dim3((unsigned)((s.N + 3) / 4), s.BH), dim3(256), 0, stream, s, o, t, lse, z, AH);
+hipError_t launch_grad_rows(const GradArgs& s, const float* o, const float* t, const float* dout, const float* lse,
+                            const float* z, float* AH, float* delta, float* lden, hipStream_t stream) {
+    hipLaunchKernelGGL(rows_kernel, dim3((unsigned)((s.N + 3) / 4), s.BH), dim3(256), 0, stream, s, o, t, dout, lse, z,
+                       AH, delta, lden);
     return hipGetLastError();
 }
 

@@ -209,6 +209,30 @@ rehyat_status rehyat_distill_grad(const rehyat_params* p, const void* q, const v
                                   float* dwk, float* dbq, float* dbk, void* ws, size_t ws_bytes,
                                   hipStream_t stream);
 
+/* Backward of the chunk-parallel forward for an upstream gradient dout = dL/dout (float32
+ * [B,H,N,D]): dq, dk, dv (float32 [B,H,N,D]), dwq, dwk (float32 [H,Dphi,D]) and dbq, dbk
+ * (float32 [H,Dphi], each may be NULL).  The forward is recomputed (float output and the
+ * per-part outputs lse, z); with w_ij the weight of key j in query i (exp(q.k/sqrt(D)) in
+ * the softmax window, kappa_ij in the linear region, blog 2.2.1), a_i = dout_i / den_i and
+ * h_i = (dout_i . o_i) / den_i:
+ *   dv_j  = sum_i w_ij a_i;
+ *   softmax window: dS_ij = (w_ij / den_i) (dout_i . v_j - dout_i . o_i) / sqrt(D),
+ *                   dq_i += sum_j dS_ij k_j, dk_j += sum_i dS_ij q_i (per chunk window);
+ *   linear region: as rehyat_distill_grad through the chunk states (blog 2.3), plus
+ *                  dq += dpre_q W_q and dk += dpre_k W_k through the feature map.
+ * Every sum runs in a fixed order (bitwise reproducible); the softmax branch is computed one
+ * chunk window at a time for all slabs, so the workspace holds two float32
+ * [B*H, Tc*n, (Tc+To)*n] score-sized buffers (2.8 GB for a 12-head Wan 5 s layer) on top of
+ * the gradient buffers of rehyat_distill_grad.  Inputs as for rehyat_forward_parallel;
+ * p->out_dtype is ignored.  Status: REHYAT_EALIGN for null or misaligned pointers (dout,
+ * dq, dk, dv 16-byte aligned), REHYAT_EWORKSPACE, REHYAT_EINVAL as for rehyat_distill_grad. */
+size_t rehyat_backward_workspace_bytes(const rehyat_params* p);
+rehyat_status rehyat_backward(const rehyat_params* p, const void* q, const void* k, const void* v,
+                              const void* wq, const void* wk, const float* bq, const float* bk,
+                              const float* dout, float* dq, float* dk, float* dv, float* dwq,
+                              float* dwk, float* dbq, float* dbk, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -191,3 +191,23 @@ def test_distill_grad_checks(L):
     big = WAN.with_(T=2 ** 28 // 1560 + 1).c()
     assert L.rehyat_distill_grad_workspace_bytes(ctypes.byref(big)) == 0
     assert f(ctypes.byref(big), *[FAKE] * 5, None, None, *outs, FAKE, 1 << 50, None) == EINVAL
+
+
+def test_backward_checks(L):
+    p = WAN.c()
+    need = L.rehyat_backward_workspace_bytes(ctypes.byref(p))
+    # two float32 chunk-window buffers (4,680 queries x 6,240 keys per slab) at least
+    assert need > 2 * 12 * 4680 * 6240 * 4
+    f = L.rehyat_backward
+    ins = [FAKE] * 5 + [None, None, FAKE]             # q, k, v, wq, wk, bq, bk, dout
+    outs = [FAKE] * 5 + [None, None]                 # dq, dk, dv, dwq, dwk, dbq, dbk
+    assert f(ctypes.byref(p), *ins, *outs, FAKE, need - 1, None) == EWORKSPACE
+    assert f(ctypes.byref(p), *ins, *outs, ctypes.c_void_p(0x10010), need, None) == EWORKSPACE
+    for i in range(5):
+        bad = list(outs)
+        bad[i] = None
+        assert f(ctypes.byref(p), *ins, *bad, FAKE, need, None) == EALIGN
+    bad = list(ins)
+    bad[7] = MISALIGNED
+    assert f(ctypes.byref(p), *bad, *outs, FAKE, need, None) == EALIGN
+    assert L.rehyat_backward_workspace_bytes(ctypes.byref(WAN.with_(D=48).c())) == 0
