@@ -14,7 +14,8 @@ on the stream it runs on), the full-softmax comparator on the same shapes, the 1
 streaming form with its peak memory at 21/41/81 frames, the chunking and feature-map
 variants the pages discuss (Tc/To presets and ablations, higher polynomial degree) on the
 same inputs, the distillation objective (hybrid vs full-softmax teacher, squared L2 per
-slab) and its gradients with respect to the feature-map weights, and the CPU oracle timed on a bounded sample of the same workload (which
+slab) and its gradients with respect to the feature-map weights, the backward for an
+upstream gradient (dq, dk, dv and the feature-map gradients), and the CPU oracle timed on a bounded sample of the same workload (which
 also serves as a parity spot check).
 """
 from __future__ import annotations
@@ -242,6 +243,7 @@ def main():
         res["variants"] = variants_leg(rh, torch, p, d, ms)
         res["distill_loss"] = distill_leg(rh, torch, p, d, w)
         res["distill_grad"] = distill_grad_leg(rh, torch, p, d, w, res["distill_loss"]["ms"])
+        res["backward"] = backward_leg(rh, torch, p, d, w, ms)
 
     if not args.no_cpu_baseline:
         cb, parity = cpu_baseline(w, x, out)
@@ -345,6 +347,45 @@ def distill_grad_leg(rh, torch, p, d, w, loss_ms, reps=3):
            "gradient_tflops": round(gfl / (bw * 1e-3) / 1e12, 2), "peak_fp32_matrix_tflops": 157.3,
            "workspace_bytes": int(ws.numel())}
     del ws
+    return res
+
+
+def backward_flops(B, H, D, T, n, Tc, To, Dphi, P, linear_only=0):
+    """Algorithmic FLOPs of rehyat_backward after its forward recompute: five products per
+    chunk window in the softmax branch (scores, dP, dV, dK, dQ), the feature-map gradients,
+    and the linear branch's input gradients (dq, dk through W, dv through the chunk sums)."""
+    F = P * Dphi
+    sch = schedule(T, Tc, To, linear_only)
+    soft = sum((f1 - f0) * n * (we - ws) * n for f0, f1, ws, we, ls in sch)
+    n_s = sch[-1][4] * n
+    N = T * n
+    return (B * H * (10 * D * soft + 4 * N * Dphi * D + 2 * n_s * F * D)
+            + grad_flops(B, H, D, T, n, Tc, To, Dphi, P, linear_only))
+
+
+def backward_leg(rh, torch, p, d, w, fwd_ms, reps=2):
+    """rehyat_backward for a seeded upstream gradient: ms per call (forward recompute
+    included), the backward stages' share (call minus the forward step) and their TFLOP/s."""
+    g = torch.Generator(device=d["q"].device)
+    g.manual_seed(7)
+    dout = torch.randn((p.B, p.H, p.N, p.D), generator=g, device=d["q"].device)
+    ws = rh.alloc_bytes(rh.backward_workspace_bytes(p), d["q"].device)
+    call = lambda: rh.backward(p, d["q"], d["k"], d["v"], d["wq"], d["wk"], dout, ws=ws)
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    bms = e0.elapsed_time(e1) / reps
+    fl = backward_flops(w.B, w.H, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P)
+    st = max(bms - fwd_ms, 1e-6)
+    res = {"ms": round(bms, 3), "backward_stages_ms": round(st, 3), "backward_flops": fl,
+           "backward_tflops": round(fl / (st * 1e-3) / 1e12, 2), "peak_fp32_matrix_tflops": 157.3,
+           "workspace_bytes": int(ws.numel())}
+    del ws, dout
     return res
 
 
