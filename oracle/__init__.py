@@ -504,3 +504,71 @@ def _phi_backward_x(p, pre, u, x, w, dphi):
         du[:, elem[f]] += power[f] * u[:, elem[f]] ** (power[f] - 1) * dphi[:, f]
     dpre = du / (1.0 + np.exp(-pre))
     return dpre.T @ x, dpre.sum(axis=0), dpre @ w
+
+
+def backward_chunked(p: Params, q, k, v, wq, wk, dout, bq=None, bk=None, heads=None):
+    """The backward through the chunk structure (blog 2.2.1-2.3): the outputs and their
+    per-part outputs from the chunk-parallel oracle (den = exp(lse) + z); the softmax branch
+    one chunk window at a time (scores of the chunk's queries against the window's keys);
+    the linear branch through the chunk states S_c, Z_c for the queries and the reverse sums
+    of R_c, r_c over chunks for the keys, dv_j += R^T phi_k(k_j).  Memory O(N F + Lq Lk) per
+    slab, so whole Wan-sized slabs fit.  heads: restrict to these heads (others zero)."""
+    q, k, v, wq, wk, G = map(_f64, (q, k, v, wq, wk, dout))
+    bq = None if bq is None else np.asarray(bq, dtype=np.float64)
+    bk = None if bk is None else np.asarray(bk, dtype=np.float64)
+    sch = schedule(p)
+    n = p.n
+    rs = 1.0 / np.sqrt(p.D)
+    res = dict(dq=np.zeros(q.shape), dk=np.zeros(k.shape), dv=np.zeros(v.shape), dwq=np.zeros(wq.shape),
+               dwk=np.zeros(wk.shape), dbq=np.zeros(wq.shape[:2]), dbk=np.zeros(wk.shape[:2]))
+    p1 = replace(p, B=1, H=1)
+    for b in range(p.B):
+        for h in (range(p.H) if heads is None else heads):
+            sl = lambda a: a[b:b + 1, h:h + 1]
+            o, ax = parallel_rows(p1, sl(q), sl(k), sl(v), wq[h:h + 1], wk[h:h + 1], np.arange(p.N),
+                                  None if bq is None else bq[h:h + 1], None if bk is None else bk[h:h + 1])
+            den = np.exp(ax["lse"]) + ax["z"]
+            qq, kk, vv, g = q[b, h], k[b, h], v[b, h], G[b, h]
+            a = g / den[:, None]
+            delta = (g * o).sum(axis=1)
+            hv = delta / den
+            # softmax branch per chunk window
+            for f0, f1, ws, we, ls in sch:
+                if we <= ws:
+                    continue
+                qs, ks = slice(f0 * n, f1 * n), slice(ws * n, we * n)
+                pr = np.exp(qq[qs] @ kk[ks].T * rs - np.log(den[qs])[:, None])   # w_ij / den_i
+                res["dv"][b, h][ks] += pr.T @ g[qs]
+                ds = pr * (g[qs] @ vv[ks].T - delta[qs][:, None]) * rs
+                res["dq"][b, h][qs] += ds @ kk[ks]
+                res["dk"][b, h][ks] += ds.T @ qq[qs]
+            # linear branch
+            prq, uq, fq = _phi_parts(p, qq, wq[h], None if bq is None else bq[h])
+            prk, uk, fk = _phi_parts(p, kk, wk[h], None if bk is None else bk[h])
+            dfq = np.zeros_like(fq)
+            dfk = np.zeros_like(fk)
+            R = np.zeros((fq.shape[1], p.D))
+            r = np.zeros(fq.shape[1])
+            for c in range(len(sch) - 1, -1, -1):
+                f0, f1, ws, we, ls = sch[c]
+                lo, hi = f0 * n, f1 * n
+                if ls > 0:
+                    keys = slice(0, ls * n)
+                    S = fk[keys].T @ vv[keys]
+                    Z = fk[keys].sum(axis=0)
+                    dfq[lo:hi] = a[lo:hi] @ S.T - hv[lo:hi, None] * Z[None, :]
+                R += fq[lo:hi].T @ a[lo:hi]
+                r += fq[lo:hi].T @ hv[lo:hi]
+                lprev = sch[c - 1][4] if c > 0 else 0
+                ks = slice(lprev * n, ls * n)
+                dfk[ks] = vv[ks] @ R.T - r[None, :]
+                res["dv"][b, h][ks] += fk[ks] @ R
+            dwq, dbq, dxq = _phi_backward_x(p, prq, uq, qq, wq[h], dfq)
+            dwk, dbk, dxk = _phi_backward_x(p, prk, uk, kk, wk[h], dfk)
+            res["dq"][b, h] += dxq
+            res["dk"][b, h] += dxk
+            res["dwq"][h] += dwq
+            res["dbq"][h] += dbq
+            res["dwk"][h] += dwk
+            res["dbk"][h] += dbk
+    return res

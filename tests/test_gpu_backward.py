@@ -60,3 +60,35 @@ def test_backward_matches_oracle(shape):
         e = max(float(np.abs(gk[h] - ref[key][h]).max() / np.abs(ref[key][h]).max()) for h in range(p.H))
         print(f"  {key}: max head rel err {e:.2e}", flush=True)
         assert e <= tol, (key, e)
+
+
+def test_backward_fullsize_head0():
+    """Wan 5 s layer (12 heads x 32,760 tokens, bf16, B = 1) with a seeded upstream
+    gradient: dq, dk, dv of slab (0, 0) and the parameter gradients of head 0 against the
+    oracle's chunked form over the whole slab."""
+    from synth_inputs import WORKLOADS, make_inputs
+    w = WORKLOADS["wan_5s"]
+    p = rh.Params(w.B, w.H, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P, 0, rh.BF16, rh.BF16)
+    print("[backward wan_5s] inputs", flush=True)
+    x = make_inputs(w, seed=1)
+    d = {key: torch.from_numpy(val).to("cuda", torch.bfloat16).contiguous() for key, val in x.items()}
+    del x
+    g = np.random.default_rng(5).standard_normal((w.B, w.H, w.N, w.D), dtype=np.float32)
+    got = rh.backward(p, d["q"], d["k"], d["v"], d["wq"], d["wk"], torch.from_numpy(g).cuda(), biases=False)
+    torch.cuda.synchronize()
+    for key in got:
+        assert torch.isfinite(got[key]).all(), key
+    xs = make_inputs(w, seed=1, slabs=[(0, 0)])
+    p1 = oracle.Params(1, 1, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P)
+    print("[backward wan_5s] oracle (chunked form, slab 0, 0)", flush=True)
+    ref = oracle.backward_chunked(p1, xs["q"], xs["k"], xs["v"], xs["wq"], xs["wk"], g[:, :1])
+    tol = TOL[rh.BF16]
+    for key in ("dq", "dk", "dv"):
+        e = slab_err(got[key][:1, :1].cpu().numpy(), ref[key])
+        print(f"  {key}: slab rel err {e:.2e}", flush=True)
+        assert e <= tol, (key, e)
+    for key in ("dwq", "dwk"):
+        gk = got[key][0].cpu().numpy().astype(np.float64)
+        e = float(np.abs(gk - ref[key][0]).max() / np.abs(ref[key][0]).max())
+        print(f"  {key}: head 0 rel err {e:.2e}", flush=True)
+        assert e <= tol, (key, e)

@@ -80,3 +80,21 @@ def test_one_chunk_is_softmax_attention_backward():
         assert np.abs(gr[name] - ref).max() <= 1e-12 * np.abs(ref).max(), name
     for key in ("dwq", "dwk", "dbq", "dbk"):
         assert not gr[key].any()
+
+
+@pytest.mark.parametrize("shape,bias", [
+    ((1, 2, 8, 7, 4, 3, 1, 8, 2, 0), True),
+    ((2, 1, 6, 6, 5, 2, 0, 9, 3, 0), False),
+    ((1, 1, 8, 8, 3, 2, 3, 8, 2, 0), True),      # To > Tc
+    ((1, 2, 4, 5, 4, 2, 1, 8, 4, 1), False),     # empty softmax window
+    ((1, 1, 8, 9, 2, 1, 0, 8, 1, 0), True),      # Tc = 1, To = 0, P = 1
+    ((1, 1, 8, 4, 5, 4, 1, 8, 2, 0), False),     # one chunk
+])
+def test_chunked_backward_equals_brute_force(shape, bias):
+    p = oracle.Params(*shape)
+    x = rand(p, 12, bias)
+    a = bwd(p, x)
+    b = oracle.backward_chunked(p, x["q"], x["k"], x["v"], x["wq"], x["wk"], x["g"], x["bq"], x["bk"])
+    for key in a:
+        scale = max(np.abs(a[key]).max(), 1e-300)
+        assert np.abs(a[key] - b[key]).max() <= 1e-10 * scale, key
