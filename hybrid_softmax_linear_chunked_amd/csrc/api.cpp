@@ -1091,15 +1091,53 @@ rehyat_status rehyat_backward(const rehyat_params* p, const void* q, const void*
             a.group_rows = Lq;
             a.ngroups = 1;
             a.accumulate = acc;
-            return launch_nt(a, s, xbf, ybf, stream);
+            // bf16 inputs: operands rounded to bf16 on the bf16 matrix core (as in the forward)
+            return bf ? launch_nt16(a, s, xbf, ybf, stream) : launch_nt(a, s, xbf, ybf, stream);
         };
-        // S = Q_c K_w^T and dP = G_c V_w^T, then P and dS in place
-        GRAD_TRY(nt(qc, bf, ND, s.D, kw, bf, ND, s.D, s.D, Lk, F32(L.sbuf), pbt, L.ldp, 0));
-        GRAD_TRY(nt(dout + (size_t)r0 * s.D, false, ND, s.D, vw, bf, ND, s.D, s.D, Lk, F32(L.dpbuf), pbt, L.ldp, 0));
-        GRAD_TRY(launch_softmax_bwd(F32(L.sbuf), F32(L.dpbuf), F32(L.lden) + r0, F32(L.delta) + r0, N, s.BH, Lq, Lk,
-                                    L.ldp, pbt, scale, stream));
+        if (bf) {
+            // bf16 inputs: P = exp(Q_c K_w^T / sqrt(D) - log den) and dS = P (G_c V_w^T - delta)
+            // / sqrt(D) leave the two products' epilogues as bf16 (the forward's P precision)
+            auto nt_epi = [&](const void* x, bool xbf, const void* y, int epi, void* c16, const void* p16) {
+                NtArgs a;
+                std::memset(&a, 0, sizeof(a));
+                a.x = x;
+                a.x_bt_stride = ND;
+                a.ldx = s.D;
+                a.y = y;
+                a.y_mat_stride = ND;
+                a.ldy = s.D;
+                a.nmat = s.BH;
+                a.mode = 3;
+                a.K = s.D;
+                a.ncols = Lk;
+                a.sub_col = -1;
+                a.c_bt_stride = pbt;
+                a.ldc = L.ldp;
+                a.rows = Lq;
+                a.group_rows = Lq;
+                a.ngroups = 1;
+                a.epi = epi;
+                a.ncols_pad = std::min(L.ldp, (Lk + 7) / 8 * 8);
+                a.stat0 = F32(L.lden) + r0;
+                a.stat1 = F32(L.delta) + r0;
+                a.stat_bt_stride = N;
+                a.scale = scale;
+                a.p16 = p16;
+                a.c16 = c16;
+                return launch_nt16(a, s, xbf, true, stream);
+            };
+            GRAD_TRY(nt_epi(qc, true, kw, 1, w + L.sbuf, nullptr));
+            GRAD_TRY(nt_epi(dout + (size_t)r0 * s.D, false, vw, 2, w + L.dpbuf, w + L.sbuf));
+        } else {
+            // S = Q_c K_w^T and dP = G_c V_w^T, then P and dS in place
+            GRAD_TRY(nt(qc, bf, ND, s.D, kw, bf, ND, s.D, s.D, Lk, F32(L.sbuf), pbt, L.ldp, 0));
+            GRAD_TRY(nt(dout + (size_t)r0 * s.D, false, ND, s.D, vw, bf, ND, s.D, s.D, Lk, F32(L.dpbuf), pbt, L.ldp,
+                        0));
+            GRAD_TRY(launch_softmax_bwd(F32(L.sbuf), F32(L.dpbuf), F32(L.lden) + r0, F32(L.delta) + r0, N, s.BH, Lq,
+                                        Lk, L.ldp, pbt, scale, stream));
+        }
         // dV_w += P^T G_c and dK_w += dS^T Q_c: partial sums over query segments, then added
-        auto tn_add = [&](const float* X, const void* Y, bool ybf, float* out) -> hipError_t {
+        auto tn_add = [&](const void* X, const void* Y, bool ybf, float* out) -> hipError_t {
             TnArgs t;
             std::memset(&t, 0, sizeof(t));
             t.x = X;
@@ -1116,17 +1154,17 @@ rehyat_status rehyat_backward(const rehyat_params* p, const void* q, const void*
             t.ngroups = 1;
             t.seg_rows = kSoftSegRows;
             t.nseg = (Lq + kSoftSegRows - 1) / kSoftSegRows;
-            hipError_t e = launch_tn(t, s.BH, ybf, stream);
+            hipError_t e = bf ? launch_tn16(t, s.BH, true, ybf, stream) : launch_tn(t, s.BH, ybf, stream);
             if (e == hipSuccess)
                 e = launch_grad_reduce(F32(L.pp), out + (size_t)k0 * s.D, 1, s.BH, t.nseg, (int64_t)Lk * s.D, stream,
                                        ND, true);
             return e;
         };
-        GRAD_TRY(tn_add(F32(L.sbuf), dout + (size_t)r0 * s.D, false, dv));
-        GRAD_TRY(tn_add(F32(L.dpbuf), qc, bf, dk));
+        GRAD_TRY(tn_add(w + L.sbuf, dout + (size_t)r0 * s.D, false, dv));
+        GRAD_TRY(tn_add(w + L.dpbuf, qc, bf, dk));
         // dQ_c += dS K_w with K_w transposed (zero past Lk)
         GRAD_TRY(launch_transpose(kw, bf, ND, s.D, F32(L.kt), (int64_t)s.D * L.ldp, L.ldp, Lk, s.D, s.BH, stream));
-        GRAD_TRY(nt(F32(L.dpbuf), false, pbt, L.ldp, F32(L.kt), false, (int64_t)s.D * L.ldp, L.ldp, Lk, s.D,
+        GRAD_TRY(nt(w + L.dpbuf, bf, pbt, L.ldp, F32(L.kt), false, (int64_t)s.D * L.ldp, L.ldp, Lk, s.D,
                     dq + (size_t)r0 * s.D, ND, s.D, 1));
     }
     return REHYAT_OK;

@@ -217,6 +217,183 @@ __global__ __launch_bounds__(256) void tn_kernel(const TnArgs a) {
     }
 }
 
+// bf16 matrix-core forms of the two products, for the softmax branch of the backward with
+// bf16 inputs: operands rounded to bf16 (ties to even) while staged, products accumulated
+// in fp32 on v_mfma_f32_32x32x16_bf16.  LDS rows hold 32 contraction elements plus 8 of
+// padding; a lane reads its 8 consecutive contraction slots with one 16-byte read.
+constexpr int kLd16 = 40;
+
+__device__ inline bf16 to_bf16(float x) { return (bf16)x; }
+
+// rows [r0, r0 + 64) x contraction [c0, c0 + 32) of a row-major source -> dst[r][c] (bf16)
+template <class T>
+__device__ inline void stage16_rows(const T* src, int64_t ld, int r0, int rlim, int c0, int clim, bf16* dst) {
+    const int t = threadIdx.x;
+    if constexpr (sizeof(T) == 2) {
+        const int r = t / 4, c = (t % 4) * 8;
+        bf16x8 v;
+        if (r0 + r < rlim && c0 + c < clim) {
+            v = *reinterpret_cast<const bf16x8*>(src + (int64_t)(r0 + r) * ld + c0 + c);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = to_bf16(0.f);
+        }
+        *reinterpret_cast<bf16x8*>(dst + r * kLd16 + c) = v;
+    } else {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int q = t + 256 * u, r = q / 8, c = (q % 8) * 4;
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (r0 + r < rlim && c0 + c < clim)
+                x = *reinterpret_cast<const float4*>(src + (int64_t)(r0 + r) * ld + c0 + c);
+            bf16x4 v;
+            v[0] = to_bf16(x.x);
+            v[1] = to_bf16(x.y);
+            v[2] = to_bf16(x.z);
+            v[3] = to_bf16(x.w);
+            *reinterpret_cast<bf16x4*>(dst + r * kLd16 + c) = v;
+        }
+    }
+}
+
+// contraction rows [k0, k0 + 32) x columns [c0, c0 + 64) of a row-major source, stored
+// transposed: dst[c][k] (bf16)
+template <class T>
+__device__ inline void stage16_cols(const T* src, int64_t ld, int k0, int klim, int c0, int clim, bf16* dst) {
+    const int t = threadIdx.x;
+    if constexpr (sizeof(T) == 2) {
+        const int k = t / 8, c = (t % 8) * 8;
+        bf16x8 v;
+        if (k0 + k < klim && c0 + c < clim) {
+            v = *reinterpret_cast<const bf16x8*>(src + (int64_t)(k0 + k) * ld + c0 + c);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = to_bf16(0.f);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[(c + e) * kLd16 + k] = v[e];
+    } else {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int q = t + 256 * u, k = q / 16, c = (q % 16) * 4;
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (k0 + k < klim && c0 + c < clim)
+                x = *reinterpret_cast<const float4*>(src + (int64_t)(k0 + k) * ld + c0 + c);
+            dst[(c + 0) * kLd16 + k] = to_bf16(x.x);
+            dst[(c + 1) * kLd16 + k] = to_bf16(x.y);
+            dst[(c + 2) * kLd16 + k] = to_bf16(x.z);
+            dst[(c + 3) * kLd16 + k] = to_bf16(x.w);
+        }
+    }
+}
+
+__device__ inline f32x16 mma16(const bf16* a, const bf16* b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(a),
+                                                   *reinterpret_cast<const bf16x8*>(b), c, 0, 0, 0);
+}
+
+// nt_kernel on bf16 operands (modes 0, 1 and 3; no column bias or subtraction), with the
+// softmax-backward epilogues of NtArgs::epi
+template <class TX, class TY>
+__global__ __launch_bounds__(256) void nt16_kernel(const NtArgs a, const GradArgs s) {
+    __shared__ __align__(16) bf16 xs[64 * kLd16], ys[64 * kLd16];
+    const int bt = blockIdx.z;
+    const int grp = blockIdx.y / a.tiles_per_group, t = blockIdx.y % a.tiles_per_group;
+    const int row0 = grp * a.group_rows + t * 64;
+    const int rend = min((grp + 1) * a.group_rows, a.rows);
+    if (row0 >= rend) return;
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
+    const int wr = wave / 2, wc = wave % 2;
+    const int c0 = blockIdx.x * 64;
+    const int m = a.mode == 0 ? bt % s.H : a.mode == 1 ? bt * a.nmat + grp : bt;
+    const TX* xb = reinterpret_cast<const TX*>(a.x) + (int64_t)bt * a.x_bt_stride;
+    const TY* yb = reinterpret_cast<const TY*>(a.y) + (int64_t)m * a.y_mat_stride;
+    f32x16 acc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+    for (int d0 = 0; d0 < a.K; d0 += 32) {
+        __syncthreads();
+        stage16_rows<TX>(xb, a.ldx, row0, rend, d0, a.K, xs);
+        stage16_rows<TY>(yb, a.ldy, c0, a.ncols, d0, a.K, ys);
+        __syncthreads();
+        const bf16* xr = xs + (wr * 32 + col) * kLd16 + h * 8;
+        const bf16* yr = ys + (wc * 32 + col) * kLd16 + h * 8;
+        acc = mma16(xr, yr, acc);
+        acc = mma16(xr + 16, yr + 16, acc);
+    }
+    const int f = c0 + wc * 32 + col;
+    if (a.epi != 0) {
+        if (f >= a.ncols_pad) return;
+        const bool fv = f < a.ncols;
+        bf16* cb = reinterpret_cast<bf16*>(a.c16) + (int64_t)bt * a.c_bt_stride;
+        const bf16* pb = reinterpret_cast<const bf16*>(a.p16) + (int64_t)bt * a.c_bt_stride;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int rr = row0 + wr * 32 + crow(q, h);
+            if (rr >= rend) continue;
+            const int64_t at = (int64_t)rr * a.ldc + f;
+            float val = 0.f;
+            if (fv) {
+                if (a.epi == 1) {
+                    val = expf(acc[q] * a.scale - a.stat0[(int64_t)bt * a.stat_bt_stride + rr]);
+                } else {
+                    val = (float)pb[at] * (acc[q] - a.stat1[(int64_t)bt * a.stat_bt_stride + rr]) * a.scale;
+                }
+            }
+            cb[at] = to_bf16(val);
+        }
+        return;
+    }
+    if (f >= a.ncols) return;
+    float* cb = a.c + (int64_t)bt * a.c_bt_stride;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int rr = row0 + wr * 32 + crow(q, h);
+        if (rr < rend) {
+            float* dst = cb + (int64_t)rr * a.ldc + f;
+            *dst = a.accumulate ? *dst + acc[q] : acc[q];
+        }
+    }
+}
+
+// tn_kernel on bf16 operands
+template <class TX, class TY>
+__global__ __launch_bounds__(256) void tn16_kernel(const TnArgs a) {
+    __shared__ __align__(16) bf16 xs[64 * kLd16], ys[64 * kLd16];
+    const int bt = blockIdx.z;
+    const int grp = blockIdx.y / a.nseg, sg = blockIdx.y % a.nseg;
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
+    const int wm = wave / 2, wn = wave % 2;
+    const int ntn = (a.ncols + 63) / 64;
+    const int m0 = (blockIdx.x / ntn) * 64, n0 = (blockIdx.x % ntn) * 64;
+    const int gend = min((grp + 1) * a.group_rows, a.rows);
+    const int k0 = grp * a.group_rows + sg * a.seg_rows;
+    const int k1 = min(k0 + a.seg_rows, gend);
+    const TX* xb = reinterpret_cast<const TX*>(a.x) + (int64_t)bt * a.x_bt_stride;
+    const TY* yb = reinterpret_cast<const TY*>(a.y) + (int64_t)bt * a.y_bt_stride;
+    f32x16 acc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+    for (int k = k0; k < k1; k += 32) {
+        __syncthreads();
+        stage16_cols<TX>(xb, a.ldx, k, k1, m0, a.mrows, xs);
+        stage16_cols<TY>(yb, a.ldy, k, k1, n0, a.ncols, ys);
+        __syncthreads();
+        const bf16* xr = xs + (wm * 32 + col) * kLd16 + h * 8;
+        const bf16* yr = ys + (wn * 32 + col) * kLd16 + h * 8;
+        acc = mma16(xr, yr, acc);
+        acc = mma16(xr + 16, yr + 16, acc);
+    }
+    const int mm = m0 + wm * 32, nn = n0 + wn * 32;
+    if (mm >= a.mrows || nn + col >= a.ncols) return;
+    float* out = a.part + (((int64_t)bt * a.ngroups + grp) * a.nseg + sg) * a.mrows * a.ncols;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int r = mm + crow(q, h);
+        if (r < a.mrows) out[(int64_t)r * a.ncols + nn + col] = acc[q];
+    }
+}
+
 // out[o * ostride + e] (+)= sum_{b < nb} sum_{s < ns} part[((b * no + o) * ns + s) * E + e],
 // summed in that order (and then added to out when accumulating)
 __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ part, float* __restrict__ out, int nb,
@@ -469,6 +646,34 @@ hipError_t launch_nt(const NtArgs& a, const GradArgs& s, bool x_bf16, bool y_bf1
     if (x_bf16) return launch_nt_t<bf16, float>(a, s, stream);
     if (y_bf16) return launch_nt_t<float, bf16>(a, s, stream);
     return launch_nt_t<float, float>(a, s, stream);
+}
+
+hipError_t launch_nt16(NtArgs a, const GradArgs& s, bool x_bf16, bool y_bf16, hipStream_t stream) {
+    a.tiles_per_group = (a.group_rows + 63) / 64;
+    const dim3 grid((a.ncols + 63) / 64, a.ngroups * a.tiles_per_group, s.BH);
+    if (x_bf16 && y_bf16)
+        hipLaunchKernelGGL((nt16_kernel<bf16, bf16>), grid, dim3(256), 0, stream, a, s);
+    else if (x_bf16)
+        hipLaunchKernelGGL((nt16_kernel<bf16, float>), grid, dim3(256), 0, stream, a, s);
+    else if (y_bf16)
+        hipLaunchKernelGGL((nt16_kernel<float, bf16>), grid, dim3(256), 0, stream, a, s);
+    else
+        hipLaunchKernelGGL((nt16_kernel<float, float>), grid, dim3(256), 0, stream, a, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_tn16(const TnArgs& a, int BH, bool x_bf16, bool y_bf16, hipStream_t stream) {
+    const int blocks = ((a.mrows + 63) / 64) * ((a.ncols + 63) / 64);
+    const dim3 grid(blocks, a.ngroups * a.nseg, BH);
+    if (x_bf16 && y_bf16)
+        hipLaunchKernelGGL((tn16_kernel<bf16, bf16>), grid, dim3(256), 0, stream, a);
+    else if (x_bf16)
+        hipLaunchKernelGGL((tn16_kernel<bf16, float>), grid, dim3(256), 0, stream, a);
+    else if (y_bf16)
+        hipLaunchKernelGGL((tn16_kernel<float, bf16>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((tn16_kernel<float, float>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_tn(const TnArgs& a, int BH, bool y_bf16, hipStream_t stream) {
