@@ -10,6 +10,7 @@
 
 #include "../../include/rehyat.h"
 #include "kernels.hpp"
+#include "grad.hpp"
 
 using namespace rehyat;
 

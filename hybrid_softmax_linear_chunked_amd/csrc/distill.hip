@@ -8,7 +8,7 @@
 // 16-byte chunks, and every sum runs in a fixed order (per-lane sequence, xor butterfly in
 // the wave, waves in index order, segments in index order), so the result does not depend
 // on scheduling and repeated calls give identical bits.
-#include "kernels.hpp"
+#include "grad.hpp"
 
 namespace rehyat {
 

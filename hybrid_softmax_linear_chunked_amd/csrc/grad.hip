@@ -21,7 +21,7 @@
 // and each wave reads its MFMA operands from there (one 32x32 output block per wave);
 // and every sum over segments, frames, chunks or batches runs in a fixed order, so the
 // gradients are bitwise reproducible.
-#include "kernels.hpp"
+#include "grad.hpp"
 #include "common.hpp"
 
 namespace rehyat {

@@ -118,86 +118,5 @@ hipError_t launch_scan(const ScanArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_phi(const PhiArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_zero(float* p, int64_t count, hipStream_t stream);
-// Distillation gradients (grad.hip).  Shapes and the chunk schedule of one call.
-struct GradArgs {
-    int H, BH, N, n, D, Dphi, P, F, T, Tc, To, linear_only, nc, G;
-};
-
-// C[bt][i][f] (+)= sum_{d < K} X[bt][i][d] Y_m[f][d] (+ colbias[h][f]) (- Y_m[f][sub_col])
-// over row groups of group_rows rows (row tiles never cross a group); the matrix m of a
-// group: mode 0 the head of bt, mode 1 chunk = group, mode 2 the earliest chunk whose linear
-// region holds key frame = group (none: the rows get zeros, or are left as they are when
-// accumulating), mode 3 the slab bt itself.  accumulate: add to C instead of storing.
-struct NtArgs {
-    const void* x;
-    int64_t x_bt_stride;
-    int ldx;
-    const void* y;
-    int64_t y_mat_stride;
-    int ldy;
-    int nmat, mode, K, ncols, sub_col;
-    const float* colbias;
-    int64_t colbias_head_stride;
-    float* c;
-    int64_t c_bt_stride;
-    int ldc;
-    int rows, group_rows, ngroups, tiles_per_group;
-    int accumulate;
-    // bf16 product only (launch_nt16 with epi != 0): the result goes to c16 (bf16, same
-    // strides as c) as epi 1: P = exp(C * scale - stat0[row]), epi 2: dS = P (C - stat1[row])
-    // * scale with P read from p16 at the same position; columns [ncols, ncols_pad) get 0.
-    int epi, ncols_pad;
-    const float* stat0;
-    const float* stat1;
-    int64_t stat_bt_stride;
-    float scale;
-    const void* p16;
-    void* c16;
-};
-
-// part[bt][group][seg][m][n] = sum over the rows k of segment seg of group of X[k][m] Y[k][n]
-struct TnArgs {
-    const void* x;
-    int64_t x_bt_stride;
-    int ldx;
-    const void* y;
-    int64_t y_bt_stride;
-    int ldy;
-    int mrows, ncols;
-    float* part;
-    int rows, group_rows, ngroups, seg_rows, nseg;
-};
-
-hipError_t launch_nt(const NtArgs& a, const GradArgs& s, bool x_bf16, bool y_bf16, hipStream_t stream);
-hipError_t launch_tn(const TnArgs& a, int BH, bool y_bf16, hipStream_t stream);
-// The same products with operands rounded to bf16 and the bf16 matrix core (nt: modes 0, 1,
-// 3 without colbias / sub_col; tn: float X).
-hipError_t launch_nt16(NtArgs a, const GradArgs& s, bool x_bf16, bool y_bf16, hipStream_t stream);
-hipError_t launch_tn16(const TnArgs& a, int BH, bool x_bf16, bool y_bf16, hipStream_t stream);
-hipError_t launch_grad_reduce(const float* part, float* out, int nb, int no, int ns, int64_t E, hipStream_t stream,
-                              int64_t out_stride = -1, bool accumulate = false);
-hipError_t launch_grad_suffix(float* R, int BH, int nc, int64_t E, hipStream_t stream);
-hipError_t launch_grad_state_sz(const GradArgs& s, const float* Sp, const float* Zp, float* SZ, hipStream_t stream);
-hipError_t launch_grad_rows(const GradArgs& s, const float* o, const float* t, const float* dout, const float* lse,
-                            const float* z, float* AH, float* delta, float* lden, hipStream_t stream);
-// Softmax branch of the backward on one chunk window (Lq queries x Lk keys, rows of ldp
-// floats, slab stride bt_stride): S (raw q.k) becomes P = exp(S / sqrt(D) - log den_i) and
-// dP (G_i . v_j) becomes dS = P (dP - delta_i) / sqrt(D); columns Lk..ldp-1 become zero.
-hipError_t launch_softmax_bwd(float* S, float* dP, const float* lden, const float* delta, int64_t stat_bt_stride,
-                              int BH, int Lq, int Lk, int ldp, int64_t bt_stride, float scale, hipStream_t stream);
-// out[bt][c][r] = in[bt][r][c] as float for r < rows, c < cols; out rows hold ldo floats and
-// entries r in [rows, ldo) are set to zero.
-hipError_t launch_transpose(const void* in, bool in_bf16, int64_t in_bt_stride, int ldi, float* out,
-                            int64_t out_bt_stride, int ldo, int rows, int cols, int nbt, hipStream_t stream);
-hipError_t launch_grad_phi_fwd(const GradArgs& s, float* U, float* phi, hipStream_t stream);
-hipError_t launch_grad_phi_bwd(const GradArgs& s, float* U, const float* dphi, hipStream_t stream);
-hipError_t launch_grad_colsum(const float* X, int BH, int64_t rows, int cols, int seg_rows, float* part,
-                              hipStream_t stream);
-
-// Squared distance per slab between two float tensors [BH, len] (distill.hip): partial
-// holds BH * sqdist_segments(len) floats, loss BH floats; len must be a multiple of 4.
-int sqdist_segments(int64_t len);
-hipError_t launch_sqdist(const float* a, const float* b, int64_t len, int BH, float* partial, float* loss,
-                         hipStream_t stream);
 
 }  // namespace rehyat
