@@ -34,6 +34,8 @@ SHAPES = [
     (2, 2, 64, 8, 29, 3, 0, 64, 1, 0, rh.BF16),
     (1, 2, 32, 6, 40, 2, 1, 32, 2, 1, rh.BF16),
     (1, 1, 128, 4, 100, 5, 1, 96, 2, 0, rh.BF16),   # one chunk: student = teacher
+    (2, 1, 64, 9, 1, 2, 1, 32, 3, 0, rh.FP32),      # one-token frames
+    (1, 2, 64, 5, 70, 1, 0, 64, 2, 0, rh.BF16),     # Tc = 1, To = 0
 ]
 
 
