@@ -1097,38 +1097,10 @@ rehyat_status rehyat_backward(const rehyat_params* p, const void* q, const void*
         };
         if (bf) {
             // bf16 inputs: P = exp(Q_c K_w^T / sqrt(D) - log den) and dS = P (G_c V_w^T - delta)
-            // / sqrt(D) leave the two products' epilogues as bf16 (the forward's P precision)
-            auto nt_epi = [&](const void* x, bool xbf, const void* y, int epi, void* c16, const void* p16) {
-                NtArgs a;
-                std::memset(&a, 0, sizeof(a));
-                a.x = x;
-                a.x_bt_stride = ND;
-                a.ldx = s.D;
-                a.y = y;
-                a.y_mat_stride = ND;
-                a.ldy = s.D;
-                a.nmat = s.BH;
-                a.mode = 3;
-                a.K = s.D;
-                a.ncols = Lk;
-                a.sub_col = -1;
-                a.c_bt_stride = pbt;
-                a.ldc = L.ldp;
-                a.rows = Lq;
-                a.group_rows = Lq;
-                a.ngroups = 1;
-                a.epi = epi;
-                a.ncols_pad = std::min(L.ldp, (Lk + 7) / 8 * 8);
-                a.stat0 = F32(L.lden) + r0;
-                a.stat1 = F32(L.delta) + r0;
-                a.stat_bt_stride = N;
-                a.scale = scale;
-                a.p16 = p16;
-                a.c16 = c16;
-                return launch_nt16(a, s, xbf, true, stream);
-            };
-            GRAD_TRY(nt_epi(qc, true, kw, 1, w + L.sbuf, nullptr));
-            GRAD_TRY(nt_epi(dout + (size_t)r0 * s.D, false, vw, 2, w + L.dpbuf, w + L.sbuf));
+            // / sqrt(D) from one pass over the window, as bf16 (the forward's P precision)
+            GRAD_TRY(launch_sdp16(qc, kw, dout + (size_t)r0 * s.D, vw, ND, s.D, Lq, Lk,
+                                  std::min(L.ldp, (Lk + 7) / 8 * 8), F32(L.lden) + r0, F32(L.delta) + r0, N, scale,
+                                  w + L.sbuf, w + L.dpbuf, pbt, L.ldp, s.BH, stream));
         } else {
             // S = Q_c K_w^T and dP = G_c V_w^T, then P and dS in place
             GRAD_TRY(nt(qc, bf, ND, s.D, kw, bf, ND, s.D, s.D, Lk, F32(L.sbuf), pbt, L.ldp, 0));

@@ -292,8 +292,7 @@ __device__ inline f32x16 mma16(const bf16* a, const bf16* b, f32x16 c) {
                                                    *reinterpret_cast<const bf16x8*>(b), c, 0, 0, 0);
 }
 
-// nt_kernel on bf16 operands (modes 0, 1 and 3; no column bias or subtraction), with the
-// softmax-backward epilogues of NtArgs::epi
+// nt_kernel on bf16 operands (modes 0, 1 and 3; no column bias or subtraction)
 template <class TX, class TY>
 __global__ __launch_bounds__(256) void nt16_kernel(const NtArgs a, const GradArgs s) {
     __shared__ __align__(16) bf16 xs[64 * kLd16], ys[64 * kLd16];
@@ -322,28 +321,6 @@ __global__ __launch_bounds__(256) void nt16_kernel(const NtArgs a, const GradArg
         acc = mma16(xr + 16, yr + 16, acc);
     }
     const int f = c0 + wc * 32 + col;
-    if (a.epi != 0) {
-        if (f >= a.ncols_pad) return;
-        const bool fv = f < a.ncols;
-        bf16* cb = reinterpret_cast<bf16*>(a.c16) + (int64_t)bt * a.c_bt_stride;
-        const bf16* pb = reinterpret_cast<const bf16*>(a.p16) + (int64_t)bt * a.c_bt_stride;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int rr = row0 + wr * 32 + crow(q, h);
-            if (rr >= rend) continue;
-            const int64_t at = (int64_t)rr * a.ldc + f;
-            float val = 0.f;
-            if (fv) {
-                if (a.epi == 1) {
-                    val = expf(acc[q] * a.scale - a.stat0[(int64_t)bt * a.stat_bt_stride + rr]);
-                } else {
-                    val = (float)pb[at] * (acc[q] - a.stat1[(int64_t)bt * a.stat_bt_stride + rr]) * a.scale;
-                }
-            }
-            cb[at] = to_bf16(val);
-        }
-        return;
-    }
     if (f >= a.ncols) return;
     float* cb = a.c + (int64_t)bt * a.c_bt_stride;
 #pragma unroll
@@ -353,6 +330,61 @@ __global__ __launch_bounds__(256) void nt16_kernel(const NtArgs a, const GradArg
             float* dst = cb + (int64_t)rr * a.ldc + f;
             *dst = a.accumulate ? *dst + acc[q] : acc[q];
         }
+    }
+}
+
+// The two score-shaped products of a chunk window in one pass (bf16 inputs): per 64 x 64
+// tile of (query, key), S = Q K^T and dP = G V^T accumulate side by side over D, then
+// P = exp(S / sqrt(D) - log den_i) and dS = P (dP - delta_i) / sqrt(D) are written as bf16
+// (columns [Lk, ncols_pad) as zeros).  Q, K, V bf16 [rows][D]; G float [rows][D].
+__global__ __launch_bounds__(256) void sdp16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                    const float* __restrict__ g, const bf16* __restrict__ v,
+                                                    int64_t bt_stride, int D, int Lq, int Lk, int ncols_pad,
+                                                    const float* __restrict__ lden, const float* __restrict__ delta,
+                                                    int64_t stat_bt_stride, float scale, bf16* __restrict__ P,
+                                                    bf16* __restrict__ dS, int64_t p_bt_stride, int ldp) {
+    __shared__ __align__(16) bf16 qs[64 * kLd16], ks[64 * kLd16], gs[64 * kLd16], vs[64 * kLd16];
+    const int bt = blockIdx.z, row0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
+    const int wr = wave / 2, wc = wave % 2;
+    const bf16* qb = q + (int64_t)bt * bt_stride;
+    const bf16* kb = k + (int64_t)bt * bt_stride;
+    const float* gb = g + (int64_t)bt * bt_stride;
+    const bf16* vb = v + (int64_t)bt * bt_stride;
+    f32x16 sa, pa;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sa[r] = pa[r] = 0.f;
+    for (int d0 = 0; d0 < D; d0 += 32) {
+        __syncthreads();
+        stage16_rows<bf16>(qb, D, row0, Lq, d0, D, qs);
+        stage16_rows<bf16>(kb, D, c0, Lk, d0, D, ks);
+        stage16_rows<float>(gb, D, row0, Lq, d0, D, gs);
+        stage16_rows<bf16>(vb, D, c0, Lk, d0, D, vs);
+        __syncthreads();
+        const int ao = (wr * 32 + col) * kLd16 + h * 8, bo = (wc * 32 + col) * kLd16 + h * 8;
+        sa = mma16(qs + ao, ks + bo, sa);
+        sa = mma16(qs + ao + 16, ks + bo + 16, sa);
+        pa = mma16(gs + ao, vs + bo, pa);
+        pa = mma16(gs + ao + 16, vs + bo + 16, pa);
+    }
+    const int f = c0 + wc * 32 + col;
+    if (f >= ncols_pad) return;
+    const bool fv = f < Lk;
+    bf16* pb = P + (int64_t)bt * p_bt_stride;
+    bf16* db = dS + (int64_t)bt * p_bt_stride;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int rr = row0 + wr * 32 + crow(r, h);
+        if (rr >= Lq) continue;
+        float pr = 0.f, ds = 0.f;
+        if (fv) {
+            pr = expf(sa[r] * scale - lden[(int64_t)bt * stat_bt_stride + rr]);
+            // dS from the bf16-rounded P, as the products that consume P see it
+            const float prb = (float)to_bf16(pr);
+            ds = prb * (pa[r] - delta[(int64_t)bt * stat_bt_stride + rr]) * scale;
+        }
+        pb[(int64_t)rr * ldp + f] = to_bf16(pr);
+        db[(int64_t)rr * ldp + f] = to_bf16(ds);
     }
 }
 
@@ -673,6 +705,17 @@ hipError_t launch_tn16(const TnArgs& a, int BH, bool x_bf16, bool y_bf16, hipStr
         hipLaunchKernelGGL((tn16_kernel<float, bf16>), grid, dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL((tn16_kernel<float, float>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_sdp16(const void* q, const void* k, const float* g, const void* v, int64_t bt_stride, int D,
+                        int Lq, int Lk, int ncols_pad, const float* lden, const float* delta, int64_t stat_bt_stride,
+                        float scale, void* P, void* dS, int64_t p_bt_stride, int ldp, int BH, hipStream_t stream) {
+    const dim3 grid((unsigned)((ncols_pad + 63) / 64), (unsigned)((Lq + 63) / 64), BH);
+    hipLaunchKernelGGL(sdp16_kernel, grid, dim3(256), 0, stream, reinterpret_cast<const bf16*>(q),
+                       reinterpret_cast<const bf16*>(k), g, reinterpret_cast<const bf16*>(v), bt_stride, D, Lq, Lk,
+                       ncols_pad, lden, delta, stat_bt_stride, scale, reinterpret_cast<bf16*>(P),
+                       reinterpret_cast<bf16*>(dS), p_bt_stride, ldp);
     return hipGetLastError();
 }
 

@@ -32,16 +32,6 @@ struct NtArgs {
     int ldc;
     int rows, group_rows, ngroups, tiles_per_group;
     int accumulate;
-    // bf16 product only (launch_nt16 with epi != 0): the result goes to c16 (bf16, same
-    // strides as c) as epi 1: P = exp(C * scale - stat0[row]), epi 2: dS = P (C - stat1[row])
-    // * scale with P read from p16 at the same position; columns [ncols, ncols_pad) get 0.
-    int epi, ncols_pad;
-    const float* stat0;
-    const float* stat1;
-    int64_t stat_bt_stride;
-    float scale;
-    const void* p16;
-    void* c16;
 };
 
 // part[bt][group][seg][m][n] = sum over the rows k of segment seg of group of X[k][m] Y[k][n]
@@ -63,6 +53,12 @@ hipError_t launch_tn(const TnArgs& a, int BH, bool y_bf16, hipStream_t stream);
 // 3 without colbias / sub_col; tn: float X).
 hipError_t launch_nt16(NtArgs a, const GradArgs& s, bool x_bf16, bool y_bf16, hipStream_t stream);
 hipError_t launch_tn16(const TnArgs& a, int BH, bool x_bf16, bool y_bf16, hipStream_t stream);
+// Scores and dP of a chunk window in one pass (bf16 q, k, v; float g, all [rows][D] with slab
+// stride bt_stride, pointers at the window / chunk start): P and dS written as bf16 rows of
+// ldp (slab stride p_bt_stride), columns [Lk, ncols_pad) zero.
+hipError_t launch_sdp16(const void* q, const void* k, const float* g, const void* v, int64_t bt_stride, int D,
+                        int Lq, int Lk, int ncols_pad, const float* lden, const float* delta, int64_t stat_bt_stride,
+                        float scale, void* P, void* dS, int64_t p_bt_stride, int ldp, int BH, hipStream_t stream);
 hipError_t launch_grad_reduce(const float* part, float* out, int nb, int no, int ns, int64_t E, hipStream_t stream,
                               int64_t out_stride = -1, bool accumulate = false);
 hipError_t launch_grad_suffix(float* R, int BH, int nc, int64_t E, hipStream_t stream);
