@@ -23,6 +23,7 @@
 // gradients are bitwise reproducible.
 #include "grad.hpp"
 #include "common.hpp"
+#include "dma.hpp"
 
 namespace rehyat {
 
@@ -220,7 +221,8 @@ __global__ __launch_bounds__(256) void tn_kernel(const TnArgs a) {
 // bf16 matrix-core forms of the two products, for the softmax branch of the backward with
 // bf16 inputs: operands rounded to bf16 (ties to even) while staged, products accumulated
 // in fp32 on v_mfma_f32_32x32x16_bf16.  LDS rows hold 32 contraction elements plus 8 of
-// padding; a lane reads its 8 consecutive contraction slots with one 16-byte read.
+// padding; a lane reads its 8 consecutive contraction slots with one 16-byte read (the
+// segment product reads transposed slices, below).
 constexpr int kLd16 = 40;
 
 __device__ inline bf16 to_bf16(float x) { return (bf16)x; }
@@ -252,37 +254,6 @@ __device__ inline void stage16_rows(const T* src, int64_t ld, int r0, int rlim, 
             v[2] = to_bf16(x.z);
             v[3] = to_bf16(x.w);
             *reinterpret_cast<bf16x4*>(dst + r * kLd16 + c) = v;
-        }
-    }
-}
-
-// contraction rows [k0, k0 + 32) x columns [c0, c0 + 64) of a row-major source, stored
-// transposed: dst[c][k] (bf16)
-template <class T>
-__device__ inline void stage16_cols(const T* src, int64_t ld, int k0, int klim, int c0, int clim, bf16* dst) {
-    const int t = threadIdx.x;
-    if constexpr (sizeof(T) == 2) {
-        const int k = t / 8, c = (t % 8) * 8;
-        bf16x8 v;
-        if (k0 + k < klim && c0 + c < clim) {
-            v = *reinterpret_cast<const bf16x8*>(src + (int64_t)(k0 + k) * ld + c0 + c);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = to_bf16(0.f);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dst[(c + e) * kLd16 + k] = v[e];
-    } else {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int q = t + 256 * u, k = q / 16, c = (q % 16) * 4;
-            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (k0 + k < klim && c0 + c < clim)
-                x = *reinterpret_cast<const float4*>(src + (int64_t)(k0 + k) * ld + c0 + c);
-            dst[(c + 0) * kLd16 + k] = to_bf16(x.x);
-            dst[(c + 1) * kLd16 + k] = to_bf16(x.y);
-            dst[(c + 2) * kLd16 + k] = to_bf16(x.z);
-            dst[(c + 3) * kLd16 + k] = to_bf16(x.w);
         }
     }
 }
@@ -388,10 +359,47 @@ __global__ __launch_bounds__(256) void sdp16_kernel(const bf16* __restrict__ q, 
     }
 }
 
-// tn_kernel on bf16 operands
+// tn_kernel on bf16 operands.  Slices of 32 contraction rows x 64 columns are staged row
+// major (rows of kTrLd bf16), and each lane reads its 8 contraction slots of one column with
+// gfx950's transposing LDS read, in the layout the forward kernel uses for its V^T operand
+// (DmaTiles<64, 4>::vfrag: column db*32 + lane%32, slot order depending only on the lane
+// half, identical for both operands, so the products pair the same rows).
+using TrTile = DmaTiles<64, 4>;
+constexpr int kTrLd = TrTile::VLD;  // 96
+
+template <class T>
+__device__ inline void stage_tr(const T* src, int64_t ld, int k0, int klim, int c0, int clim, bf16* dst) {
+    const int t = threadIdx.x;
+    if constexpr (sizeof(T) == 2) {
+        const int k = t / 8, c = (t % 8) * 8;  // 32 rows x 8 chunks of 8
+        bf16x8 v;
+        if (k0 + k < klim && c0 + c < clim) {
+            v = *reinterpret_cast<const bf16x8*>(src + (int64_t)(k0 + k) * ld + c0 + c);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = to_bf16(0.f);
+        }
+        *reinterpret_cast<bf16x8*>(dst + k * kTrLd + c) = v;
+    } else {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int q = t + 256 * u, k = q / 16, c = (q % 16) * 4;  // 32 rows x 16 chunks of 4
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (k0 + k < klim && c0 + c < clim)
+                x = *reinterpret_cast<const float4*>(src + (int64_t)(k0 + k) * ld + c0 + c);
+            bf16x4 v;
+            v[0] = to_bf16(x.x);
+            v[1] = to_bf16(x.y);
+            v[2] = to_bf16(x.z);
+            v[3] = to_bf16(x.w);
+            *reinterpret_cast<bf16x4*>(dst + k * kTrLd + c) = v;
+        }
+    }
+}
+
 template <class TX, class TY>
 __global__ __launch_bounds__(256) void tn16_kernel(const TnArgs a) {
-    __shared__ __align__(16) bf16 xs[64 * kLd16], ys[64 * kLd16];
+    __shared__ __align__(16) bf16 xs[32 * kTrLd], ys[32 * kTrLd];
     const int bt = blockIdx.z;
     const int grp = blockIdx.y / a.nseg, sg = blockIdx.y % a.nseg;
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
@@ -403,18 +411,19 @@ __global__ __launch_bounds__(256) void tn16_kernel(const TnArgs a) {
     const int k1 = min(k0 + a.seg_rows, gend);
     const TX* xb = reinterpret_cast<const TX*>(a.x) + (int64_t)bt * a.x_bt_stride;
     const TY* yb = reinterpret_cast<const TY*>(a.y) + (int64_t)bt * a.y_bt_stride;
+    const int vl = TrTile::vlane(lane);
     f32x16 acc;
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = 0.f;
     for (int k = k0; k < k1; k += 32) {
         __syncthreads();
-        stage16_cols<TX>(xb, a.ldx, k, k1, m0, a.mrows, xs);
-        stage16_cols<TY>(yb, a.ldy, k, k1, n0, a.ncols, ys);
+        stage_tr<TX>(xb, a.ldx, k, k1, m0, a.mrows, xs);
+        stage_tr<TY>(yb, a.ldy, k, k1, n0, a.ncols, ys);
         __syncthreads();
-        const bf16* xr = xs + (wm * 32 + col) * kLd16 + h * 8;
-        const bf16* yr = ys + (wn * 32 + col) * kLd16 + h * 8;
-        acc = mma16(xr, yr, acc);
-        acc = mma16(xr + 16, yr + 16, acc);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TrTile::vfrag(xs, vl, wm, 0, t),
+                                                          TrTile::vfrag(ys, vl, wn, 0, t), acc, 0, 0, 0);
     }
     const int mm = m0 + wm * 32, nn = n0 + wn * 32;
     if (mm >= a.mrows || nn + col >= a.ncols) return;
