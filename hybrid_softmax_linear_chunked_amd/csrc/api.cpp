@@ -652,7 +652,7 @@ constexpr int kSoftSegRows = 1024;    // query rows per dK / dV partial of a win
 
 struct GradLayout {
     size_t stu, tea, lse, z, sqd, fwd_s, fwd_t, ah, u, phi, dphi, sz, rp, r, wp, bp;
-    size_t delta, lden, wt, rt, sbuf, dpbuf, kt, pp, total;
+    size_t delta, lden, wt, rt, sbuf, dpbuf, kt, pp, g16, total;
     int nseg_sq, nseg_w, nseg_b, lq_max, lk_max, ldp, nseg_s;
 };
 
@@ -734,6 +734,7 @@ GradLayout grad_layout(const rehyat_params* p, bool backward) {
     L.dpbuf = take(bw * BH * L.lq_max * L.ldp * f4);
     L.kt = take(bw * BH * s.D * L.ldp * f4);
     L.pp = take(bw * BH * L.nseg_s * (size_t)L.lk_max * s.D * f4);
+    L.g16 = take(backward && p->in_dtype == REHYAT_BF16 ? BH * N * s.D * 2 : 0);
     L.total = off;
     return L;
 }
@@ -1058,6 +1059,8 @@ rehyat_status rehyat_backward(const rehyat_params* p, const void* q, const void*
         if (st != REHYAT_OK) return st;
     }
 
+    // bf16 inputs: the upstream gradient rounded to bf16 once (the products' operand precision)
+    if (bf) GRAD_TRY(launch_to_bf16(dout, w + L.g16, (int64_t)s.BH * ND, stream));
     // softmax branch, one chunk window at a time (blog 2.2.1 window, scores q.k / sqrt(D))
     const float scale = (float)(1.0 / std::sqrt((double)s.D));
     const int64_t pbt = (int64_t)L.lq_max * L.ldp;
@@ -1098,7 +1101,7 @@ rehyat_status rehyat_backward(const rehyat_params* p, const void* q, const void*
         if (bf) {
             // bf16 inputs: P = exp(Q_c K_w^T / sqrt(D) - log den) and dS = P (G_c V_w^T - delta)
             // / sqrt(D) from one pass over the window, as bf16 (the forward's P precision)
-            GRAD_TRY(launch_sdp16(qc, kw, dout + (size_t)r0 * s.D, vw, ND, s.D, Lq, Lk,
+            GRAD_TRY(launch_sdp16(qc, kw, w + L.g16 + (size_t)r0 * s.D * 2, vw, ND, s.D, Lq, Lk,
                                   std::min(L.ldp, (Lk + 7) / 8 * 8), F32(L.lden) + r0, F32(L.delta) + r0, N, scale,
                                   w + L.sbuf, w + L.dpbuf, pbt, L.ldp, s.BH, stream));
         } else {
@@ -1133,7 +1136,8 @@ rehyat_status rehyat_backward(const rehyat_params* p, const void* q, const void*
                                        ND, true);
             return e;
         };
-        GRAD_TRY(tn_add(w + L.sbuf, dout + (size_t)r0 * s.D, false, dv));
+        if (bf) GRAD_TRY(tn_add(w + L.sbuf, w + L.g16 + (size_t)r0 * s.D * 2, true, dv));
+        else GRAD_TRY(tn_add(w + L.sbuf, dout + (size_t)r0 * s.D, false, dv));
         GRAD_TRY(tn_add(w + L.dpbuf, qc, bf, dk));
         // dQ_c += dS K_w with K_w transposed (zero past Lk)
         GRAD_TRY(launch_transpose(kw, bf, ND, s.D, F32(L.kt), (int64_t)s.D * L.ldp, L.ldp, Lk, s.D, s.BH, stream));

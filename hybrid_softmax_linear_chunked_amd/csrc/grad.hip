@@ -307,9 +307,9 @@ __global__ __launch_bounds__(256) void nt16_kernel(const NtArgs a, const GradArg
 // The two score-shaped products of a chunk window in one pass (bf16 inputs): per 64 x 64
 // tile of (query, key), S = Q K^T and dP = G V^T accumulate side by side over D, then
 // P = exp(S / sqrt(D) - log den_i) and dS = P (dP - delta_i) / sqrt(D) are written as bf16
-// (columns [Lk, ncols_pad) as zeros).  Q, K, V bf16 [rows][D]; G float [rows][D].
+// (columns [Lk, ncols_pad) as zeros).  Q, K, V, G bf16 [rows][D].
 __global__ __launch_bounds__(256) void sdp16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                                    const float* __restrict__ g, const bf16* __restrict__ v,
+                                                    const bf16* __restrict__ g, const bf16* __restrict__ v,
                                                     int64_t bt_stride, int D, int Lq, int Lk, int ncols_pad,
                                                     const float* __restrict__ lden, const float* __restrict__ delta,
                                                     int64_t stat_bt_stride, float scale, bf16* __restrict__ P,
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(256) void sdp16_kernel(const bf16* __restrict__ q, 
     const int wr = wave / 2, wc = wave % 2;
     const bf16* qb = q + (int64_t)bt * bt_stride;
     const bf16* kb = k + (int64_t)bt * bt_stride;
-    const float* gb = g + (int64_t)bt * bt_stride;
+    const bf16* gb = g + (int64_t)bt * bt_stride;
     const bf16* vb = v + (int64_t)bt * bt_stride;
     f32x16 sa, pa;
 #pragma unroll
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(256) void sdp16_kernel(const bf16* __restrict__ q, 
         __syncthreads();
         stage16_rows<bf16>(qb, D, row0, Lq, d0, D, qs);
         stage16_rows<bf16>(kb, D, c0, Lk, d0, D, ks);
-        stage16_rows<float>(gb, D, row0, Lq, d0, D, gs);
+        stage16_rows<bf16>(gb, D, row0, Lq, d0, D, gs);
         stage16_rows<bf16>(vb, D, c0, Lk, d0, D, vs);
         __syncthreads();
         const int ao = (wr * 32 + col) * kLd16 + h * 8, bo = (wc * 32 + col) * kLd16 + h * 8;
@@ -717,12 +717,36 @@ hipError_t launch_tn16(const TnArgs& a, int BH, bool x_bf16, bool y_bf16, hipStr
     return hipGetLastError();
 }
 
-hipError_t launch_sdp16(const void* q, const void* k, const float* g, const void* v, int64_t bt_stride, int D,
+__global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ in, bf16* __restrict__ out,
+                                                      int64_t n4) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+        const float4 x = reinterpret_cast<const float4*>(in)[i];
+        bf16x4 v;
+        v[0] = to_bf16(x.x);
+        v[1] = to_bf16(x.y);
+        v[2] = to_bf16(x.z);
+        v[3] = to_bf16(x.w);
+        reinterpret_cast<bf16x4*>(out)[i] = v;
+    }
+}
+
+hipError_t launch_to_bf16(const float* in, void* out, int64_t n, hipStream_t stream) {
+    const int64_t n4 = n / 4;
+    int64_t blocks = (n4 + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) return hipSuccess;
+    hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in, reinterpret_cast<bf16*>(out),
+                       n4);
+    return hipGetLastError();
+}
+
+hipError_t launch_sdp16(const void* q, const void* k, const void* g, const void* v, int64_t bt_stride, int D,
                         int Lq, int Lk, int ncols_pad, const float* lden, const float* delta, int64_t stat_bt_stride,
                         float scale, void* P, void* dS, int64_t p_bt_stride, int ldp, int BH, hipStream_t stream) {
     const dim3 grid((unsigned)((ncols_pad + 63) / 64), (unsigned)((Lq + 63) / 64), BH);
     hipLaunchKernelGGL(sdp16_kernel, grid, dim3(256), 0, stream, reinterpret_cast<const bf16*>(q),
-                       reinterpret_cast<const bf16*>(k), g, reinterpret_cast<const bf16*>(v), bt_stride, D, Lq, Lk,
+                       reinterpret_cast<const bf16*>(k), reinterpret_cast<const bf16*>(g),
+                       reinterpret_cast<const bf16*>(v), bt_stride, D, Lq, Lk,
                        ncols_pad, lden, delta, stat_bt_stride, scale, reinterpret_cast<bf16*>(P),
                        reinterpret_cast<bf16*>(dS), p_bt_stride, ldp);
     return hipGetLastError();
