@@ -89,48 +89,35 @@ def stored_traffic():
         return None
 
 
-def cpu_baseline(w, x, out_gpu, budget_s=20.0):
-    """The fp64 oracle (as it stands) on a bounded sample of the same workload: head 0 with
-    its fp64 states built in full, plus a seeded sample of query rows spread over all chunks;
-    extrapolated linearly to every head and row.  Also returns the parity of the GPU output
-    on the sampled rows."""
+def cpu_baseline(w, x, out_gpu, budget_s=12.0):
+    """The fp64 oracle (as it stands) on a bounded sample of the same workload: whole heads,
+    every query row with the fp64 states built in full, head after head until about
+    budget_s of wall time has passed (at least one head); extrapolated linearly to every
+    head.  Also returns the parity of the GPU output on the heads computed."""
     import numpy as np
     import oracle
     p1 = oracle.Params(1, 1, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P)
-    h0 = {key: x[key][:, :1] if key in ("q", "k", "v") else x[key][:1] for key in ("q", "k", "v", "wq", "wk")}
-    h0 = {key: val.astype(np.float64) for key, val in h0.items()}
     N = w.N
-    rng = np.random.default_rng(123)
-    t0 = time.perf_counter()
-    oracle.parallel_rows(p1, h0["q"], h0["k"], h0["v"], h0["wq"], h0["wk"], np.array([0]))
-    t_state = time.perf_counter() - t0
-    R = 256
-    rows = np.sort(rng.choice(N, size=R, replace=False))
-    t0 = time.perf_counter()
-    ref, _ = oracle.parallel_rows(p1, h0["q"], h0["k"], h0["v"], h0["wq"], h0["wk"], rows)
-    t_rows = time.perf_counter() - t0
-    per_row = max(t_rows - t_state, 1e-9) / R
-    # grow the sample while the CPU budget allows
-    extra = int(min(max((budget_s - 2 * t_state - t_rows) / per_row, 0), 8192))
-    if extra >= 256:
-        more = np.sort(rng.choice(np.setdiff1d(np.arange(N), rows), size=extra, replace=False))
+    rows = np.arange(N)
+    done, spent, err = 0, 0.0, 0.0
+    while done < w.H and (done == 0 or spent < budget_s):
+        h = done
+        sl = {key: (x[key][:, h:h + 1] if key in ("q", "k", "v") else x[key][h:h + 1]).astype(np.float64)
+              for key in ("q", "k", "v", "wq", "wk")}
         t0 = time.perf_counter()
-        ref2, _ = oracle.parallel_rows(p1, h0["q"], h0["k"], h0["v"], h0["wq"], h0["wk"], more)
-        t_more = time.perf_counter() - t0
-        per_row = max(t_more - t_state, 1e-9) / extra
-        rows = np.concatenate([rows, more])
-        ref = np.concatenate([ref, ref2])
-        order = np.argsort(rows)
-        rows, ref = rows[order], ref[order]
-    full_s = w.B * w.H * (t_state + N * per_row)
+        ref, _ = oracle.parallel_rows(p1, sl["q"], sl["k"], sl["v"], sl["wq"], sl["wk"], rows)
+        spent += time.perf_counter() - t0
+        g = out_gpu[0, h].float().cpu().numpy()
+        err = max(err, float(np.abs(g - ref).max() / np.abs(ref).max()))
+        done += 1
+    per_head = spent / done
+    full_s = w.B * w.H * per_head
     cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
-    g = out_gpu[0, 0].float().cpu().numpy()[rows]
-    err = float(np.abs(g - ref).max() / np.abs(ref).max())
     return dict(value=round(w.B * N / full_s, 3), unit="tokens/s", cores=cores, kind="oracle",
-                sample=(f"head 0 of {w.H}: fp64 states over all {w.T} frames in full "
-                        f"({t_state:.2f} s) + {len(rows)} of {N} query rows ({per_row * 1e3:.2f} ms/row); "
-                        f"extrapolated linearly to {w.H} heads x {N} rows = {full_s:.1f} s per layer")), \
-        dict(max_rel_err=err, rows=int(len(rows)), head=0, tol=2e-2)
+                sample=(f"{done} of {w.H} heads (batch 0) in full: fp64 states over all {w.T} frames and all "
+                        f"{N} query rows, {spent:.1f} s ({per_head:.2f} s per head); extrapolated linearly "
+                        f"to {w.B * w.H} heads = {full_s:.1f} s per layer")), \
+        dict(max_rel_err=err, rows=int(N * done), heads=done, tol=2e-2)
 
 
 def main():
