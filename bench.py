@@ -133,7 +133,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
