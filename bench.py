@@ -369,8 +369,12 @@ def backward_leg(rh, torch, p, d, w, fwd_ms, reps=2):
     bms = e0.elapsed_time(e1) / reps
     fl = backward_flops(w.B, w.H, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P)
     st = max(bms - fwd_ms, 1e-6)
+    tf = fl / (st * 1e-3) / 1e12
     res = {"ms": round(bms, 3), "backward_stages_ms": round(st, 3), "backward_flops": fl,
-           "backward_tflops": round(fl / (st * 1e-3) / 1e12, 2), "peak_fp32_matrix_tflops": 157.3,
+           "backward_tflops": round(tf, 2), "peak_tflops": PEAK_BF16_TFLOPS,
+           "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+           "bound": "mfma: softmax-branch products on the bf16 matrix core (bf16 inputs), linear branch "
+                    "on the fp32 matrix core (157.3 TFLOP/s peak)",
            "workspace_bytes": int(ws.numel())}
     del ws, dout
     return res
