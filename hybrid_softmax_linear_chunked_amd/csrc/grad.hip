@@ -307,14 +307,19 @@ __global__ __launch_bounds__(256) void nt16_kernel(const NtArgs a, const GradArg
 // The two score-shaped products of a chunk window in one pass (bf16 inputs): per 64 x 64
 // tile of (query, key), S = Q K^T and dP = G V^T accumulate side by side over D, then
 // P = exp(S / sqrt(D) - log den_i) and dS = P (dP - delta_i) / sqrt(D) are written as bf16
-// (columns [Lk, ncols_pad) as zeros).  Q, K, V, G bf16 [rows][D].
+// (columns [Lk, ncols_pad) as zeros).  Q, K, V, G bf16 [rows][D].  The two output tiles go
+// back through LDS so that every global store is a 16-byte run of a row.
+constexpr int kSdpOutLd = 72;  // bf16 per row of a staged 64 x 64 output tile
+
 __global__ __launch_bounds__(256) void sdp16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                     const bf16* __restrict__ g, const bf16* __restrict__ v,
                                                     int64_t bt_stride, int D, int Lq, int Lk, int ncols_pad,
                                                     const float* __restrict__ lden, const float* __restrict__ delta,
                                                     int64_t stat_bt_stride, float scale, bf16* __restrict__ P,
                                                     bf16* __restrict__ dS, int64_t p_bt_stride, int ldp) {
-    __shared__ __align__(16) bf16 qs[64 * kLd16], ks[64 * kLd16], gs[64 * kLd16], vs[64 * kLd16];
+    constexpr int TILE = 64 * kLd16, IN = 4 * TILE, OUT = 2 * 64 * kSdpOutLd;
+    __shared__ __align__(16) bf16 lds[IN > OUT ? IN : OUT];
+    bf16 *qs = lds, *ks = lds + TILE, *gs = lds + 2 * TILE, *vs = lds + 3 * TILE;
     const int bt = blockIdx.z, row0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
     const int wr = wave / 2, wc = wave % 2;
@@ -338,24 +343,35 @@ __global__ __launch_bounds__(256) void sdp16_kernel(const bf16* __restrict__ q, 
         pa = mma16(gs + ao, vs + bo, pa);
         pa = mma16(gs + ao + 16, vs + bo + 16, pa);
     }
-    const int f = c0 + wc * 32 + col;
-    if (f >= ncols_pad) return;
+    __syncthreads();  // every wave is done with the operand tiles: reuse the LDS for the outputs
+    bf16 *po = lds, *dso = lds + 64 * kSdpOutLd;
+    const int fl = wc * 32 + col, f = c0 + fl;
     const bool fv = f < Lk;
-    bf16* pb = P + (int64_t)bt * p_bt_stride;
-    bf16* db = dS + (int64_t)bt * p_bt_stride;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int rr = row0 + wr * 32 + crow(r, h);
-        if (rr >= Lq) continue;
+        const int rl = wr * 32 + crow(r, h), rr = row0 + rl;
         float pr = 0.f, ds = 0.f;
-        if (fv) {
+        if (fv && rr < Lq) {
             pr = expf(sa[r] * scale - lden[(int64_t)bt * stat_bt_stride + rr]);
             // dS from the bf16-rounded P, as the products that consume P see it
             const float prb = (float)to_bf16(pr);
             ds = prb * (pa[r] - delta[(int64_t)bt * stat_bt_stride + rr]) * scale;
         }
-        pb[(int64_t)rr * ldp + f] = to_bf16(pr);
-        db[(int64_t)rr * ldp + f] = to_bf16(ds);
+        po[rl * kSdpOutLd + fl] = to_bf16(pr);
+        dso[rl * kSdpOutLd + fl] = to_bf16(ds);
+    }
+    __syncthreads();
+    bf16* pb = P + (int64_t)bt * p_bt_stride;
+    bf16* db = dS + (int64_t)bt * p_bt_stride;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int qd = threadIdx.x + 256 * u, rl = qd / 8, cl = (qd % 8) * 8;  // 64 rows x 8 chunks
+        // ncols_pad is a multiple of 8, so a chunk is wholly inside or wholly outside
+        if (row0 + rl < Lq && c0 + cl < ncols_pad) {
+            const int64_t o = (int64_t)(row0 + rl) * ldp + c0 + cl;
+            *reinterpret_cast<bf16x8*>(pb + o) = *reinterpret_cast<const bf16x8*>(po + rl * kSdpOutLd + cl);
+            *reinterpret_cast<bf16x8*>(db + o) = *reinterpret_cast<const bf16x8*>(dso + rl * kSdpOutLd + cl);
+        }
     }
 }
 
@@ -746,9 +762,9 @@ hipError_t launch_sdp16(const void* q, const void* k, const void* g, const void*
     const dim3 grid((unsigned)((ncols_pad + 63) / 64), (unsigned)((Lq + 63) / 64), BH);
     hipLaunchKernelGGL(sdp16_kernel, grid, dim3(256), 0, stream, reinterpret_cast<const bf16*>(q),
                        reinterpret_cast<const bf16*>(k), reinterpret_cast<const bf16*>(g),
-                       reinterpret_cast<const bf16*>(v), bt_stride, D, Lq, Lk,
-                       ncols_pad, lden, delta, stat_bt_stride, scale, reinterpret_cast<bf16*>(P),
-                       reinterpret_cast<bf16*>(dS), p_bt_stride, ldp);
+                       reinterpret_cast<const bf16*>(v), bt_stride, D, Lq, Lk, ncols_pad, lden, delta,
+                       stat_bt_stride, scale, reinterpret_cast<bf16*>(P), reinterpret_cast<bf16*>(dS), p_bt_stride,
+                       ldp);
     return hipGetLastError();
 }
 
