@@ -311,7 +311,7 @@ __global__ __launch_bounds__(256) void nt16_kernel(const NtArgs a, const GradArg
 // back through LDS so that every global store is a 16-byte run of a row.
 constexpr int kSdpOutLd = 72;  // bf16 per row of a staged 64 x 64 output tile
 
-__global__ __launch_bounds__(256) void sdp16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void sdp16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                     const bf16* __restrict__ g, const bf16* __restrict__ v,
                                                     int64_t bt_stride, int D, int Lq, int Lk, int ncols_pad,
                                                     const float* __restrict__ lden, const float* __restrict__ delta,
