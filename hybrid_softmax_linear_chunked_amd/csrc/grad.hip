@@ -21,6 +21,8 @@
 // and each wave reads its MFMA operands from there (one 32x32 output block per wave);
 // and every sum over segments, frames, chunks or batches runs in a fixed order, so the
 // gradients are bitwise reproducible.
+#include <type_traits>
+
 #include "grad.hpp"
 #include "common.hpp"
 #include "dma.hpp"
@@ -227,35 +229,60 @@ constexpr int kLd16 = 40;
 
 __device__ inline bf16 to_bf16(float x) { return (bf16)x; }
 
-// rows [r0, r0 + 64) x contraction [c0, c0 + 32) of a row-major source -> dst[r][c] (bf16)
-template <class T>
-__device__ inline void stage16_rows(const T* src, int64_t ld, int r0, int rlim, int c0, int clim, bf16* dst) {
-    const int t = threadIdx.x;
-    if constexpr (sizeof(T) == 2) {
-        const int r = t / 4, c = (t % 4) * 8;
-        bf16x8 v;
-        if (r0 + r < rlim && c0 + c < clim) {
-            v = *reinterpret_cast<const bf16x8*>(src + (int64_t)(r0 + r) * ld + c0 + c);
-        } else {
+// One thread's share of an R x C block of a row-major source (rows [r0, r0 + R), columns
+// [c0, c0 + C), zero outside rlim / clim), read as 16-byte chunks into registers and written
+// to dst[r * LD + c] as bf16.  Reading and writing are separate steps so that a loop can read
+// its next block while it multiplies the current one.
+template <class T, int R, int C, int LD>
+struct Slice {
+    static constexpr int EPC = sizeof(T) == 2 ? 8 : 4;  // elements per 16-byte chunk
+    static constexpr int CPR = C / EPC, N = R * CPR / 256;
+    static_assert(R * CPR % 256 == 0, "block is not a whole number of chunks per thread");
+    using V = std::conditional_t<sizeof(T) == 2, bf16x8, float4>;
+    V v[N];
+
+    __device__ inline void load(const T* src, int64_t ld, int r0, int rlim, int c0, int clim) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = to_bf16(0.f);
-        }
-        *reinterpret_cast<bf16x8*>(dst + r * kLd16 + c) = v;
-    } else {
+        for (int u = 0; u < N; ++u) {
+            const int qd = threadIdx.x + 256 * u, r = qd / CPR, c = (qd % CPR) * EPC;
+            if (r0 + r < rlim && c0 + c < clim) {
+                v[u] = *reinterpret_cast<const V*>(src + (int64_t)(r0 + r) * ld + c0 + c);
+            } else if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int q = t + 256 * u, r = q / 8, c = (q % 8) * 4;
-            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (r0 + r < rlim && c0 + c < clim)
-                x = *reinterpret_cast<const float4*>(src + (int64_t)(r0 + r) * ld + c0 + c);
-            bf16x4 v;
-            v[0] = to_bf16(x.x);
-            v[1] = to_bf16(x.y);
-            v[2] = to_bf16(x.z);
-            v[3] = to_bf16(x.w);
-            *reinterpret_cast<bf16x4*>(dst + r * kLd16 + c) = v;
+                for (int e = 0; e < 8; ++e) v[u][e] = to_bf16(0.f);
+            } else {
+                v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
     }
+
+    __device__ inline void store(bf16* dst) const {
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            const int qd = threadIdx.x + 256 * u, r = qd / CPR, c = (qd % CPR) * EPC;
+            if constexpr (sizeof(T) == 2) {
+                *reinterpret_cast<bf16x8*>(dst + r * LD + c) = v[u];
+            } else {
+                bf16x4 w;
+                w[0] = to_bf16(v[u].x);
+                w[1] = to_bf16(v[u].y);
+                w[2] = to_bf16(v[u].z);
+                w[3] = to_bf16(v[u].w);
+                *reinterpret_cast<bf16x4*>(dst + r * LD + c) = w;
+            }
+        }
+    }
+};
+
+// rows [r0, r0 + 64) x contraction [c0, c0 + 32) of a row-major source -> dst[r][c] (bf16)
+template <class T>
+using RowSlice = Slice<T, 64, 32, kLd16>;
+
+template <class T>
+__device__ inline void stage16_rows(const T* src, int64_t ld, int r0, int rlim, int c0, int clim, bf16* dst) {
+    RowSlice<T> sl;
+    sl.load(src, ld, r0, rlim, c0, clim);
+    sl.store(dst);
 }
 
 __device__ inline f32x16 mma16(const bf16* a, const bf16* b, f32x16 c) {
@@ -281,10 +308,18 @@ __global__ __launch_bounds__(256) void nt16_kernel(const NtArgs a, const GradArg
     f32x16 acc;
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+    RowSlice<TX> sx;
+    RowSlice<TY> sy;
+    sx.load(xb, a.ldx, row0, rend, 0, a.K);
+    sy.load(yb, a.ldy, c0, a.ncols, 0, a.K);
     for (int d0 = 0; d0 < a.K; d0 += 32) {
         __syncthreads();
-        stage16_rows<TX>(xb, a.ldx, row0, rend, d0, a.K, xs);
-        stage16_rows<TY>(yb, a.ldy, c0, a.ncols, d0, a.K, ys);
+        sx.store(xs);
+        sy.store(ys);
+        if (d0 + 32 < a.K) {  // the next slice is read while this one is multiplied
+            sx.load(xb, a.ldx, row0, rend, d0 + 32, a.K);
+            sy.load(yb, a.ldy, c0, a.ncols, d0 + 32, a.K);
+        }
         __syncthreads();
         const bf16* xr = xs + (wr * 32 + col) * kLd16 + h * 8;
         const bf16* yr = ys + (wc * 32 + col) * kLd16 + h * 8;
@@ -383,38 +418,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void s
 using TrTile = DmaTiles<64, 4>;
 constexpr int kTrLd = TrTile::VLD;  // 96
 
+// contraction rows [k0, k0 + 32) x columns [c0, c0 + 64), row major (rows of kTrLd bf16)
 template <class T>
-__device__ inline void stage_tr(const T* src, int64_t ld, int k0, int klim, int c0, int clim, bf16* dst) {
-    const int t = threadIdx.x;
-    if constexpr (sizeof(T) == 2) {
-        const int k = t / 8, c = (t % 8) * 8;  // 32 rows x 8 chunks of 8
-        bf16x8 v;
-        if (k0 + k < klim && c0 + c < clim) {
-            v = *reinterpret_cast<const bf16x8*>(src + (int64_t)(k0 + k) * ld + c0 + c);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = to_bf16(0.f);
-        }
-        *reinterpret_cast<bf16x8*>(dst + k * kTrLd + c) = v;
-    } else {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int q = t + 256 * u, k = q / 16, c = (q % 16) * 4;  // 32 rows x 16 chunks of 4
-            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (k0 + k < klim && c0 + c < clim)
-                x = *reinterpret_cast<const float4*>(src + (int64_t)(k0 + k) * ld + c0 + c);
-            bf16x4 v;
-            v[0] = to_bf16(x.x);
-            v[1] = to_bf16(x.y);
-            v[2] = to_bf16(x.z);
-            v[3] = to_bf16(x.w);
-            *reinterpret_cast<bf16x4*>(dst + k * kTrLd + c) = v;
-        }
-    }
-}
+using TrSlice = Slice<T, 32, 64, kTrLd>;
 
 template <class TX, class TY>
-__global__ __launch_bounds__(256) void tn16_kernel(const TnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void tn16_kernel(const TnArgs a) {
     __shared__ __align__(16) bf16 xs[32 * kTrLd], ys[32 * kTrLd];
     const int bt = blockIdx.z;
     const int grp = blockIdx.y / a.nseg, sg = blockIdx.y % a.nseg;
@@ -431,10 +440,20 @@ __global__ __launch_bounds__(256) void tn16_kernel(const TnArgs a) {
     f32x16 acc;
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+    TrSlice<TX> sx;
+    TrSlice<TY> sy;
+    if (k0 < k1) {
+        sx.load(xb, a.ldx, k0, k1, m0, a.mrows);
+        sy.load(yb, a.ldy, k0, k1, n0, a.ncols);
+    }
     for (int k = k0; k < k1; k += 32) {
         __syncthreads();
-        stage_tr<TX>(xb, a.ldx, k, k1, m0, a.mrows, xs);
-        stage_tr<TY>(yb, a.ldy, k, k1, n0, a.ncols, ys);
+        sx.store(xs);
+        sy.store(ys);
+        if (k + 32 < k1) {  // the next slice is read while this one is multiplied
+            sx.load(xb, a.ldx, k + 32, k1, m0, a.mrows);
+            sy.load(yb, a.ldy, k + 32, k1, n0, a.ncols);
+        }
         __syncthreads();
 #pragma unroll
         for (int t = 0; t < 2; ++t)
