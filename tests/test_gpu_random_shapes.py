@@ -5,7 +5,8 @@ sizes 32-128 with 1-4 powers (uneven parts), fp32 and bf16 inputs, biases, and t
 softmax window.  Per shape: the chunk-parallel forward at the output bar, the streamed form
 against the parallel form (bit for bit outside tail-split chunk-0 tiles, which agree to the
 merge's rounding), and the backward for a seeded upstream gradient at the same bars
-(vanishing score gradients against their natural scale, as in test_gpu_backward)."""
+(vanishing score gradients against their natural scale, as in test_gpu_backward), and the
+distillation loss and feature-map gradients (blog 3.1.1) on the same shapes."""
 import numpy as np
 import pytest
 import torch
@@ -81,3 +82,34 @@ def test_random_shape(shape):
         e = max(float(np.abs(gk[h] - bref[key][h]).max() / np.abs(bref[key][h]).max()) for h in range(p.H))
         print(f"  {key}: {e:.2e}", flush=True)
         assert e <= tol, (key, e)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"s{i}" for i in range(len(SHAPES))])
+def test_random_shape_distill(shape):
+    """The distillation objective and its feature-map gradients on the same random shapes
+    (blog 3.1.1), against the oracle's loss and its brute-force gradients."""
+    from test_gpu_distill import check_loss
+    from test_gpu_distill_grad import GRAD_TOL, compare
+    *pp, bias = shape
+    p = rh.Params(*pp, out_dtype=rh.BF16)
+    print(f"random shape distill {shape}", flush=True)
+    x = rand_inputs(p, seed=sum(pp[:9]) * 7 + 2, bias=bias)
+    d = to_dev(x, p)
+    po = oracle_params(p)
+    loss, stu, tea = rh.distill_loss(p, d["q"], d["k"], d["v"], d["wq"], d["wk"], d["bq"], d["bk"], outputs=True)
+    got = rh.distill_grad(p, d["q"], d["k"], d["v"], d["wq"], d["wk"], d["bq"], d["bk"])
+    torch.cuda.synchronize()
+    assert torch.equal(got["loss"], loss)
+    hyb = oracle.parallel(po, x["q"], x["k"], x["v"], x["wq"], x["wk"], x["bq"], x["bk"])
+    soft = oracle.full_softmax(po, x["q"], x["k"], x["v"])
+    BH = p.B * p.H
+    check_loss(loss.cpu().numpy().reshape(BH).astype(np.float64),
+               stu.cpu().numpy().reshape(BH, -1).astype(np.float64),
+               tea.cpu().numpy().reshape(BH, -1).astype(np.float64),
+               hyb.reshape(BH, -1), soft.reshape(BH, -1), TOL[p.in_dtype])
+    ref = oracle.distill_phi_grads(po, x["q"], x["k"], x["v"], x["wq"], x["wk"], x["bq"], x["bk"])
+    if not any(ref[key].any() for key in ("dwq", "dwk", "dbq", "dbk")):
+        for key in ("dwq", "dwk", "dbq", "dbk"):
+            assert not got[key].any(), key
+        return
+    compare(got, ref, range(p.H), GRAD_TOL[p.in_dtype], str(shape[:10]))
