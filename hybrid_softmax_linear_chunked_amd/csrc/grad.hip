@@ -45,40 +45,69 @@ __device__ inline int ls_of(const GradArgs& a, int c) {
     return a.linear_only ? f1 : max(0, f0 - a.To);
 }
 
-// Rows [r0, r0 + 64) x columns [c0, c0 + 32) of a row-major source into LDS as float,
-// dst[r][c] with row stride 33 (conflict-free column reads); rows at or past rlim and
-// columns at or past clim (a multiple of 4, or of 8 for bf16) read as zero.
-template <class T>
-__device__ inline void stage_rows(const T* src, int64_t ld, int r0, int rlim, int c0, int clim, float* dst) {
-    const int t = threadIdx.x;
-    if constexpr (sizeof(T) == 2) {
-        const int r = t / 4, c = (t % 4) * 8;  // 64 rows x 4 chunks of 8
-        float v[8];
-        const bool ok = r0 + r < rlim && c0 + c < clim;
-        if (ok) {
-            const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + (int64_t)(r0 + r) * ld + c0 + c);
+__device__ inline bf16 to_bf16(float x) { return (bf16)x; }
+
+// One thread's share of an R x C block of a row-major source (rows [r0, r0 + R), columns
+// [c0, c0 + C), zero outside rlim / clim), read as 16-byte chunks into registers and written
+// to dst[r * LD + c] as DT (bf16 or float).  Reading and writing are separate steps so that a
+// loop can read its next block while it multiplies the current one.
+template <class T, int R, int C, int LD, class DT = bf16>
+struct Slice {
+    static constexpr int EPC = sizeof(T) == 2 ? 8 : 4;  // elements per 16-byte chunk
+    static constexpr int CPR = C / EPC, N = R * CPR / 256;
+    static_assert(R * CPR % 256 == 0, "block is not a whole number of chunks per thread");
+    using V = std::conditional_t<sizeof(T) == 2, bf16x8, float4>;
+    V v[N];
+
+    __device__ inline void load(const T* src, int64_t ld, int r0, int rlim, int c0, int clim) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
-        } else {
+        for (int u = 0; u < N; ++u) {
+            const int qd = threadIdx.x + 256 * u, r = qd / CPR, c = (qd % CPR) * EPC;
+            if (r0 + r < rlim && c0 + c < clim) {
+                v[u] = *reinterpret_cast<const V*>(src + (int64_t)(r0 + r) * ld + c0 + c);
+            } else if constexpr (sizeof(T) == 2) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = 0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dst[r * 33 + c + e] = v[e];
-    } else {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int q = t + 256 * u, r = q / 8, c = (q % 8) * 4;  // 64 rows x 8 chunks of 4
-            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (r0 + r < rlim && c0 + c < clim)
-                x = *reinterpret_cast<const float4*>(src + (int64_t)(r0 + r) * ld + c0 + c);
-            dst[r * 33 + c] = x.x;
-            dst[r * 33 + c + 1] = x.y;
-            dst[r * 33 + c + 2] = x.z;
-            dst[r * 33 + c + 3] = x.w;
+                for (int e = 0; e < 8; ++e) v[u][e] = to_bf16(0.f);
+            } else {
+                v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
     }
-}
+
+    __device__ inline void store(DT* dst) const {
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            const int qd = threadIdx.x + 256 * u, r = qd / CPR, c = (qd % CPR) * EPC;
+            DT* d = dst + r * LD + c;
+            if constexpr (sizeof(DT) == 2 && sizeof(T) == 2) {
+                *reinterpret_cast<bf16x8*>(d) = v[u];
+            } else if constexpr (sizeof(DT) == 2) {
+                bf16x4 w;
+                w[0] = to_bf16(v[u].x);
+                w[1] = to_bf16(v[u].y);
+                w[2] = to_bf16(v[u].z);
+                w[3] = to_bf16(v[u].w);
+                *reinterpret_cast<bf16x4*>(d) = w;
+            } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) d[e] = (float)v[u][e];
+            } else if constexpr (LD % 4 == 0) {
+                *reinterpret_cast<float4*>(d) = v[u];
+            } else {
+                d[0] = v[u].x;
+                d[1] = v[u].y;
+                d[2] = v[u].z;
+                d[3] = v[u].w;
+            }
+        }
+    }
+};
+
+// Rows [r0, r0 + 64) x columns [c0, c0 + 32) of a row-major source as float, dst[r][c] with
+// row stride 33 (conflict-free column reads); rows at or past rlim and columns at or past clim
+// (a multiple of 4, or of 8 for bf16) read as zero.
+template <class T>
+using FRowSlice = Slice<T, 64, 32, 33, float>;
 
 // 64 rows x 64 columns per workgroup, one 32x32 block per wave; X and Y slices of 32
 // contraction elements staged through LDS with coalesced 16-byte loads.
@@ -124,10 +153,18 @@ __global__ __launch_bounds__(256) void nt_kernel(const NtArgs a, const GradArgs 
     f32x16 acc;
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+    FRowSlice<TX> sx;
+    FRowSlice<TY> sy;
+    sx.load(xb, a.ldx, row0, rend, 0, a.K);
+    sy.load(yb, a.ldy, c0, a.ncols, 0, a.K);
     for (int d0 = 0; d0 < a.K; d0 += 32) {
         __syncthreads();  // the previous slice has been read
-        stage_rows<TX>(xb, a.ldx, row0, rend, d0, a.K, xs);
-        stage_rows<TY>(yb, a.ldy, c0, a.ncols, d0, a.K, ys);
+        sx.store(xs);
+        sy.store(ys);
+        if (d0 + 32 < a.K) {  // the next slice is read while this one is multiplied
+            sx.load(xb, a.ldx, row0, rend, d0 + 32, a.K);
+            sy.load(yb, a.ldy, c0, a.ncols, d0 + 32, a.K);
+        }
         __syncthreads();
         const float* xr = xs + (wr * 32 + col) * 33 + h;
         const float* yr = ys + (wc * 32 + col) * 33 + h;
@@ -149,41 +186,16 @@ __global__ __launch_bounds__(256) void nt_kernel(const NtArgs a, const GradArgs 
     }
 }
 
-// Slice [k0, k0 + 32) x [c0, c0 + 64) of a row-major source into LDS as float, dst[k][c]
-// with row stride 68; rows at or past klim and columns at or past clim read as zero.
+// Slice [k0, k0 + 32) x [c0, c0 + 64) of a row-major source as float, dst[k][c] with row
+// stride 68; rows at or past klim and columns at or past clim read as zero.
 template <class T>
-__device__ inline void stage_cols(const T* src, int64_t ld, int k0, int klim, int c0, int clim, float* dst) {
-    const int t = threadIdx.x;
-    if constexpr (sizeof(T) == 2) {
-        const int k = t / 8, c = (t % 8) * 8;  // 32 rows x 8 chunks of 8
-        float v[8];
-        if (k0 + k < klim && c0 + c < clim) {
-            const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + (int64_t)(k0 + k) * ld + c0 + c);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = 0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dst[k * 68 + c + e] = v[e];
-    } else {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int q = t + 256 * u, k = q / 16, c = (q % 16) * 4;  // 32 rows x 16 chunks of 4
-            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (k0 + k < klim && c0 + c < clim)
-                x = *reinterpret_cast<const float4*>(src + (int64_t)(k0 + k) * ld + c0 + c);
-            *reinterpret_cast<float4*>(dst + k * 68 + c) = x;
-        }
-    }
-}
+using FColSlice = Slice<T, 32, 64, 68, float>;
 
 // Partial C[m][n] = sum over the rows k of one segment of X[k][m] Y[k][n]: 64 x 64 outputs
 // per workgroup (one 32x32 block per wave), rows staged 32 at a time through LDS; empty
 // segments store zeros.
 template <class TX, class TY>
-__global__ __launch_bounds__(256) void tn_kernel(const TnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void tn_kernel(const TnArgs a) {
     __shared__ __align__(16) float xs[32 * 68], ys[32 * 68];
     const int bt = blockIdx.z;
     const int grp = blockIdx.y / a.nseg, sg = blockIdx.y % a.nseg;
@@ -199,10 +211,20 @@ __global__ __launch_bounds__(256) void tn_kernel(const TnArgs a) {
     f32x16 acc;
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+    FColSlice<TX> sx;
+    FColSlice<TY> sy;
+    if (k0 < k1) {
+        sx.load(xb, a.ldx, k0, k1, m0, a.mrows);
+        sy.load(yb, a.ldy, k0, k1, n0, a.ncols);
+    }
     for (int k = k0; k < k1; k += 32) {
         __syncthreads();
-        stage_cols<TX>(xb, a.ldx, k, k1, m0, a.mrows, xs);
-        stage_cols<TY>(yb, a.ldy, k, k1, n0, a.ncols, ys);
+        sx.store(xs);
+        sy.store(ys);
+        if (k + 32 < k1) {  // the next slice is read while this one is multiplied
+            sx.load(xb, a.ldx, k + 32, k1, m0, a.mrows);
+            sy.load(yb, a.ldy, k + 32, k1, n0, a.ncols);
+        }
         __syncthreads();
         const float* xr = xs + h * 68 + wm * 32 + col;
         const float* yr = ys + h * 68 + wn * 32 + col;
@@ -227,52 +249,6 @@ __global__ __launch_bounds__(256) void tn_kernel(const TnArgs a) {
 // segment product reads transposed slices, below).
 constexpr int kLd16 = 40;
 
-__device__ inline bf16 to_bf16(float x) { return (bf16)x; }
-
-// One thread's share of an R x C block of a row-major source (rows [r0, r0 + R), columns
-// [c0, c0 + C), zero outside rlim / clim), read as 16-byte chunks into registers and written
-// to dst[r * LD + c] as bf16.  Reading and writing are separate steps so that a loop can read
-// its next block while it multiplies the current one.
-template <class T, int R, int C, int LD>
-struct Slice {
-    static constexpr int EPC = sizeof(T) == 2 ? 8 : 4;  // elements per 16-byte chunk
-    static constexpr int CPR = C / EPC, N = R * CPR / 256;
-    static_assert(R * CPR % 256 == 0, "block is not a whole number of chunks per thread");
-    using V = std::conditional_t<sizeof(T) == 2, bf16x8, float4>;
-    V v[N];
-
-    __device__ inline void load(const T* src, int64_t ld, int r0, int rlim, int c0, int clim) {
-#pragma unroll
-        for (int u = 0; u < N; ++u) {
-            const int qd = threadIdx.x + 256 * u, r = qd / CPR, c = (qd % CPR) * EPC;
-            if (r0 + r < rlim && c0 + c < clim) {
-                v[u] = *reinterpret_cast<const V*>(src + (int64_t)(r0 + r) * ld + c0 + c);
-            } else if constexpr (sizeof(T) == 2) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[u][e] = to_bf16(0.f);
-            } else {
-                v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-        }
-    }
-
-    __device__ inline void store(bf16* dst) const {
-#pragma unroll
-        for (int u = 0; u < N; ++u) {
-            const int qd = threadIdx.x + 256 * u, r = qd / CPR, c = (qd % CPR) * EPC;
-            if constexpr (sizeof(T) == 2) {
-                *reinterpret_cast<bf16x8*>(dst + r * LD + c) = v[u];
-            } else {
-                bf16x4 w;
-                w[0] = to_bf16(v[u].x);
-                w[1] = to_bf16(v[u].y);
-                w[2] = to_bf16(v[u].z);
-                w[3] = to_bf16(v[u].w);
-                *reinterpret_cast<bf16x4*>(dst + r * LD + c) = w;
-            }
-        }
-    }
-};
 
 // rows [r0, r0 + 64) x contraction [c0, c0 + 32) of a row-major source -> dst[r][c] (bf16)
 template <class T>
