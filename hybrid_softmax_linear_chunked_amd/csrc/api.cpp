@@ -648,7 +648,7 @@ namespace {
 
 constexpr int kGradSegRows = 2048;    // token rows per dW partial
 constexpr int kColsumSegRows = 256;   // token rows per bias-gradient partial
-constexpr int kSoftSegRows = 1024;    // query rows per dK / dV partial of a window
+constexpr int kSoftSegRows = 2048;    // query rows per dK / dV partial of a window
 
 struct GradLayout {
     size_t stu, tea, lse, z, sqd, fwd_s, fwd_t, ah, u, phi, dphi, sz, rp, r, wp, bp;
