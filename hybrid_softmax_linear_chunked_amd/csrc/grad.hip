@@ -598,6 +598,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
 // per * Dphi idle) of the workgroup's kPhiRows rows; feature (j, p) of a row sits at
 // feat(j, 1) + (p - 1) * len(part of j).
 constexpr int kPhiRows = 32;
+constexpr int kPhiBatch = 8;  // rows whose loads a thread issues together
 
 __device__ inline int part_len(int j, int Dphi, int P) {
     const int q = Dphi / P, r = Dphi % P;
@@ -612,18 +613,29 @@ __global__ __launch_bounds__(256) void phi_fwd_kernel(const GradArgs s, float* _
     const int f1 = feat_index(j, 1, s.Dphi, s.P), step = part_len(j, s.Dphi, s.P);
     const int64_t rows = (int64_t)s.BH * s.N;
     const int64_t r0 = (int64_t)blockIdx.x * kPhiRows;
-    for (int rr = r_off; rr < kPhiRows; rr += per) {
-        const int64_t row = r0 + rr;
-        if (row >= rows) break;
-        float* up = U + row * s.Dphi + j;
-        const float x = *up;
-        const float u = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
-        *up = u;
-        float pw = u;
-        float* out = phi + row * s.F + f1;
-        for (int p = 0; p < s.P; ++p) {
-            out[p * step] = pw;
-            pw *= u;
+    // the thread's rows r_off, r_off + per, ... in batches of kPhiBatch: every load of a
+    // batch is issued before the first result is needed
+    for (int b0 = r_off; b0 < kPhiRows; b0 += kPhiBatch * per) {
+        float x[kPhiBatch];
+#pragma unroll
+        for (int i = 0; i < kPhiBatch; ++i) {
+            const int rr = b0 + i * per;
+            const int64_t row = r0 + rr;
+            x[i] = rr < kPhiRows && row < rows ? U[row * s.Dphi + j] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < kPhiBatch; ++i) {
+            const int rr = b0 + i * per;
+            const int64_t row = r0 + rr;
+            if (rr >= kPhiRows || row >= rows) break;
+            const float u = fmaxf(x[i], 0.f) + log1pf(expf(-fabsf(x[i])));
+            U[row * s.Dphi + j] = u;
+            float pw = u;
+            float* out = phi + row * s.F + f1;
+            for (int p = 0; p < s.P; ++p) {
+                out[p * step] = pw;
+                pw *= u;
+            }
         }
     }
 }
@@ -638,18 +650,39 @@ __global__ __launch_bounds__(256) void phi_bwd_kernel(const GradArgs s, float* _
     const int f1 = feat_index(j, 1, s.Dphi, s.P), step = part_len(j, s.Dphi, s.P);
     const int64_t rows = (int64_t)s.BH * s.N;
     const int64_t r0 = (int64_t)blockIdx.x * kPhiRows;
-    for (int rr = r_off; rr < kPhiRows; rr += per) {
-        const int64_t row = r0 + rr;
-        if (row >= rows) break;
-        float* up = U + row * s.Dphi + j;
-        const float u = *up;
-        const float* dp = dphi + row * s.F + f1;
-        float du = 0.f, upow = 1.f;
-        for (int p = 0; p < s.P; ++p) {
-            du += (float)(p + 1) * upow * dp[p * step];
-            upow *= u;
+    // batches of kPhiBatch rows as in phi_fwd_kernel; dphi of power p + 1 of every row of
+    // the batch is loaded before any is used
+    for (int b0 = r_off; b0 < kPhiRows; b0 += kPhiBatch * per) {
+        float u[kPhiBatch], du[kPhiBatch], upow[kPhiBatch];
+#pragma unroll
+        for (int i = 0; i < kPhiBatch; ++i) {
+            const int rr = b0 + i * per;
+            const int64_t row = r0 + rr;
+            u[i] = rr < kPhiRows && row < rows ? U[row * s.Dphi + j] : 0.f;
+            du[i] = 0.f;
+            upow[i] = 1.f;
         }
-        *up = du * -expm1f(-u);
+        for (int p = 0; p < s.P; ++p) {
+            float d[kPhiBatch];
+#pragma unroll
+            for (int i = 0; i < kPhiBatch; ++i) {
+                const int rr = b0 + i * per;
+                const int64_t row = r0 + rr;
+                d[i] = rr < kPhiRows && row < rows ? dphi[row * s.F + f1 + p * step] : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < kPhiBatch; ++i) {
+                du[i] += (float)(p + 1) * upow[i] * d[i];
+                upow[i] *= u[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kPhiBatch; ++i) {
+            const int rr = b0 + i * per;
+            const int64_t row = r0 + rr;
+            if (rr >= kPhiRows || row >= rows) break;
+            U[row * s.Dphi + j] = du[i] * -expm1f(-u[i]);
+        }
     }
 }
 
