@@ -460,6 +460,33 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
     *dst = accumulate ? *dst + acc : acc;
 }
 
+// reduce_kernel four elements per thread (E, ostride and both base addresses multiples of 4
+// floats), each element summed in the same order
+__global__ __launch_bounds__(256) void reduce4_kernel(const float* __restrict__ part, float* __restrict__ out, int nb,
+                                                      int no, int ns, int64_t E, int64_t ostride, int accumulate) {
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    const int o = blockIdx.y;
+    if (e >= E) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int b = 0; b < nb; ++b)
+        for (int s = 0; s < ns; ++s) {
+            const float4 x = *reinterpret_cast<const float4*>(part + (((int64_t)b * no + o) * ns + s) * E + e);
+            acc.x += x.x;
+            acc.y += x.y;
+            acc.z += x.z;
+            acc.w += x.w;
+        }
+    float4* dst = reinterpret_cast<float4*>(out + (int64_t)o * ostride + e);
+    if (accumulate) {
+        const float4 y = *dst;
+        acc.x = y.x + acc.x;
+        acc.y = y.y + acc.y;
+        acc.z = y.z + acc.z;
+        acc.w = y.w + acc.w;
+    }
+    *dst = acc;
+}
+
 // R[bt][c] <- sum over c' >= c of R[bt][c'] (from the last chunk), in place
 __global__ __launch_bounds__(256) void suffix_kernel(float* __restrict__ R, int nc, int64_t E) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -802,8 +829,15 @@ hipError_t launch_tn(const TnArgs& a, int BH, bool y_bf16, hipStream_t stream) {
 
 hipError_t launch_grad_reduce(const float* part, float* out, int nb, int no, int ns, int64_t E, hipStream_t stream,
                               int64_t out_stride, bool accumulate) {
-    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((E + 255) / 256), no), dim3(256), 0, stream, part, out, nb, no,
-                       ns, E, out_stride < 0 ? E : out_stride, accumulate ? 1 : 0);
+    const int64_t os = out_stride < 0 ? E : out_stride;
+    const bool v4 = E % 4 == 0 && os % 4 == 0 && reinterpret_cast<uintptr_t>(part) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(out) % 16 == 0;
+    if (v4)
+        hipLaunchKernelGGL(reduce4_kernel, dim3((unsigned)((E / 4 + 255) / 256), no), dim3(256), 0, stream, part, out,
+                           nb, no, ns, E, os, accumulate ? 1 : 0);
+    else
+        hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((E + 255) / 256), no), dim3(256), 0, stream, part, out, nb,
+                           no, ns, E, os, accumulate ? 1 : 0);
     return hipGetLastError();
 }
 
