@@ -530,55 +530,71 @@ __global__ __launch_bounds__(256) void state_sz_kernel(const GradArgs s, const f
     }
 }
 
-// Per query row (one wave per row): g = dout, or 2 (o - t) for the distillation objective;
-// 1/den from lse and z; AH[i] = [g / den | (g . o) / den | 0 ...] (D + 32 columns), and
-// when asked, delta_i = g . o and log den_i
+// Per query row (kRowsPerWave rows per wave, their loads issued together): g = dout, or
+// 2 (o - t) for the distillation objective; 1/den from lse and z; AH[i] = [g / den |
+// (g . o) / den | 0 ...] (D + 32 columns), and when asked, delta_i = g . o and log den_i
+constexpr int kRowsPerWave = 4;
+
 __global__ __launch_bounds__(256) void rows_kernel(const GradArgs s, const float* __restrict__ o,
                                                    const float* __restrict__ t, const float* __restrict__ dout,
                                                    const float* __restrict__ lse, const float* __restrict__ z,
                                                    float* __restrict__ AH, float* __restrict__ delta,
                                                    float* __restrict__ lden) {
     const int bt = blockIdx.y, wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    const int64_t i = (int64_t)blockIdx.x * 4 + wave;
-    if (i >= s.N) return;
+    const int64_t i0 = ((int64_t)blockIdx.x * 4 + wave) * kRowsPerWave;
     const int D = s.D, LD = D + 32;
-    const int64_t row = (int64_t)bt * s.N + i;
-    float gv[2], dot = 0.f;
+    float ov[kRowsPerWave][2], gv[kRowsPerWave][2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int d = lane + 64 * u;
-        gv[u] = 0.f;
-        if (d < D) {
-            const float ov = o[row * D + d];
-            gv[u] = dout ? dout[row * D + d] : 2.f * (ov - t[row * D + d]);
-            dot += gv[u] * ov;
+    for (int k = 0; k < kRowsPerWave; ++k) {
+        const int64_t row = (int64_t)bt * s.N + i0 + k;
+        const bool ok = i0 + k < s.N;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int d = lane + 64 * u;
+            ov[k][u] = 0.f;
+            gv[k][u] = 0.f;
+            if (ok && d < D) {
+                ov[k][u] = o[row * D + d];
+                gv[k][u] = dout ? dout[row * D + d] : t[row * D + d];
+            }
         }
     }
 #pragma unroll
-    for (int msk = 32; msk >= 1; msk >>= 1) dot += __shfl_xor(dot, msk, 64);
-    const float L = lse[row], zz = z[row];
-    float inv;
-    if (L == -INFINITY) {
-        inv = 1.f / zz;
-    } else if (zz <= 0.f || L > logf(zz)) {
-        const float e = expf(-L);
-        inv = e / (1.f + zz * e);
-    } else {
-        inv = 1.f / (zz + expf(L));
-    }
-    float* ah = AH + row * LD;
+    for (int k = 0; k < kRowsPerWave; ++k) {
+        if (i0 + k >= s.N) break;
+        const int64_t row = (int64_t)bt * s.N + i0 + k;
+        float dot = 0.f;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int d = lane + 64 * u;
-        if (d < D) ah[d] = gv[u] * inv;
-    }
-    if (lane < 32) ah[D + lane] = lane == 0 ? dot * inv : 0.f;
-    if (lane == 0 && delta) {
-        delta[row] = dot;
-        // log(exp(L) + z), stable for either term dominating
-        const float lz = zz > 0.f ? logf(zz) : -INFINITY;
-        const float hi = fmaxf(L, lz), lo = fminf(L, lz);
-        lden[row] = lo == -INFINITY ? hi : hi + log1pf(expf(lo - hi));
+        for (int u = 0; u < 2; ++u) {
+            if (!dout) gv[k][u] = 2.f * (ov[k][u] - gv[k][u]);
+            dot += gv[k][u] * ov[k][u];
+        }
+#pragma unroll
+        for (int msk = 32; msk >= 1; msk >>= 1) dot += __shfl_xor(dot, msk, 64);
+        const float L = lse[row], zz = z[row];
+        float inv;
+        if (L == -INFINITY) {
+            inv = 1.f / zz;
+        } else if (zz <= 0.f || L > logf(zz)) {
+            const float e = expf(-L);
+            inv = e / (1.f + zz * e);
+        } else {
+            inv = 1.f / (zz + expf(L));
+        }
+        float* ah = AH + row * LD;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int d = lane + 64 * u;
+            if (d < D) ah[d] = gv[k][u] * inv;
+        }
+        if (lane < 32) ah[D + lane] = lane == 0 ? dot * inv : 0.f;
+        if (lane == 0 && delta) {
+            delta[row] = dot;
+            // log(exp(L) + z), stable for either term dominating
+            const float lz = zz > 0.f ? logf(zz) : -INFINITY;
+            const float hi = fmaxf(L, lz), lo = fminf(L, lz);
+            lden[row] = lo == -INFINITY ? hi : hi + log1pf(expf(lo - hi));
+        }
     }
 }
 
@@ -873,8 +889,9 @@ hipError_t launch_grad_state_sz(const GradArgs& s, const float* Sp, const float*
 
 hipError_t launch_grad_rows(const GradArgs& s, const float* o, const float* t, const float* dout, const float* lse,
                             const float* z, float* AH, float* delta, float* lden, hipStream_t stream) {
-    hipLaunchKernelGGL(rows_kernel, dim3((unsigned)((s.N + 3) / 4), s.BH), dim3(256), 0, stream, s, o, t, dout, lse, z,
-                       AH, delta, lden);
+    const int per_wg = 4 * kRowsPerWave;
+    hipLaunchKernelGGL(rows_kernel, dim3((unsigned)((s.N + per_wg - 1) / per_wg), s.BH), dim3(256), 0, stream, s, o, t,
+                       dout, lse, z, AH, delta, lden);
     return hipGetLastError();
 }
 
