@@ -740,8 +740,11 @@ __global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ X
     const int per = 256 / cols, j = t % cols, r_off = t / cols;
     const int64_t r0 = (int64_t)sg * seg_rows, r1 = min(r0 + seg_rows, rows);
     float acc = 0.f;
-    if (r_off < per)
-        for (int64_t r = r0 + r_off; r < r1; r += per) acc += X[((int64_t)bt * rows + r) * cols + j];
+    if (r_off < per) {
+        const float* xb = X + (int64_t)bt * rows * cols + j;
+#pragma unroll 8
+        for (int64_t r = r0 + r_off; r < r1; r += per) acc += xb[r * cols];
+    }
     red[t] = acc;
     __syncthreads();
     if (t < cols) {
