@@ -2,10 +2,15 @@
 // part and the shared normalisation fused into its epilogue (ReHyAt blog,
 // maplevalley.com.cn, sections 2.2.1-2.3).
 //
-// One workgroup = 4 waves x 64 queries (two 32-query blocks per wave) of one chunk of one
-// (batch, head), one wave per SIMD with the whole register file.  Every K or V operand read
-// from LDS feeds two MFMAs (one per query block): half the LDS read traffic per product of
-// a 32-query wave, which is what bounds that layout on this part.
+// One workgroup = 8 waves x 32 queries of one chunk of one (batch, head): two waves per
+// SIMD, so that while one wave runs the softmax of a sub-step on the vector ALU (and its
+// LDS operand reads and tile copies), the other keeps the matrix core busy.  A single wave
+// per SIMD issues one instruction at a time, and the softmax, operand reads and copies of a
+// 64-query wave do not fit in the shadow of its own products (measured on this part: 0.56
+// to 0.71 of the MFMA rate for one wave, 0.9 for two).  The 8 waves share one ring of K/V
+// tiles, so the HBM and LDS-write traffic per query is that of the 4-wave layout; each K or
+// V operand read from LDS now feeds one product, which the LDS read rate (256 B/clk per CU)
+// carries at half load.
 //
 // The window is swept in 32-token sub-steps.  Sub-step u runs
 //   (a) S_{u+1}^T = K_{u+1} Q^T          on the matrix core (scores one sub-step ahead),
@@ -21,9 +26,9 @@
 // never rescaled.  Any fixed m gives the exact result, because the final normalisation
 // uses the same m; the only risk is range.  The row sum bounds every p, so a sum above
 // 2^64 (or an infinite one) sends the workgroup through a second pass whose reference is
-// the exact row maximum, found by a score-only sweep over the window.  Row sums are taken
-// from the bf16 P actually fed to the value product (dot2 against ones), so numerator
-// and denominator see the same rounded weights.
+// the exact row maximum, found by a score-only sweep over the window.  Row sums add the
+// fp32 weights with plain adds (the packed bf16 dot product runs on the matrix pipe and
+// stalls behind the products); the value product takes the same weights rounded to bf16.
 #include <type_traits>
 
 #include "attn_common.hpp"
@@ -33,16 +38,56 @@ namespace rehyat {
 
 static constexpr float kWideSumLimit = 18446744073709551616.0f;  // 2^64
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Workgroup layout of the wide kernel: waves, and 32-query blocks per wave.
+static constexpr int kWideWaves = 8, kWideQB = 1;
 
-// sum of the 8 bf16 of an operand, accumulated in fp32
-__device__ inline float sum8(bf16x8 v, float acc) {
-    const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
-    return acc;
+// The sweep as scheduled assembly (generated, wide_substep.inc).  sa / sb hold the scores of
+// the current and of the next sub-step (PAR picks which is current), o the unnormalised O^T
+// accumulators, q the Q operands, k the K operands of the next scores (read one sub-step
+// ahead), vf the V^T operands, pf the bf16 weights, lsum the row sum, m the reference of the
+// exponent (log2 domain), sc the score scale (log2(e)/sqrt(D)).  Sub-steps are pipelined: the
+// value products of the second key half of a sub-step run in the next one.
+// wide_pipe: one sub-step at the given V^T / K read addresses (FIRST: none deferred from a
+// previous one).  wide_flush: the deferred products of the last sub-step.  wide_loop: sweep
+// positions i0 .. iend-1 with the copy of K tile i+3 and V tile i+2 (clamped to the last tile
+// `last`; a streaming window's tiles come from segment 1 below token len1, else segment 2)
+// into the rings at LDS byte addresses kring / vring, lane read offsets klane / vlane; this
+// wave copies 1 KB chunks kc[j] / vc[j] of a tile from its lane offsets koff[j] / voff[j], the
+// last under kmask / vmask where waves issue unequal counts.
+#define WIDE_PIPE_ARGS(D)                                                                           \
+    f32x16 &sa, f32x16 &sb, f32x16(&o)[D / 32][1], const bf16x8(&q)[1][D / 16], bf16x8(&k)[D / 16], \
+        bf16x8(&vf)[D / 16], bf16x8(&pf)[2], float &lsum, float m, float sc, uint32_t vaddr, uint32_t kaddr
+#define WIDE_FLUSH_ARGS(D)                                                                          \
+    f32x16 &sa, f32x16 &sb, f32x16(&o)[D / 32][1], bf16x8(&k)[D / 16], bf16x8(&vf)[D / 16], bf16x8(&pf)[2]
+#define WIDE_LOOP_ARGS(D)                                                                                        \
+    f32x16 &sa, f32x16 &sb, f32x16(&o)[D / 32][1], const bf16x8(&q)[1][D / 16], bf16x8(&k)[D / 16],              \
+        bf16x8(&vf)[D / 16], bf16x8(&pf)[2], float &lsum, float m, float sc, int i0, int iend, int last, int len1, \
+        const void *k1, const void *v1, const void *k2, const void *v2, uint32_t kring, uint32_t vring,             \
+        uint32_t klane, uint32_t vlane, const uint32_t(&kc)[3], const uint32_t(&vc)[3], const uint32_t(&koff)[3],   \
+        const uint32_t(&voff)[3], uint64_t kmask, uint64_t vmask
+template <int D, int PAR, bool FIRST>
+__device__ inline void wide_pipe(WIDE_PIPE_ARGS(D));
+template <int D>
+__device__ inline void wide_flush(WIDE_FLUSH_ARGS(D));
+template <int D, bool STREAM>
+__device__ inline void wide_loop(WIDE_LOOP_ARGS(D));
+// Wait states between the last product of a sweep and compiler code reading S or O.
+template <int D>
+__device__ inline void wide_guard(f32x16& sa, f32x16& sb, f32x16 (&o)[D / 32][1]);
+#include "wide_substep.inc"
+
+// This wave's part of the copy of a 64-token tile: LDS byte offsets of its 1 KB chunks
+// (a missing last one gets a valid address), lane byte offsets, and the exec mask of the last.
+template <int NI, int PW, int NW>
+__device__ inline void copy_share(int wave, const uint32_t (&off)[PW], uint32_t (&c)[3], uint32_t (&o)[3], uint64_t& mask) {
+    static_assert(PW <= 3, "more than three copy instructions per wave");
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        c[j] = __builtin_amdgcn_readfirstlane((uint32_t)min(wave + j * NW, NI - 1) * 1024u);
+        o[j] = j < PW ? off[j] * (uint32_t)sizeof(bf16) : 0u;
+    }
+    const bool on = wave + (PW - 1) * NW < NI;
+    mask = __builtin_amdgcn_read_exec() & (0ull - (uint64_t)on);
 }
 
 // LDS bytes of the one-shot epilogue staging: W_q [Dphi][D + 8], the P powers of the state
@@ -79,14 +124,14 @@ __device__ inline void dma_rows(const void* src, int rows, int row_bytes, bool p
 // u = W_q q on MFMA from the Q operand registers, phi = per-part powers of softplus(u + b),
 // y = sum over powers of S_c^T phi on MFMA (phi straight from the u registers),
 // z = phi . Z_c, and merges with its softmax part.
-template <class OT, int D, int NW>
+template <class OT, int D, int NW, int QB>
 __device__ inline void wide_linear_and_merge(const AttnArgs& a, const Window<bf16>& w, unsigned char* smem, int qw,
                                              int wave, bool has_soft, bool has_lin,
-                                             const bf16x8 (&qf)[2][D / 16], const f32x16 (&oacc)[D / 32][2],
-                                             const float (&m_ref)[2], const float (&l_tot)[2]) {
+                                             const bf16x8 (&qf)[QB][D / 16], const f32x16 (&oacc)[D / 32][QB],
+                                             const float (&m_ref)[QB], const float (&l_tot)[QB]) {
     using T = bf16;
     using M = Mfma<T>;
-    constexpr int QB = 2, KS = M::KS, EPL = M::EPL, NS = D / KS, NDB = D / 32, TPB = 16 / EPL;
+    constexpr int KS = M::KS, EPL = M::EPL, NS = D / KS, NDB = D / 32, TPB = 16 / EPL;
     const int lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
     const int Dphi = a.Dphi, P = a.P, NJB = Dphi / 32;
     constexpr int WLD = D + 8;
@@ -166,10 +211,10 @@ __device__ inline void wide_linear_and_merge(const AttnArgs& a, const Window<bf1
 }
 
 template <class OT, int D, bool STREAM, bool EPI_ALL>
-__global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(kWideWaves * 64, 1) void attn_wide_kernel(const AttnArgs a) {
     using T = bf16;
     using M = Mfma<T>;
-    constexpr int QB = 2, NW = 4, NT = NW * 64, BQ = NW * QB * 32;
+    constexpr int QB = kWideQB, NW = kWideWaves, NT = NW * 64, BQ = NW * QB * 32;
     using Tile = DmaTiles<D, NW>;
     constexpr int KS = M::KS, EPL = M::EPL, NS = D / KS, NDB = D / 32;
     constexpr int TPB = 32 / KS;  // value-product steps per 32-token sub-step
@@ -239,7 +284,7 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
     const int vl = Tile::vlane(lane);
 
     auto kslot = [&](int t) { return kring + (t & 3) * Tile::K_ELEMS; };
-    auto vslot = [&](int t) { return vring + (t % 3) * Tile::V_ELEMS; };
+    auto vslot = [&](int t) { return vring + (t & 3) * Tile::V_ELEMS; };
     // start the DMA of the K / V tile at sweep position i into the given slot (completion:
     // vmcnt + barrier)
     auto dma_k = [&](int i, T* dst) {
@@ -301,84 +346,40 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
 
     f32x16 oacc[NDB][QB];
     float m_ref[QB], l_run[QB];
+    f32x16 SA[QB], SB[QB];
 
-    // K operands of the look-ahead scores, read one sub-step before their products so the
-    // LDS latency is covered by a whole sub-step of work (one wave per SIMD has no other
-    // wave to hide it behind)
-    typename M::frag kpre[NS];
-    auto read_k = [&](int u) {
-        const T* Ks = kslot(u >> 1);
-#pragma unroll
-        for (int st = 0; st < NS; ++st) kpre[st] = Tile::kfrag(Ks, u & 1, st, col, h);
-    };
-
-    // Sub-step u (kpre holds the K operands of u+1), one basic block cut by scheduling
-    // fences into
-    //   V operand reads of u | scores of u+1 with the softmax of u | value product of u with
-    //   the K operand reads of u+2.
-    // The scores and the softmax are written as 16 segments [MFMA, 1/16 of the softmax]; the
-    // compiler's MFMA/exp interleaving places the vector work between the products.  MASK
-    // (the last tile, swept first): keys of u from key_limit(u) on get a score of -inf.  At
-    // the end of the sweep the look-ahead and the K reads land in ring slots whose contents
-    // are never used; every read stays inside the ring.
-    auto sub_full = [&](int u, f32x16 (&Sc)[QB], f32x16 (&Sn)[QB], auto mask_tag, auto&& dma_part) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        const int kl = MASK ? key_limit(u) : 32;
-        if (MASK && kl < 32) {
+    // Sub-step u (generated assembly, wide_substep.inc): the score products of u+1 with the
+    // softmax of u and the V^T operand reads of u, then the value products of u with the K
+    // operand reads of u+2 and this wave's part of a tile copy.  MASK (the last tile, swept
+    // first): keys of u from key_limit(u) on get a score of -inf first.  At the end of the
+    // sweep the look-ahead scores and K reads use ring slots whose contents are never used;
+    // every read stays inside the ring.
+    static_assert(QB == 1, "the sub-step assembly holds one 32-query block per wave");
+    const uint32_t kring_b = lds_addr(kring), vring_b = lds_addr(vring);
+    const uint32_t klane_b = (uint32_t)((col * Tile::KLD + h * 8) * 2), vlane_b = (uint32_t)(vl * 2);
+    auto kslot_b = [&](int t) { return kring_b + (uint32_t)((t & 3) * Tile::K_ELEMS * 2); };
+    auto vslot_b = [&](int t) { return vring_b + (uint32_t)((t & 3) * Tile::V_ELEMS * 2); };
+    typename M::frag kf[NS], vfr[NS], pfr[2];
+    auto substep = [&](int u, auto par_tag, auto first_tag, bool mask) {
+        constexpr int PAR = decltype(par_tag)::value;
+        constexpr bool FIRST = decltype(first_tag)::value;
+        f32x16& Sc = PAR == 0 ? SA[0] : SB[0];
+        // keys of the ragged last tile (swept first) past the window: -inf
+        const int kl = mask ? key_limit(u) : 32;
+        if (kl < 32) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                if (crow(r, h) >= kl)
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) Sc[qb][r] = -INFINITY;
+                if (crow(r, h) >= kl) Sc[r] = -INFINITY;
         }
-        const T* Vs = vslot(u >> 1);
-        constexpr int NV = TPB * NDB;
-        typename M::frag vf[NV];
-#pragma unroll
-        for (int i = 0; i < NV; ++i) vf[i] = Tile::vfrag(Vs, vl, i % NDB, u & 1, i / NDB);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_iglp_opt(2);
-        typename M::frag pf[TPB][QB];
-        float lsum[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) lsum[qb] = l_run[qb];
-        float pv[QB * 16];
-        constexpr int NSEG = NS * QB;
-        constexpr int PER = QB * 16 / NSEG;  // softmax values per segment
-#pragma unroll
-        for (int i = 0; i < NSEG; ++i) {
-            const int st = i / QB, qb = i % QB;
-            Sn[qb] = M::mma(kpre[st], qf[qb][st], st == 0 ? zero16() : Sn[qb]);
-#pragma unroll
-            for (int e = 0; e < PER; ++e) {
-                const int idx = i * PER + e, q2 = idx / 16, r = idx % 16;
-                pv[idx] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[q2][r], sc, -m_ref[q2]));
-                if ((idx + 1) % EPL == 0) {
-                    const int t = r / EPL;
-                    pf[t][q2] = M::pack(pv + idx + 1 - EPL);
-                    lsum[q2] = sum8(pf[t][q2], lsum[q2]);
-                }
-            }
-        }
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) l_run[qb] = lsum[qb];
-        read_k(u + 2);  // unfenced: the scheduler spreads these reads over the value product
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int db = i % NDB, t = i / NDB;
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = M::mma(vf[i], pf[t][qb], oacc[db][qb]);
-            // one DMA instruction of the tile copy after each pair of products, so that the
-            // copies issue in the shadow of the products instead of in a burst ahead of them
-            if (i < PWMAX) {
-                __builtin_amdgcn_sched_barrier(0);
-                dma_part(i);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
+        const uint32_t vaddr = vlane_b + vslot_b(u >> 1) + (uint32_t)((u & 1) * 32 * Tile::VLD * 2);
+        const uint32_t kaddr = klane_b + kslot_b((u + 2) >> 1) + (uint32_t)((u & 1) * 32 * Tile::KLD * 2);
+        wide_pipe<D, PAR, FIRST>(SA[0], SB[0], oacc, qf, kf, vfr, pfr, l_run[0], m_ref[0], sc, vaddr, kaddr);
     };
+    uint32_t kc[3], vc[3], koff_b[3], voff_b[3];
+    uint64_t kmask, vmask;
+    copy_share<Tile::NIK, Tile::PWK, NW>(wave, tile.koff, kc, koff_b, kmask);
+    copy_share<Tile::NIV, Tile::PWV, NW>(wave, tile.voff, vc, voff_b, vmask);
 
-    f32x16 SA[QB], SB[QB];
     // one sweep of the window with the current reference; returns the row sums
     auto run = [&](bool first, float (&l_tot)[QB]) {
 #pragma unroll
@@ -387,6 +388,12 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) oacc[db][qb] = zero16();
         }
+        // Every register the sweep's assembly pins holds a defined value before its first
+        // block, so that the compiler places no other operand of that block there.
+        SB[0] = zero16();
+#pragma unroll
+        for (int i = 0; i < NS; ++i) vfr[i] = bf16x8{};
+        pfr[0] = pfr[1] = bf16x8{};
         if (p1 > p0) {
             // prologue: positions p0 and p0+1 (K) and p0 (V) in LDS, K of p0+2 and V of p0+1
             // in flight (the batch of position p0-1); scores of the first sub-step
@@ -398,71 +405,68 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
             if (p0 + 1 < p1) dma_v(p0 + 1, vslot(p0 + 1));
             if (wave_live) {
                 qk(kslot(p0), 2 * p0, SA);
-                read_k(2 * p0 + 1);
+#pragma unroll
+                for (int st = 0; st < NS; ++st) kf[st] = Tile::kfrag(kslot(p0), 1, st, col, h);
+                wide_guard<D>(SA[0], SB[0], oacc);  // the products above wrote SA
                 if (first) {
-                    float mx[QB] = {-INFINITY, -INFINITY};
+                    float mx[QB];
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) mx[qb] = -INFINITY;
                     rowmax(2 * p0, SA, mx);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) m_ref[qb] = pair_max(mx[qb]) * sc;
                 }
             }
-            // sweep position i holds sub-steps 2i and 2i+1; position 0 (the last tile of the
-            // window) is the only one that can hold a ragged or an empty sub-step
-            auto none = [](int) {};
-            // Sweep position i: batch K of i+3 and V of i+2, into the slots position i-1 used
-            // (free once its barrier has passed), and sub-steps 2i and 2i+1.
-            //   UPFRONT: the batch is issued ahead of the products, by the general copy (clamped
-            //   to the window, and split between the two segments of a streaming window).  For
-            //   position 0 (with the ragged tile), and in the chunk-parallel kernel for waves
-            //   without queries.
-            //   Otherwise the copy is spread over the products, K over the first sub-step and V
-            //   over the second (waves of a streaming window without queries issue it at once):
-            //   tiles past position 0 are whole tiles with a uniform base, in one segment.  Near
-            //   the end, where no tile is left to fetch, the copy is still issued, of a whole
-            //   tile into the slot just freed (nothing reads that slot again in this sweep, and
-            //   the next workgroup barrier waits for it), so the loop has no branches and the
-            //   wait one count.
-            auto position = [&](int i, auto mask_tag, auto upfront_tag) {
-                constexpr bool UPFRONT = decltype(upfront_tag)::value;
+            // Sweep position i holds sub-steps 2i and 2i+1 and issues the batch K of tile i+3
+            // and V of tile i+2, into the slots position i-1 used (free once its barrier has
+            // passed).  Position p0 (with the ragged tile when p0 = 0) issues it ahead of its
+            // products by the general copy (clamped to the window, split between the two
+            // segments of a streaming window).  Positions p0+1 .. p1-1 run in wide_loop, whose
+            // copies are spread over the value products: those tiles are whole, each in one
+            // segment (a streaming window's segment boundary is a multiple of 64 tokens or past
+            // the last whole tile).  Near the end, where no tile is left to fetch, wide_loop
+            // still copies, the last tile into the slot just freed (nothing reads that slot
+            // again in this sweep, and the next barrier waits for it), so its loop has no
+            // branches and its wait one count.  Waves without queries only copy: in the
+            // chunk-parallel kernel by the general copy, in a streaming window the whole tiles.
+            {
+                const int i = p0;
                 const bool kis = i + 3 < p1, vis = i + 2 < p1;
-                if (UPFRONT || (!STREAM && !wave_live)) {
-                    if (kis) dma_k(i + 3, kslot(i + 3));
-                    if (vis) dma_v(i + 2, vslot(i + 2));
-                    if (wave_live) {
-                        sub_full(2 * i, SA, SB, mask_tag, none);
-                        sub_full(2 * i + 1, SB, SA, mask_tag, none);
-                    }
-                    tile_sync(kis, vis);
-                    return;
+                if (kis) dma_k(i + 3, kslot(i + 3));
+                if (vis) dma_v(i + 2, vslot(i + 2));
+                if (wave_live) {
+                    substep(2 * i, std::integral_constant<int, 0>{}, std::true_type{}, p0 == 0);
+                    substep(2 * i + 1, std::integral_constant<int, 1>{}, std::false_type{}, p0 == 0);
                 }
-                const int last = p1 - 1;  // >= i >= 1: a whole tile
-                const int tk = tile_of(min(i + 3, last)) * BK, tv = tile_of(min(i + 2, last)) * BK;
-                // a streaming window's segment boundary is a multiple of 64 tokens (or past
-                // the last whole tile), so each of these tiles lies in one segment
-                const T* const kb = STREAM ? w.src.krow(tk, D) : w.src.k1 + (int64_t)tk * D;
-                const T* const vb = STREAM ? w.src.vrow(tv, D) : w.src.v1 + (int64_t)tv * D;
-                T* const kd = kslot(i + 3);
-                T* const vd = vslot(i + 2);
-                auto kpart = [&](int j) {
-                    if (j < Tile::PWK) tile.issue_k_at(j, kb, kd, wave);
-                };
-                auto vpart = [&](int j) {
-                    if (j < Tile::PWV) tile.issue_v_at(j, vb, vd, wave);
-                };
-                if (!STREAM || wave_live) {
-                    sub_full(2 * i, SA, SB, mask_tag, kpart);
-                    sub_full(2 * i + 1, SB, SA, mask_tag, vpart);
+                tile_sync(kis, vis);
+            }
+            if (p0 + 1 < p1) {
+                if (wave_live) {
+                    wide_loop<D, STREAM>(SA[0], SB[0], oacc, qf, kf, vfr, pfr, l_run[0], m_ref[0], sc, p0 + 1, p1, p1 - 1,
+                                         STREAM ? w.src.len1 : (1 << 30), uniform_ptr(w.src.k1), uniform_ptr(w.src.v1),
+                                         uniform_ptr(w.src.k2), uniform_ptr(w.src.v2), kring_b, vring_b, klane_b,
+                                         vlane_b, kc, vc, koff_b, voff_b, kmask, vmask);
                 } else {
+                    const int last = p1 - 1;
+                    for (int i = p0 + 1; i < p1; ++i) {
+                        if (!STREAM) {
+                            const bool kis = i + 3 < p1, vis = i + 2 < p1;
+                            if (kis) dma_k(i + 3, kslot(i + 3));
+                            if (vis) dma_v(i + 2, vslot(i + 2));
+                            tile_sync(kis, vis);
+                        } else {
+                            const int tk = tile_of(min(i + 3, last)) * BK, tv = tile_of(min(i + 2, last)) * BK;
 #pragma unroll
-                    for (int j = 0; j < Tile::PWK; ++j) kpart(j);
+                            for (int j = 0; j < Tile::PWK; ++j) tile.issue_k_at(j, w.src.krow(tk, D), kslot(i + 3), wave);
 #pragma unroll
-                    for (int j = 0; j < Tile::PWV; ++j) vpart(j);
+                            for (int j = 0; j < Tile::PWV; ++j) tile.issue_v_at(j, w.src.vrow(tv, D), vslot(i + 2), wave);
+                            tile_sync(true, true);
+                        }
+                    }
                 }
-                tile_sync(true, true);
-            };
-            if (p0 == 0) position(0, std::true_type{}, std::true_type{});
-            else position(p0, std::false_type{}, std::true_type{});
-            for (int i = p0 + 1; i < p1; ++i) position(i, std::false_type{}, std::false_type{});
+            }
+            if (wave_live) wide_flush<D>(SA[0], SB[0], oacc, kf, vfr, pfr);
+            wide_guard<D>(SA[0], SB[0], oacc);
         }
         bool over = false;
 #pragma unroll
@@ -476,7 +480,9 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
     float l_tot[QB];
     if (run(true, l_tot)) {
         // exact row maxima by a score-only sweep, as the reference of a second sweep
-        float mx[QB] = {-INFINITY, -INFINITY};
+        float mx[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) mx[qb] = -INFINITY;
         for (int i = p0; i < p1; ++i) {
             dma_k(i, kslot(0));
             dma_sync();
@@ -550,16 +556,16 @@ __global__ __launch_bounds__(256, 1) void attn_wide_kernel(const AttnArgs a) {
         if (tid == 0) a.split_cnt[w.split] = 0u;  // ready for the next launch
     }
 
-    if constexpr (EPI_ALL) wide_linear_and_merge<OT, D, NW>(a, w, smem, qw, wave, has_soft, has_lin, qf, oacc, m_ref, l_tot);
+    if constexpr (EPI_ALL) wide_linear_and_merge<OT, D, NW, QB>(a, w, smem, qw, wave, has_soft, has_lin, qf, oacc, m_ref, l_tot);
     else linear_and_merge<T, OT, D, QB, NT>(a, w, smem, qw, has_soft, has_lin, qf, oacc, m_ref, l_tot);
 }
 
 template <class OT, int D, bool STREAM>
 static hipError_t launch_wide_one(const AttnArgs& a, hipStream_t stream) {
-    constexpr int NW = 4, QB = 2;
+    constexpr int NW = kWideWaves, QB = kWideQB;
     constexpr size_t kLdsMax = 160 * 1024;
     using Tile = DmaTiles<D, NW>;
-    const size_t kv = (4 * (size_t)Tile::K_ELEMS + 3 * (size_t)Tile::V_ELEMS) * sizeof(bf16);
+    const size_t kv = (4 * (size_t)Tile::K_ELEMS + 4 * (size_t)Tile::V_ELEMS) * sizeof(bf16);
     const size_t epi_all = wide_epilogue_lds_bytes(D, a.Dphi, a.P);
     const bool all = epi_all <= kLdsMax;
     const size_t epi = all ? epi_all : epilogue_lds_bytes<bf16, D>(a.Dphi);
@@ -589,7 +595,7 @@ static hipError_t launch_wide_d(const AttnArgs& a, hipStream_t stream) {
 // 64-token tiles and a longer class exists (otherwise the grid is a single wave of equal
 // tiles and halves do not shorten it).  Sets a.split_per_xcd; returns the split count.
 int wide_split_plan(AttnArgs& a) {
-    constexpr int kSplitPerXcd = 8, NW = 4, QB = 2;
+    constexpr int kSplitPerXcd = 8, NW = kWideWaves, QB = kWideQB;
     a.split_per_xcd = 0;
     if (a.stream || a.linear_only || a.nchunks < 2) return 0;
     const int lk0 = (a.Tc < a.T ? a.Tc : a.T) * a.n;
@@ -599,10 +605,10 @@ int wide_split_plan(AttnArgs& a) {
     return attn_grid(b, NW * QB * 32);
 }
 
-// Scratch bytes of one split: two halves x 4 waves x 64 lanes x (O + reference + sum).
+// Scratch bytes of one split: two halves x waves x 64 lanes x (O + reference + sum).
 size_t wide_split_part_bytes(int D) {
-    const size_t nr = (size_t)(D / 32) * 2 * 16 + 4;
-    return 2 * 4 * 64 * nr * sizeof(float);
+    const size_t nr = (size_t)(D / 32) * kWideQB * 16 + 2 * kWideQB;
+    return 2 * (size_t)kWideWaves * 64 * nr * sizeof(float);
 }
 
 hipError_t launch_attn_wide(const AttnArgs& a, int out_dtype, hipStream_t stream) {

@@ -114,10 +114,14 @@ struct DmaTiles {
         if (may_miss && j >= NI) return;
         const uint32_t lds = lds_addr(dst + j * 512);
         // token of this lane's chunk (clamped to the window) and its segment; each
-        // segment is a uniform base, the lanes of the other one sit out (exec mask)
-        int g = t0 + (int)(off[i] / D);
+        // segment is a uniform base, the lanes of the other one sit out (exec mask).  The
+        // offset is opaque here, so these few instructions run where the copy is issued
+        // instead of being hoisted and held in registers across the whole sweep.
+        uint32_t o = off[i];
+        asm volatile("" : "+v"(o));
+        int g = t0 + (int)(o / D);
         if (CHECK) g = min(g, Lk - 1);
-        const uint32_t col = off[i] % D;
+        const uint32_t col = o % D;
         if (TWO && g >= len1) dma16_s(b2, ((uint32_t)(g - len1) * D + col) * (uint32_t)sizeof(T), lds);
         else dma16_s(b1, ((uint32_t)g * D + col) * (uint32_t)sizeof(T), lds);
     }
