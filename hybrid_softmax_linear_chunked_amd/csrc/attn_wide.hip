@@ -49,11 +49,12 @@ static constexpr int kWideWaves = 8, kWideQB = 1;
 // value products of the second key half of a sub-step run in the next one.
 // wide_pipe: one sub-step at the given V^T / K read addresses (FIRST: none deferred from a
 // previous one).  wide_flush: the deferred products of the last sub-step.  wide_loop: sweep
-// positions i0 .. iend-1 with the copy of K tile i+3 and V tile i+2 (clamped to the last tile
-// `last`; a streaming window's tiles come from segment 1 below token len1, else segment 2)
-// into the rings at LDS byte addresses kring / vring, lane read offsets klane / vlane; this
-// wave copies 1 KB chunks kc[j] / vc[j] of a tile from its lane offsets koff[j] / voff[j], the
-// last under kmask / vmask where waves issue unequal counts.
+// positions i0 .. iend-1 (ring slots counted from position i0 - 1) with the copy of K tile i+3
+// and V tile i+2 into the rings at LDS byte addresses kring / vring, lane read offsets klane /
+// vlane.  The copies start at tokens kt0 / vt0 of the window (64 more per position, held at the
+// last tile's ktl; a streaming window's tiles come from segment 1 below token len1, else from
+// segment 2); this wave copies 1 KB chunks to kcr[j] / vcr[j] (ring plus chunk offset) from its
+// lane offsets koff[j] / voff[j], the last under kmask / vmask where waves issue unequal counts.
 #define WIDE_PIPE_ARGS(D)                                                                           \
     f32x16 &sa, f32x16 &sb, f32x16(&o)[D / 32][1], const bf16x8(&q)[1][D / 16], bf16x8(&k)[D / 16], \
         bf16x8(&vf)[D / 16], bf16x8(&pf)[2], float &lsum, float m, float sc, uint32_t vaddr, uint32_t kaddr
@@ -61,10 +62,10 @@ static constexpr int kWideWaves = 8, kWideQB = 1;
     f32x16 &sa, f32x16 &sb, f32x16(&o)[D / 32][1], bf16x8(&k)[D / 16], bf16x8(&vf)[D / 16], bf16x8(&pf)[2]
 #define WIDE_LOOP_ARGS(D)                                                                                        \
     f32x16 &sa, f32x16 &sb, f32x16(&o)[D / 32][1], const bf16x8(&q)[1][D / 16], bf16x8(&k)[D / 16],              \
-        bf16x8(&vf)[D / 16], bf16x8(&pf)[2], float &lsum, float m, float sc, int i0, int iend, int last, int len1, \
-        const void *k1, const void *v1, const void *k2, const void *v2, uint32_t kring, uint32_t vring,             \
-        uint32_t klane, uint32_t vlane, const uint32_t(&kc)[3], const uint32_t(&vc)[3], const uint32_t(&koff)[3],   \
-        const uint32_t(&voff)[3], uint64_t kmask, uint64_t vmask
+        bf16x8(&vf)[D / 16], bf16x8(&pf)[2], float &lsum, float m, float sc, int i0, int iend, int kt0, int vt0,   \
+        int ktl, int len1, const void *k1, const void *v1, const void *k2, const void *v2, uint32_t kring,           \
+        uint32_t vring, uint32_t klane, uint32_t vlane, const uint32_t(&kcr)[3], const uint32_t(&vcr)[3],            \
+        const uint32_t(&koff)[3], const uint32_t(&voff)[3], uint64_t kmask, uint64_t vmask
 template <int D, int PAR, bool FIRST>
 __device__ inline void wide_pipe(WIDE_PIPE_ARGS(D));
 template <int D>
@@ -283,8 +284,10 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void attn_wide_kernel(const Att
     tile.init(wave, lane);
     const int vl = Tile::vlane(lane);
 
-    auto kslot = [&](int t) { return kring + (t & 3) * Tile::K_ELEMS; };
-    auto vslot = [&](int t) { return vring + (t & 3) * Tile::V_ELEMS; };
+    // ring slots count from the first sweep position p0 of this workgroup (the sweep loop has
+    // them at fixed offsets)
+    auto kslot = [&](int t) { return kring + ((t - p0) & 3) * Tile::K_ELEMS; };
+    auto vslot = [&](int t) { return vring + ((t - p0) & 3) * Tile::V_ELEMS; };
     // start the DMA of the K / V tile at sweep position i into the given slot (completion:
     // vmcnt + barrier)
     auto dma_k = [&](int i, T* dst) {
@@ -357,8 +360,8 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void attn_wide_kernel(const Att
     static_assert(QB == 1, "the sub-step assembly holds one 32-query block per wave");
     const uint32_t kring_b = lds_addr(kring), vring_b = lds_addr(vring);
     const uint32_t klane_b = (uint32_t)((col * Tile::KLD + h * 8) * 2), vlane_b = (uint32_t)(vl * 2);
-    auto kslot_b = [&](int t) { return kring_b + (uint32_t)((t & 3) * Tile::K_ELEMS * 2); };
-    auto vslot_b = [&](int t) { return vring_b + (uint32_t)((t & 3) * Tile::V_ELEMS * 2); };
+    auto kslot_b = [&](int t) { return kring_b + (uint32_t)(((t - p0) & 3) * Tile::K_ELEMS * 2); };
+    auto vslot_b = [&](int t) { return vring_b + (uint32_t)(((t - p0) & 3) * Tile::V_ELEMS * 2); };
     typename M::frag kf[NS], vfr[NS], pfr[2];
     auto substep = [&](int u, auto par_tag, auto first_tag, bool mask) {
         constexpr int PAR = decltype(par_tag)::value;
@@ -379,6 +382,11 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void attn_wide_kernel(const Att
     uint64_t kmask, vmask;
     copy_share<Tile::NIK, Tile::PWK, NW>(wave, tile.koff, kc, koff_b, kmask);
     copy_share<Tile::NIV, Tile::PWV, NW>(wave, tile.voff, vc, voff_b, vmask);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        kc[j] += kring_b;
+        vc[j] += vring_b;
+    }
 
     // one sweep of the window with the current reference; returns the row sums
     auto run = [&](bool first, float (&l_tot)[QB]) {
@@ -442,7 +450,10 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void attn_wide_kernel(const Att
             }
             if (p0 + 1 < p1) {
                 if (wave_live) {
-                    wide_loop<D, STREAM>(SA[0], SB[0], oacc, qf, kf, vfr, pfr, l_run[0], m_ref[0], sc, p0 + 1, p1, p1 - 1,
+                    // first tokens of the tiles the first loop position copies (tile_of(x) = x - 1 there)
+                    const int last = p1 - 1;
+                    wide_loop<D, STREAM>(SA[0], SB[0], oacc, qf, kf, vfr, pfr, l_run[0], m_ref[0], sc, p0 + 1, p1,
+                                         (min(p0 + 4, last) - 1) * BK, (min(p0 + 3, last) - 1) * BK, (last - 1) * BK,
                                          STREAM ? w.src.len1 : (1 << 30), uniform_ptr(w.src.k1), uniform_ptr(w.src.v1),
                                          uniform_ptr(w.src.k2), uniform_ptr(w.src.v2), kring_b, vring_b, klane_b,
                                          vlane_b, kc, vc, koff_b, voff_b, kmask, vmask);

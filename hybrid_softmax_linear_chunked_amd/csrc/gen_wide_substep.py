@@ -357,46 +357,49 @@ def cxx_flush(D):
 
 
 def cxx_loop(D, stream, no_barrier=False, no_dma=False):
-    """The steady-state loop over sweep positions i0 .. iend-1 (pipelined sub-steps 2i, 2i+1;
-    the deferred value products of sub-step 2*i0-1 are pending on entry, those of the last
-    sub-step on exit).  no_barrier / no_dma: variants for timing the loop's parts."""
+    """The steady-state loop over sweep positions i0 .. iend-1, unrolled by the four ring slots.
+    Slots count from the workgroup's first position p0 = i0 - 1 (position i uses V^T slot
+    (i - p0) & 3, reads K of the next tile from slot (i - p0 + 1) & 3, and copies K of tile i+3
+    into slot (i - p0 + 3) & 3 and V of tile i+2 into (i - p0 + 2) & 3), so the four unrolled
+    positions have fixed slot offsets.  The copy sources run as token counters kt, vt (first
+    tokens of the tiles to copy, 64 more per position, held at the last tile `ktl`); a
+    streaming window's tile lies below token len1 in segment 1, else in segment 2.  Pipelined
+    sub-steps: the deferred value products of sub-step 2*i0 - 1 are pending on entry, those of
+    the last sub-step on exit.  no_barrier / no_dma: variants for timing the loop's parts."""
     L = layout(D)
     R = L["reg"]
     b = Block()
     K1, V1, K2, V2, KB, VB = SP, SP + 2, SP + 4, SP + 6, SP + 8, SP + 10
     s = lambda i: f"s{i}"
-    VA, KA = R["T"] + 4, R["T"] + 5
+    VA0, VA2, KA = R["T"] + 4, R["T"] + 5, R["T"] + 6
     tok_shift = {128: 8, 64: 7, 32: 6}[D]   # bytes per token row = 2 D = 1 << tok_shift
+    KB_, VB_ = L["K_BYTES"], L["V_BYTES"]
 
-    def tile_src(which, ahead, dst):
-        # source of the copy at position i: tile min(i + ahead, last) - 1, 64 tokens each
+    def tile_src(which, dst):
+        tok = "%[kt]" if which == "k" else "%[vt]"
         src1, src2 = (K1, K2) if which == "k" else (V1, V2)
-        b.emit(f"s_add_i32 %[t0], %[i], {ahead}")
-        b.emit("s_min_i32 %[t0], %[t0], %[last]")
-        b.emit("s_add_i32 %[t0], %[t0], -1")
-        b.emit("s_lshl_b32 %[t0], %[t0], 6")               # first token of the tile
         if stream:
-            # tiles of a streaming window lie in one segment: [0, len1) or [len1, ..)
             # (the selects read SCC of the compare; the shift after them writes SCC)
-            b.emit("s_sub_i32 %[t1], %[t0], %[len1]")
-            b.emit("s_cmp_lt_i32 %[t0], %[len1]")
-            b.emit(f"s_cselect_b32 %[t1], %[t0], %[t1]")
+            b.emit(f"s_sub_i32 %[t1], {tok}, %[len1]")
+            b.emit(f"s_cmp_lt_i32 {tok}, %[len1]")
+            b.emit(f"s_cselect_b32 %[t1], {tok}, %[t1]")
             b.emit(f"s_cselect_b32 {s(dst)}, {s(src1)}, {s(src2)}")
             b.emit(f"s_cselect_b32 {s(dst + 1)}, {s(src1 + 1)}, {s(src2 + 1)}")
             b.emit(f"s_lshl_b32 %[t1], %[t1], {tok_shift}")
             b.emit(f"s_add_u32 {s(dst)}, {s(dst)}, %[t1]")
             b.emit(f"s_addc_u32 {s(dst + 1)}, {s(dst + 1)}, 0")
         else:
-            b.emit(f"s_lshl_b32 %[t1], %[t0], {tok_shift}")
+            b.emit(f"s_lshl_b32 %[t1], {tok}, {tok_shift}")
             b.emit(f"s_add_u32 {s(dst)}, {s(src1)}, %[t1]")
             b.emit(f"s_addc_u32 {s(dst + 1)}, {s(src1 + 1)}, 0")
 
-    def copy_ops(which, slot_reg):
+    def copy_ops(which, slot):
         if no_dma:
             return []
         pw = L["PWK"] if which == "k" else L["PWV"]
         ni = L["NIK"] if which == "k" else L["NIV"]
         src = KB if which == "k" else VB
+        off = slot * (KB_ if which == "k" else VB_)
         ops = []
         for j in range(pw):
             masked = (ni % NW != 0) and j == pw - 1
@@ -405,7 +408,7 @@ def cxx_loop(D, stream, no_barrier=False, no_dma=False):
                 out = []
                 if masked:
                     out += ["s_mov_b64 %[es], exec", f"s_mov_b64 exec, %[{which}mask]"]
-                out += [f"s_add_u32 m0, {slot_reg}, %[{which}c{j}]", "s_nop 0",
+                out += [f"s_add_u32 m0, %[{which}cr{j}], {off}", "s_nop 0",
                         f"global_load_lds_dwordx4 %[{which}off{j}], s[{src}:{src + 1}]"]
                 if masked:
                     out += ["s_mov_b64 exec, %[es]"]
@@ -413,64 +416,58 @@ def cxx_loop(D, stream, no_barrier=False, no_dma=False):
             ops.append(op)
         return ops
 
-    def k_address(reg, ahead_expr):
-        # reg = klane + kring + ((i + ahead) & 3) * K_BYTES
-        b.emit(f"s_add_i32 %[t1], %[i], {ahead_expr}")
-        b.emit("s_and_b32 %[t1], %[t1], 3")
-        b.emit(f"s_mulk_i32 %[t1], {L['K_BYTES']}")
-        b.emit("s_add_i32 %[t1], %[t1], %[kring]")
-        b.valu(reg, [], text=f"v_add_u32 {v(reg)}, %[t1], %[klane]")
-
     b.emit("s_mov_b32 %[m0s], m0")
     b.emit("s_mov_b32 %[i], %[i0]")
-    b.emit("1:")
-    # position i: copy sources and slots (K of tile i+3 into slot (i+3) & 3, V of i+2 into (i+2) & 3)
-    tile_src("k", 3, KB)
-    tile_src("v", 2, VB)
-    b.emit("s_add_i32 %[t0], %[i], 3")
-    b.emit("s_and_b32 %[t0], %[t0], 3")
-    b.emit(f"s_mulk_i32 %[t0], {L['K_BYTES']}")
-    b.emit("s_add_i32 %[ks], %[t0], %[kring]")
-    b.emit("s_add_i32 %[t0], %[i], 2")
-    b.emit("s_and_b32 %[t0], %[t0], 3")
-    b.emit(f"s_mulk_i32 %[t0], {L['V_BYTES']}")
-    b.emit("s_add_i32 %[vs], %[t0], %[vring]")
-    # operand read addresses: V^T of tile i (slot i & 3), K of tile i+1 (slot (i+1) & 3)
-    b.emit("s_and_b32 %[t0], %[i], 3")
-    b.emit(f"s_mulk_i32 %[t0], {L['V_BYTES']}")
-    b.emit("s_add_i32 %[t0], %[t0], %[vring]")
-    b.valu(VA, [], text=f"v_add_u32 {v(VA)}, %[t0], %[vlane]")
-    k_address(KA, 1)
+    b.emit("s_mov_b32 %[kt], %[kt0]")
+    b.emit("s_mov_b32 %[vt], %[vt0]")
+    # operand read bases: V^T slots 0-1 and 2-3 (offsets stay below 64 KB), K
+    b.valu(VA0, [], text=f"v_add_u32 {v(VA0)}, %[vring], %[vlane]")
+    b.emit(f"s_add_u32 %[t0], %[vring], {2 * VB_}")
+    b.valu(VA2, [], text=f"v_add_u32 {v(VA2)}, %[t0], %[vlane]")
+    b.valu(KA, [], text=f"v_add_u32 {v(KA)}, %[kring], %[klane]")
     b.emit("s_nop 1")
     vx, kx = 32 * L["VLD"] * 2, 32 * L["KLD"] * 2
-    pipe_substep(b, L, 0, v(VA), v(KA), 0, 0, copy_ops("k", "%[ks]"))
-    pipe_substep(b, L, 1, v(VA), v(KA), vx, kx, copy_ops("v", "%[vs]"))
-    b.wait_all_lds()
-    # the copies issued one position earlier are complete in every wave
-    nmin = 0 if no_dma else L["NIK"] // NW + L["NIV"] // NW
-    b.emit(f"s_waitcnt vmcnt({nmin})")
-    if not no_barrier:
-        b.emit("s_barrier")
-    b.emit("s_add_i32 %[i], %[i], 1")
-    b.emit("s_cmp_lt_i32 %[i], %[iend]")
-    b.emit("s_cbranch_scc1 1b")
+    b.emit("1:")
+    for ph in (1, 2, 3, 0):
+        # position i with (i - p0) & 3 = ph
+        tile_src("k", KB)
+        tile_src("v", VB)
+        va = v(VA0) if ph < 2 else v(VA2)
+        vo = (ph % 2) * VB_
+        ko = ((ph + 1) & 3) * KB_
+        pipe_substep(b, L, 0, va, v(KA), vo, ko, copy_ops("k", (ph + 3) & 3))
+        pipe_substep(b, L, 1, va, v(KA), vo + vx, ko + kx, copy_ops("v", (ph + 2) & 3))
+        b.wait_all_lds()
+        # the copies issued one position earlier are complete in every wave
+        nmin = 0 if no_dma else L["NIK"] // NW + L["NIV"] // NW
+        b.emit(f"s_waitcnt vmcnt({nmin})")
+        if not no_barrier:
+            b.emit("s_barrier")
+        b.emit("s_add_i32 %[kt], %[kt], 64")
+        b.emit("s_min_i32 %[kt], %[kt], %[ktl]")
+        b.emit("s_add_i32 %[vt], %[vt], 64")
+        b.emit("s_min_i32 %[vt], %[vt], %[ktl]")
+        b.emit("s_add_i32 %[i], %[i], 1")
+        b.emit("s_cmp_lt_i32 %[i], %[iend]")
+        b.emit("s_cbranch_scc0 2f" if ph != 0 else "s_cbranch_scc1 1b")
+    b.emit("2:")
     b.emit("s_mov_b32 m0, %[m0s]")
 
     outs = pinned_outs(L) + pinned_vp(L) + ['[m0s] "=&s"(m0s)', '[i] "=&s"(it)', '[t0] "=&s"(t0)', '[t1] "=&s"(t1)',
-                                            '[ks] "=&s"(ks)', '[vs] "=&s"(vs)', '[es] "=&s"(es)']
+                                            '[kt] "=&s"(kt)', '[vt] "=&s"(vt)', '[es] "=&s"(es)']
     ins = pinned_ins(L) + [
-        '[i0] "s"(i0)', '[iend] "s"(iend)', '[last] "s"(last)', '[len1] "s"(len1)',
+        '[i0] "s"(i0)', '[iend] "s"(iend)', '[kt0] "s"(kt0)', '[vt0] "s"(vt0)', '[ktl] "s"(ktl)', '[len1] "s"(len1)',
         f'[k1] "{{s[{K1}:{K1 + 1}]}}"(k1)', f'[v1] "{{s[{V1}:{V1 + 1}]}}"(v1)',
         f'[k2] "{{s[{K2}:{K2 + 1}]}}"(k2)', f'[v2] "{{s[{V2}:{V2 + 1}]}}"(v2)',
         '[kring] "s"(kring)', '[vring] "s"(vring)', '[klane] "v"(klane)', '[vlane] "v"(vlane)',
-        '[kc0] "s"(kc[0])', '[kc1] "s"(kc[1])', '[kc2] "s"(kc[2])',
-        '[vc0] "s"(vc[0])', '[vc1] "s"(vc[1])', '[vc2] "s"(vc[2])',
+        '[kcr0] "s"(kcr[0])', '[kcr1] "s"(kcr[1])', '[kcr2] "s"(kcr[2])',
+        '[vcr0] "s"(vcr[0])', '[vcr1] "s"(vcr[1])', '[vcr2] "s"(vcr[2])',
         '[koff0] "v"(koff[0])', '[koff1] "v"(koff[1])', '[koff2] "v"(koff[2])',
         '[voff0] "v"(voff[0])', '[voff1] "v"(voff[1])', '[voff2] "v"(voff[2])',
         '[kmask] "s"(kmask)', '[vmask] "s"(vmask)']
     clob = tclobbers(L) + [f'"s{i}"' for i in range(KB, KB + 4)] + ['"scc"', '"memory"']
     return (f"template <> __device__ inline void wide_loop<{D}, {str(stream).lower()}>(WIDE_LOOP_ARGS({D})) {{\n"
-            "    uint32_t m0s, it, t0, t1, ks, vs;\n    uint64_t es;\n"
+            "    uint32_t m0s, it, t0, t1, kt, vt;\n    uint64_t es;\n"
             + asm_stmt(b.lines, outs, ins, clob, L["reg"]["END"]) + "}\n")
 
 

@@ -177,22 +177,46 @@ def test_pipelined_sweep_dataflow(D):
 
 
 @pytest.mark.parametrize("D", [32, 64, 128])
-def test_loop_copies_and_waits(D):
-    # the loop body issues this wave's share of one K and one V tile copy, waits for the
-    # previous position's copies with the count of the wave with the fewest, and meets the
-    # barrier once per position; every LDS read is waited for before the position ends
+@pytest.mark.parametrize("stream", [False, True])
+def test_loop_copies_slots_and_waits(D, stream):
+    # The loop body holds the four ring phases of a sweep position (slots counted from the
+    # workgroup's first position p0; the loop starts at p0 + 1, phase 1).  Each position issues
+    # this wave's share of one K and one V tile copy, into slots (ph + 3) & 3 and (ph + 2) & 3,
+    # reads V^T of slot ph and K of slot (ph + 1) & 3, waits for the previous position's copies
+    # with the count of the wave with the fewest, waits for every LDS read, and meets the
+    # barrier once.
     L = g.layout(D)
-    text = g.cxx_loop(D, False)
+    text = g.cxx_loop(D, stream)
     body = re.search(r'asm volatile\("(.*?)"\n', text, re.S).group(1).split("\\n\\t")
-    copies = [l for l in body if l.startswith("global_load_lds_dwordx4")]
-    assert len(copies) == L["PWK"] + L["PWV"]
-    assert body.count("s_barrier") == 1
-    vm = [l for l in body if l.startswith("s_waitcnt vmcnt")]
-    assert vm == [f"s_waitcnt vmcnt({L['NIK'] // g.NW + L['NIV'] // g.NW})"]
-    i_bar = body.index("s_barrier")
-    assert "s_waitcnt lgkmcnt(0)" in body[:i_bar]
-    last_lds = max(i for i, l in enumerate(body) if l.startswith("ds_read"))
-    assert any(l == "s_waitcnt lgkmcnt(0)" for l in body[last_lds:i_bar])
+    start = body.index("1:")
+    bars = [i for i, l in enumerate(body) if l == "s_barrier"]
+    assert len(bars) == 4
+    KB, VB = L["K_BYTES"], L["V_BYTES"]
+    VX, KX = 32 * L["VLD"] * 2, 32 * L["KLD"] * 2
+    R = L["reg"]
+    VA0, VA2, KA = R["T"] + 4, R["T"] + 5, R["T"] + 6
+    prev = start
+    for ph, bar in zip((1, 2, 3, 0), bars):
+        pos = body[prev:bar]
+        m0 = [l for l in pos if l.startswith("s_add_u32 m0")]
+        assert len(m0) == L["PWK"] + L["PWV"]
+        assert all(l.endswith(f", {((ph + 3) & 3) * KB}") for l in m0[:L["PWK"]]), m0
+        assert all(l.endswith(f", {((ph + 2) & 3) * VB}") for l in m0[L["PWK"]:]), m0
+        vreads = [l for l in pos if l.startswith("ds_read_b64_tr_b16")]
+        base = f"v{VA0}" if ph < 2 else f"v{VA2}"
+        for l in vreads:
+            off = int(l.rsplit("offset:", 1)[1])
+            assert f", {base} " in l and (ph % 2) * VB <= off < (ph % 2) * VB + VB, l
+        kreads = [l for l in pos if l.startswith("ds_read_b128")]
+        for l in kreads:
+            off = int(l.rsplit("offset:", 1)[1])
+            k0 = ((ph + 1) & 3) * KB
+            assert f", v{KA} " in l and k0 <= off < k0 + KB, l
+        assert len(vreads) == 2 * 2 * L["NV"] and len(kreads) == 2 * L["NS"]
+        tail = body[max(i for i, l in enumerate(body[:bar]) if l.startswith("ds_read")):bar]
+        assert "s_waitcnt lgkmcnt(0)" in tail
+        assert body[bar - 1] == f"s_waitcnt vmcnt({L['NIK'] // g.NW + L['NIV'] // g.NW})"
+        prev = bar
 
 
 def test_generated_file_is_current():
