@@ -21,11 +21,12 @@ LIB_PATH = os.path.join(_PKG, "librehyat.so")
 
 FP32, BF16 = 0, 1
 _STATUS = {0: "REHYAT_OK", 1: "REHYAT_EINVAL", 2: "REHYAT_ESHAPE", 3: "REHYAT_EALIGN",
-           4: "REHYAT_EWORKSPACE", 5: "REHYAT_ESTATE", 6: "REHYAT_EHIP"}
+           4: "REHYAT_EWORKSPACE", 5: "REHYAT_ESTATE", 6: "REHYAT_EHIP", 7: "REHYAT_ESCRATCH"}
 
 EXPORTS = (
     "rehyat_status_string", "rehyat_features", "rehyat_phi", "rehyat_workspace_bytes",
-    "rehyat_forward_parallel", "rehyat_forward_parallel_aux", "rehyat_state_bytes",
+    "rehyat_forward_parallel", "rehyat_forward_parallel_aux", "rehyat_forward_parallel_noalloc",
+    "rehyat_state_bytes",
     "rehyat_stream_workspace_bytes", "rehyat_state_init", "rehyat_chunk_step",
     "rehyat_parallel_states", "rehyat_parallel_attend", "rehyat_distill_workspace_bytes",
     "rehyat_distill_loss", "rehyat_distill_grad_workspace_bytes", "rehyat_distill_grad",
@@ -78,6 +79,8 @@ def lib():
             getattr(L, name).restype = ctypes.c_size_t
         L.rehyat_forward_parallel.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.rehyat_forward_parallel.restype = ctypes.c_int
+        L.rehyat_forward_parallel_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.rehyat_forward_parallel_noalloc.restype = ctypes.c_int
         L.rehyat_forward_parallel_aux.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp,
                                                   ctypes.POINTER(_CAux), vp, ctypes.c_size_t, vp]
         L.rehyat_forward_parallel_aux.restype = ctypes.c_int
@@ -201,6 +204,29 @@ def phi(p: Params, x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor
     _check(out, (p.B, p.H, p.N, p.F), dt, "out")
     _raise(lib().rehyat_phi(ctypes.byref(p.c()), _ptr(x), _ptr(w), _ptr(bias), _ptr(out),
                             _stream_handle()), "rehyat_phi")
+    return out
+
+
+def forward_parallel_noalloc(p: Params, q, k, v, wq, wk, bq=None, bk=None, out=None):
+    """rehyat_forward_parallel_noalloc: the chunk-parallel forward with the library's static
+    scratch area as workspace (64 MiB per GPU; raises REHYAT_ESCRATCH beyond).  Calls on one
+    GPU that overlap race on that area."""
+    dt = torch_dtype(p.in_dtype)
+    shape = (p.B, p.H, p.N, p.D)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, shape, dt, name)
+    for name, t in (("wq", wq), ("wk", wk)):
+        _check(t, (p.H, p.Dphi, p.D), dt, name)
+    for name, t in (("bq", bq), ("bk", bk)):
+        if t is not None:
+            _check(t, (p.H, p.Dphi), torch.float32, name)
+    if out is None:
+        out = torch.empty(shape, dtype=torch_dtype(p.out_dtype), device=q.device)
+    _check(out, shape, torch_dtype(p.out_dtype), "out")
+    c = p.c()
+    _raise(lib().rehyat_forward_parallel_noalloc(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk),
+                                                 _ptr(bq), _ptr(bk), _ptr(out), _stream_handle()),
+           "rehyat_forward_parallel_noalloc")
     return out
 
 

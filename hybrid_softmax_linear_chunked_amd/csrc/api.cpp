@@ -165,6 +165,7 @@ const char* rehyat_status_string(rehyat_status s) {
         case REHYAT_EWORKSPACE: return "workspace missing or too small";
         case REHYAT_ESTATE: return "invalid streaming state or call";
         case REHYAT_EHIP: return "HIP launch error";
+        case REHYAT_ESCRATCH: return "workspace exceeds the static scratch area (64 MiB per GPU)";
     }
     return "unknown status";
 }

@@ -51,7 +51,9 @@ typedef enum {
     REHYAT_EALIGN = 3,     /* a required pointer is NULL or not 16-byte aligned */
     REHYAT_EWORKSPACE = 4, /* workspace pointer NULL or ws_bytes below the required size */
     REHYAT_ESTATE = 5,     /* streaming misuse: frames out of range, stream closed, bad handle */
-    REHYAT_EHIP = 6        /* a kernel launch failed */
+    REHYAT_EHIP = 6,       /* a kernel launch failed */
+    REHYAT_ESCRATCH = 7    /* rehyat_forward_parallel_noalloc: the call needs more workspace than
+                              the library's static scratch area (64 MiB per GPU) */
 } rehyat_status;
 
 typedef enum { REHYAT_FP32 = 0, REHYAT_BF16 = 1 } rehyat_dtype;
@@ -115,6 +117,20 @@ rehyat_status rehyat_forward_parallel(const rehyat_params* p, const void* q, con
                                       const void* v, const void* wq, const void* wk,
                                       const float* bq, const float* bk, void* out, void* ws,
                                       size_t ws_bytes, hipStream_t stream);
+
+/* rehyat_forward_parallel without a caller workspace, for callers that cannot allocate
+ * device memory (code under graph capture, serving loops, harnesses that forbid allocation).
+ * The workspace is a static area of the library, 64 MiB on every GPU it runs on, held until
+ * the process ends; the call allocates nothing (its first call on a device looks the area up).
+ * Same operation, arguments (without ws, ws_bytes), layouts and results as
+ * rehyat_forward_parallel.  REHYAT_ESCRATCH when rehyat_workspace_bytes(p) exceeds 64 MiB
+ * (for example the 20 s, B = 2 layer; the 5 s Wan2.1-1.3B layer needs about 50 MB), before
+ * any launch.  Every call on a GPU uses the same area: calls that overlap on one GPU (other
+ * streams, other host threads) race; calls in stream order do not. */
+rehyat_status rehyat_forward_parallel_noalloc(const rehyat_params* p, const void* q, const void* k,
+                                              const void* v, const void* wq, const void* wk,
+                                              const float* bq, const float* bk, void* out,
+                                              hipStream_t stream);
 
 /* Same as rehyat_forward_parallel, also writing the per-part outputs that are non-NULL
  * in *aux (aux itself may be NULL). */
