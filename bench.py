@@ -15,8 +15,10 @@ streaming form with its peak memory at 21/41/81 frames, the chunking and feature
 variants the pages discuss (Tc/To presets and ablations, higher polynomial degree) on the
 same inputs, the distillation objective (hybrid vs full-softmax teacher, squared L2 per
 slab) and its gradients with respect to the feature-map weights, the backward for an
-upstream gradient (dq, dk, dv and the feature-map gradients), and the CPU oracle timed on a bounded sample of the same workload (which
-also serves as a parity spot check).
+upstream gradient (dq, dk, dv and the feature-map gradients), the 20 s clip at batch 2 and
+the 14B-shaped 720x1280 layer with P = 3 (each with its own oracle sample and spot check),
+and the CPU oracle timed on a bounded sample of the same workload (which also serves as a
+parity spot check).
 """
 from __future__ import annotations
 
@@ -37,6 +39,14 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "hybrid-attn tokens/s & TFLOP/s (% bf16 MFMA peak), 32760-token 12-head layer"
 KERNEL_SOURCES = ["attn_wide.hip", "attn_common.hpp", "dma.hpp", "tiles.hpp", "common.hpp", "kernels.hpp"]
 COUNTER_FILE = os.path.join(ROOT, "profiles", "attn_kernel_wan_5s_counters.txt")
+
+
+LEGS = ("comparator", "stream", "variants", "distill_loss", "distill_grad", "backward", "wan_20s", "wan14b_720p")
+
+
+def progress(msg):
+    """One line per finished leg on stderr, so that a long run shows it is alive."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def schedule(T, Tc, To, linear_only=0):
@@ -126,7 +136,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the comparator and streaming legs")
+    ap.add_argument("--no-extras", action="store_true", help="skip every leg after the main step")
+    ap.add_argument("--legs", default="all",
+                    help="comma-separated legs to run after the main step (comparator, stream, variants, "
+                         "distill_loss, distill_grad, backward, wan_20s, wan14b_720p), or all")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 dispatches): the reference for scaling "
                          "the FETCH_SIZE / WRITE_SIZE counters")
@@ -208,7 +221,16 @@ def main():
                      "algorithmic_flops_per_launch": fl["attn_kernel"]},
     }
 
-    if not args.no_extras:
+    want = set(LEGS) if args.legs == "all" else set(args.legs.split(","))
+    if args.no_extras:
+        want = set()
+    unknown = want - set(LEGS)
+    if unknown:
+        print(f"unknown legs: {sorted(unknown)}", file=sys.stderr)
+        sys.exit(2)
+    if "distill_grad" in want:
+        want.add("distill_loss")
+    if "comparator" in want:
         # full-softmax comparator: the same tile kernel with one window over all frames
         pc = p.with_(Tc=w.T)
         outc = torch.empty_like(out)
@@ -226,17 +248,77 @@ def main():
         res["full_softmax_comparator"] = {"ms": round(cms, 3), "tflops": round(cfl / (cms * 1e-3) / 1e12, 2),
                                           "speedup_of_hybrid": round(cms / ms, 2)}
         del outc
-        res["stream"] = stream_leg(rh, torch, WORKLOADS["wan_10s_stream"], dev)
-        res["variants"] = variants_leg(rh, torch, p, d, ms)
-        res["distill_loss"] = distill_leg(rh, torch, p, d, w)
-        res["distill_grad"] = distill_grad_leg(rh, torch, p, d, w, res["distill_loss"]["ms"])
-        res["backward"] = backward_leg(rh, torch, p, d, w, ms)
+    if want:
+        legs = [("stream", lambda: stream_leg(rh, torch, WORKLOADS["wan_10s_stream"], dev)),
+                ("variants", lambda: variants_leg(rh, torch, p, d, ms)),
+                ("distill_loss", lambda: distill_leg(rh, torch, p, d, w)),
+                ("distill_grad", lambda: distill_grad_leg(rh, torch, p, d, w, res["distill_loss"]["ms"])),
+                ("backward", lambda: backward_leg(rh, torch, p, d, w, ms))]
+        for name, seed in (("wan_20s", 3), ("wan14b_720p", 4)):
+            legs.append((name, lambda name=name, seed=seed: workload_leg(
+                rh, torch, WORKLOADS[name], seed, dev, with_cpu=not args.no_cpu_baseline)))
+        for name, leg in legs:
+            if name not in want:
+                continue
+            t0 = time.perf_counter()
+            res[name] = leg()
+            progress(f"{name} leg done in {time.perf_counter() - t0:.1f} s")
 
     if not args.no_cpu_baseline:
         cb, parity = cpu_baseline(w, x, out)
         res["cpu_baseline"] = cb
         res["parity_spot_check"] = parity
+        progress("cpu baseline done")
     print(json.dumps(res), flush=True)
+
+
+def workload_leg(rh, torch, w, seed, dev, with_cpu=True, reps=5):
+    """Chunk-parallel forward of a further measured workload (the 20 s clip at batch 2, the
+    14B-shaped layer with P = 3) on its own seeded inputs: ms per forward, state/scan and
+    attention stages, tokens/s, TFLOP/s of the FLOP model and fractions of the bf16 peak;
+    then the CPU oracle on a bounded sample of it, which is also a parity spot check."""
+    from synth_inputs import make_inputs
+    p = rh.Params(w.B, w.H, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P, 0, rh.BF16, rh.BF16)
+    x = make_inputs(w, seed=seed)
+    d = {key: torch.from_numpy(val).to(dev, torch.bfloat16).contiguous() for key, val in x.items()}
+    out = torch.empty((p.B, p.H, p.N, p.D), dtype=torch.bfloat16, device=dev)
+    ws = rh.alloc_bytes(rh.workspace_bytes(p), dev)
+
+    def step(ev_mid=None):
+        rh.parallel_states(p, d["k"], d["v"], d["wk"], None, ws)
+        if ev_mid is not None:
+            ev_mid.record()
+        rh.parallel_attend(p, d["q"], d["k"], d["v"], d["wq"], None, out, ws)
+
+    step()
+    step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for e in ev:
+        e[0].record()
+        step(e[1])
+        e[2].record()
+    torch.cuda.synchronize()
+    ms = sum(e[0].elapsed_time(e[2]) for e in ev) / reps
+    state_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / reps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / reps
+    fl = flop_model(w.B, w.H, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P)
+    tf = fl["total"] / (ms * 1e-3) / 1e12
+    atf = fl["attn_kernel"] / (attn_ms * 1e-3) / 1e12
+    res = {"workload": w.name, "B": w.B, "heads": w.H, "frames": w.T, "frame_tokens": w.n,
+           "tokens_per_sample": w.N, "Tc": w.Tc, "To": w.To, "Dphi": w.Dphi, "P": w.P,
+           "ms": round(ms, 4), "stages_ms": {"state_and_scan": round(state_ms, 4), "attn_kernel": round(attn_ms, 4)},
+           "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1), "tflops": round(tf, 2),
+           "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+           "attn_kernel_frac_of_bf16_peak": round(atf / PEAK_BF16_TFLOPS, 4), "flops": fl["total"]}
+    del ws, d
+    if with_cpu:
+        cb, parity = cpu_baseline(w, x, out, budget_s=6.0)
+        res["cpu_baseline"] = cb
+        res["parity_spot_check"] = parity
+    del out, x
+    torch.cuda.empty_cache()
+    return res
 
 
 # chunking and feature-map variants the pages discuss (ReHyAt blog 3.2, 5.2, 5.3, 6;
@@ -253,20 +335,26 @@ def variants_leg(rh, torch, p, d, base_ms, reps=5):
         pv = p.with_(**kw)
         ws = rh.alloc_bytes(rh.workspace_bytes(pv), d["q"].device)
         out = torch.empty((p.B, p.H, p.N, p.D), dtype=torch.bfloat16, device=d["q"].device)
-        call = lambda: rh.forward_parallel(pv, d["q"], d["k"], d["v"], d["wq"], d["wk"], out=out, ws=ws)
+
+        def call(ev_mid=None):
+            rh.parallel_states(pv, d["k"], d["v"], d["wk"], None, ws)
+            if ev_mid is not None:
+                ev_mid.record()
+            rh.parallel_attend(pv, d["q"], d["k"], d["v"], d["wq"], None, out, ws)
         call()
         call()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            call()
-        e1.record()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        for e in ev:
+            e[0].record()
+            call(e[1])
+            e[2].record()
         torch.cuda.synchronize()
-        vms = e0.elapsed_time(e1) / reps
+        vms = sum(e[0].elapsed_time(e[2]) for e in ev) / reps
+        sms = sum(e[0].elapsed_time(e[1]) for e in ev) / reps
         fl = flop_model(pv.B, pv.H, pv.D, pv.T, pv.n, pv.Tc, pv.To, pv.Dphi, pv.P)["total"]
         tf = fl / (vms * 1e-3) / 1e12
-        res[name] = {"Tc": pv.Tc, "To": pv.To, "P": pv.P, "ms": round(vms, 4),
+        res[name] = {"Tc": pv.Tc, "To": pv.To, "P": pv.P, "ms": round(vms, 4), "state_and_scan_ms": round(sms, 4),
                      "tokens_per_s": round(pv.B * pv.N / (vms * 1e-3), 1), "tflops": round(tf, 2),
                      "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2), "flops": fl}
         del ws, out

@@ -72,12 +72,14 @@ __device__ inline void dma16_s_if(const void* gbase, uint32_t voff, uint32_t lds
 // DMA instruction is active and the per-tile work is a uniform base plus fixed lane
 // offsets.  Tokens past the end (ragged last tile) are clamped to the last token: the
 // consumer masks their contributions, so only finite values are needed there.
-template <int D, int NW>
+// VLD_ overrides the V row length for readers with another access pattern (0: the
+// default above).
+template <int D, int NW, int VLD_ = 0>
 struct DmaTiles {
     using T = bf16;
     static constexpr int BK = 64;
     static constexpr int KLD = D + 8;
-    static constexpr int VLD = D == 128 ? 160 : D == 64 ? 96 : 32;
+    static constexpr int VLD = VLD_ ? VLD_ : D == 128 ? 160 : D == 64 ? 96 : 32;
     static constexpr int CPK = KLD / 8, CPV = VLD / 8;  // 16-byte chunks per row
     static constexpr int NIK = BK * CPK / 64, NIV = BK * CPV / 64;  // DMA instructions per tile
     static constexpr int PWK = (NIK + NW - 1) / NW, PWV = (NIV + NW - 1) / NW;

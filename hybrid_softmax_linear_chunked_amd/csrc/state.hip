@@ -6,9 +6,11 @@
 //   Delta_f = phi_k(K_f)^T V_f  (F x D)  and  sum_tokens phi_k(K_f)  (F),
 //   with phi computed on the fly: u = K W_k^T on MFMA (tokens x Dphi), softplus, powers,
 //   then Delta += phi^T V on MFMA with phi taken straight from the u registers (the C
-//   tile's rows are the tokens, which is the contraction of the second product).  Wave
-//   (jb, ts) owns the 32 phi rows j in block jb and the 32-token half ts of every 64-token
-//   tile; the two halves are summed through LDS in a fixed order at the end.
+//   tile's rows are the tokens, which is the contraction of the second product).  Two
+//   forms: state16_kernel (bf16 inputs: 16x16x32 products, each wave owning 16 phi rows
+//   over whole tiles, K/V moved by LDS-DMA) and state_kernel (float32 inputs: 32x32x2
+//   products, wave (jb, ts) owning the 32 phi rows of block jb and the 32-token half ts
+//   of every 64-token tile, the two halves summed through LDS in a fixed order).
 // scan_kernel: running sum over frame partials in frame order, either in place (prefix
 //   over the clip, chunk-parallel form) or added to a carried state (streaming form).
 //   Both forms add the same partials in the same order, so they agree bit for bit.
@@ -168,28 +170,53 @@ __global__ __launch_bounds__(StateShape<P>::NW * 64) void state_kernel(const Sta
     }
 }
 
-// bf16 form of state_kernel (P <= 2): the same per-(batch-head, frame) partials and wave roles, with
-// the K/V tiles moved to LDS by LDS-DMA two tiles ahead (ring of three) and the V operand
-// of phi^T V read with transposing LDS reads (see dma.hpp).  The frame's ragged last tile
-// is processed first, with the padded tokens given phi = 0, so full tiles carry no bounds
-// arithmetic.  Sums run in a fixed order, so the result does not depend on timing.
+// bf16 form of state_kernel: the same per-(batch-head, frame) partials on 16x16x32 bf16
+// products (v_mfma_f32_16x16x32_bf16; lane l = 16 g + a holds row a and contraction slots
+// 8 g .. 8 g + 7 of the A operand, column a and the same slots of B, and column a, rows
+// 4 g .. 4 g + 3 of C).  Wave w owns the 16 phi rows 16 w .. 16 w + 15 and takes every
+// token of a 64-token tile:
+//   u = K W_k^T: four C tiles of 16 tokens x 16 phi rows, lane (a, g) holding phi row a of
+//     tokens 16 tb + 4 g + i (i = 0..3); A = K rows from LDS, B = W_k rows in registers;
+//   Delta += phi^T V: the eight values of C tiles 2 c and 2 c + 1 in a lane are, as they
+//     stand, the A operand of contraction block c (tokens 32 c + 4 g + i in slots i and
+//     32 c + 16 + 4 g + i in slots 4 + i), and the V operand is read in the same slot
+//     order with two transposing LDS reads; one accumulator tile per (power, 16 d).
+// So the P x D/16 accumulator tiles of a wave hold 2 P D registers (P = 4 at D = 128: 128)
+// and no partial is exchanged between waves.  K/V tiles move to LDS by LDS-DMA three
+// tiles ahead (ring of four); V rows are D + 16 elements long, so the eight rows a
+// transposing read spans fall in eight different 32-byte bank groups.  The frame's ragged
+// last tile is processed first, with the padded tokens given phi = 0, so full tiles carry
+// no bounds arithmetic.  Sums run in a fixed order, so the result does not depend on
+// timing.
+constexpr int kState16Waves = 8;  // Dphi <= 128: 16 phi rows per wave
+constexpr int kState16Ring = 4;
+
+template <int D>
+using State16Tiles = DmaTiles<D, kState16Waves, D + 16>;
+
+__device__ inline f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 template <int D, int P>
-__global__ __launch_bounds__(StateShape<P>::NW * 64) void state_dma_kernel(const StateArgs a) {
+__global__ __launch_bounds__(kState16Waves * 64) void state16_kernel(const StateArgs a) {
     using T = bf16;
-    using M = Mfma<T>;
-    constexpr int TS = StateShape<P>::TS, NW = StateShape<P>::NW;
-    using Tile = DmaTiles<D, NW>;
-    constexpr int KS = M::KS, EPL = M::EPL, NS = D / KS, NDB = D / 32, TPB = 16 / EPL, BK = Tile::BK;
+    using Tile = State16Tiles<D>;
+    constexpr int NW = kState16Waves, R = kState16Ring, BK = Tile::BK;
+    constexpr int NS = D / 32;   // contraction steps of u
+    constexpr int ND = D / 16;   // 16-column blocks of Delta
+    constexpr int KLD = Tile::KLD, VLD = Tile::VLD;
+    static_assert(BK == 64, "four 16-token C tiles per tile");
 
     extern __shared__ __align__(16) unsigned char smem[];
     T* const kring = reinterpret_cast<T*>(smem);
-    T* const vring = kring + 3 * Tile::K_ELEMS;
+    T* const vring = kring + R * Tile::K_ELEMS;
 
     const int gi = blockIdx.x % a.G;
     const int bh = blockIdx.x / a.G;
     const int hh = bh % a.H;
     const int g = a.g0 + gi;
-    const int n = a.n, Dphi = a.Dphi, F = Dphi * P, NJB = Dphi / 32;
+    const int n = a.n, Dphi = a.Dphi, F = Dphi * P;
 
     KeySrc<T> src;
     if (g < a.nf1) {
@@ -206,38 +233,40 @@ __global__ __launch_bounds__(StateShape<P>::NW * 64) void state_dma_kernel(const
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform
     __builtin_assume(wave >= 0 && wave < NW);
-    const int lane = tid % 64, col = lane % 32, h = lane / 32;
-    const bool active = wave < TS * NJB;
-    const int jb = wave / TS, ts = wave % TS;
-    const int j = jb * 32 + col;  // this lane's phi row
+    const int lane = tid % 64, la = lane % 16, lg = lane / 16;
+    const bool active = wave * 16 < Dphi;
+    const int j = wave * 16 + la;  // this lane's phi row
 
-    typename M::frag wf[NS];
+    bf16x8 wf[NS];  // B operand of u: W_k row j, d = 32 s + 8 lg .. + 7
     float bias = 0.f;
     if (active) {
-        const T* wk = reinterpret_cast<const T*>(a.wk) + ((int64_t)hh * Dphi + j) * D;
+        const T* wk = reinterpret_cast<const T*>(a.wk) + ((int64_t)hh * Dphi + j) * D + 8 * lg;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) wf[s] = M::load(wk + s * KS + h * EPL);
+        for (int s = 0; s < NS; ++s) wf[s] = *reinterpret_cast<const bf16x8*>(wk + 32 * s);
         if (a.bk) bias = a.bk[(int64_t)hh * Dphi + j];
     }
 
-    f32x16 acc[P][NDB];
+    f32x4 acc[P][ND];
     float zacc[P];
 #pragma unroll
     for (int pw = 0; pw < P; ++pw) {
         zacc[pw] = 0.f;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[pw][db] = zero16();
+        for (int dc = 0; dc < ND; ++dc) acc[pw][dc] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     Tile tile;
     tile.init(wave, lane);
-    const int vl = Tile::vlane(lane);
+    // A operand of u: token 16 tb + la, d = 32 s + 8 lg; V operand: token 4 lg + la / 4 of
+    // the contraction block, d = 4 (la % 4) of the 16-column block
+    const int ka = la * KLD + 8 * lg;
+    const int va = (4 * lg + la / 4) * VLD + 4 * (la % 4);
     const int nt = (n + BK - 1) / BK;
     const int last_len = n - (nt - 1) * BK;
     const bool ragged = last_len < BK;
     auto tile_of = [&](int i) { return i == 0 ? nt - 1 : i - 1; };  // ragged tile first
-    auto kslot = [&](int i) { return kring + (i % 3) * Tile::K_ELEMS; };
-    auto vslot = [&](int i) { return vring + (i % 3) * Tile::V_ELEMS; };
+    auto kslot = [&](int i) { return kring + (i % R) * Tile::K_ELEMS; };
+    auto vslot = [&](int i) { return vring + (i % R) * Tile::V_ELEMS; };
     auto dma = [&](int i) {
         const int t0 = tile_of(i) * BK;
         if (ragged && i == 0) {
@@ -248,29 +277,62 @@ __global__ __launch_bounds__(StateShape<P>::NW * 64) void state_dma_kernel(const
             tile.template issue_v<false, false>(src, t0, n, vslot(i), wave);
         }
     };
-    // end of tile i: the batch issued at tile i-1 is complete in every wave (vector memory
-    // completes in issue order, so each wave waits until at most the batch it issued at
-    // tile i, counted for the wave with the fewest DMA instructions, is outstanding)
-    auto tile_sync = [&](bool issued) {
-        constexpr int NMIN = Tile::NIK / NW + Tile::NIV / NW;
-        static_assert(NMIN <= 15, "vmcnt immediate range");
-        if (issued) __builtin_amdgcn_s_waitcnt(0x0070 | NMIN);  // + lgkmcnt(0)
+    // wait until the copy of tile i + 1 is complete in every wave: vector memory completes
+    // in issue order, so each wave lets at most the batches of the later tiles it has
+    // issued be outstanding, counted for the wave with the fewest DMA instructions (a
+    // wave with more waits a little longer); lgkmcnt(0) retires this wave's reads of the
+    // slot that the next copy overwrites
+    constexpr int NMIN = Tile::NIK / NW + Tile::NIV / NW;
+    static_assert(2 * NMIN <= 15, "vmcnt immediate range");
+    auto tile_sync = [&](int later) {
+        if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0070 | (2 * NMIN));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0070 | NMIN);
         else __builtin_amdgcn_s_waitcnt(0x0070);
         asm volatile("s_barrier" ::: "memory");
     };
 
-    // phi of the 32 tokens of block sub (valid: tokens below kl) and its products
-    auto block = [&](const T* Ks, const T* Vs, int sub, int kl) {
-        f32x16 u = zero16();
+    // one 64-token tile; kl = valid tokens (64 unless the tile is ragged).  One body for
+    // both kinds of tile (two copies in the loop would not fit in the registers together)
+    auto process = [&](const T* Ks, const T* Vs, int kl) {
+        // operands are read one step ahead of their products, and the scheduler is kept
+        // from hoisting more reads (all of them in flight at once would not fit beside
+        // the accumulators)
+        auto kread = [&](int s, bf16x8 (&kf)[4]) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) u = M::mma(Tile::kfrag(Ks, sub, s, col, h), wf[s], u);
-        float uu[16], ph[16];
+            for (int tb = 0; tb < 4; ++tb) kf[tb] = *reinterpret_cast<const bf16x8*>(Ks + ka + tb * 16 * KLD + 32 * s);
+        };
+        f32x4 u[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            uu[r] = softplus_fast<T>(u[r] + bias);
-            if (kl < 32 && crow(r, h) >= kl) uu[r] = 0.f;
-            ph[r] = uu[r];
+        for (int tb = 0; tb < 4; ++tb) u[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 kf[4], kn[4];
+        kread(0, kf);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            if (s + 1 < NS) kread(s + 1, kn);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) u[tb] = mma16(kf[tb], wf[s], u[tb]);
+            if (s + 1 < NS) {
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) kf[tb] = kn[tb];
+            }
         }
+        float uu[16], ph[16];  // value i of C tile tb at 4 tb + i
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uu[4 * tb + i] = softplus_fast<T>(u[tb][i] + bias);
+            }
+        }
+        if (kl < BK) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (16 * (r / 4) + 4 * lg + r % 4 >= kl) uu[r] = 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ph[r] = uu[r];
+        bf16x8 af[P][2];
 #pragma unroll
         for (int pw = 0; pw < P; ++pw) {
             if (pw > 0) {
@@ -280,68 +342,58 @@ __global__ __launch_bounds__(StateShape<P>::NW * 64) void state_dma_kernel(const
 #pragma unroll
             for (int r = 0; r < 16; ++r) zacc[pw] += ph[r];
 #pragma unroll
-            for (int t = 0; t < TPB; ++t) {
-                const typename M::frag af = M::pack(ph + t * EPL);
+            for (int c = 0; c < 2; ++c) {
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) acc[pw][db] = M::mma(af, Tile::vfrag(Vs, vl, db, sub, t), acc[pw][db]);
+                for (int e = 0; e < 8; ++e) af[pw][c][e] = (bf16)ph[8 * c + e];
             }
         }
-    };
-    auto process = [&](int i, auto mask_tag) {
-        constexpr bool MASK = decltype(mask_tag)::value;
+        auto vread = [&](int idx) {  // idx = c * ND + dc
+            typedef short v4i16 __attribute__((ext_vector_type(4)));
+            typedef short v8i16 __attribute__((ext_vector_type(8)));
+            const T* p = Vs + va + 32 * (idx / ND) * VLD + 16 * (idx % ND);
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p + 16 * VLD));
+            return __builtin_bit_cast(bf16x8, (v8i16)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        bf16x8 vf = vread(0);
 #pragma unroll
-        for (int sub = ts; sub < 2; sub += TS) {
-            const int kl = MASK ? min(32, max(0, last_len - sub * 32)) : 32;
-            block(kslot(i), vslot(i), sub, kl);
+        for (int idx = 0; idx < 2 * ND; ++idx) {
+            const bf16x8 vn = idx + 1 < 2 * ND ? vread(idx + 1) : vf;
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int pw = 0; pw < P; ++pw) acc[pw][idx % ND] = mma16(af[pw][idx / ND], vf, acc[pw][idx % ND]);
+            vf = vn;
         }
     };
 
+    // prologue: copies of tiles 0 .. R-2, all complete (together with the W_k operands
+    // above, so that no wait for those is left inside the loop)
     dma(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
     if (nt > 1) dma(1);
+    if (nt > 2) dma(2);
+    tile_sync(0);
     for (int i = 0; i < nt; ++i) {
-        const bool issue = i + 2 < nt;
-        if (issue) dma(i + 2);  // into the slot tile i-1 used
-        if (active) {
-            if (i == 0 && ragged) process(i, std::true_type{});
-            else process(i, std::false_type{});
-        }
-        tile_sync(issue);
+        if (i + R - 1 < nt) dma(i + R - 1);  // into the slot tile i - 1 used
+        if (active) process(kslot(i), vslot(i), i == 0 ? last_len : BK);
+        tile_sync(min(nt - 2 - i, 2));
     }
 
-    // with TS = 2, the ts = 1 wave hands its tiles to ts = 0 through LDS; then store
-    float* red = reinterpret_cast<float*>(smem);  // [NJB][16 regs][64 lanes]
-    float* Sp = a.Sp + ((int64_t)bh * a.G + gi) * F * D;
-    float* Zp = a.Zp + ((int64_t)bh * a.G + gi) * F;
+    if (active) {
+        float* Sp = a.Sp + ((int64_t)bh * a.G + gi) * F * D;
+        float* Zp = a.Zp + ((int64_t)bh * a.G + gi) * F;
 #pragma unroll
-    for (int pw = 0; pw < P; ++pw) {
+        for (int pw = 0; pw < P; ++pw) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            if (TS == 2) {
-                if (active && ts == 1) {
+            for (int i = 0; i < 4; ++i) {
+                const int f = feat_index(wave * 16 + 4 * lg + i, pw + 1, Dphi, P);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) red[(jb * 16 + r) * 64 + lane] = acc[pw][db][r];
-                }
-                __syncthreads();
+                for (int dc = 0; dc < ND; ++dc) Sp[(int64_t)f * D + 16 * dc + la] = acc[pw][dc][i];
             }
-            if (active && ts == 0) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float v = acc[pw][db][r] + (TS == 2 ? red[(jb * 16 + r) * 64 + lane] : 0.f);
-                    const int f = feat_index(jb * 32 + crow(r, h), pw + 1, Dphi, P);
-                    Sp[(int64_t)f * D + db * 32 + col] = v;
-                }
-            }
-            if (TS == 2) __syncthreads();
+            // phi row j's column sum: the four lane groups, in a fixed order
+            float z = zacc[pw] + __shfl_xor(zacc[pw], 16);
+            z += __shfl_xor(z, 32);
+            if (lg == 0) Zp[feat_index(j, pw + 1, Dphi, P)] = z;
         }
-        const float zt = zacc[pw] + other_half(zacc[pw]);
-        if (TS == 2) {
-            if (active && ts == 1 && h == 0) red[jb * 32 + col] = zt;
-            __syncthreads();
-        }
-        if (active && ts == 0 && h == 0) Zp[feat_index(j, pw + 1, Dphi, P)] = zt + (TS == 2 ? red[jb * 32 + col] : 0.f);
-        if (TS == 2) __syncthreads();
     }
 }
 
@@ -471,24 +523,21 @@ __global__ __launch_bounds__(256) void copy_kernel(const CopyArgs a) {
 
 template <class T, int D, int P>
 static hipError_t launch_state_t(const StateArgs& a, hipStream_t stream) {
-    constexpr int NT = StateShape<P>::NW * 64;
-    // bf16 with P <= 2 (two waves per 64-token tile) takes the LDS-DMA kernel; with larger P
-    // the P x D/32 accumulators leave no registers for its operand prefetch, and the
-    // register-staged kernel spills less
-    constexpr bool kUseDma = sizeof(T) == 2 && P <= 2;
-    const size_t red = (size_t)(a.Dphi / 32) * 16 * 64 * sizeof(float);
-    size_t kv;
+    // bf16 takes the 16x16x32 LDS-DMA kernel, float32 the register-staged one
+    constexpr bool kBf16 = sizeof(T) == 2;
+    size_t lds;
     const void* fn;
-    if constexpr (kUseDma) {
-        using Tile = DmaTiles<D, StateShape<P>::NW>;
-        kv = 3 * (size_t)(Tile::K_ELEMS + Tile::V_ELEMS) * sizeof(T);
-        fn = reinterpret_cast<const void*>(state_dma_kernel<D, P>);
+    if constexpr (kBf16) {
+        using Tile = State16Tiles<D>;
+        lds = kState16Ring * (size_t)(Tile::K_ELEMS + Tile::V_ELEMS) * sizeof(T);
+        fn = reinterpret_cast<const void*>(state16_kernel<D, P>);
     } else {
-        using Tile = KVTile<T, D, NT>;
-        kv = 2 * (size_t)(Tile::K_ELEMS + Tile::V_ELEMS) * sizeof(T);
+        using Tile = KVTile<T, D, StateShape<P>::NW * 64>;
+        const size_t kv = 2 * (size_t)(Tile::K_ELEMS + Tile::V_ELEMS) * sizeof(T);
+        const size_t red = (size_t)(a.Dphi / 32) * 16 * 64 * sizeof(float);
+        lds = kv > red ? kv : red;
         fn = reinterpret_cast<const void*>(state_kernel<T, D, P>);
     }
-    const size_t lds = kv > red ? kv : red;
     // raise the dynamic LDS limit of this instantiation once per device (idempotent, so a
     // race between host threads only repeats the call)
     static size_t lds_set[64] = {};
@@ -499,12 +548,12 @@ static hipError_t launch_state_t(const StateArgs& a, hipStream_t stream) {
         if (e != hipSuccess) return e;
         lds_set[dev] = lds;
     }
-    if constexpr (kUseDma) {
-        auto kfn = state_dma_kernel<D, P>;
-        hipLaunchKernelGGL(kfn, dim3(a.BH * a.G), dim3(NT), lds, stream, a);
+    if constexpr (kBf16) {
+        auto kfn = state16_kernel<D, P>;
+        hipLaunchKernelGGL(kfn, dim3(a.BH * a.G), dim3(kState16Waves * 64), lds, stream, a);
     } else {
         auto kfn = state_kernel<T, D, P>;
-        hipLaunchKernelGGL(kfn, dim3(a.BH * a.G), dim3(NT), lds, stream, a);
+        hipLaunchKernelGGL(kfn, dim3(a.BH * a.G), dim3(StateShape<P>::NW * 64), lds, stream, a);
     }
     return hipGetLastError();
 }

@@ -20,6 +20,8 @@ is its index in the list of measured workloads (tiny 0, 5 s 1, 10 s 2, 20 s 3, 1
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
@@ -95,8 +97,13 @@ def make_inputs(w: Workload, seed: int, slabs=None):
     for t, key in enumerate(("q", "k", "v")):
         if slabs is None:
             a = np.empty((w.B, w.H, w.N, w.D), dtype=np.float32)
-            for b, h in pairs:
-                a[b, h] = _slab(seed, t, (b, h), (w.N, w.D), 1.0, bf)
+
+            def fill(bh, t=t, a=a):
+                a[bh[0], bh[1]] = _slab(seed, t, bh, (w.N, w.D), 1.0, bf)
+            # slabs are independent streams, so filling them on several threads (numpy
+            # drops the interpreter lock while it draws) gives the same values
+            with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+                list(ex.map(fill, pairs))
         else:
             a = np.stack([_slab(seed, t, (b, h), (w.N, w.D), 1.0, bf)[None] for b, h in pairs])
         out[key] = a
