@@ -438,9 +438,10 @@ rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stre
     float* Zp = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256((size_t)BH * p->Tc * F * p->D * sizeof(float)));
 
     // Fold the window frames [from, to) (global frame numbers) into S, Z: per-frame
-    // partials, then added to the state in frame order.
-    auto absorb = [&](int64_t from, int64_t to) -> rehyat_status {
-        if (to <= from) return REHYAT_OK;
+    // partials, then added to the state in frame order.  With `partials_done` the partials
+    // are already in the workspace (computed inside the attention launch) and only the
+    // scan runs.
+    auto state_args = [&](int64_t from, int64_t to) {
         StateArgs sa = state_common(p, wk, bk);
         sa.k1 = ovk;
         sa.v1 = ovv;
@@ -453,8 +454,15 @@ rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stre
         sa.G = (int)(to - from);
         sa.Sp = Sp;
         sa.Zp = Zp;
-        rehyat_status r = hip_status(launch_state(sa, p->in_dtype, stream));
-        if (r != REHYAT_OK) return r;
+        return sa;
+    };
+    auto absorb = [&](int64_t from, int64_t to, bool partials_done, const CopyArgs* with) -> rehyat_status {
+        if (to <= from) return with ? hip_status(launch_copy(*with, stream)) : REHYAT_OK;
+        const StateArgs sa = state_args(from, to);
+        if (!partials_done) {
+            rehyat_status r = hip_status(launch_state(sa, p->in_dtype, stream));
+            if (r != REHYAT_OK) return r;
+        }
         ScanArgs sc;
         std::memset(&sc, 0, sizeof(sc));
         sc.Sp = Sp;
@@ -469,12 +477,16 @@ rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stre
         sc.D = p->D;
         sc.Dphi = p->Dphi;
         sc.P = p->P;
+        if (with) {
+            sc.copy = *with;
+            sc.copy_blocks = copy_blocks(*with);
+        }
         return hip_status(launch_scan(sc, p->in_dtype, stream));
     };
 
     // 1. frames that belong to this chunk's linear region but are not yet in the state
     //    (only with an empty softmax window, where the chunk itself is linear)
-    s = absorb(absorbed, ls);
+    s = absorb(absorbed, ls, false, nullptr);
     if (s != REHYAT_OK) return s;
 
     // 2. softmax over [held overlap | chunk], linear part from the state.  The first rows
@@ -524,17 +536,26 @@ rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stre
     a.s_ls = (int)ls;
     a.s_pad = pad;
     a.nchunks = 1;
+    // 3. frames leaving the window before the next chunk.  Their partials read only K/V
+    //    of the held frames and of the chunk, so for bf16 inputs they run inside the
+    //    attention launch, in workgroups after the tiles; the scan into S, Z follows it
+    //    (the attention reads the state image the scan rewrites).
+    const int64_t from = ls > absorbed ? ls : absorbed;
+    const bool side = p->in_dtype == REHYAT_BF16 && next_abs > from;
+    if (side) {
+        a.side = state_args(from, next_abs);
+        a.side_blocks = a.side.BH * a.side.G;
+    }
     s = hip_status(launch_attn(a, p->in_dtype, p->out_dtype, stream));
     if (s != REHYAT_OK) return s;
 
-    // 3. frames leaving the window before the next chunk
-    const int64_t from = ls > absorbed ? ls : absorbed;
-    s = absorb(from, next_abs);
-    if (s != REHYAT_OK) return s;
-
-    // 4. keep frames [next_abs, f1) as the next overlap (into the other buffer)
-    if (!p->linear_only && f1 > next_abs) {
-        CopyArgs c;
+    // 4. keep frames [next_abs, f1) as the next overlap (into the other buffer); the copy
+    //    runs in the scan's launch (it reads the held frames and the chunk, writes the
+    //    buffer nothing else in this step reads)
+    CopyArgs c;
+    std::memset(&c, 0, sizeof(c));
+    const bool keep = !p->linear_only && f1 > next_abs;
+    if (keep) {
         c.s1k = ovk;
         c.s1v = ovv;
         c.s1_bh_stride = ov_bh;
@@ -551,10 +572,10 @@ rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stre
         c.n = n;
         c.D = p->D;
         c.elem_bytes = (int)elem_bytes(p->in_dtype);
-        s = hip_status(launch_copy(c, stream));
-        if (s != REHYAT_OK) return s;
-        st->overlap_slot = slot ^ 1;
     }
+    s = absorb(from, next_abs, side, keep ? &c : nullptr);
+    if (s != REHYAT_OK) return s;
+    if (keep) st->overlap_slot = slot ^ 1;
     st->frames_seen = f1;
     st->frames_absorbed = next_abs;
     if (frames < p->Tc) st->closed = 1;

@@ -33,6 +33,7 @@
 
 #include "attn_common.hpp"
 #include "dma.hpp"
+#include "state16.hpp"
 
 namespace rehyat {
 
@@ -227,6 +228,15 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void attn_wide_kernel(const Att
     T* const kring = reinterpret_cast<T*>(smem);
     T* const vring = kring + 4 * Tile::K_ELEMS;
 
+    if constexpr (STREAM) {
+        // workgroups after the attention tiles: state partials of the frames that leave the
+        // window (placed last, so they take the CUs the tiles leave free)
+        const int side = (int)blockIdx.x - 8 * a.per_xcd;
+        if (side >= 0) {
+            if (side < a.side_blocks) state16_any_p<D>(a.side, side, smem);
+            return;
+        }
+    }
     Window<T> w;
     if (!decode_window<T, D, STREAM>(a, w)) return;
     if (w.qt * BQ >= w.Lq) return;
@@ -580,14 +590,15 @@ static hipError_t launch_wide_one(const AttnArgs& a, hipStream_t stream) {
     const size_t epi_all = wide_epilogue_lds_bytes(D, a.Dphi, a.P);
     const bool all = epi_all <= kLdsMax;
     const size_t epi = all ? epi_all : epilogue_lds_bytes<bf16, D>(a.Dphi);
-    const size_t lds = kv > epi ? kv : epi;
+    size_t lds = kv > epi ? kv : epi;
+    if (STREAM && a.side_blocks > 0 && state16_lds_bytes<D>() > lds) lds = state16_lds_bytes<D>();
     auto fn = all ? attn_wide_kernel<OT, D, STREAM, true> : attn_wide_kernel<OT, D, STREAM, false>;
     static size_t lds_set[2][64] = {};
     hipError_t e = ensure_lds(reinterpret_cast<const void*>(fn), lds, lds_set[all ? 1 : 0]);
     if (e != hipSuccess) return e;
     AttnArgs b = a;
     attn_grid(b, NW * QB * 32);
-    hipLaunchKernelGGL(fn, dim3(8 * b.per_xcd), dim3(NW * 64), lds, stream, b);
+    hipLaunchKernelGGL(fn, dim3(8 * b.per_xcd + (STREAM ? b.side_blocks : 0)), dim3(NW * 64), lds, stream, b);
     return hipGetLastError();
 }
 

@@ -6,6 +6,23 @@
 
 namespace rehyat {
 
+// Per-frame partials of phi_k(K)^T V and sum phi_k(K) (state.hip).
+struct StateArgs {
+    const void* k1;         // frames [0, nf1) of the source
+    const void* v1;
+    int64_t kv1_bh_stride;
+    int nf1;
+    const void* k2;         // frames [nf1, ..) of the source
+    const void* v2;
+    int64_t kv2_bh_stride;
+    int g0, G;              // process source frames [g0, g0 + G)
+    const void* wk;
+    const float* bk;
+    float* Sp;              // [BH, G, F, D]
+    float* Zp;              // [BH, G, F]
+    int H, BH, D, n, Dphi, P;
+};
+
 // Windowed softmax + fused linear part (attn.hip).
 struct AttnArgs {
     const void* q;          // [BH, tokens_q, D] (slab stride q_bh_stride elements)
@@ -47,23 +64,26 @@ struct AttnArgs {
     // so that the segment boundary falls on a 64-token tile boundary (the second segment
     // then starts s_pad rows into the chunk)
     int s_pad;
+    // streaming, bf16: side_blocks more workgroups after the attention tiles compute the
+    // state partials of side (the frames leaving the window after this chunk), on the CUs
+    // the attention tiles leave free
+    int side_blocks;
+    StateArgs side;
 };
 
-// Per-frame partials of phi_k(K)^T V and sum phi_k(K) (state.hip).
-struct StateArgs {
-    const void* k1;         // frames [0, nf1) of the source
-    const void* v1;
-    int64_t kv1_bh_stride;
+// Copy of frames [f0, f0 + cnt) of a two-segment source into dst frames [0, cnt).
+struct CopyArgs {
+    const void* s1k;
+    const void* s1v;
+    int64_t s1_bh_stride;
     int nf1;
-    const void* k2;         // frames [nf1, ..) of the source
-    const void* v2;
-    int64_t kv2_bh_stride;
-    int g0, G;              // process source frames [g0, g0 + G)
-    const void* wk;
-    const float* bk;
-    float* Sp;              // [BH, G, F, D]
-    float* Zp;              // [BH, G, F]
-    int H, BH, D, n, Dphi, P;
+    const void* s2k;
+    const void* s2v;
+    int64_t s2_bh_stride;
+    void* dk;
+    void* dv;
+    int64_t d_bh_stride;
+    int f0, cnt, BH, n, D, elem_bytes;
 };
 
 // Running sum over frame partials in frame order (state.hip).  Parallel form: the sums
@@ -83,22 +103,12 @@ struct ScanArgs {
     int T, Tc, To, linear_only;  // chunk schedule (parallel form)
     unsigned* zero_cnt;     // counters to set to zero on the way (the attention stage's
     int nzero;              // tail-split arrival counters), or null
+    // streaming: copy_blocks more workgroups (along x, after the scan's) run the overlap
+    // copy `copy`, which touches none of the scan's data
+    int copy_blocks;
+    CopyArgs copy;
 };
 
-// Copy of frames [f0, f0 + cnt) of a two-segment source into dst frames [0, cnt).
-struct CopyArgs {
-    const void* s1k;
-    const void* s1v;
-    int64_t s1_bh_stride;
-    int nf1;
-    const void* s2k;
-    const void* s2v;
-    int64_t s2_bh_stride;
-    void* dk;
-    void* dv;
-    int64_t d_bh_stride;
-    int f0, cnt, BH, n, D, elem_bytes;
-};
 
 struct PhiArgs {
     const void* x;          // [BH, N, D]
@@ -116,6 +126,7 @@ size_t wide_split_part_bytes(int D);
 hipError_t launch_state(const StateArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t stream);
+int copy_blocks(const CopyArgs& a);  // workgroups along x of launch_copy (0: nothing to copy)
 hipError_t launch_phi(const PhiArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_zero(float* p, int64_t count, hipStream_t stream);
 
