@@ -194,34 +194,15 @@ rehyat_status rehyat_phi(const rehyat_params* p, const void* x, const void* w, c
     return hip_status(launch_phi(a, p->in_dtype, stream));
 }
 
-// Tail-split scratch of the attention stage, after the states: one arrival counter per
-// split, then the partials of both halves.
-struct SplitLayout {
-    int splits, split_per_xcd;
-    size_t cnt, part, total;
-};
-
-static SplitLayout split_layout(const rehyat_params* p) {
-    SplitLayout L;
+// Workspace of the chunk-parallel form: the per-frame partials and chunk state images.
+static size_t parallel_ws_bytes(const rehyat_params* p) {
     const int G = state_frames(p);
-    const size_t base = G > 0 ? parallel_layout(p, G).total : 0;
-    L.splits = 0;
-    L.split_per_xcd = 0;
-    if (p->in_dtype == REHYAT_BF16) {
-        AttnArgs a = attn_common(p, nullptr, nullptr);
-        a.nchunks = num_chunks(p);
-        L.splits = wide_split_plan(a);
-        L.split_per_xcd = a.split_per_xcd;
-    }
-    L.cnt = base;
-    L.part = L.cnt + (L.splits > 0 ? align256((size_t)L.splits * sizeof(unsigned)) : 0);
-    L.total = L.part + (size_t)L.splits * wide_split_part_bytes(p->D);
-    return L;
+    return G > 0 ? parallel_layout(p, G).total : 0;
 }
 
 size_t rehyat_workspace_bytes(const rehyat_params* p) {
     if (check_params(p, true) != REHYAT_OK) return 0;
-    return split_layout(p).total;
+    return parallel_ws_bytes(p);
 }
 
 rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, const void* v,
@@ -231,13 +212,9 @@ rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, cons
     if (st != REHYAT_OK) return st;
     if (!aligned16(k) || !aligned16(v) || !aligned16(wk) || !aligned4_or_null(bk)) return REHYAT_EALIGN;
     const int G = state_frames(p);
-    const SplitLayout SL = split_layout(p);
-    const size_t need = SL.total;
+    const size_t need = parallel_ws_bytes(p);
     if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0)) return REHYAT_EWORKSPACE;
-    // the attention stage's tail-split counters start at zero (each split's second arrival
-    // sets its counter back, so they stay zero between attention calls)
-    unsigned* const cnt = SL.splits > 0 ? reinterpret_cast<unsigned*>(reinterpret_cast<char*>(ws) + SL.cnt) : nullptr;
-    if (G == 0) return cnt ? hip_status(launch_zero(reinterpret_cast<float*>(cnt), SL.splits, stream)) : REHYAT_OK;
+    if (G == 0) return REHYAT_OK;
 
     const int64_t N = (int64_t)p->T * p->frame_tokens;
     const int BH = p->B * p->H;
@@ -275,8 +252,6 @@ rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, cons
     sc.Tc = p->Tc;
     sc.To = p->To;
     sc.linear_only = p->linear_only;
-    sc.zero_cnt = cnt;
-    sc.nzero = SL.splits;
     return hip_status(launch_scan(sc, p->in_dtype, stream));
 }
 
@@ -295,8 +270,7 @@ rehyat_status rehyat_parallel_attend(const rehyat_params* p, const void* q, cons
             return REHYAT_EALIGN;
     }
     const int G = state_frames(p);
-    const SplitLayout SL = split_layout(p);
-    const size_t need = SL.total;
+    const size_t need = parallel_ws_bytes(p);
     if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0)) return REHYAT_EWORKSPACE;
 
     const int64_t N = (int64_t)p->T * p->frame_tokens;
@@ -326,12 +300,6 @@ rehyat_status rehyat_parallel_attend(const rehyat_params* p, const void* q, cons
     a.aux_bh_stride = N;
     a.stream = 0;
     a.nchunks = num_chunks(p);
-    a.split_per_xcd = SL.split_per_xcd;
-    if (SL.splits > 0) {
-        // arrival counters: zeroed by rehyat_parallel_states, left zero by every call
-        a.split_cnt = reinterpret_cast<unsigned*>(w + SL.cnt);
-        a.split_part = reinterpret_cast<float*>(w + SL.part);
-    }
     return hip_status(launch_attn(a, p->in_dtype, p->out_dtype, stream));
 }
 
@@ -351,7 +319,7 @@ rehyat_status rehyat_forward_parallel_aux(const rehyat_params* p, const void* q,
             !aligned4_or_null(aux->lse) || !aligned4_or_null(aux->z))
             return REHYAT_EALIGN;
     }
-    const size_t need = split_layout(p).total;
+    const size_t need = parallel_ws_bytes(p);
     if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0)) return REHYAT_EWORKSPACE;
     st = rehyat_parallel_states(p, k, v, wk, bk, ws, ws_bytes, stream);
     if (st != REHYAT_OK) return st;
@@ -618,7 +586,7 @@ DistillLayout distill_layout(const rehyat_params* p) {
     L.tea = out_bytes;
     L.part = 2 * out_bytes;
     L.fwd = L.part + align256((size_t)p->B * p->H * L.nseg * sizeof(float));
-    L.total = L.fwd + std::max(split_layout(&ps).total, split_layout(&pt).total);
+    L.total = L.fwd + std::max(parallel_ws_bytes(&ps), parallel_ws_bytes(&pt));
     return L;
 }
 
@@ -736,8 +704,8 @@ GradLayout grad_layout(const rehyat_params* p, bool backward) {
     L.lse = take(BH * N * f4);
     L.z = take(BH * N * f4);
     L.sqd = take(backward ? 0 : BH * L.nseg_sq * f4);
-    L.fwd_s = take(split_layout(&ps).total);
-    L.fwd_t = take(backward ? 0 : split_layout(&pt).total);
+    L.fwd_s = take(parallel_ws_bytes(&ps));
+    L.fwd_t = take(backward ? 0 : parallel_ws_bytes(&pt));
     L.ah = take(BH * N * LD * f4);
     L.u = take(BH * N * s.Dphi * f4);
     L.phi = take(BH * N * s.F * f4);

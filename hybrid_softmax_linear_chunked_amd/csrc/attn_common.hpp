@@ -15,25 +15,18 @@ struct Window {
     int q0, Lq, Lk, ls;
     int img_slot;
     KeySrc<T> src;
-    int split, half;  // tail split index (-1: whole tile) and which half of the window
 };
 
 // Share of XCD x of N items dealt as 8 contiguous runs.
 __host__ __device__ inline int xcd_share(int64_t N, int x) { return (int)(N * (x + 1) / 8 - N * x / 8); }
-// Number of split tiles of XCD x: the last `per` of its chunk-0 tiles (all, if it has fewer).
-__host__ __device__ inline int xcd_splits(int64_t NS, int per, int x) {
-    const int ns = xcd_share(NS, x);
-    return ns < per ? ns : per;
-}
 
 // Workgroups are dealt round-robin over the 8 XCDs (workgroup g runs on XCD g % 8, as
 // the (g / 8)-th of that XCD), and each XCD hands its workgroups to its CUs in order.
 // The query tiles are two classes: those of chunks c >= 1, whose softmax window includes
 // the To overlap frames, and the shorter ones of chunk 0.  Every XCD takes an equal
 // contiguous share of each class, longer class first, so that its last workgroups are the
-// short ones (a shorter tail) and the tiles of one chunk share an XCD's L2.  With tail
-// splitting, the last split_per_xcd chunk-0 tiles of an XCD come as pairs of workgroups,
-// one per half of the window.  Returns false for the padding workgroups of the grid.
+// short ones (a shorter tail) and the tiles of one chunk share an XCD's L2.  Returns false
+// for the padding workgroups of the grid.
 template <class T, int D, bool STREAM>
 __device__ inline bool decode_window(const AttnArgs& a, Window<T>& w) {
     const int x = blockIdx.x % 8, p = blockIdx.x / 8;
@@ -41,25 +34,13 @@ __device__ inline bool decode_window(const AttnArgs& a, Window<T>& w) {
     const int NL = cl * a.BH * tpc, NS = a.BH * tpc;
     const int l0 = (int)((int64_t)NL * x / 8), nl = (int)((int64_t)NL * (x + 1) / 8) - l0;
     const int s0 = (int)((int64_t)NS * x / 8), ns = (int)((int64_t)NS * (x + 1) / 8) - s0;
-    const int ks = STREAM ? 0 : xcd_splits(NS, a.split_per_xcd, x);
-    w.split = -1;
-    w.half = 0;
     if (p < nl) {
         const int idx = l0 + p, ch = idx / tpc;
         w.qt = idx % tpc;
         w.c = 1 + ch % cl;
         w.bh = ch / cl;
-    } else if (p < nl + ns + ks) {
-        const int r = p - nl;  // whole chunk-0 tiles, then the split pairs
-        int idx = s0 + r;
-        if (r >= ns - ks) {
-            const int pr = r - (ns - ks);
-            int base = 0;
-            for (int y = 0; y < x; ++y) base += xcd_splits(NS, a.split_per_xcd, y);
-            idx = s0 + ns - ks + pr / 2;
-            w.half = pr % 2;
-            w.split = base + pr / 2;
-        }
+    } else if (p < nl + ns) {
+        const int idx = s0 + p - nl;
         w.qt = idx % tpc;
         w.c = 0;
         w.bh = idx / tpc;
@@ -115,7 +96,7 @@ __host__ __device__ inline size_t epilogue_lds_bytes(int Dphi) {
 template <class T, class OT, int D, int QB>
 __device__ inline void merge_store_block(const AttnArgs& a, const Window<T>& w, int row, bool has_soft, bool has_lin,
                                          const f32x16 (&oacc)[D / 32][QB], int qb, const f32x16 (&yacc)[D / 32],
-                                         float m_run, float l_tot, float zq) {
+                                         float m_run, float l_tot, float zq, bool store_out = true) {
     constexpr int NDB = D / 32;
     const int lane = threadIdx.x % 64, h = lane / 32;
     OT* outs = reinterpret_cast<OT*>(a.out) + (int64_t)w.bh * a.q_bh_stride + (int64_t)w.q0 * D;
@@ -137,23 +118,25 @@ __device__ inline void merge_store_block(const AttnArgs& a, const Window<T>& w, 
         cg = 1.f / zq;
     }
     OT* orow = outs + (int64_t)row * D;
+    if (store_out) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int d = db * 32 + g * 8 + h * 4;
-            float vals[4];
+            for (int g = 0; g < 4; ++g) {
+                const int d = db * 32 + g * 8 + h * 4;
+                float vals[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) vals[i] = ca * oacc[db][qb][g * 4 + i] + cg * yacc[db][g * 4 + i];
-            if constexpr (sizeof(OT) == 4) {
-                *reinterpret_cast<float4*>(orow + d) = make_float4(vals[0], vals[1], vals[2], vals[3]);
-            } else {
-                bf16x4 o4;
+                for (int i = 0; i < 4; ++i) vals[i] = ca * oacc[db][qb][g * 4 + i] + cg * yacc[db][g * 4 + i];
+                if constexpr (sizeof(OT) == 4) {
+                    *reinterpret_cast<float4*>(orow + d) = make_float4(vals[0], vals[1], vals[2], vals[3]);
+                } else {
+                    bf16x4 o4;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o4[i] = (bf16)vals[i];
-                *reinterpret_cast<bf16x4*>(orow + d) = o4;
+                    for (int i = 0; i < 4; ++i) o4[i] = (bf16)vals[i];
+                    *reinterpret_cast<bf16x4*>(orow + d) = o4;
+                }
             }
-        }
+    }
     if (a.aux_o_soft || a.aux_y) {
         const float il = has_soft ? 1.f / l_tot : 0.f;
 #pragma unroll
@@ -274,23 +257,18 @@ __device__ inline void linear_and_merge(const AttnArgs& a, const Window<T>& w, u
 }
 
 // Launch bookkeeping common to the attention kernels: workgroups per XCD (a share of each
-// class plus the second halves of its split tiles, see decode_window).  Returns the number
-// of split tiles.
-inline int attn_grid(AttnArgs& b, int BQ) {
+// class, see decode_window).
+inline void attn_grid(AttnArgs& b, int BQ) {
     const int qlen = b.stream ? b.s_frames * b.n : b.Tc * b.n;
     b.tiles_per_chunk = (qlen + BQ - 1) / BQ;
     b.total_tiles = b.tiles_per_chunk * b.nchunks * b.BH;
     const int64_t NL = (int64_t)(b.nchunks - 1) * b.BH * b.tiles_per_chunk, NS = (int64_t)b.BH * b.tiles_per_chunk;
-    const int per = b.stream ? 0 : b.split_per_xcd;
-    int most = 0, splits = 0;
+    int most = 0;
     for (int x = 0; x < 8; ++x) {
-        const int ks = xcd_splits(NS, per, x);
-        const int cnt = xcd_share(NL, x) + xcd_share(NS, x) + ks;
+        const int cnt = xcd_share(NL, x) + xcd_share(NS, x);
         most = cnt > most ? cnt : most;
-        splits += ks;
     }
     b.per_xcd = most;
-    return splits;
 }
 
 // Raise the dynamic LDS limit of a kernel once per device (idempotent, so a race between

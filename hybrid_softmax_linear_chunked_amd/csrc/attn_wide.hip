@@ -120,6 +120,75 @@ __device__ inline void dma_rows(const void* src, int rows, int row_bytes, bool p
     }
 }
 
+// LDS bytes of the output staging of wide_merge_store: per wave 32 rows of D + 16 bytes.
+template <class OT, int D>
+constexpr size_t wide_out_stage_bytes() {
+    return (size_t)kWideWaves * 32 * (D + 16 / sizeof(OT)) * sizeof(OT);
+}
+
+// Merge (ReHyAt blog, maplevalley.com.cn, 2.3: out = (2^m O + y) / (2^m l + z), both
+// scaled by 2^-max(m, 0)) and store the 32 query rows from r0 of this wave.  The values of
+// a row sit in lane (row % 32, h) of the C layout, 4 consecutive d per 16 bytes of output,
+// so they go through LDS (this wave's 32 rows, padded) and leave as whole rows: each store
+// instruction writes 1 KB of contiguous output.  Partial row writes from every lane took
+// tens of microseconds to drain at the end of a workgroup.  Every wave must be done with
+// the LDS contents before the call (the barrier below also covers the sweep's last copies,
+// once this wave has waited for them).  Aux outputs keep the per-lane path.
+template <class OT, int D>
+__device__ inline void wide_merge_store(const AttnArgs& a, const Window<bf16>& w, unsigned char* smem, int r0,
+                                        int wave, bool has_soft, bool has_lin, const f32x16 (&oacc)[D / 32][kWideQB],
+                                        int qb, const f32x16 (&yacc)[D / 32], float m_run, float l_tot, float zq) {
+    constexpr int NDB = D / 32, EV = 16 / sizeof(OT), SROW = D + EV, CPR = D / EV;
+    const int lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
+    float ca, cg;
+    if (has_soft && has_lin) {
+        const float M2 = fmaxf(m_run, 0.f);
+        const float ea = __builtin_amdgcn_exp2f(m_run - M2);
+        const float eg = __builtin_amdgcn_exp2f(-M2);
+        const float inv = 1.f / (ea * l_tot + eg * zq);
+        ca = ea * inv;
+        cg = eg * inv;
+    } else if (has_soft) {
+        ca = 1.f / l_tot;
+        cg = 0.f;
+    } else {
+        ca = 0.f;
+        cg = 1.f / zq;
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS-DMA copies have landed
+    __syncthreads();
+    OT* st = reinterpret_cast<OT*>(smem) + wave * 32 * SROW;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d = db * 32 + g * 8 + h * 4;
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = ca * oacc[db][qb][g * 4 + i] + cg * yacc[db][g * 4 + i];
+            if constexpr (sizeof(OT) == 4) {
+                *reinterpret_cast<float4*>(st + col * SROW + d) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+                bf16x4 o4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o4[i] = (bf16)v[i];
+                *reinterpret_cast<bf16x4*>(st + col * SROW + d) = o4;
+            }
+        }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the whole wave's rows are in LDS
+    __builtin_amdgcn_wave_barrier();
+    OT* outs = reinterpret_cast<OT*>(a.out) + (int64_t)w.bh * a.q_bh_stride + (int64_t)w.q0 * D;
+#pragma unroll
+    for (int it = 0; it < 32 * CPR / 64; ++it) {
+        const int c = it * 64 + lane, r = c / CPR, ch = c % CPR;
+        if (r0 + r < w.Lq)
+            *reinterpret_cast<uint4*>(outs + (int64_t)(r0 + r) * D + ch * EV) =
+                *reinterpret_cast<const uint4*>(st + r * SROW + ch * EV);
+    }
+    if (a.aux_o_soft || a.aux_y || a.aux_lse || a.aux_z)
+        merge_store_block<bf16, OT, D>(a, w, r0 + col, has_soft, has_lin, oacc, qb, yacc, m_run, l_tot, zq, false);
+}
+
 // Epilogue of the wide kernel when everything it reads fits in LDS at once (ReHyAt blog,
 // maplevalley.com.cn, 2.2.2-2.3): W_q, every power of the chunk's state image and Z are
 // staged by one round of LDS-DMA behind a single barrier, then each 32-query block computes
@@ -208,7 +277,7 @@ __device__ inline void wide_linear_and_merge(const AttnArgs& a, const Window<bf1
             }
             zq += other_half(zq);
         }
-        merge_store_block<T, OT, D>(a, w, qw + qb * 32 + col, has_soft, has_lin, oacc, qb, yacc, m_ref[qb], l_tot[qb], zq);
+        wide_merge_store<OT, D>(a, w, smem, qw + qb * 32, wave, has_soft, has_lin, oacc, qb, yacc, m_ref[qb], l_tot[qb], zq);
     }
 }
 
@@ -239,6 +308,18 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void attn_wide_kernel(const Att
     }
     Window<T> w;
     if (!decode_window<T, D, STREAM>(a, w)) return;
+    // the decode divides by run-time values on the vector ALU; state that every field is
+    // uniform, so that the fields sit in scalar registers instead of vector registers that
+    // the sweep would push out to scratch
+    {
+        auto u = [](int& x) { x = __builtin_amdgcn_readfirstlane(x); };
+        u(w.bh); u(w.hh); u(w.c); u(w.qt); u(w.q0); u(w.Lq); u(w.Lk); u(w.ls); u(w.img_slot);
+        u(w.src.len1);
+        w.src.k1 = static_cast<const T*>(uniform_ptr(w.src.k1));
+        w.src.v1 = static_cast<const T*>(uniform_ptr(w.src.v1));
+        w.src.k2 = static_cast<const T*>(uniform_ptr(w.src.k2));
+        w.src.v2 = static_cast<const T*>(uniform_ptr(w.src.v2));
+    }
     if (w.qt * BQ >= w.Lq) return;
     const int Lk = w.Lk;
     const bool has_lin = w.ls > 0;
@@ -271,13 +352,9 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void attn_wide_kernel(const Att
 
     const float sc = a.scale_log2;
     const int nt = (Lk + BK - 1) / BK;    // 64-token tiles
-    // sweep positions of this workgroup: all, or one half of a split tile's window
-    int p0 = 0, p1 = nt;
-    if (w.split >= 0) {
-        const int hp = (nt + 1) / 2;
-        if (w.half == 0) p1 = hp;
-        else p0 = hp;
-    }
+    // sweep positions [p0, p1) of this workgroup: the whole window
+    constexpr int p0 = 0;
+    const int p1 = nt;
     const bool ragged = Lk % BK != 0;
     // Tiles are processed last one first: position i of the sweep holds window tile
     // tile_of(i), so the only ragged tile (and the masking it needs) comes before the
@@ -520,62 +597,6 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void attn_wide_kernel(const Att
         run(false, l_tot);
     }
 
-    if (!STREAM && w.split >= 0) {
-        // Tail split: both halves store their partial (unnormalised O, reference, row sum);
-        // the second to arrive merges the other's into its own and goes on to the epilogue,
-        // the first is done.  Device-scope fences order the partials before the count.
-        constexpr int NR = NDB * QB * 16 + 2 * QB;  // values per lane
-        float* const pair = a.split_part + (size_t)64 * NR * NW * 2 * w.split;
-        float* const mine = pair + (size_t)64 * NR * (w.half * NW + wave) + lane;
-        int r = 0;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) mine[64 * r++] = oacc[db][qb][e];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            mine[64 * r++] = m_ref[qb];
-            mine[64 * r++] = l_tot[qb];
-        }
-        __threadfence();
-        __syncthreads();
-        unsigned prev = 0;
-        if (tid == 0) prev = atomicAdd(a.split_cnt + w.split, 1u);
-        if (!__syncthreads_or(tid == 0 && prev != 0)) return;
-        __threadfence();
-        // the merge is written in half order (half 0's terms first) whichever half runs it,
-        // so the result does not depend on the arrival order
-        const float* const other = pair + (size_t)64 * NR * ((1 - w.half) * NW + wave) + lane;
-        const bool h0 = w.half == 0;
-        float f0q[QB], f1q[QB];
-        r = NDB * QB * 16;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const float mo = other[64 * r++], lo = other[64 * r++];
-            const float m0 = h0 ? m_ref[qb] : mo, m1 = h0 ? mo : m_ref[qb];
-            const float l0 = h0 ? l_tot[qb] : lo, l1 = h0 ? lo : l_tot[qb];
-            const float mm = fmaxf(m0, m1);
-            const float f0 = __builtin_amdgcn_exp2f(m0 - mm), f1 = __builtin_amdgcn_exp2f(m1 - mm);
-            l_tot[qb] = __builtin_fmaf(l0, f0, l1 * f1);
-            m_ref[qb] = mm;
-            f0q[qb] = f0;
-            f1q[qb] = f1;
-        }
-        r = 0;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float xs = oacc[db][qb][e], xo = other[64 * r++];
-                    const float x0 = h0 ? xs : xo, x1 = h0 ? xo : xs;
-                    oacc[db][qb][e] = __builtin_fmaf(x0, f0q[qb], x1 * f1q[qb]);
-                }
-        if (tid == 0) a.split_cnt[w.split] = 0u;  // ready for the next launch
-    }
 
     if constexpr (EPI_ALL) wide_linear_and_merge<OT, D, NW, QB>(a, w, smem, qw, wave, has_soft, has_lin, qf, oacc, m_ref, l_tot);
     else linear_and_merge<T, OT, D, QB, NT>(a, w, smem, qw, has_soft, has_lin, qf, oacc, m_ref, l_tot);
@@ -591,6 +612,7 @@ static hipError_t launch_wide_one(const AttnArgs& a, hipStream_t stream) {
     const bool all = epi_all <= kLdsMax;
     const size_t epi = all ? epi_all : epilogue_lds_bytes<bf16, D>(a.Dphi);
     size_t lds = kv > epi ? kv : epi;
+    if (all && wide_out_stage_bytes<OT, D>() > lds) lds = wide_out_stage_bytes<OT, D>();
     if (STREAM && a.side_blocks > 0 && state16_lds_bytes<D>() > lds) lds = state16_lds_bytes<D>();
     auto fn = all ? attn_wide_kernel<OT, D, STREAM, true> : attn_wide_kernel<OT, D, STREAM, false>;
     static size_t lds_set[2][64] = {};
@@ -610,27 +632,6 @@ static hipError_t launch_wide_d(const AttnArgs& a, hipStream_t stream) {
         case 128: return launch_wide_one<OT, 128, STREAM>(a, stream);
         default: return hipErrorInvalidValue;
     }
-}
-
-// Tail split plan of the bf16 chunk-parallel launch: per XCD, the last kSplitPerXcd
-// chunk-0 query tiles run as two halves.  Only where the chunk-0 window spans at least four
-// 64-token tiles and a longer class exists (otherwise the grid is a single wave of equal
-// tiles and halves do not shorten it).  Sets a.split_per_xcd; returns the split count.
-int wide_split_plan(AttnArgs& a) {
-    constexpr int kSplitPerXcd = 8, NW = kWideWaves, QB = kWideQB;
-    a.split_per_xcd = 0;
-    if (a.stream || a.linear_only || a.nchunks < 2) return 0;
-    const int lk0 = (a.Tc < a.T ? a.Tc : a.T) * a.n;
-    if ((lk0 + 63) / 64 < 4) return 0;
-    a.split_per_xcd = kSplitPerXcd;
-    AttnArgs b = a;
-    return attn_grid(b, NW * QB * 32);
-}
-
-// Scratch bytes of one split: two halves x waves x 64 lanes x (O + reference + sum).
-size_t wide_split_part_bytes(int D) {
-    const size_t nr = (size_t)(D / 32) * kWideQB * 16 + 2 * kWideQB;
-    return 2 * (size_t)kWideWaves * 64 * nr * sizeof(float);
 }
 
 hipError_t launch_attn_wide(const AttnArgs& a, int out_dtype, hipStream_t stream) {

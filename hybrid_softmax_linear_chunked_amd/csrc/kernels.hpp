@@ -52,14 +52,6 @@ struct AttnArgs {
     int s_frames, s_held, s_ls;
     int nchunks, tiles_per_chunk, total_tiles, per_xcd;  // grid bookkeeping (set by the launcher)
     float scale_log2;       // log2(e) / sqrt(D)
-    // Tail split (bf16 chunk-parallel kernel only; 0 elsewhere): the last split_per_xcd
-    // chunk-0 query tiles of each XCD run as two workgroups, one per half of the window,
-    // which exchange partials through split_part ([split][half][wave][value][lane] floats)
-    // and count their arrival in split_cnt (one per split, zero before the launch; the
-    // second arrival merges and sets it back to zero).
-    int split_per_xcd;
-    float* split_part;
-    unsigned* split_cnt;
     // streaming: rows of the chunk also copied after the held frames in the first segment,
     // so that the segment boundary falls on a 64-token tile boundary (the second segment
     // then starts s_pad rows into the chunk)
@@ -101,8 +93,6 @@ struct ScanArgs {
     int slots;
     int BH, D, Dphi, P;
     int T, Tc, To, linear_only;  // chunk schedule (parallel form)
-    unsigned* zero_cnt;     // counters to set to zero on the way (the attention stage's
-    int nzero;              // tail-split arrival counters), or null
     // streaming: copy_blocks more workgroups (along x, after the scan's) run the overlap
     // copy `copy`, which touches none of the scan's data
     int copy_blocks;
@@ -121,8 +111,6 @@ struct PhiArgs {
 
 hipError_t launch_attn(const AttnArgs& a, int in_dtype, int out_dtype, hipStream_t stream);
 hipError_t launch_attn_wide(const AttnArgs& a, int out_dtype, hipStream_t stream);
-int wide_split_plan(AttnArgs& a);
-size_t wide_split_part_bytes(int D);
 hipError_t launch_state(const StateArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t stream);

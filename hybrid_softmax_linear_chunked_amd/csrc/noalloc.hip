@@ -7,8 +7,7 @@
 // an address: the device address of this GPU's copy is looked up once per device with that
 // device current (hipGetSymbolAddress) and kept.  The call runs exactly the kernels of
 // rehyat_forward_parallel on that memory.  Everything the kernels read from the workspace is
-// written earlier in the same call (per-frame partials, state images), except the tail-split
-// arrival counters, which the call's states stage sets to zero by a kernel, so the contents a
+// written earlier in the same call (per-frame partials, state images), so the contents a
 // previous call left do not matter.  Calls that overlap on one GPU (on different streams, or
 // from different host threads) share the array and race; calls in stream order do not.
 #include <hip/hip_runtime.h>

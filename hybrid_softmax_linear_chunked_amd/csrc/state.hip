@@ -195,8 +195,6 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanArgs a) {
         copy_body(a.copy, blockIdx.x - nscan, a.copy_blocks, bh);
         return;
     }
-    if (a.zero_cnt && blockIdx.x == 0 && bh == 0)
-        for (int i = tid; i < a.nzero; i += 256) a.zero_cnt[i] = 0u;
     T* img = reinterpret_cast<T*>(a.simg) + (int64_t)bh * a.slots * F * D;
     float* zimg = a.zimg + (int64_t)bh * a.slots * F;
     const int nc = (a.T + a.Tc - 1) / a.Tc;

@@ -101,11 +101,10 @@ int32_t rehyat_features(const rehyat_params* p);
 rehyat_status rehyat_phi(const rehyat_params* p, const void* x, const void* w, const float* bias,
                          void* feat, hipStream_t stream);
 
-/* Workspace bytes needed by rehyat_forward_parallel(_aux): per-frame state partials and
- * their prefix, float32 [B,H,T,F,D] + [B,H,T,F] (none if no chunk has a linear region),
- * followed by the scratch of the attention stage's tail split (bf16 inputs, several
- * chunks: at most 64 query tiles of 256 queries, each swept as two halves of its window
- * whose float32 partials meet there; about 135 KB per split at D = 128).  0 if neither. */
+/* Workspace bytes needed by rehyat_forward_parallel(_aux): per-frame state partials,
+ * float32 [B,H,G,F,D] + [B,H,G,F] for the G frames that enter some chunk's linear region,
+ * then one image of the state per chunk (S in in_dtype, Z float32).  0 if no chunk has a
+ * linear region. */
 size_t rehyat_workspace_bytes(const rehyat_params* p);
 
 /* Chunk-parallel forward (all chunks at once): per-frame partials of phi_k(K)^T [V|1],
@@ -144,11 +143,10 @@ rehyat_status rehyat_forward_parallel_aux(const rehyat_params* p, const void* q,
  * the stages separately.  rehyat_parallel_states writes the per-frame partials of
  * phi_k(K)^T [V|1] and their inclusive prefix over frames into ws (blog 2.3 state sums);
  * rehyat_parallel_attend runs the windowed softmax tile kernel with the fused linear part,
- * reading the prefix from ws and writing the tail-split scratch after it (so calls on one
- * ws must not overlap).  Same arguments, layouts and status codes as above; ws must hold
- * the states of the same k, v, wk, bk when attend runs (stream order suffices).
- * rehyat_parallel_states also sets the tail-split arrival counters to zero, and every
- * completed attend leaves them zero, so attend may run any number of times per states. */
+ * only reading ws, so it may run any number of times per states call.  Same arguments,
+ * layouts and status codes as above; ws must hold the states of the same k, v, wk, bk when
+ * attend runs (stream order suffices; a states call must not overlap an attend on the
+ * same ws). */
 rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, const void* v,
                                      const void* wk, const float* bk, void* ws, size_t ws_bytes,
                                      hipStream_t stream);
@@ -157,8 +155,8 @@ rehyat_status rehyat_parallel_attend(const rehyat_params* p, const void* q, cons
                                      const rehyat_aux* aux, void* ws, size_t ws_bytes,
                                      hipStream_t stream);
 
-/* Streaming (blog 5.2: states = init_states(); output, states = block(chunk, states)).
- * Device state bytes: S float32 [B,H,F,D], Z float32 [B,H,F], the image of the state and
+/* Streaming (ReHyAt blog 5.2, the streaming loop: the state is carried from chunk to
+ * chunk, so memory does not grow with the clip).  Device state bytes: S float32 [B,H,F,D], Z float32 [B,H,F], the image of the state and
  * two overlap buffers of K and V [B,H,To*n+64,D] in in_dtype (the held frames, then up to
  * 63 rows of the current chunk).  Independent of the clip length. */
 size_t rehyat_state_bytes(const rehyat_params* p);
@@ -174,8 +172,11 @@ rehyat_status rehyat_state_init(const rehyat_params* p, void* state, rehyat_stre
 /* Process the next chunk of `frames` frames: q, k, v, out are [B,H,frames*n,D].
  * frames must equal Tc except on a final, shorter call, after which the stream is closed
  * (REHYAT_ESTATE on further calls).  Outputs equal those of rehyat_forward_parallel on
- * the concatenated clip.  The call reads S, Z and the held overlap frames, then folds the
- * frames that leave the softmax window into S, Z and keeps the last To frames. */
+ * the concatenated clip bit for bit: the same kernels add the same partials in the same
+ * order and sweep the same window tiles.  The call reads S, Z and the held overlap frames,
+ * then folds the frames that leave the softmax window into S, Z (for bf16 inputs their
+ * partials run in the attention launch, on CUs its tiles leave free) and keeps the last
+ * To frames. */
 rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stream* st,
                                 const void* q, const void* k, const void* v, int32_t frames,
                                 const void* wq, const void* wk, const float* bq, const float* bk,

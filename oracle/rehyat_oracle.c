@@ -15,7 +15,7 @@
  *           split into P parts, each part raised to powers 1..P, concatenated;
  *           2.3 causality across chunks, states S = sum phi(K)^T V, Z = sum phi(K),
  *           S_{t+1} = S_t + sum phi_K V^T, Z_{t+1} = Z_t + sum phi_K;
- *           5.2 streaming loop states = init_states(); output, states = block(chunk, states).
+ *           5.2 streaming loop: the state is carried from chunk to chunk.
  *   [summary] mind-verse.de summary, "Temporaer segmentierte hybride Aufmerksamkeit"
  *           (softmax inside chunks, linear for all other tokens, overlapping chunks) and
  *           "Rekurrente Formulierung" (the hybrid map written as an RNN).

@@ -56,17 +56,9 @@ def test_sizes_follow_layouts(L):
     F = WAN.P * WAN.Dphi
     assert rh.features(WAN) == 256
     # chunk-parallel: per-frame partials for the 17 frames that enter some chunk's state,
-    # then one state image (S in bf16 operand order, Z in float) per chunk
-    # followed by the attention stage's tail-split scratch: per XCD (8 contiguous shares of
-    # the 12 * 19 chunk-0 query tiles of 256 queries) the last 8 tiles are split, each with an
-    # arrival counter and two halves x 4 waves x 64 lanes x (4 * 32 O values + 4) floats
-    ns = 12 * 19
-    splits = sum(min(ns * (x + 1) // 8 - ns * x // 8, 8) for x in range(8))
-    assert splits == 64
+    # then one state image (S in the input dtype, operand order, Z in float) per chunk
     assert rh.workspace_bytes(WAN) == (a(12 * 17 * F * 128 * 4) + a(12 * 17 * F * 4)
-                                       + a(12 * 7 * F * 128 * 2) + a(12 * 7 * F * 4)
-                                       + a(splits * 4) + splits * 2 * 4 * 64 * (4 * 32 + 4) * 4)
-    # fp32 inputs run the other tile kernel, which does not split
+                                       + a(12 * 7 * F * 128 * 2) + a(12 * 7 * F * 4))
     assert rh.workspace_bytes(WAN.with_(in_dtype=0)) == (a(12 * 17 * F * 128 * 4) + a(12 * 17 * F * 4)
                                                          + a(12 * 7 * F * 128 * 4) + a(12 * 7 * F * 4))
     # streaming: S, Z, the image of the current state and two overlap buffers of K and V

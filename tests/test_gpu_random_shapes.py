@@ -3,8 +3,7 @@ blog, maplevalley.com.cn, 2.2.1-2.3 and 2.2.2): batches, heads, head dims 32/64/
 counts 1-9 of 1-70 tokens (ragged 64-token tiles), chunk sizes 1-5 with overlaps 0-3, feature
 sizes 32-128 with 1-4 powers (uneven parts), fp32 and bf16 inputs, biases, and the empty
 softmax window.  Per shape: the chunk-parallel forward at the output bar, the streamed form
-against the parallel form (bit for bit outside tail-split chunk-0 tiles, which agree to the
-merge's rounding), and the backward for a seeded upstream gradient at the same bars
+against the parallel form (bit for bit), and the backward for a seeded upstream gradient at the same bars
 (vanishing score gradients against their natural scale, as in test_gpu_backward), and the
 distillation loss and feature-map gradients (blog 3.1.1) on the same shapes."""
 import numpy as np
@@ -59,12 +58,7 @@ def test_random_shape(shape):
     print(f"  forward: {e:.2e}", flush=True)
     assert e <= tol
     s_out = torch.cat(outs, dim=2)
-    first = min(p.Tc, p.T) * p.n
-    assert torch.equal(s_out[:, :, first:], out[:, :, first:])
-    if p.in_dtype == rh.FP32:
-        assert torch.equal(s_out, out)
-    d0 = (s_out[:, :, :first] - out[:, :, :first]).abs().max().item()
-    assert d0 <= 2 ** -6 * max(1.0, out[:, :, :first].abs().max().item())
+    assert torch.equal(s_out, out)
 
     g = np.random.default_rng(11).standard_normal((p.B, p.H, p.N, p.D)).astype(np.float32)
     got = rh.backward(p, d["q"], d["k"], d["v"], d["wq"], d["wk"], torch.from_numpy(g).cuda(), d["bq"], d["bk"])

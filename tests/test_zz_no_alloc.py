@@ -16,7 +16,7 @@ from gpu_common import TOL, oracle_params, rand_inputs, slab_err, to_dev
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # bf16 with several chunks and tail-split tiles (chunk-0 window of 15 key tiles)
+    # bf16 with several chunks (chunk-0 window of 15 key tiles)
     rh.Params(1, 3, 128, 7, 300, 3, 1, 128, 2, 0, rh.BF16, rh.BF16),
     # smaller: fewer heads and frames, other head dim and feature map, biases
     rh.Params(1, 2, 64, 4, 100, 3, 1, 64, 3, 0, rh.BF16, rh.FP32),
