@@ -643,6 +643,7 @@ constexpr int kSoftSegRows = 2048;    // query rows per dK / dV partial of a win
 struct GradLayout {
     size_t stu, tea, lse, z, sqd, fwd_s, fwd_t, ah, u, phi, dphi, sz, rp, r, wp, bp;
     size_t delta, lden, wt, rt, sbuf, dpbuf, kt, pp, g16, total;
+    int64_t stat_stride;  // floats from lden to delta
     int nseg_sq, nseg_w, nseg_b, lq_max, lk_max, ldp, nseg_s;
 };
 
@@ -716,14 +717,19 @@ GradLayout grad_layout(const rehyat_params* p, bool backward) {
     L.wp = take(BH * L.nseg_w * s.Dphi * s.D * f4);
     L.bp = take(BH * L.nseg_b * s.Dphi * f4);
     const size_t bw = backward ? 1 : 0;
-    L.delta = take(bw * BH * N * f4);
-    L.lden = take(bw * BH * N * f4);
+    // per-query statistics of the backward: lden, then delta, each with 32 spare values (the
+    // flash kernels read whole 32-query blocks)
+    L.stat_stride = (int64_t)((BH * N + 32 + 63) / 64 * 64);
+    L.lden = take(bw * 2 * (size_t)L.stat_stride * f4);
+    L.delta = L.lden + (size_t)L.stat_stride * f4;
     L.wt = take(bw * p->H * s.D * s.Dphi * f4);
     L.rt = take(bw * BH * s.nc * s.D * s.F * f4);
-    L.sbuf = take(bw * BH * L.lq_max * L.ldp * f4);
-    L.dpbuf = take(bw * BH * L.lq_max * L.ldp * f4);
-    L.kt = take(bw * BH * s.D * L.ldp * f4);
-    L.pp = take(bw * BH * L.nseg_s * (size_t)L.lk_max * s.D * f4);
+    // score-sized buffers of the float32 path only (bf16 inputs take the flash kernels)
+    const size_t sw = backward && p->in_dtype != REHYAT_BF16 ? 1 : 0;
+    L.sbuf = take(sw * BH * L.lq_max * L.ldp * f4);
+    L.dpbuf = take(sw * BH * L.lq_max * L.ldp * f4);
+    L.kt = take(sw * BH * s.D * L.ldp * f4);
+    L.pp = take(sw * BH * L.nseg_s * (size_t)L.lk_max * s.D * f4);
     L.g16 = take(backward && p->in_dtype == REHYAT_BF16 ? BH * N * s.D * 2 : 0);
     L.total = off;
     return L;
@@ -1051,8 +1057,35 @@ rehyat_status rehyat_backward(const rehyat_params* p, const void* q, const void*
 
     // bf16 inputs: the upstream gradient rounded to bf16 once (the products' operand precision)
     if (bf) GRAD_TRY(launch_to_bf16(dout, w + L.g16, (int64_t)s.BH * ND, stream));
-    // softmax branch, one chunk window at a time (blog 2.2.1 window, scores q.k / sqrt(D))
     const float scale = (float)(1.0 / std::sqrt((double)s.D));
+    if (bf) {
+        // softmax branch, flash style (blog 2.2.1 window, scores q.k / sqrt(D)): P and dS
+        // recomputed tile by tile from lden and delta, dK / dV and dQ in two passes
+        BwdArgs b;
+        std::memset(&b, 0, sizeof(b));
+        b.q = q;
+        b.k = k;
+        b.v = v;
+        b.g = w + L.g16;
+        b.stats = F32(L.lden);
+        b.stat_stride = L.stat_stride;
+        b.dq = dq;
+        b.dk = dk;
+        b.dv = dv;
+        b.BH = s.BH;
+        b.N = (int)N;
+        b.n = s.n;
+        b.T = s.T;
+        b.Tc = s.Tc;
+        b.To = s.To;
+        b.linear_only = s.linear_only;
+        b.nc = s.nc;
+        b.scale = scale;
+        b.scale_log2 = scale * 1.4426950408889634f;
+        GRAD_TRY(launch_bwd_softmax(b, s.D, stream));
+        return REHYAT_OK;
+    }
+    // float32 inputs: one chunk window at a time through score-sized buffers
     const int64_t pbt = (int64_t)L.lq_max * L.ldp;
     for (int c = 0; c < s.nc; ++c) {
         int r0, r1, k0, k1;

@@ -47,6 +47,25 @@ struct TnArgs {
     int rows, group_rows, ngroups, seg_rows, nseg;
 };
 
+// Softmax branch of the backward, flash style (bwd.hip), bf16 q, k, v and upstream gradient
+// g [BH][N][D]; stats = lden [BH * N + 32] then, stat_stride floats on, delta likewise
+// (natural log of each query's denominator, dout . o); dq, dk, dv [BH][N][D] float32, added to.
+struct BwdArgs {
+    const void* q;  // bf16
+    const void* k;
+    const void* v;
+    const void* g;
+    const float* stats;
+    int64_t stat_stride;
+    float* dq;
+    float* dk;
+    float* dv;
+    int BH, N, n, T, Tc, To, linear_only, nc;
+    int qtiles, kblocks;  // set by the launcher
+    float scale, scale_log2;
+};
+hipError_t launch_bwd_softmax(BwdArgs a, int D, hipStream_t stream);
+
 hipError_t launch_nt(const NtArgs& a, const GradArgs& s, bool x_bf16, bool y_bf16, hipStream_t stream);
 hipError_t launch_tn(const TnArgs& a, int BH, bool y_bf16, hipStream_t stream);
 // The same products with operands rounded to bf16 and the bf16 matrix core (nt: modes 0, 1,

@@ -3,9 +3,10 @@ forward for an upstream gradient; ReHyAt blog, maplevalley.com.cn, 2.2.1-2.3 and
 the chain rule) against the fp64 brute-force oracle, through the C ABI.
 
 Bar: per (batch, head) slab for dq, dk, dv and per head for the parameter gradients,
-max |gpu - oracle| / max |oracle| <= 1e-5 for fp32 inputs and 2e-2 for bf16 inputs (the
-products run in fp32 on the matrix core; the bf16 error comes from the recomputed
-forward's per-part outputs).  Repeated calls give identical bits.  Shapes span several
+max |gpu - oracle| / max |oracle| <= 1e-5 for fp32 inputs and 2e-2 for bf16 inputs (fp32
+inputs: products on the fp32 matrix core; bf16 inputs: products on the bf16 matrix core with
+fp32 accumulation, the softmax branch flash style with P and dS recomputed per tile and
+rounded to bf16 as operands).  Repeated calls give identical bits.  Shapes span several
 64-row tiles with ragged tails, To = 0 and To > Tc, a window with no linear region (one
 chunk) and one with no softmax window (linear_only), batches and biases.
 """
@@ -32,6 +33,8 @@ SHAPES = [
     (1, 2, 32, 1, 1, 1, 0, 32, 2, 0, rh.FP32, False),      # one token: o = v, dq = dk = 0, dv = G
     (2, 1, 64, 9, 1, 2, 1, 32, 3, 0, rh.FP32, True),       # one-token frames
     (1, 2, 64, 5, 70, 1, 0, 64, 2, 0, rh.BF16, False),     # Tc = 1, To = 0: spatial-only softmax
+    (1, 2, 32, 7, 70, 3, 2, 32, 2, 0, rh.BF16, True),      # D = 32; key blocks across windows
+    (1, 1, 128, 2, 33, 3, 1, 64, 2, 0, rh.BF16, False),    # T < Tc: one short chunk, ragged tiles
 ]
 
 
