@@ -15,15 +15,11 @@
 // adds its total to the gradient buffer (the linear branch's share is already there), so
 // the result is bitwise reproducible.  The only workspace is O(tokens): the statistics.
 //
-// Products are 32x32x16 bf16 MFMAs with fp32 accumulation; P and dS are rounded to bf16 as
-// operands (the forward's P precision).  Tiles of 32 rows move to LDS by LDS-DMA three tiles
-// ahead (ring of four), in rows of D + 8 elements that serve both the row operands (one
-// ds_read_b128 per operand) and the transposed ones (ds_read_b64_tr_b16, see dma.hpp).
-// Workgroups are dealt to the XCDs in contiguous runs, so the ones that read the same
-// tiles share an L2.  The C layout of a score tile gives
-// each lane one column and 16 rows in the order crow(r, h); read as a B (or A) operand of the
-// next product in that slot order, it pairs with a transposed read of the other matrix that
-// delivers rows 16 t + 4 h + {0..3} and 16 t + 8 + 4 h + {0..3} -- the same rows.
+// Products are 16x16x32 bf16 MFMAs with fp32 accumulation; P and dS are rounded to bf16 as
+// operands (the forward's P precision).  Tiles of 32 rows move to LDS by LDS-DMA several tiles
+// ahead (a ring of four or five slots), in one layout that serves both the row operands (ds_read_b128) and
+// the transposed ones (ds_read_b64_tr_b16, see dma.hpp).  Workgroups are dealt to the XCDs
+// in contiguous runs, so the ones that read the same tiles share an L2.
 #include "dma.hpp"
 #include "grad.hpp"
 
@@ -76,34 +72,12 @@ struct Rows32 {
     }
 };
 
-// operand of 8 consecutive elements: row `row` of a tile with rows of ld, columns 16 s + 8 h
-__device__ inline bf16x8 row_frag(const bf16* t, int ld, int row, int s, int h) {
-    return *reinterpret_cast<const bf16x8*>(t + row * ld + 16 * s + 8 * h);
-}
-
-// transposed operand: lane (n = lane % 32, h = lane / 32) receives column cb * 32 + n of rows
-// 16 u + 4 h + {0..3} and 16 u + 8 + 4 h + {0..3}; tl = tr_lane(lane, ld)
-__device__ inline int tr_lane(int lane, int ld) {
-    const int g = lane / 16, a = lane % 16;
-    return (4 * (g / 2) + a / 4) * ld + 16 * (g % 2) + 4 * (a % 4);
-}
-__device__ inline bf16x8 tr_frag(const bf16* t, int ld, int tl, int cb, int u) {
-    typedef short v4i16 __attribute__((ext_vector_type(4)));
-    typedef short v8i16 __attribute__((ext_vector_type(8)));
-    const bf16* p = t + tl + 16 * u * ld + cb * 32;
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p + 8 * ld));
-    return __builtin_bit_cast(bf16x8, (v8i16)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
 __device__ inline bf16x8 pack8(const float* x) {
     bf16x8 f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] = (bf16)x[e];
     return f;
 }
-
-__device__ inline f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) { return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0); }
 
 // chunk c of the schedule: query rows [q0, q1), window key rows [k0, k1)
 __device__ inline void chunk_span(const BwdArgs& a, int c, int& q0, int& q1, int& k0, int& k1) {
@@ -117,10 +91,13 @@ __device__ inline void chunk_span(const BwdArgs& a, int c, int& q0, int& q1, int
 
 // Rows of D + 8 elements: row operands (ds_read_b128) conflict-free, transposed reads
 // (ds_read_b64_tr_b16) two-way at most; one layout serves both, so each tile is copied once.
+// Tile rows of D + 16 elements: the eight rows of a transposing read fall in eight different
+// 32-byte bank groups, and the row reads of the 16x16x32 operands stay conflict-free too.
+constexpr int kDkvWaves = 4;  // waves (of 16 keys) per key-stationary workgroup
+
 template <int D>
 struct BwdTiles {
-    static constexpr int LD = D + 8;
-    static constexpr int LD16 = D + 16;  // 16x16x32 reads: 8 rows of a transposed read in 8 bank groups
+    static constexpr int LD16 = D + 16;
 };
 
 __device__ inline f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -138,11 +115,40 @@ __device__ inline int xcd_item(int items) {
 
 }  // namespace
 
-// Query-stationary pass: dQ of 256 queries of one chunk (8 waves x 32, two per SIMD).
+// Both passes run on 16x16x32 products (lane l = 16 g + a holds row a and contraction slots
+// 8 g .. 8 g + 7 of A, column a and the same slots of B, and column a, rows 4 g .. 4 g + 3 of
+// C).  A score tile's C values are, as they stand, the operand of the next product over the
+// same 32 rows, with slot i <-> row 4 g + i and slot 4 + i <-> row 16 + 4 g + i of the 32;
+// the other operand of that product is read with two transposing LDS reads that deliver the
+// same rows.
+
+// row operand of a 16x16x32 product: row 16 r16 + a, columns 32 s + 8 g of a tile with rows of
+// ld elements; ra = a * ld + 8 g
+__device__ inline bf16x8 rd_row(const bf16* t, int ra, int ld, int r16, int s) {
+    return *reinterpret_cast<const bf16x8*>(t + ra + 16 * r16 * ld + 32 * s);
+}
+// transposed operand: column 16 dc + a of rows 4 g + {0..3} and 16 + 4 g + {0..3};
+// ta = (4 g + a / 4) * ld + 4 (a % 4)
+__device__ inline bf16x8 rd_tr(const bf16* t, int ta, int ld, int dc) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const bf16* p = t + ta + 16 * dc;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p + 16 * ld));
+    return __builtin_bit_cast(bf16x8, (v8i16)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Query-stationary pass: dQ of 256 queries of one chunk (8 waves x 32, two per SIMD).  Per
+// 32-key tile and wave: S^T = K Q^T and dP^T = V G^T as 2 x 2 C tiles (keys 16 kh + 4 g + i,
+// this lane's query 16 qh + a), dS^T from them, dQ += dS K (A = dS^T values, B = K
+// transposed).  Accumulators: 2 x D / 16 tiles of 4 registers.  Software-pipelined: the
+// score products of tile i + 1 are issued before the softmax arithmetic of tile i (the
+// matrix core works while the vector ALU does), so tile i + 2 must have landed before a
+// step starts and the ring holds five tiles.
 template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdArgs a) {
-    constexpr int NW = 8, NS = D / 16, NDB = D / 32, R = 4;
-    constexpr int LD = BwdTiles<D>::LD;
+    constexpr int NW = 8, NK = D / 32, ND = D / 16, R = 5;
+    constexpr int LD = BwdTiles<D>::LD16;
     using Tl = Rows32<D, LD, NW>;
     constexpr int SLOT = 2 * Tl::BYTES;  // K, then V
     constexpr int NMIN = 2 * Tl::NMIN;
@@ -159,34 +165,35 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdArgs a) {
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-    const int lane = tid % 64, col = lane % 32, h = lane / 32;
+    const int lane = tid % 64, la = lane % 16, lg = lane / 16;
     const int64_t slab = (int64_t)bh * a.N;
     const bf16* qs = static_cast<const bf16*>(a.q) + slab * D;
     const bf16* ks = static_cast<const bf16*>(a.k) + slab * D;
     const bf16* vs = static_cast<const bf16*>(a.v) + slab * D;
     const bf16* gs = static_cast<const bf16*>(a.g) + slab * D;
 
-    // this lane's query (the column of the transposed score tile) and its operands
-    const int qrow = qbase + wave * 32 + col;
-    const bool qok = qrow < q1;
-    bf16x8 qf[NS], gf[NS];
+    // this lane's queries (columns of the transposed score tiles) and their operands
+    bf16x8 qf[2][NK], gf[2][NK];
+    float l2[2], dl[2];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        if (qok) {
-            qf[s] = row_frag(qs, D, qrow, s, h);
-            gf[s] = row_frag(gs, D, qrow, s, h);
-        } else {
-            qf[s] = bf16x8{};
-            gf[s] = bf16x8{};
+    for (int qh = 0; qh < 2; ++qh) {
+        const int qrow = qbase + wave * 32 + 16 * qh + la;
+        const bool ok = qrow < q1;
+#pragma unroll
+        for (int s = 0; s < NK; ++s) {
+            qf[qh][s] = ok ? *reinterpret_cast<const bf16x8*>(qs + (int64_t)qrow * D + 32 * s + 8 * lg) : bf16x8{};
+            gf[qh][s] = ok ? *reinterpret_cast<const bf16x8*>(gs + (int64_t)qrow * D + 32 * s + 8 * lg) : bf16x8{};
         }
+        l2[qh] = ok ? a.stats[slab + qrow] * kLog2e : INFINITY;
+        dl[qh] = ok ? a.stats[a.stat_stride + slab + qrow] : 0.f;
     }
-    const float l2 = qok ? a.stats[slab + qrow] * kLog2e : INFINITY;
-    const float dl = qok ? a.stats[a.stat_stride + slab + qrow] : 0.f;
     const float sl = a.scale_log2, sc = a.scale;
 
-    f32x16 acc[NDB];
+    f32x4 acc[2][ND];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[db] = zero16();
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+        for (int dc = 0; dc < ND; ++dc) acc[qh][dc] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nkt = (Lk + 31) / 32;
     auto slot = [&](int i) { return smem + (i % R) * SLOT; };
@@ -196,63 +203,96 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdArgs a) {
         Tl::issue(ks, r0, k1 - 1, s0, wave, lane);
         Tl::issue(vs, r0, k1 - 1, s0 + Tl::BYTES, wave, lane);
     };
-    // end of tile i: the copy of tile i + 1 has landed in every wave (later batches may
-    // still be in flight; counted for the wave with the fewest instructions)
     auto sync = [&](int later) {
         if (later >= 2) wait_vm_lds<2 * NMIN>();
         else if (later == 1) wait_vm_lds<NMIN>();
         else wait_vm_lds<0>();
         asm volatile("s_barrier" ::: "memory");
     };
-    const int tl = tr_lane(lane, LD);
+    const int ra = la * LD + 8 * lg;
+    const int ta = (4 * lg + la / 4) * LD + 4 * (la % 4);
+    // S^T and dP^T of tile i: [kh][qh]
+    auto scores = [&](int i, f32x4 (&S)[2][2], f32x4 (&P)[2][2]) {
+        const bf16* Kt = reinterpret_cast<const bf16*>(slot(i));
+        const bf16* Vt = reinterpret_cast<const bf16*>(slot(i) + Tl::BYTES);
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int qh = 0; qh < 2; ++qh) {
+                S[kh][qh] = f32x4{0.f, 0.f, 0.f, 0.f};
+                P[kh][qh] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+        for (int s = 0; s < NK; ++s)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const bf16x8 kr = rd_row(Kt, ra, LD, kh, s), vr = rd_row(Vt, ra, LD, kh, s);
+#pragma unroll
+                for (int qh = 0; qh < 2; ++qh) {
+                    S[kh][qh] = mma16(kr, qf[qh][s], S[kh][qh]);
+                    P[kh][qh] = mma16(vr, gf[qh][s], P[kh][qh]);
+                }
+            }
+    };
+    // dS^T of tile i from its scores, then dQ += dS K
+    auto products = [&](int i, const f32x4 (&S)[2][2], const f32x4 (&P)[2][2]) {
+        const bf16* Kt = reinterpret_cast<const bf16*>(slot(i));
+        const int klim = Lk - 32 * i;  // keys of this tile inside the window
+        bf16x8 af[2];
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {
+            float ds[8];
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float p = __builtin_amdgcn_exp2f(S[kh][qh][e] * sl - l2[qh]);
+                    if (klim < 32 && 16 * kh + 4 * lg + e >= klim) p = 0.f;
+                    ds[4 * kh + e] = p * (P[kh][qh][e] - dl[qh]) * sc;
+                }
+            af[qh] = pack8(ds);
+        }
+#pragma unroll
+        for (int dc = 0; dc < ND; ++dc) {
+            const bf16x8 kt = rd_tr(Kt, ta, LD, dc);
+#pragma unroll
+            for (int qh = 0; qh < 2; ++qh) acc[qh][dc] = mma16(af[qh], kt, acc[qh][dc]);
+        }
+    };
 
     // the operand loads above complete before the first copy is issued: the compiler does
     // not count the copies, and a wait for those loads inside the loop would drain them
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    dma(0);
-    if (nkt > 1) dma(1);
-    if (nkt > 2) dma(2);
-    sync(min(nkt - 1, 2));
-    for (int i = 0; i < nkt; ++i) {
-        if (i + 3 < nkt) dma(i + 3);  // into the slot tile i - 1 used
-        const bf16* Kt_ = reinterpret_cast<const bf16*>(slot(i));
-        const bf16* Vt_ = reinterpret_cast<const bf16*>(slot(i) + Tl::BYTES);
-        // S^T = K Q^T and dP^T = V G^T: lane column = this lane's query, rows = keys crow(r, h)
-        f32x16 S = zero16(), dP = zero16();
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            S = mma(row_frag(Kt_, LD, col, s, h), qf[s], S);
-            dP = mma(row_frag(Vt_, LD, col, s, h), gf[s], dP);
-        }
-        const int klim = Lk - 32 * i;  // keys of this tile inside the window
-        float ds[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float p = __builtin_amdgcn_exp2f(S[r] * sl - l2);
-            if (klim < 32 && crow(r, h) >= klim) p = 0.f;
-            ds[r] = p * (dP[r] - dl) * sc;
-        }
-        // dQ += dS K: A = dS (rows = queries, slots = keys in C order), B = K transposed
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const bf16x8 af = pack8(ds + 8 * t);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[db] = mma(af, tr_frag(Kt_, LD, tl, db, t), acc[db]);
-        }
-        sync(min(nkt - 2 - i, 2));
+    for (int i = 0; i < R - 1 && i < nkt; ++i) dma(i);
+    sync(min(nkt - 2, 2));  // tiles 0 and 1 landed
+    f32x4 SA[2][2], PA[2][2], SB[2][2], PB[2][2];
+    scores(0, SA, PA);
+    auto step = [&](int i, f32x4 (&Sc)[2][2], f32x4 (&Pc)[2][2], f32x4 (&Sn)[2][2], f32x4 (&Pn)[2][2]) {
+        if (i + R - 1 < nkt) dma(i + R - 1);  // into the slot tile i - 1 used
+        if (i + 1 < nkt) scores(i + 1, Sn, Pn);
+        products(i, Sc, Pc);
+        sync(min(nkt - 3 - i, 2));  // tile i + 2 landed; every wave is done with tile i
+    };
+    for (int i = 0; i < nkt; i += 2) {
+        step(i, SA, PA, SB, PB);
+        if (i + 1 < nkt) step(i + 1, SB, PB, SA, PA);
     }
-    // acc[db]: column d = 32 db + col, rows = queries wave * 32 + crow(r, h)
+    // acc[qh][dc]: column d = 16 dc + a, rows = queries 16 qh + 4 g + {0..3} of this wave
     float* dq = a.dq + slab * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int qr = qbase + wave * 32 + crow(r, h);
-            if (qr < q1) dq[(int64_t)qr * D + 32 * db + col] += acc[db][r];
+        for (int e = 0; e < 4; ++e) {
+            const int qr = qbase + wave * 32 + 16 * qh + 4 * lg + e;
+            if (qr < q1) {
+#pragma unroll
+                for (int dc = 0; dc < ND; ++dc) dq[(int64_t)qr * D + 16 * dc + la] += acc[qh][dc][e];
+            }
         }
 }
 
-// Key-stationary pass: dK and dV of 128 keys (8 waves x 16, two per SIMD), on 16x16x32
+// Key-stationary pass: dK and dV of 64 keys (4 waves x 16; two workgroups per CU, which do
+// not wait for each other's barriers, so one's arithmetic overlaps the other's products), on 16x16x32
 // products (lane l = 16 g + a holds row a and contraction slots 8 g .. 8 g + 7 of A, column a
 // and the same slots of B, and column a, rows 4 g .. 4 g + 3 of C).  Per 32-query tile and
 // wave:
@@ -263,8 +303,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdArgs a) {
 //     reads that deliver the same queries for column 16 dc + a.
 // The accumulators of a wave are 2 D / 16 tiles of 4 registers (64 at D = 128).
 template <int D>
-__global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(const BwdArgs a) {
-    constexpr int NW = 8, KW = 16, NK = D / 32, ND = D / 16, R = 4;
+__global__ __launch_bounds__(kDkvWaves * 64, 2) void bwd_dkv_kernel(const BwdArgs a) {
+    constexpr int NW = kDkvWaves, KW = 16, NK = D / 32, ND = D / 16, R = 4;
     constexpr int LD = BwdTiles<D>::LD16;
     using Tl = Rows32<D, LD, NW>;
     constexpr int STAT = 256;  // lden of the 32 queries, then delta
@@ -459,16 +499,15 @@ hipError_t lds_limit(const void* fn, size_t lds, size_t (&done)[64]) {
 
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
-    constexpr int LD = BwdTiles<D>::LD;
-    const size_t lds_q = 4 * (size_t)(2 * Rows32<D, LD, 8>::BYTES);
-    const size_t lds_k = 4 * (size_t)(2 * Rows32<D, BwdTiles<D>::LD16, 8>::BYTES + 256);
+    const size_t lds_q = 5 * (size_t)(2 * Rows32<D, BwdTiles<D>::LD16, 8>::BYTES);
+    const size_t lds_k = 4 * (size_t)(2 * Rows32<D, BwdTiles<D>::LD16, kDkvWaves>::BYTES + 256);
     static size_t set_q[64] = {}, set_k[64] = {};
     hipError_t e = lds_limit(reinterpret_cast<const void*>(bwd_dkv_kernel<D>), lds_k, set_k);
     if (e != hipSuccess) return e;
     e = lds_limit(reinterpret_cast<const void*>(bwd_dq_kernel<D>), lds_q, set_q);
     if (e != hipSuccess) return e;
     const int nk = a.BH * a.kblocks, nq = a.BH * a.nc * a.qtiles;
-    hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3((unsigned)((nk + 7) / 8 * 8)), dim3(512), lds_k, stream, a);
+    hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3((unsigned)((nk + 7) / 8 * 8)), dim3(kDkvWaves * 64), lds_k, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)((nq + 7) / 8 * 8)), dim3(512), lds_q, stream, a);
@@ -479,7 +518,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_bwd_softmax(BwdArgs a, int D, hipStream_t stream) {
     a.qtiles = (a.Tc * a.n + 255) / 256;
-    a.kblocks = (a.N + 127) / 128;
+    a.kblocks = (a.N + kDkvWaves * 16 - 1) / (kDkvWaves * 16);
     switch (D) {
         case 32: return launch_bwd_d<32>(a, stream);
         case 64: return launch_bwd_d<64>(a, stream);

@@ -237,10 +237,13 @@ rehyat_status rehyat_distill_grad(const rehyat_params* p, const void* q, const v
  *                   dq_i += sum_j dS_ij k_j, dk_j += sum_i dS_ij q_i (per chunk window);
  *   linear region: as rehyat_distill_grad through the chunk states (blog 2.3), plus
  *                  dq += dpre_q W_q and dk += dpre_k W_k through the feature map.
- * Every sum runs in a fixed order (bitwise reproducible); the softmax branch is computed one
- * chunk window at a time for all slabs, so the workspace holds two float32
- * [B*H, Tc*n, (Tc+To)*n] score-sized buffers (2.8 GB for a 12-head Wan 5 s layer) on top of
- * the gradient buffers of rehyat_distill_grad.  Inputs as for rehyat_forward_parallel;
+ * Every sum runs in a fixed order (bitwise reproducible).  bf16 inputs: the softmax branch
+ * runs flash style (P and dS recomputed tile by tile from the saved log-denominator and
+ * delta, dK / dV in a key-stationary pass and dQ in a query-stationary one), so beyond the
+ * gradient buffers of rehyat_distill_grad the workspace holds only per-token statistics and
+ * the upstream gradient in bf16: it grows with the clip, not with the window.  float32
+ * inputs take the softmax branch one chunk window at a time through two float32
+ * [B*H, Tc*n, (Tc+To)*n] score-sized buffers.  Inputs as for rehyat_forward_parallel;
  * p->out_dtype is ignored.  Status: REHYAT_EALIGN for null or misaligned pointers (dout,
  * dq, dk, dv 16-byte aligned), REHYAT_EWORKSPACE, REHYAT_EINVAL as for rehyat_distill_grad. */
 size_t rehyat_backward_workspace_bytes(const rehyat_params* p);
