@@ -18,6 +18,9 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "librehyat.so")
+# the host-sanitized build of the same sources (build_sanitized), for the sanitizer test
+if os.environ.get("REHYAT_LIB"):
+    LIB_PATH = os.environ["REHYAT_LIB"]
 
 FP32, BF16 = 0, 1
 _STATUS = {0: "REHYAT_OK", 1: "REHYAT_EINVAL", 2: "REHYAT_ESHAPE", 3: "REHYAT_EALIGN",

@@ -46,6 +46,22 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+def build_sanitized(out_dir: str) -> str:
+    """The oracle under AddressSanitizer and UndefinedBehaviorSanitizer (clang, the runtime
+    the sanitized librehyat uses; no OpenMP, so the pragmas are ignored).  Test tooling."""
+    os.makedirs(out_dir, exist_ok=True)
+    path = os.path.join(out_dir, "librehyat_oracle_san.so")
+    tmp = path + ".tmp"
+    subprocess.run(
+        ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+         "-fno-omit-frame-pointer", "-shared-libsan", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
+         "-Wno-unknown-pragmas", "-o", tmp, _SRC, "-lm"],
+        check=True,
+    )
+    os.replace(tmp, path)
+    return path
+
+
 class _Params(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int) for name in
                 ("B", "H", "D", "T", "n", "Tc", "To", "Dphi", "P", "linear_only")]
