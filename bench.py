@@ -37,7 +37,8 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBS = 8000.0
 METRIC = "hybrid-attn tokens/s & TFLOP/s (% bf16 MFMA peak), 32760-token 12-head layer"
-KERNEL_SOURCES = ["attn_wide.hip", "attn_common.hpp", "dma.hpp", "tiles.hpp", "common.hpp", "kernels.hpp"]
+KERNEL_SOURCES = ["attn_wide.hip", "attn_common.hpp", "dma.hpp", "tiles.hpp", "common.hpp", "kernels.hpp",
+                  "state16.hpp", "wide_substep.inc", "gen_wide_substep.py"]
 COUNTER_FILE = os.path.join(ROOT, "profiles", "attn_kernel_wan_5s_counters.txt")
 
 
@@ -82,21 +83,26 @@ def sources_digest():
 
 
 def stored_traffic():
-    """HBM bytes per launch of the attention kernel from the committed counter summary, if it
-    was taken on the current kernel sources (else None)."""
+    """HBM bytes per launch of the attention kernel from the committed counter summary (two
+    rocprofv3 passes, FETCH_SIZE and WRITE_SIZE, scaled by a copy kernel's readings), and
+    where they come from.  The value is None unless the summary was taken on the current
+    kernel sources (same sha256 over KERNEL_SOURCES)."""
+    src = {"profile": os.path.relpath(COUNTER_FILE, ROOT), "sources_sha256": None,
+           "current_sources_sha256": sources_digest(), "measured_in_this_run": False}
     if not os.path.exists(COUNTER_FILE):
-        return None
+        return None, src
     kv = {}
     for line in open(COUNTER_FILE):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             kv[key.strip()] = val.strip()
+    src["sources_sha256"] = kv.get("sources_sha256")
     try:
-        if kv.get("sources_sha256") != sources_digest():
-            return None
-        return float(kv["hbm_bytes_per_dispatch"])
+        if kv.get("sources_sha256") != src["current_sources_sha256"]:
+            return None, src
+        return float(kv["hbm_bytes_per_dispatch"]), src
     except (KeyError, ValueError):
-        return None
+        return None, src
 
 
 def cpu_baseline(w, x, out_gpu, budget_s=12.0):
@@ -201,6 +207,7 @@ def main():
     state_ms = sum(starts[i].elapsed_time(mids[i]) for i in range(args.steps)) / args.steps
 
     fl = flop_model(w.B, w.H, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P)
+    traffic, traffic_src = stored_traffic()
     tokens = w.B * w.N
     tflops = fl["total"] / (ms * 1e-3) / 1e12
     attn_tflops = fl["attn_kernel"] / (attn_ms * 1e-3) / 1e12
@@ -217,8 +224,8 @@ def main():
         "stages_ms": {"state_and_scan": round(state_ms, 4), "attn_kernel": round(attn_ms, 4)},
         "roofline": {"kernel": "attn_kernel (windowed softmax + fused linear combine)", "bound": "mfma",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic(),
-                     "algorithmic_flops_per_launch": fl["attn_kernel"]},
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "traffic_source": traffic_src, "algorithmic_flops_per_launch": fl["attn_kernel"]},
     }
 
     want = set(LEGS) if args.legs == "all" else set(args.legs.split(","))
