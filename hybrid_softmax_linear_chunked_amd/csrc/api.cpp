@@ -59,14 +59,6 @@ size_t partial_bytes(const rehyat_params* p, int frames) {
     return align256(BH * frames * F * p->D * sizeof(float)) + align256(BH * frames * F * sizeof(float));
 }
 
-// Per-slot state image: S rows in the attention kernel's operand order (input dtype) and
-// Z reordered by power (float).
-size_t image_bytes(const rehyat_params* p, int slots) {
-    const size_t F = (size_t)p->P * p->Dphi;
-    const size_t BH = (size_t)p->B * p->H;
-    return align256(BH * slots * F * p->D * elem_bytes(p->in_dtype)) + align256(BH * slots * F * sizeof(float));
-}
-
 // Chunk-parallel workspace: per-frame partials [BH, G, F, D] + [BH, G, F], then the
 // state images of every chunk [BH, nc, ...].
 struct ParallelLayout {
@@ -1085,19 +1077,19 @@ rehyat_status rehyat_backward(const rehyat_params* p, const void* q, const void*
         GRAD_TRY(launch_bwd_softmax(b, s.D, stream));
         return REHYAT_OK;
     }
-    // float32 inputs: one chunk window at a time through score-sized buffers
+    // float32 inputs: one chunk window at a time through score-sized buffers (products on the
+    // fp32 matrix core)
     const int64_t pbt = (int64_t)L.lq_max * L.ldp;
     for (int c = 0; c < s.nc; ++c) {
         int r0, r1, k0, k1;
         chunk_rows(p, c, r0, r1, k0, k1);
         const int Lq = r1 - r0, Lk = k1 - k0;
         if (Lk == 0) continue;
-        const size_t es = bf ? 2 : 4;
-        const char* qc = reinterpret_cast<const char*>(q) + (size_t)r0 * s.D * es;
-        const char* kw = reinterpret_cast<const char*>(k) + (size_t)k0 * s.D * es;
-        const char* vw = reinterpret_cast<const char*>(v) + (size_t)k0 * s.D * es;
-        auto nt = [&](const void* x, bool xbf, int64_t xbs, int ldx, const void* y, bool ybf, int64_t ybs, int ldy,
-                      int K, int ncols, float* c_, int64_t cbs, int ldc, int acc) {
+        const float* qc = reinterpret_cast<const float*>(q) + (size_t)r0 * s.D;
+        const float* kw = reinterpret_cast<const float*>(k) + (size_t)k0 * s.D;
+        const float* vw = reinterpret_cast<const float*>(v) + (size_t)k0 * s.D;
+        auto nt = [&](const float* x, int64_t xbs, int ldx, const float* y, int64_t ybs, int ldy, int K, int ncols,
+                      float* c_, int64_t cbs, int ldc, int acc) {
             NtArgs a;
             std::memset(&a, 0, sizeof(a));
             a.x = x;
@@ -1118,25 +1110,15 @@ rehyat_status rehyat_backward(const rehyat_params* p, const void* q, const void*
             a.group_rows = Lq;
             a.ngroups = 1;
             a.accumulate = acc;
-            // bf16 inputs: operands rounded to bf16 on the bf16 matrix core (as in the forward)
-            return bf ? launch_nt16(a, s, xbf, ybf, stream) : launch_nt(a, s, xbf, ybf, stream);
+            return launch_nt(a, s, false, false, stream);
         };
-        if (bf) {
-            // bf16 inputs: P = exp(Q_c K_w^T / sqrt(D) - log den) and dS = P (G_c V_w^T - delta)
-            // / sqrt(D) from one pass over the window, as bf16 (the forward's P precision)
-            GRAD_TRY(launch_sdp16(qc, kw, w + L.g16 + (size_t)r0 * s.D * 2, vw, ND, s.D, Lq, Lk,
-                                  std::min(L.ldp, (Lk + 7) / 8 * 8), F32(L.lden) + r0, F32(L.delta) + r0, N, scale,
-                                  w + L.sbuf, w + L.dpbuf, pbt, L.ldp, s.BH, stream));
-        } else {
-            // S = Q_c K_w^T and dP = G_c V_w^T, then P and dS in place
-            GRAD_TRY(nt(qc, bf, ND, s.D, kw, bf, ND, s.D, s.D, Lk, F32(L.sbuf), pbt, L.ldp, 0));
-            GRAD_TRY(nt(dout + (size_t)r0 * s.D, false, ND, s.D, vw, bf, ND, s.D, s.D, Lk, F32(L.dpbuf), pbt, L.ldp,
-                        0));
-            GRAD_TRY(launch_softmax_bwd(F32(L.sbuf), F32(L.dpbuf), F32(L.lden) + r0, F32(L.delta) + r0, N, s.BH, Lq,
-                                        Lk, L.ldp, pbt, scale, stream));
-        }
+        // S = Q_c K_w^T and dP = G_c V_w^T, then P and dS in place
+        GRAD_TRY(nt(qc, ND, s.D, kw, ND, s.D, s.D, Lk, F32(L.sbuf), pbt, L.ldp, 0));
+        GRAD_TRY(nt(dout + (size_t)r0 * s.D, ND, s.D, vw, ND, s.D, s.D, Lk, F32(L.dpbuf), pbt, L.ldp, 0));
+        GRAD_TRY(launch_softmax_bwd(F32(L.sbuf), F32(L.dpbuf), F32(L.lden) + r0, F32(L.delta) + r0, N, s.BH, Lq, Lk,
+                                    L.ldp, pbt, scale, stream));
         // dV_w += P^T G_c and dK_w += dS^T Q_c: partial sums over query segments, then added
-        auto tn_add = [&](const void* X, const void* Y, bool ybf, float* out) -> hipError_t {
+        auto tn_add = [&](const float* X, const float* Y, float* out) -> hipError_t {
             TnArgs t;
             std::memset(&t, 0, sizeof(t));
             t.x = X;
@@ -1153,19 +1135,18 @@ rehyat_status rehyat_backward(const rehyat_params* p, const void* q, const void*
             t.ngroups = 1;
             t.seg_rows = kSoftSegRows;
             t.nseg = (Lq + kSoftSegRows - 1) / kSoftSegRows;
-            hipError_t e = bf ? launch_tn16(t, s.BH, true, ybf, stream) : launch_tn(t, s.BH, ybf, stream);
+            hipError_t e = launch_tn(t, s.BH, false, stream);
             if (e == hipSuccess)
                 e = launch_grad_reduce(F32(L.pp), out + (size_t)k0 * s.D, 1, s.BH, t.nseg, (int64_t)Lk * s.D, stream,
                                        ND, true);
             return e;
         };
-        if (bf) GRAD_TRY(tn_add(w + L.sbuf, w + L.g16 + (size_t)r0 * s.D * 2, true, dv));
-        else GRAD_TRY(tn_add(w + L.sbuf, dout + (size_t)r0 * s.D, false, dv));
-        GRAD_TRY(tn_add(w + L.dpbuf, qc, bf, dk));
+        GRAD_TRY(tn_add(F32(L.sbuf), dout + (size_t)r0 * s.D, dv));
+        GRAD_TRY(tn_add(F32(L.dpbuf), qc, dk));
         // dQ_c += dS K_w with K_w transposed (zero past Lk)
-        GRAD_TRY(launch_transpose(kw, bf, ND, s.D, F32(L.kt), (int64_t)s.D * L.ldp, L.ldp, Lk, s.D, s.BH, stream));
-        GRAD_TRY(nt(w + L.dpbuf, bf, pbt, L.ldp, F32(L.kt), false, (int64_t)s.D * L.ldp, L.ldp, Lk, s.D,
-                    dq + (size_t)r0 * s.D, ND, s.D, 1));
+        GRAD_TRY(launch_transpose(kw, false, ND, s.D, F32(L.kt), (int64_t)s.D * L.ldp, L.ldp, Lk, s.D, s.BH, stream));
+        GRAD_TRY(nt(F32(L.dpbuf), pbt, L.ldp, F32(L.kt), (int64_t)s.D * L.ldp, L.ldp, Lk, s.D, dq + (size_t)r0 * s.D,
+                    ND, s.D, 1));
     }
     return REHYAT_OK;
 }

@@ -1,4 +1,4 @@
-// attn_wide.hip -- bf16 windowed softmax tile kernel, 64 queries per wave, with the linear
+// attn_wide.hip -- bf16 windowed softmax tile kernel, 32 queries per wave, with the linear
 // part and the shared normalisation fused into its epilogue (ReHyAt blog,
 // maplevalley.com.cn, sections 2.2.1-2.3).
 //

@@ -242,210 +242,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void t
     }
 }
 
-// bf16 matrix-core forms of the two products, for the softmax branch of the backward with
-// bf16 inputs: operands rounded to bf16 (ties to even) while staged, products accumulated
-// in fp32 on v_mfma_f32_32x32x16_bf16.  LDS rows hold 32 contraction elements plus 8 of
-// padding; a lane reads its 8 consecutive contraction slots with one 16-byte read (the
-// segment product reads transposed slices, below).
-constexpr int kLd16 = 40;
-
-
-// rows [r0, r0 + 64) x contraction [c0, c0 + 32) of a row-major source -> dst[r][c] (bf16)
-template <class T>
-using RowSlice = Slice<T, 64, 32, kLd16>;
-
-template <class T>
-__device__ inline void stage16_rows(const T* src, int64_t ld, int r0, int rlim, int c0, int clim, bf16* dst) {
-    RowSlice<T> sl;
-    sl.load(src, ld, r0, rlim, c0, clim);
-    sl.store(dst);
-}
-
-__device__ inline f32x16 mma16(const bf16* a, const bf16* b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(a),
-                                                   *reinterpret_cast<const bf16x8*>(b), c, 0, 0, 0);
-}
-
-// nt_kernel on bf16 operands (modes 0, 1 and 3; no column bias or subtraction)
-template <class TX, class TY>
-__global__ __launch_bounds__(256) void nt16_kernel(const NtArgs a, const GradArgs s) {
-    __shared__ __align__(16) bf16 xs[64 * kLd16], ys[64 * kLd16];
-    const int bt = blockIdx.z;
-    const int grp = blockIdx.y / a.tiles_per_group, t = blockIdx.y % a.tiles_per_group;
-    const int row0 = grp * a.group_rows + t * 64;
-    const int rend = min((grp + 1) * a.group_rows, a.rows);
-    if (row0 >= rend) return;
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
-    const int wr = wave / 2, wc = wave % 2;
-    const int c0 = blockIdx.x * 64;
-    const int m = a.mode == 0 ? bt % s.H : a.mode == 1 ? bt * a.nmat + grp : bt;
-    const TX* xb = reinterpret_cast<const TX*>(a.x) + (int64_t)bt * a.x_bt_stride;
-    const TY* yb = reinterpret_cast<const TY*>(a.y) + (int64_t)m * a.y_mat_stride;
-    f32x16 acc;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) acc[q] = 0.f;
-    RowSlice<TX> sx;
-    RowSlice<TY> sy;
-    sx.load(xb, a.ldx, row0, rend, 0, a.K);
-    sy.load(yb, a.ldy, c0, a.ncols, 0, a.K);
-    for (int d0 = 0; d0 < a.K; d0 += 32) {
-        __syncthreads();
-        sx.store(xs);
-        sy.store(ys);
-        if (d0 + 32 < a.K) {  // the next slice is read while this one is multiplied
-            sx.load(xb, a.ldx, row0, rend, d0 + 32, a.K);
-            sy.load(yb, a.ldy, c0, a.ncols, d0 + 32, a.K);
-        }
-        __syncthreads();
-        const bf16* xr = xs + (wr * 32 + col) * kLd16 + h * 8;
-        const bf16* yr = ys + (wc * 32 + col) * kLd16 + h * 8;
-        acc = mma16(xr, yr, acc);
-        acc = mma16(xr + 16, yr + 16, acc);
-    }
-    const int f = c0 + wc * 32 + col;
-    if (f >= a.ncols) return;
-    float* cb = a.c + (int64_t)bt * a.c_bt_stride;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const int rr = row0 + wr * 32 + crow(q, h);
-        if (rr < rend) {
-            float* dst = cb + (int64_t)rr * a.ldc + f;
-            *dst = a.accumulate ? *dst + acc[q] : acc[q];
-        }
-    }
-}
-
-// The two score-shaped products of a chunk window in one pass (bf16 inputs): per 64 x 64
-// tile of (query, key), S = Q K^T and dP = G V^T accumulate side by side over D, then
-// P = exp(S / sqrt(D) - log den_i) and dS = P (dP - delta_i) / sqrt(D) are written as bf16
-// (columns [Lk, ncols_pad) as zeros).  Q, K, V, G bf16 [rows][D].  The two output tiles go
-// back through LDS so that every global store is a 16-byte run of a row.
-constexpr int kSdpOutLd = 72;  // bf16 per row of a staged 64 x 64 output tile
-
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void sdp16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                                    const bf16* __restrict__ g, const bf16* __restrict__ v,
-                                                    int64_t bt_stride, int D, int Lq, int Lk, int ncols_pad,
-                                                    const float* __restrict__ lden, const float* __restrict__ delta,
-                                                    int64_t stat_bt_stride, float scale, bf16* __restrict__ P,
-                                                    bf16* __restrict__ dS, int64_t p_bt_stride, int ldp) {
-    constexpr int TILE = 64 * kLd16, IN = 4 * TILE, OUT = 2 * 64 * kSdpOutLd;
-    __shared__ __align__(16) bf16 lds[IN > OUT ? IN : OUT];
-    bf16 *qs = lds, *ks = lds + TILE, *gs = lds + 2 * TILE, *vs = lds + 3 * TILE;
-    const int bt = blockIdx.z, row0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
-    const int wr = wave / 2, wc = wave % 2;
-    const bf16* qb = q + (int64_t)bt * bt_stride;
-    const bf16* kb = k + (int64_t)bt * bt_stride;
-    const bf16* gb = g + (int64_t)bt * bt_stride;
-    const bf16* vb = v + (int64_t)bt * bt_stride;
-    f32x16 sa, pa;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sa[r] = pa[r] = 0.f;
-    for (int d0 = 0; d0 < D; d0 += 32) {
-        __syncthreads();
-        stage16_rows<bf16>(qb, D, row0, Lq, d0, D, qs);
-        stage16_rows<bf16>(kb, D, c0, Lk, d0, D, ks);
-        stage16_rows<bf16>(gb, D, row0, Lq, d0, D, gs);
-        stage16_rows<bf16>(vb, D, c0, Lk, d0, D, vs);
-        __syncthreads();
-        const int ao = (wr * 32 + col) * kLd16 + h * 8, bo = (wc * 32 + col) * kLd16 + h * 8;
-        sa = mma16(qs + ao, ks + bo, sa);
-        sa = mma16(qs + ao + 16, ks + bo + 16, sa);
-        pa = mma16(gs + ao, vs + bo, pa);
-        pa = mma16(gs + ao + 16, vs + bo + 16, pa);
-    }
-    __syncthreads();  // every wave is done with the operand tiles: reuse the LDS for the outputs
-    bf16 *po = lds, *dso = lds + 64 * kSdpOutLd;
-    const int fl = wc * 32 + col, f = c0 + fl;
-    const bool fv = f < Lk;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int rl = wr * 32 + crow(r, h), rr = row0 + rl;
-        float pr = 0.f, ds = 0.f;
-        if (fv && rr < Lq) {
-            pr = expf(sa[r] * scale - lden[(int64_t)bt * stat_bt_stride + rr]);
-            // dS from the bf16-rounded P, as the products that consume P see it
-            const float prb = (float)to_bf16(pr);
-            ds = prb * (pa[r] - delta[(int64_t)bt * stat_bt_stride + rr]) * scale;
-        }
-        po[rl * kSdpOutLd + fl] = to_bf16(pr);
-        dso[rl * kSdpOutLd + fl] = to_bf16(ds);
-    }
-    __syncthreads();
-    bf16* pb = P + (int64_t)bt * p_bt_stride;
-    bf16* db = dS + (int64_t)bt * p_bt_stride;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int qd = threadIdx.x + 256 * u, rl = qd / 8, cl = (qd % 8) * 8;  // 64 rows x 8 chunks
-        // ncols_pad is a multiple of 8, so a chunk is wholly inside or wholly outside
-        if (row0 + rl < Lq && c0 + cl < ncols_pad) {
-            const int64_t o = (int64_t)(row0 + rl) * ldp + c0 + cl;
-            *reinterpret_cast<bf16x8*>(pb + o) = *reinterpret_cast<const bf16x8*>(po + rl * kSdpOutLd + cl);
-            *reinterpret_cast<bf16x8*>(db + o) = *reinterpret_cast<const bf16x8*>(dso + rl * kSdpOutLd + cl);
-        }
-    }
-}
-
-// tn_kernel on bf16 operands.  Slices of 32 contraction rows x 64 columns are staged row
-// major (rows of kTrLd bf16), and each lane reads its 8 contraction slots of one column with
-// gfx950's transposing LDS read, in the layout the forward kernel uses for its V^T operand
-// (DmaTiles<64, 4>::vfrag: column db*32 + lane%32, slot order depending only on the lane
-// half, identical for both operands, so the products pair the same rows).
-using TrTile = DmaTiles<64, 4>;
-constexpr int kTrLd = TrTile::VLD;  // 96
-
-// contraction rows [k0, k0 + 32) x columns [c0, c0 + 64), row major (rows of kTrLd bf16)
-template <class T>
-using TrSlice = Slice<T, 32, 64, kTrLd>;
-
-template <class TX, class TY>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void tn16_kernel(const TnArgs a) {
-    __shared__ __align__(16) bf16 xs[32 * kTrLd], ys[32 * kTrLd];
-    const int bt = blockIdx.z;
-    const int grp = blockIdx.y / a.nseg, sg = blockIdx.y % a.nseg;
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
-    const int wm = wave / 2, wn = wave % 2;
-    const int ntn = (a.ncols + 63) / 64;
-    const int m0 = (blockIdx.x / ntn) * 64, n0 = (blockIdx.x % ntn) * 64;
-    const int gend = min((grp + 1) * a.group_rows, a.rows);
-    const int k0 = grp * a.group_rows + sg * a.seg_rows;
-    const int k1 = min(k0 + a.seg_rows, gend);
-    const TX* xb = reinterpret_cast<const TX*>(a.x) + (int64_t)bt * a.x_bt_stride;
-    const TY* yb = reinterpret_cast<const TY*>(a.y) + (int64_t)bt * a.y_bt_stride;
-    const int vl = TrTile::vlane(lane);
-    f32x16 acc;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) acc[q] = 0.f;
-    TrSlice<TX> sx;
-    TrSlice<TY> sy;
-    if (k0 < k1) {
-        sx.load(xb, a.ldx, k0, k1, m0, a.mrows);
-        sy.load(yb, a.ldy, k0, k1, n0, a.ncols);
-    }
-    for (int k = k0; k < k1; k += 32) {
-        __syncthreads();
-        sx.store(xs);
-        sy.store(ys);
-        if (k + 32 < k1) {  // the next slice is read while this one is multiplied
-            sx.load(xb, a.ldx, k + 32, k1, m0, a.mrows);
-            sy.load(yb, a.ldy, k + 32, k1, n0, a.ncols);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TrTile::vfrag(xs, vl, wm, 0, t),
-                                                          TrTile::vfrag(ys, vl, wn, 0, t), acc, 0, 0, 0);
-    }
-    const int mm = m0 + wm * 32, nn = n0 + wn * 32;
-    if (mm >= a.mrows || nn + col >= a.ncols) return;
-    float* out = a.part + (((int64_t)bt * a.ngroups + grp) * a.nseg + sg) * a.mrows * a.ncols;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const int r = mm + crow(q, h);
-        if (r < a.mrows) out[(int64_t)r * a.ncols + nn + col] = acc[q];
-    }
-}
-
 // out[o * ostride + e] (+)= sum_{b < nb} sum_{s < ns} part[((b * no + o) * ns + s) * E + e],
 // summed in that order (and then added to out when accumulating)
 __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ part, float* __restrict__ out, int nb,
@@ -779,34 +575,6 @@ hipError_t launch_nt(const NtArgs& a, const GradArgs& s, bool x_bf16, bool y_bf1
     return launch_nt_t<float, float>(a, s, stream);
 }
 
-hipError_t launch_nt16(NtArgs a, const GradArgs& s, bool x_bf16, bool y_bf16, hipStream_t stream) {
-    a.tiles_per_group = (a.group_rows + 63) / 64;
-    const dim3 grid((a.ncols + 63) / 64, a.ngroups * a.tiles_per_group, s.BH);
-    if (x_bf16 && y_bf16)
-        hipLaunchKernelGGL((nt16_kernel<bf16, bf16>), grid, dim3(256), 0, stream, a, s);
-    else if (x_bf16)
-        hipLaunchKernelGGL((nt16_kernel<bf16, float>), grid, dim3(256), 0, stream, a, s);
-    else if (y_bf16)
-        hipLaunchKernelGGL((nt16_kernel<float, bf16>), grid, dim3(256), 0, stream, a, s);
-    else
-        hipLaunchKernelGGL((nt16_kernel<float, float>), grid, dim3(256), 0, stream, a, s);
-    return hipGetLastError();
-}
-
-hipError_t launch_tn16(const TnArgs& a, int BH, bool x_bf16, bool y_bf16, hipStream_t stream) {
-    const int blocks = ((a.mrows + 63) / 64) * ((a.ncols + 63) / 64);
-    const dim3 grid(blocks, a.ngroups * a.nseg, BH);
-    if (x_bf16 && y_bf16)
-        hipLaunchKernelGGL((tn16_kernel<bf16, bf16>), grid, dim3(256), 0, stream, a);
-    else if (x_bf16)
-        hipLaunchKernelGGL((tn16_kernel<bf16, float>), grid, dim3(256), 0, stream, a);
-    else if (y_bf16)
-        hipLaunchKernelGGL((tn16_kernel<float, bf16>), grid, dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL((tn16_kernel<float, float>), grid, dim3(256), 0, stream, a);
-    return hipGetLastError();
-}
-
 __global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ in, bf16* __restrict__ out,
                                                       int64_t n4) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
@@ -827,18 +595,6 @@ hipError_t launch_to_bf16(const float* in, void* out, int64_t n, hipStream_t str
     if (blocks < 1) return hipSuccess;
     hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in, reinterpret_cast<bf16*>(out),
                        n4);
-    return hipGetLastError();
-}
-
-hipError_t launch_sdp16(const void* q, const void* k, const void* g, const void* v, int64_t bt_stride, int D,
-                        int Lq, int Lk, int ncols_pad, const float* lden, const float* delta, int64_t stat_bt_stride,
-                        float scale, void* P, void* dS, int64_t p_bt_stride, int ldp, int BH, hipStream_t stream) {
-    const dim3 grid((unsigned)((ncols_pad + 63) / 64), (unsigned)((Lq + 63) / 64), BH);
-    hipLaunchKernelGGL(sdp16_kernel, grid, dim3(256), 0, stream, reinterpret_cast<const bf16*>(q),
-                       reinterpret_cast<const bf16*>(k), reinterpret_cast<const bf16*>(g),
-                       reinterpret_cast<const bf16*>(v), bt_stride, D, Lq, Lk, ncols_pad, lden, delta,
-                       stat_bt_stride, scale, reinterpret_cast<bf16*>(P), reinterpret_cast<bf16*>(dS), p_bt_stride,
-                       ldp);
     return hipGetLastError();
 }
 

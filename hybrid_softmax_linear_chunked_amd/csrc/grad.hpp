@@ -68,18 +68,8 @@ hipError_t launch_bwd_softmax(BwdArgs a, int D, hipStream_t stream);
 
 hipError_t launch_nt(const NtArgs& a, const GradArgs& s, bool x_bf16, bool y_bf16, hipStream_t stream);
 hipError_t launch_tn(const TnArgs& a, int BH, bool y_bf16, hipStream_t stream);
-// The same products with operands rounded to bf16 and the bf16 matrix core (nt: modes 0, 1,
-// 3 without colbias / sub_col; tn: float X).
-hipError_t launch_nt16(NtArgs a, const GradArgs& s, bool x_bf16, bool y_bf16, hipStream_t stream);
-hipError_t launch_tn16(const TnArgs& a, int BH, bool x_bf16, bool y_bf16, hipStream_t stream);
 // out[i] = in[i] rounded to bf16 (ties to even), n a multiple of 4
 hipError_t launch_to_bf16(const float* in, void* out, int64_t n, hipStream_t stream);
-// Scores and dP of a chunk window in one pass (bf16 q, k, v, g, all [rows][D] with slab
-// stride bt_stride, pointers at the window / chunk start): P and dS written as bf16 rows of
-// ldp (slab stride p_bt_stride), columns [Lk, ncols_pad) zero.
-hipError_t launch_sdp16(const void* q, const void* k, const void* g, const void* v, int64_t bt_stride, int D,
-                        int Lq, int Lk, int ncols_pad, const float* lden, const float* delta, int64_t stat_bt_stride,
-                        float scale, void* P, void* dS, int64_t p_bt_stride, int ldp, int BH, hipStream_t stream);
 hipError_t launch_grad_reduce(const float* part, float* out, int nb, int no, int ns, int64_t E, hipStream_t stream,
                               int64_t out_stride = -1, bool accumulate = false);
 hipError_t launch_grad_suffix(float* R, int BH, int nc, int64_t E, hipStream_t stream);
