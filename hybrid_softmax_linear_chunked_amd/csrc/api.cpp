@@ -186,10 +186,59 @@ rehyat_status rehyat_phi(const rehyat_params* p, const void* x, const void* w, c
     return hip_status(launch_phi(a, p->in_dtype, stream));
 }
 
-// Workspace of the chunk-parallel form: the per-frame partials and chunk state images.
-static size_t parallel_ws_bytes(const rehyat_params* p) {
+// Workspace of the chunk-parallel form: the per-frame partials and chunk state images, then
+// the attention stage's tail-split scratch (bf16 inputs): one arrival counter per split
+// tile, then the partials of both halves.
+struct ParallelWs {
+    int splits, split_per_xcd;
+    size_t cnt, part, total;
+};
+
+static ParallelWs parallel_ws(const rehyat_params* p) {
+    ParallelWs L;
     const int G = state_frames(p);
-    return G > 0 ? parallel_layout(p, G).total : 0;
+    const size_t base = G > 0 ? parallel_layout(p, G).total : 0;
+    L.splits = 0;
+    L.split_per_xcd = 0;
+    if (p->in_dtype == REHYAT_BF16) {
+        AttnArgs a = attn_common(p, nullptr, nullptr);
+        a.nchunks = num_chunks(p);
+        L.splits = wide_split_plan(a);
+        L.split_per_xcd = a.split_per_xcd;
+    }
+    L.cnt = base;
+    L.part = L.cnt + (L.splits > 0 ? align256((size_t)L.splits * sizeof(unsigned)) : 0);
+    L.total = L.part + (size_t)L.splits * wide_split_part_bytes(p->D);
+    return L;
+}
+
+static size_t parallel_ws_bytes(const rehyat_params* p) { return parallel_ws(p).total; }
+
+// Workspace of a streaming chunk step: the per-frame partials of up to Tc frames, then for
+// bf16 inputs the tail-split scratch of the first chunk's attention launch, which splits
+// the same tiles as the chunk-parallel grid (counters zeroed by the first step).
+struct StreamWs {
+    int splits, split_per_xcd;
+    size_t cnt, part, total;
+};
+
+static StreamWs stream_ws(const rehyat_params* p) {
+    StreamWs L;
+    L.splits = 0;
+    L.split_per_xcd = 0;
+    if (p->in_dtype == REHYAT_BF16) {
+        AttnArgs a = attn_common(p, nullptr, nullptr);
+        a.stream = 1;
+        a.s_frames = p->Tc;
+        a.nchunks = 1;
+        a.split_per_xcd = 1;  // asked for; the plan decides
+        L.splits = wide_split_plan(a);
+        L.split_per_xcd = a.split_per_xcd;
+    }
+    L.cnt = partial_bytes(p, p->Tc);
+    L.part = L.cnt + (L.splits > 0 ? align256((size_t)L.splits * sizeof(unsigned)) : 0);
+    L.total = L.part + (size_t)L.splits * wide_split_part_bytes(p->D);
+    return L;
 }
 
 size_t rehyat_workspace_bytes(const rehyat_params* p) {
@@ -204,9 +253,13 @@ rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, cons
     if (st != REHYAT_OK) return st;
     if (!aligned16(k) || !aligned16(v) || !aligned16(wk) || !aligned4_or_null(bk)) return REHYAT_EALIGN;
     const int G = state_frames(p);
-    const size_t need = parallel_ws_bytes(p);
+    const ParallelWs WL = parallel_ws(p);
+    const size_t need = WL.total;
     if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0)) return REHYAT_EWORKSPACE;
-    if (G == 0) return REHYAT_OK;
+    // the attention stage's tail-split counters start at zero (each split's second arrival
+    // sets its counter back, so they stay zero between attention calls)
+    unsigned* const cnt = WL.splits > 0 ? reinterpret_cast<unsigned*>(reinterpret_cast<char*>(ws) + WL.cnt) : nullptr;
+    if (G == 0) return cnt ? hip_status(launch_zero(reinterpret_cast<float*>(cnt), WL.splits, stream)) : REHYAT_OK;
 
     const int64_t N = (int64_t)p->T * p->frame_tokens;
     const int BH = p->B * p->H;
@@ -244,6 +297,8 @@ rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, cons
     sc.Tc = p->Tc;
     sc.To = p->To;
     sc.linear_only = p->linear_only;
+    sc.zero_cnt = cnt;
+    sc.nzero = WL.splits;
     return hip_status(launch_scan(sc, p->in_dtype, stream));
 }
 
@@ -262,7 +317,8 @@ rehyat_status rehyat_parallel_attend(const rehyat_params* p, const void* q, cons
             return REHYAT_EALIGN;
     }
     const int G = state_frames(p);
-    const size_t need = parallel_ws_bytes(p);
+    const ParallelWs WL = parallel_ws(p);
+    const size_t need = WL.total;
     if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0)) return REHYAT_EWORKSPACE;
 
     const int64_t N = (int64_t)p->T * p->frame_tokens;
@@ -292,6 +348,12 @@ rehyat_status rehyat_parallel_attend(const rehyat_params* p, const void* q, cons
     a.aux_bh_stride = N;
     a.stream = 0;
     a.nchunks = num_chunks(p);
+    a.split_per_xcd = WL.split_per_xcd;
+    if (WL.splits > 0) {
+        // arrival counters: zeroed by rehyat_parallel_states, left zero by every call
+        a.split_cnt = reinterpret_cast<unsigned*>(w + WL.cnt);
+        a.split_part = reinterpret_cast<float*>(w + WL.part);
+    }
     return hip_status(launch_attn(a, p->in_dtype, p->out_dtype, stream));
 }
 
@@ -332,7 +394,7 @@ size_t rehyat_state_bytes(const rehyat_params* p) {
 
 size_t rehyat_stream_workspace_bytes(const rehyat_params* p) {
     if (check_params(p, false) != REHYAT_OK) return 0;
-    return partial_bytes(p, p->Tc);
+    return stream_ws(p).total;
 }
 
 rehyat_status rehyat_state_init(const rehyat_params* p, void* state, rehyat_stream* st,
@@ -368,7 +430,8 @@ rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stre
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(wq) || !aligned16(wk) ||
         !aligned16(out) || !aligned4_or_null(bq) || !aligned4_or_null(bk))
         return REHYAT_EALIGN;
-    const size_t need = partial_bytes(p, p->Tc);
+    const StreamWs WS = stream_ws(p);
+    const size_t need = WS.total;
     if (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0) return REHYAT_EWORKSPACE;
 
     const StateLayout L = state_layout(p);
@@ -496,6 +559,20 @@ rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stre
     a.s_ls = (int)ls;
     a.s_pad = pad;
     a.nchunks = 1;
+    if (f0 == 0 && WS.splits > 0) {
+        // the first chunk splits the tiles the chunk-parallel grid splits (a first chunk
+        // shorter than Tc, the whole clip, at most as many as a full one); its counters
+        // start at zero here and every second arrival sets its counter back
+        a.split_per_xcd = 1;  // asked for; the plan decides
+        const int splits = wide_split_plan(a);
+        if (splits > 0) {
+            char* const wsb = reinterpret_cast<char*>(ws);
+            a.split_cnt = reinterpret_cast<unsigned*>(wsb + WS.cnt);
+            a.split_part = reinterpret_cast<float*>(wsb + WS.part);
+            s = hip_status(launch_zero(reinterpret_cast<float*>(a.split_cnt), splits, stream));
+            if (s != REHYAT_OK) return s;
+        }
+    }
     // 3. frames leaving the window before the next chunk.  Their partials read only K/V
     //    of the held frames and of the chunk, so for bf16 inputs they run inside the
     //    attention launch, in workgroups after the tiles; the scan into S, Z follows it

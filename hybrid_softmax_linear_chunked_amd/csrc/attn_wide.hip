@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void attn_wide_kernel(const Att
     {
         auto u = [](int& x) { x = __builtin_amdgcn_readfirstlane(x); };
         u(w.bh); u(w.hh); u(w.c); u(w.qt); u(w.q0); u(w.Lq); u(w.Lk); u(w.ls); u(w.img_slot);
-        u(w.src.len1);
+        u(w.src.len1); u(w.split); u(w.half);
         w.src.k1 = static_cast<const T*>(uniform_ptr(w.src.k1));
         w.src.v1 = static_cast<const T*>(uniform_ptr(w.src.v1));
         w.src.k2 = static_cast<const T*>(uniform_ptr(w.src.k2));
@@ -352,9 +352,13 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void attn_wide_kernel(const Att
 
     const float sc = a.scale_log2;
     const int nt = (Lk + BK - 1) / BK;    // 64-token tiles
-    // sweep positions [p0, p1) of this workgroup: the whole window
-    constexpr int p0 = 0;
-    const int p1 = nt;
+    // sweep positions [p0, p1) of this workgroup: all, or one half of a split tile's window
+    int p0 = 0, p1 = nt;
+    if (w.split >= 0) {
+        const int hp = (nt + 1) / 2;
+        if (w.half == 0) p1 = hp;
+        else p0 = hp;
+    }
     const bool ragged = Lk % BK != 0;
     // Tiles are processed last one first: position i of the sweep holds window tile
     // tile_of(i), so the only ragged tile (and the masking it needs) comes before the
@@ -597,6 +601,70 @@ __global__ __launch_bounds__(kWideWaves * 64, 1) void attn_wide_kernel(const Att
         run(false, l_tot);
     }
 
+    if (w.split >= 0) {
+        // Tail split: both halves store their partial (unnormalised O, reference, row sum);
+        // the second to arrive merges the other's into its own and goes on to the epilogue,
+        // the first is done.  Partials and arrival count are agent-scope atomic accesses
+        // (stores written through to the level every CU of the device sees, loads served
+        // from it), and every wave waits for its stores to complete before the barrier that
+        // precedes the count, so the second arrival reads complete partials.  No device-wide
+        // fence: on this part it writes back and invalidates the whole L2 of the XCD.
+        constexpr int NR = NDB * QB * 16 + 2 * QB;  // values per lane
+        float* const pair = a.split_part + (size_t)64 * NR * NW * 2 * w.split;
+        float* const mine = pair + (size_t)64 * NR * (w.half * NW + wave) + lane;
+        auto put = [](float* p, float x) { __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+        auto get = [](const float* p) {
+            return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        int r = 0;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) put(mine + 64 * r++, oacc[db][qb][e]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            put(mine + 64 * r++, m_ref[qb]);
+            put(mine + 64 * r++, l_tot[qb]);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are complete
+        __syncthreads();
+        unsigned prev = 0;
+        if (tid == 0) prev = __hip_atomic_fetch_add(a.split_cnt + w.split, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!__syncthreads_or(tid == 0 && prev != 0)) return;
+        // the merge is written in half order (half 0's terms first) whichever half runs it,
+        // so the result does not depend on the arrival order
+        const float* const other = pair + (size_t)64 * NR * ((1 - w.half) * NW + wave) + lane;
+        const bool h0 = w.half == 0;
+        float f0q[QB], f1q[QB];
+        r = NDB * QB * 16;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float mo = get(other + 64 * r++), lo = get(other + 64 * r++);
+            const float m0 = h0 ? m_ref[qb] : mo, m1 = h0 ? mo : m_ref[qb];
+            const float l0 = h0 ? l_tot[qb] : lo, l1 = h0 ? lo : l_tot[qb];
+            const float mm = fmaxf(m0, m1);
+            const float f0 = __builtin_amdgcn_exp2f(m0 - mm), f1 = __builtin_amdgcn_exp2f(m1 - mm);
+            l_tot[qb] = __builtin_fmaf(l0, f0, l1 * f1);
+            m_ref[qb] = mm;
+            f0q[qb] = f0;
+            f1q[qb] = f1;
+        }
+        r = 0;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float xs = oacc[db][qb][e], xo = get(other + 64 * r++);
+                    const float x0 = h0 ? xs : xo, x1 = h0 ? xo : xs;
+                    oacc[db][qb][e] = __builtin_fmaf(x0, f0q[qb], x1 * f1q[qb]);
+                }
+        if (tid == 0) __hip_atomic_store(a.split_cnt + w.split, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
 
     if constexpr (EPI_ALL) wide_linear_and_merge<OT, D, NW, QB>(a, w, smem, qw, wave, has_soft, has_lin, qf, oacc, m_ref, l_tot);
     else linear_and_merge<T, OT, D, QB, NT>(a, w, smem, qw, has_soft, has_lin, qf, oacc, m_ref, l_tot);
@@ -632,6 +700,31 @@ static hipError_t launch_wide_d(const AttnArgs& a, hipStream_t stream) {
         case 128: return launch_wide_one<OT, 128, STREAM>(a, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+// Tail split plan of a bf16 launch: per XCD, the last kSplitPerXcd chunk-0 query tiles run
+// as two halves, where chunk 0's window spans at least four 64-token tiles (each half then
+// sweeps two or more).  The rule and the tiles depend on chunk 0 alone (its min(Tc, T)
+// frames), so a streaming launch of the first chunk (which splits when the host asks for
+// it) splits exactly the tiles the chunk-parallel grid splits, and a one-chunk clip splits
+// the same tiles whatever Tc >= T it is run with: the outputs stay equal bit for bit.
+// Sets a.split_per_xcd; returns the number of split tiles.
+int wide_split_plan(AttnArgs& a) {
+    constexpr int kSplitPerXcd = 8, NW = kWideWaves, QB = kWideQB;
+    const int want = a.split_per_xcd;
+    a.split_per_xcd = 0;
+    if (a.linear_only || (a.stream && want == 0)) return 0;
+    const int f = a.stream ? a.s_frames : (a.Tc < a.T ? a.Tc : a.T);
+    if ((f * a.n + 63) / 64 < 4) return 0;
+    a.split_per_xcd = kSplitPerXcd;
+    AttnArgs b = a;
+    return attn_grid(b, NW * QB * 32);
+}
+
+// Scratch bytes of one split: two halves x waves x 64 lanes x (O + reference + sum).
+size_t wide_split_part_bytes(int D) {
+    const size_t nr = (size_t)(D / 32) * kWideQB * 16 + 2 * kWideQB;
+    return 2 * (size_t)kWideWaves * 64 * nr * sizeof(float);
 }
 
 hipError_t launch_attn_wide(const AttnArgs& a, int out_dtype, hipStream_t stream) {

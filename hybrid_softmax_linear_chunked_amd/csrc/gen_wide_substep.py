@@ -316,16 +316,18 @@ def tclobbers(L):
     return [f'"v{i}"' for i in range(R["T"], R["END"])]
 
 
-def asm_stmt(lines, outs, ins, clob, end=None):
-    # first line: a comment naming the compiler-assigned operands and the pinned range, which
-    # a test checks in the compiled kernel (no such operand may land in a pinned register)
+def asm_stmt(lines, outs, ins, clob, end=None, scalars=False):
+    # first line: a comment naming the compiler-assigned operands and the pinned range (the
+    # scalar range only where the block pins it), which a test checks in the compiled
+    # kernel (no such operand may land in a pinned register)
     free = []
     for op in outs + ins:
         m = re.match(r'\[(\w+)\] "[=+&]*([vs])"', op)
         if m:
             free.append(f"{m.group(1)}=%[{m.group(1)}]")
     if end is not None:
-        lines = [f"; pinned v0-v{end - 1} s{SP}-s{SP + 11}; free " + " ".join(free)] + lines
+        srange = f" s{SP}-s{SP + 11}" if scalars else ""
+        lines = [f"; pinned v0-v{end - 1}{srange}; free " + " ".join(free)] + lines
     body = "\\n\\t".join(lines)
     return (f'    asm volatile("{body}"\n        : ' + ",\n          ".join(outs)
             + "\n        : " + ",\n          ".join(ins)
@@ -468,7 +470,7 @@ def cxx_loop(D, stream, no_barrier=False, no_dma=False):
     clob = tclobbers(L) + [f'"s{i}"' for i in range(KB, KB + 4)] + ['"scc"', '"memory"']
     return (f"template <> __device__ inline void wide_loop<{D}, {str(stream).lower()}>(WIDE_LOOP_ARGS({D})) {{\n"
             "    uint32_t m0s, it, t0, t1, kt, vt;\n    uint64_t es;\n"
-            + asm_stmt(b.lines, outs, ins, clob, L["reg"]["END"]) + "}\n")
+            + asm_stmt(b.lines, outs, ins, clob, L["reg"]["END"], scalars=True) + "}\n")
 
 
 def guard(D):

@@ -61,6 +61,14 @@ struct AttnArgs {
     // the attention tiles leave free
     int side_blocks;
     StateArgs side;
+    // Tail split (bf16 kernel; 0 elsewhere): the last split_per_xcd chunk-0 query tiles of
+    // each XCD run as two workgroups, one per half of the window's sweep positions, which
+    // exchange their partials through split_part ([split][half][wave][value][lane] floats)
+    // and count their arrival in split_cnt (one per split, zero before the launch; the
+    // second arrival merges and sets it back to zero).
+    int split_per_xcd;
+    float* split_part;
+    unsigned* split_cnt;
 };
 
 // Copy of frames [f0, f0 + cnt) of a two-segment source into dst frames [0, cnt).
@@ -97,6 +105,8 @@ struct ScanArgs {
     // copy `copy`, which touches none of the scan's data
     int copy_blocks;
     CopyArgs copy;
+    unsigned* zero_cnt;     // counters to set to zero on the way (the attention stage's
+    int nzero;              // tail-split arrival counters), or null
 };
 
 
@@ -111,6 +121,10 @@ struct PhiArgs {
 
 hipError_t launch_attn(const AttnArgs& a, int in_dtype, int out_dtype, hipStream_t stream);
 hipError_t launch_attn_wide(const AttnArgs& a, int out_dtype, hipStream_t stream);
+// Tail split plan of a bf16 attention launch (sets a.split_per_xcd; returns the number of
+// split tiles) and the scratch bytes of one split.
+int wide_split_plan(AttnArgs& a);
+size_t wide_split_part_bytes(int D);
 hipError_t launch_state(const StateArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t stream);

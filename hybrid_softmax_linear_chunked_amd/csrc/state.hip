@@ -191,6 +191,8 @@ __global__ __launch_bounds__(256) void scan_kernel(const ScanArgs a) {
     const int Dphi = a.Dphi, P = a.P, D = a.D, F = Dphi * P, NJB = Dphi / 32, NDB = D / 32;
     const int bh = blockIdx.y, tid = threadIdx.x;
     const int nscan = P * NJB * NDB + 1;
+    if (a.zero_cnt && blockIdx.x == 0 && bh == 0)
+        for (int i = tid; i < a.nzero; i += 256) a.zero_cnt[i] = 0u;
     if ((int)blockIdx.x >= nscan) {
         copy_body(a.copy, blockIdx.x - nscan, a.copy_blocks, bh);
         return;

@@ -28,7 +28,10 @@
  *   - Asynchrony: all work is enqueued on the caller's stream; the return value reports
  *     validation (checked before any HIP call) and launch errors.  Device faults appear
  *     at the caller's next synchronisation.
- *   - Determinism: no atomics; repeated calls on the same inputs give identical bits.
+ *   - Determinism: repeated calls on the same inputs give identical bits.  The only atomic
+ *     is the arrival counter of the bf16 attention kernel's tail split (the last chunk-0
+ *     query tiles of each XCD run as two workgroups over the two halves of the window; the
+ *     second to finish merges both partials, in the same order whichever it is).
  *   - Thread safety: no shared mutable state beyond a per-device cache of kernel LDS limits
  *     (idempotent); one in-flight call per streaming state.
  */
@@ -103,8 +106,11 @@ rehyat_status rehyat_phi(const rehyat_params* p, const void* x, const void* w, c
 
 /* Workspace bytes needed by rehyat_forward_parallel(_aux): per-frame state partials,
  * float32 [B,H,G,F,D] + [B,H,G,F] for the G frames that enter some chunk's linear region,
- * then one image of the state per chunk (S in in_dtype, Z float32).  0 if no chunk has a
- * linear region. */
+ * then one image of the state per chunk (S in in_dtype, Z float32); then, for bf16 inputs
+ * whose first chunk is a whole chunk (Tc frames) with a window of at least four 64-token
+ * tiles, the attention stage's tail-split scratch: one uint32 arrival counter per split
+ * tile (up to 8 per XCD; zeroed by the states stage, left zero by every attend) and per
+ * split 2 x 8 waves x 64 lanes x (D/2 + 2) float32 partials.  0 if none of these is needed. */
 size_t rehyat_workspace_bytes(const rehyat_params* p);
 
 /* Chunk-parallel forward (all chunks at once): per-frame partials of phi_k(K)^T [V|1],
@@ -123,7 +129,7 @@ rehyat_status rehyat_forward_parallel(const rehyat_params* p, const void* q, con
  * the process ends; the call allocates nothing (its first call on a device looks the area up).
  * Same operation, arguments (without ws, ws_bytes), layouts and results as
  * rehyat_forward_parallel.  REHYAT_ESCRATCH when rehyat_workspace_bytes(p) exceeds 64 MiB
- * (for example the 20 s, B = 2 layer; the 5 s Wan2.1-1.3B layer needs about 50 MB), before
+ * (for example the 20 s, B = 2 layer; the 5 s Wan2.1-1.3B layer needs about 56 MB), before
  * any launch.  Every call on a GPU uses the same area: calls that overlap on one GPU (other
  * streams, other host threads) race; calls in stream order do not. */
 rehyat_status rehyat_forward_parallel_noalloc(const rehyat_params* p, const void* q, const void* k,
@@ -141,12 +147,13 @@ rehyat_status rehyat_forward_parallel_aux(const rehyat_params* p, const void* q,
 
 /* The two stages of rehyat_forward_parallel_aux, for callers that reuse the states or time
  * the stages separately.  rehyat_parallel_states writes the per-frame partials of
- * phi_k(K)^T [V|1] and their inclusive prefix over frames into ws (blog 2.3 state sums);
- * rehyat_parallel_attend runs the windowed softmax tile kernel with the fused linear part,
- * only reading ws, so it may run any number of times per states call.  Same arguments,
- * layouts and status codes as above; ws must hold the states of the same k, v, wk, bk when
- * attend runs (stream order suffices; a states call must not overlap an attend on the
- * same ws). */
+ * phi_k(K)^T [V|1] and their inclusive prefix over frames into ws (blog 2.3 state sums)
+ * and zeroes the tail-split counters; rehyat_parallel_attend runs the windowed softmax
+ * tile kernel with the fused linear part, reading the states and using only the
+ * tail-split scratch of ws, whose counters it leaves zero, so it may run any number of
+ * times per states call.  Same arguments, layouts and status codes as above; ws must hold
+ * the states of the same k, v, wk, bk when attend runs (stream order suffices; calls on
+ * the same ws must not overlap). */
 rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, const void* v,
                                      const void* wk, const float* bk, void* ws, size_t ws_bytes,
                                      hipStream_t stream);
@@ -162,7 +169,10 @@ rehyat_status rehyat_parallel_attend(const rehyat_params* p, const void* q, cons
 size_t rehyat_state_bytes(const rehyat_params* p);
 
 /* Workspace bytes for rehyat_chunk_step: per-frame partials for up to Tc frames,
- * float32 [B,H,Tc,F,D] + [B,H,Tc,F].  Independent of the clip length. */
+ * float32 [B,H,Tc,F,D] + [B,H,Tc,F], then for bf16 inputs the tail-split scratch of the
+ * first chunk's attention launch (the same layout and split tiles as the chunk-parallel
+ * form's; its counters are zeroed by the first chunk step).  Independent of the clip
+ * length. */
 size_t rehyat_stream_workspace_bytes(const rehyat_params* p);
 
 /* Zero S and Z on `stream` and reset the host handle (frames_seen = 0). */
@@ -173,7 +183,7 @@ rehyat_status rehyat_state_init(const rehyat_params* p, void* state, rehyat_stre
  * frames must equal Tc except on a final, shorter call, after which the stream is closed
  * (REHYAT_ESTATE on further calls).  Outputs equal those of rehyat_forward_parallel on
  * the concatenated clip bit for bit: the same kernels add the same partials in the same
- * order and sweep the same window tiles.  The call reads S, Z and the held overlap frames,
+ * order, sweep the same window tiles and, on the first chunk, split the same tiles.  The call reads S, Z and the held overlap frames,
  * then folds the frames that leave the softmax window into S, Z (for bf16 inputs their
  * partials run in the attention launch, on CUs its tiles leave free) and keeps the last
  * To frames. */

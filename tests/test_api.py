@@ -56,9 +56,18 @@ def test_sizes_follow_layouts(L):
     F = WAN.P * WAN.Dphi
     assert rh.features(WAN) == 256
     # chunk-parallel: per-frame partials for the 17 frames that enter some chunk's state,
-    # then one state image (S in the input dtype, operand order, Z in float) per chunk
+    # then one state image (S in the input dtype, operand order, Z in float) per chunk,
+    # followed by the attention stage's tail-split scratch (bf16 inputs): per XCD (8
+    # contiguous shares of the 12 * 19 chunk-0 query tiles of 256 queries) the last 8 tiles
+    # are split, each with an arrival counter and two halves x 8 waves x 64 lanes x
+    # (4 * 16 O values + reference + row sum) floats
+    ns = 12 * 19
+    splits = sum(min(ns * (x + 1) // 8 - ns * x // 8, 8) for x in range(8))
+    assert splits == 64
+    split_bytes = a(splits * 4) + splits * 2 * 8 * 64 * (4 * 16 + 2) * 4
     assert rh.workspace_bytes(WAN) == (a(12 * 17 * F * 128 * 4) + a(12 * 17 * F * 4)
-                                       + a(12 * 7 * F * 128 * 2) + a(12 * 7 * F * 4))
+                                       + a(12 * 7 * F * 128 * 2) + a(12 * 7 * F * 4) + split_bytes)
+    # fp32 inputs run the other tile kernel, which does not split
     assert rh.workspace_bytes(WAN.with_(in_dtype=0)) == (a(12 * 17 * F * 128 * 4) + a(12 * 17 * F * 4)
                                                          + a(12 * 7 * F * 128 * 4) + a(12 * 7 * F * 4))
     # streaming: S, Z, the image of the current state and two overlap buffers of K and V
@@ -67,9 +76,18 @@ def test_sizes_follow_layouts(L):
     assert rh.state_bytes(WAN) == (a(12 * F * 128 * 4) + a(12 * F * 4) + a(12 * F * 128 * 2)
                                    + a(12 * F * 4) + 4 * a(ov))
     assert rh.state_bytes(WAN.with_(T=81)) == rh.state_bytes(WAN)
-    assert rh.stream_workspace_bytes(WAN) == a(12 * 3 * F * 128 * 4) + a(12 * 3 * F * 4)
-    # one chunk covering the clip has no linear region and needs no workspace
-    assert rh.workspace_bytes(WAN.with_(Tc=21)) == 0
+    # the step's workspace: partials of up to Tc frames, then the first chunk's split
+    # scratch (the same tiles as the chunk-parallel grid splits)
+    assert rh.stream_workspace_bytes(WAN) == a(12 * 3 * F * 128 * 4) + a(12 * 3 * F * 4) + split_bytes
+    assert rh.stream_workspace_bytes(WAN.with_(in_dtype=0)) == a(12 * 3 * F * 128 * 4) + a(12 * 3 * F * 4)
+    # one chunk covering the clip has no linear region; bf16 inputs need only the split
+    # scratch (12 * 128 tiles, 8 split per XCD), fp32 inputs nothing
+    assert rh.workspace_bytes(WAN.with_(Tc=21)) == a(64 * 4) + 64 * 2 * 8 * 64 * (4 * 16 + 2) * 4
+    assert rh.workspace_bytes(WAN.with_(Tc=21, in_dtype=0)) == 0
+    # a clip shorter than one chunk splits the tiles of its T frames (2 frames: 12 * 13 tiles,
+    # still 8 per XCD); a window under four tiles splits nothing
+    assert rh.workspace_bytes(WAN.with_(T=2)) == a(64 * 4) + 64 * 2 * 8 * 64 * (4 * 16 + 2) * 4
+    assert rh.workspace_bytes(WAN.with_(n=50, Tc=3, T=3)) == 0
 
 
 @pytest.mark.parametrize("change,status", [
