@@ -841,7 +841,8 @@ rehyat_status linear_branch(const rehyat_params* p, const GradArgs& s, const Gra
         a.rows = s.N;
         return a;
     };
-    auto pre = [&](const void* x, const void* wmat, const float* bias) {
+    // u = softplus(W x + b) into L.u and, when phi_out, its powers (blog 2.2.2) into L.phi
+    auto pre = [&](const void* x, const void* wmat, const float* bias, bool phi_out) {
         NtArgs a = nt_base();
         a.x = x;
         a.x_bt_stride = N * s.D;
@@ -860,7 +861,10 @@ rehyat_status linear_branch(const rehyat_params* p, const GradArgs& s, const Gra
         a.ldc = s.Dphi;
         a.group_rows = s.N;
         a.ngroups = 1;
-        return launch_nt(a, s, bf, bf, stream);
+        a.softplus = 1;
+        a.phi = phi_out ? F32(L.phi) : nullptr;
+        a.phi_bt_stride = N * s.F;
+        return launch_nt(a, s, bf, bf, stream, bf);
     };
     auto dw = [&](const void* x, float* dwout, float* dbout) -> hipError_t {
         TnArgs t;
@@ -879,7 +883,7 @@ rehyat_status linear_branch(const rehyat_params* p, const GradArgs& s, const Gra
         t.ngroups = 1;
         t.seg_rows = kGradSegRows;
         t.nseg = L.nseg_w;
-        hipError_t e = launch_tn(t, s.BH, bf, stream);
+        hipError_t e = launch_tn(t, s.BH, bf, stream, bf);
         if (e == hipSuccess) e = launch_grad_reduce(F32(L.wp), dwout, p->B, p->H, L.nseg_w, (int64_t)s.Dphi * s.D, stream);
         if (e == hipSuccess && dbout) {
             e = launch_grad_colsum(F32(L.u), s.BH, N, s.Dphi, kColsumSegRows, F32(L.bp), stream);
@@ -909,12 +913,14 @@ rehyat_status linear_branch(const rehyat_params* p, const GradArgs& s, const Gra
         a.group_rows = s.N;
         a.ngroups = 1;
         a.accumulate = 1;
-        return launch_nt(a, s, false, false, stream);
+        return launch_nt(a, s, false, false, stream, bf);
     };
 
+    // bf16 inputs with whole-block parts: the feature gradients write dpre over u directly
+    const bool fuse = bf && ntf16_fusable(s);
+
     // query side: phi_q, dphi_q = [S_c | -Z_c] [a | h], R per chunk, dpre_q, dW_q, db_q
-    GRAD_TRY(pre(q, wq, bq));
-    GRAD_TRY(launch_grad_phi_fwd(s, F32(L.u), F32(L.phi), stream));
+    GRAD_TRY(pre(q, wq, bq, true));
     {
         NtArgs a = nt_base();
         a.x = F32(L.ah);
@@ -932,7 +938,14 @@ rehyat_status linear_branch(const rehyat_params* p, const GradArgs& s, const Gra
         a.ldc = s.F;
         a.group_rows = s.Tc * s.n;
         a.ngroups = s.nc;
-        GRAD_TRY(launch_nt(a, s, false, false, stream));
+        if (fuse) {
+            a.c = F32(L.u);
+            a.c_bt_stride = N * s.Dphi;
+            a.ldc = s.Dphi;
+            GRAD_TRY(launch_ntf16(a, s, false, stream));
+        } else {
+            GRAD_TRY(launch_nt(a, s, false, false, stream, bf));
+        }
     }
     {
         TnArgs t;
@@ -951,18 +964,18 @@ rehyat_status linear_branch(const rehyat_params* p, const GradArgs& s, const Gra
         t.ngroups = s.nc;
         t.seg_rows = s.n;
         t.nseg = s.Tc;
-        GRAD_TRY(launch_tn(t, s.BH, false, stream));
+        GRAD_TRY(launch_tn(t, s.BH, false, stream, bf));
         const int64_t E = (int64_t)s.F * LD;
         GRAD_TRY(launch_grad_reduce(F32(L.rp), F32(L.r), 1, s.BH * s.nc, s.Tc, E, stream));
         GRAD_TRY(launch_grad_suffix(F32(L.r), s.BH, s.nc, E, stream));
     }
-    GRAD_TRY(launch_grad_phi_bwd(s, F32(L.u), F32(L.dphi), stream));
+    if (!fuse) GRAD_TRY(launch_grad_phi_bwd(s, F32(L.u), F32(L.dphi), stream));
     GRAD_TRY(dw(q, dwq, dbq));
     if (dq) GRAD_TRY(dx(wq, dq));
 
-    // key side: phi_k, (dv += R^T phi_k), dphi_k = R v - r per key frame, dpre_k, dW_k, db_k
-    GRAD_TRY(pre(k, wk, bk));
-    GRAD_TRY(launch_grad_phi_fwd(s, F32(L.u), F32(L.phi), stream));
+    // key side: u_k (phi_k only for dv += R^T phi_k), dphi_k = R v - r per key frame, dpre_k,
+    // dW_k, db_k
+    GRAD_TRY(pre(k, wk, bk, dv != nullptr));
     if (dv) {
         GRAD_TRY(launch_transpose(F32(L.r), false, (int64_t)s.F * LD, LD, F32(L.rt), (int64_t)s.D * s.F, s.F, s.F, s.D,
                                   s.BH * s.nc, stream));
@@ -983,7 +996,7 @@ rehyat_status linear_branch(const rehyat_params* p, const GradArgs& s, const Gra
         a.group_rows = s.n;
         a.ngroups = s.T;
         a.accumulate = 1;
-        GRAD_TRY(launch_nt(a, s, false, false, stream));
+        GRAD_TRY(launch_nt(a, s, false, false, stream, bf));
     }
     {
         NtArgs a = nt_base();
@@ -1003,9 +1016,16 @@ rehyat_status linear_branch(const rehyat_params* p, const GradArgs& s, const Gra
         a.ldc = s.F;
         a.group_rows = s.n;
         a.ngroups = s.T;
-        GRAD_TRY(launch_nt(a, s, bf, false, stream));
+        if (fuse) {
+            a.c = F32(L.u);
+            a.c_bt_stride = N * s.Dphi;
+            a.ldc = s.Dphi;
+            GRAD_TRY(launch_ntf16(a, s, true, stream));
+        } else {
+            GRAD_TRY(launch_nt(a, s, bf, false, stream, bf));
+        }
     }
-    GRAD_TRY(launch_grad_phi_bwd(s, F32(L.u), F32(L.dphi), stream));
+    if (!fuse) GRAD_TRY(launch_grad_phi_bwd(s, F32(L.u), F32(L.dphi), stream));
     GRAD_TRY(dw(k, dwk, dbk));
     if (dk) GRAD_TRY(dx(wk, dk));
     return REHYAT_OK;

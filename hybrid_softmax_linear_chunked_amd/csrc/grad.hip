@@ -12,12 +12,14 @@
 // and the feature map (blog 2.2.2: u = softplus(W x + b), per-part powers u^p) gives
 // dpre = sigmoid(pre) sum_p p u^(p-1) dphi_(j,p), dW = sum dpre x^T, db = sum dpre.
 //
-// The dense products run on the fp32 matrix core (v_mfma_f32_32x32x2f32) so that fp32
-// and bf16 inputs share one exact-product path:
+// The dense products:
 //   nt_kernel: C[i][f] = sum_d X[i][d] Y_m[f][d] for row groups that each read one matrix
 //              Y_m (a head's W, a chunk's [S | -Z], a key frame's suffix R);
 //   tn_kernel: per token segment, C[m][n] = sum_k X[k][m] Y[k][n] (dW and R partials);
-// both stage 64 x 32 slices of their operands through LDS with 16-byte loads along rows,
+// for fp32 inputs on the fp32 matrix core (v_mfma_f32_32x32x2f32, exact products); for
+// bf16 inputs (nt16_kernel, tn16_kernel) on the bf16 matrix core with every float operand
+// taken as the sum of two bf16 parts (about 2^-15 relative error per product).  Both stage
+// 32-element contraction slices of their operands through LDS with 16-byte loads along rows,
 // and each wave reads its MFMA operands from there (one 32x32 output block per wave);
 // and every sum over segments, frames, chunks or batches runs in a fixed order, so the
 // gradients are bitwise reproducible.
@@ -101,7 +103,84 @@ struct Slice {
             }
         }
     }
+
+    // Rows gathered: block row r comes from source row rowof(r).
+    template <class RowOf>
+    __device__ inline void load_rows(const T* src, int64_t ld, RowOf rowof, int c0, int clim) {
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            const int qd = threadIdx.x + 256 * u, r = qd / CPR, c = (qd % CPR) * EPC;
+            if (c0 + c < clim) {
+                v[u] = *reinterpret_cast<const V*>(src + (int64_t)rowof(r) * ld + c0 + c);
+            } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[u][e] = to_bf16(0.f);
+            } else {
+                v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+    }
+
+    // As bf16 parts for the bf16 matrix core: a bf16 source as it is (into hi only), a
+    // float source as hi = bf16(x) (ties to even) and lo = bf16(x - hi).
+    __device__ inline void store_split(bf16* hi, bf16* lo) const {
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            const int qd = threadIdx.x + 256 * u, r = qd / CPR, c = (qd % CPR) * EPC;
+            if constexpr (sizeof(T) == 2) {
+                *reinterpret_cast<bf16x8*>(hi + r * LD + c) = v[u];
+            } else {
+                const float x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                bf16x4 wh, wl;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    wh[e] = to_bf16(x[e]);
+                    wl[e] = to_bf16(x[e] - (float)wh[e]);
+                }
+                *reinterpret_cast<bf16x4*>(hi + r * LD + c) = wh;
+                *reinterpret_cast<bf16x4*>(lo + r * LD + c) = wl;
+            }
+        }
+    }
 };
+
+__device__ inline int part_len(int j, int Dphi, int P);
+
+// Epilogue of the nt products: lane (col, h) holds column f of rows r0 + crow(q, h).
+__device__ inline void nt_store(const NtArgs& a, const GradArgs& s, int bt, float* cb, int r0, int rend, int f, int h,
+                                const f32x16& acc, float add) {
+    if (a.softplus) {
+        // u = softplus(pre) (the form the feature-map kernel uses) and its powers
+        const int f1 = feat_index(f, 1, s.Dphi, s.P), step = part_len(f, s.Dphi, s.P);
+        float* const pb = a.phi ? a.phi + (int64_t)bt * a.phi_bt_stride + f1 : nullptr;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int rr = r0 + crow(q, h);
+            if (rr < rend) {
+                const float x = acc[q] + add;
+                const float u = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+                cb[(int64_t)rr * a.ldc + f] = u;
+                if (pb) {
+                    float pw = u;
+                    float* out = pb + (int64_t)rr * s.F;
+                    for (int p = 0; p < s.P; ++p) {
+                        out[p * step] = pw;
+                        pw *= u;
+                    }
+                }
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int rr = r0 + crow(q, h);
+        if (rr < rend) {
+            float* dst = cb + (int64_t)rr * a.ldc + f;
+            *dst = a.accumulate ? *dst + (acc[q] + add) : acc[q] + add;
+        }
+    }
+}
 
 // Rows [r0, r0 + 64) x columns [c0, c0 + 32) of a row-major source as float, dst[r][c] with
 // row stride 33 (conflict-free column reads); rows at or past rlim and columns at or past clim
@@ -176,14 +255,7 @@ __global__ __launch_bounds__(256) void nt_kernel(const NtArgs a, const GradArgs 
     float add = 0.f;
     if (a.colbias) add += a.colbias[(int64_t)(bt % s.H) * a.colbias_head_stride + f];
     if (a.sub_col >= 0) add -= load1<TY>(yrow + a.sub_col);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const int rr = row0 + wr * 32 + crow(q, h);
-        if (rr < rend) {
-            float* dst = cb + (int64_t)rr * a.ldc + f;
-            *dst = a.accumulate ? *dst + (acc[q] + add) : acc[q] + add;
-        }
-    }
+    nt_store(a, s, bt, cb, row0 + wr * 32, rend, f, h, acc, add);
 }
 
 // Slice [k0, k0 + 32) x [c0, c0 + 64) of a row-major source as float, dst[k][c] with row
@@ -235,6 +307,270 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void t
     if (mm >= a.mrows || nn >= a.ncols) return;
     float* out = a.part + (((int64_t)bt * a.ngroups + grp) * a.nseg + sg) * a.mrows * a.ncols;
     if (nn + col >= a.ncols) return;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int r = mm + crow(q, h);
+        if (r < a.mrows) out[(int64_t)r * a.ncols + nn + col] = acc[q];
+    }
+}
+
+// bf16 matrix-core forms of the two products, for bf16 inputs: a bf16 operand enters
+// v_mfma_f32_32x32x16_bf16 as it is (exactly), a float operand as two bf16 parts,
+// hi = bf16(x) and lo = bf16(x - hi), with |x - hi - lo| <= 2^-16 |x|.  A product takes
+// lo*hi + hi*lo + hi*hi (the dropped lo*lo is below 2^-16 of it), so it carries about
+// 2^-15 relative error where one bf16 rounding of a float operand would leave 2^-8;
+// accumulation is fp32.  Three matrix-core products (one when both operands are bf16) at
+// 16 times the fp32 rate.
+constexpr int kLd16 = 40;  // bf16 per LDS row of a 32-element contraction slice (8 of padding)
+
+__device__ inline f32x16 mma16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Tile (x, y, z) of a gx x gy x gz tiling for workgroup blockIdx.x of a one-dimensional grid
+// of 8 * ceil(gx gy gz / 8): workgroup g runs on XCD g % 8, and each XCD takes a contiguous
+// run of tiles with x fastest, so the tiles that read the same rows (the x of one y, z)
+// share an L2.  False for the padding workgroups.
+__device__ inline bool xcd_tile(int gx, int gy, int gz, int& x, int& y, int& z) {
+    const int total = gx * gy * gz, per = (total + 7) / 8;
+    const int t = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (t >= total) return false;
+    x = t % gx;
+    y = (t / gx) % gy;
+    z = t / (gx * gy);
+    return true;
+}
+
+__host__ inline unsigned xcd_grid(int64_t total) { return (unsigned)(8 * ((total + 7) / 8)); }
+
+// C (+)= X Y^T as nt_kernel (every mode, column bias, subtracted column, accumulation),
+// contraction slices of 32 staged as bf16 parts; a lane reads its 8 consecutive contraction
+// slots of a row with one 16-byte LDS read.
+template <class TX, class TY>
+__global__ __launch_bounds__(256) void nt16_kernel(const NtArgs a, const GradArgs s) {
+    constexpr bool XS = sizeof(TX) == 4, YS = sizeof(TY) == 4;  // float operands: hi and lo
+    constexpr int TILE = 64 * kLd16;
+    __shared__ __align__(16) bf16 xs[(XS ? 2 : 1) * TILE], ys[(YS ? 2 : 1) * TILE];
+    int bx, by, bt;
+    if (!xcd_tile((a.ncols + 63) / 64, a.ngroups * a.tiles_per_group, s.BH, bx, by, bt)) return;
+    const int grp = by / a.tiles_per_group, t = by % a.tiles_per_group;
+    const int row0 = grp * a.group_rows + t * 64;
+    const int rend = min((grp + 1) * a.group_rows, a.rows);
+    if (row0 >= rend) return;
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
+    const int wr = wave / 2, wc = wave % 2;
+    const int c0 = bx * 64;
+
+    int m;
+    if (a.mode == 0) {
+        m = bt % s.H;
+    } else if (a.mode == 1) {
+        m = bt * a.nmat + grp;
+    } else if (a.mode == 3) {
+        m = bt;
+    } else {
+        // earliest chunk whose linear region holds key frame grp
+        int c = 0;
+        while (c < a.nmat && ls_of(s, c) <= grp) ++c;
+        m = c < a.nmat ? bt * a.nmat + c : -1;
+    }
+    float* cb = a.c + (int64_t)bt * a.c_bt_stride;
+    const int f = c0 + wc * 32 + col;
+    const bool fv = f < a.ncols;
+    if (m < 0) {
+        if (a.accumulate) return;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int rr = row0 + wr * 32 + crow(q, h);
+            if (rr < rend && fv) cb[(int64_t)rr * a.ldc + f] = 0.f;
+        }
+        return;
+    }
+    const TX* xb = reinterpret_cast<const TX*>(a.x) + (int64_t)bt * a.x_bt_stride;
+    const TY* yb = reinterpret_cast<const TY*>(a.y) + (int64_t)m * a.y_mat_stride;
+    f32x16 acc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+    Slice<TX, 64, 32, kLd16> sx;
+    Slice<TY, 64, 32, kLd16> sy;
+    sx.load(xb, a.ldx, row0, rend, 0, a.K);
+    sy.load(yb, a.ldy, c0, a.ncols, 0, a.K);
+    const int xo = (wr * 32 + col) * kLd16 + h * 8, yo = (wc * 32 + col) * kLd16 + h * 8;
+    for (int d0 = 0; d0 < a.K; d0 += 32) {
+        __syncthreads();  // the previous slice has been read
+        sx.store_split(xs, xs + TILE);
+        sy.store_split(ys, ys + TILE);
+        if (d0 + 32 < a.K) {  // the next slice is read while this one is multiplied
+            sx.load(xb, a.ldx, row0, rend, d0 + 32, a.K);
+            sy.load(yb, a.ldy, c0, a.ncols, d0 + 32, a.K);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const bf16x8 xh = *reinterpret_cast<const bf16x8*>(xs + xo + 16 * u);
+            const bf16x8 yh = *reinterpret_cast<const bf16x8*>(ys + yo + 16 * u);
+            if constexpr (XS) acc = mma16(*reinterpret_cast<const bf16x8*>(xs + TILE + xo + 16 * u), yh, acc);
+            if constexpr (YS) acc = mma16(xh, *reinterpret_cast<const bf16x8*>(ys + TILE + yo + 16 * u), acc);
+            acc = mma16(xh, yh, acc);
+        }
+    }
+    if (!fv) return;
+    const TY* yrow = yb + (int64_t)f * a.ldy;
+    float add = 0.f;
+    if (a.colbias) add += a.colbias[(int64_t)(bt % s.H) * a.colbias_head_stride + f];
+    if (a.sub_col >= 0) add -= load1<TY>(yrow + a.sub_col);
+    nt_store(a, s, bt, cb, row0 + wr * 32, rend, f, h, acc, add);
+}
+
+// The feature gradients (nt modes 1 and 2) with the feature map's backward fused (blog
+// 2.2.2), bf16 matrix core as nt16_kernel.  The 64 output columns of a workgroup are the
+// JB = 64 / P features j0 .. j0 + JB - 1 with all P powers (column c: power c / JB + 1 of
+// feature j0 + c % JB; the rows of Y are read in that order), so the epilogue holds dphi of
+// every power of its features and writes, over u in C (= U [bt][N][Dphi], in place),
+//   dpre[i][j] = sigmoid(pre) sum_p p u^(p-1) dphi[i][feat(j, p)],  sigmoid(pre) = 1 - exp(-u),
+// in the arithmetic of phi_bwd_kernel; dphi itself is never stored.  Each output column's
+// sums are those of nt16_kernel, so the result is the same.  Requires every part length to
+// be a multiple of JB: P = 1, 2 or 4 and Dphi a multiple of 64.
+template <class TX, class TY, int P>
+__global__ __launch_bounds__(256) void ntf16_kernel(const NtArgs a, const GradArgs s) {
+    constexpr int JB = 64 / P, CLD = 65;
+    constexpr bool XS = sizeof(TX) == 4, YS = sizeof(TY) == 4;
+    constexpr int TILE = 64 * kLd16;
+    __shared__ __align__(16) bf16 xs[(XS ? 2 : 1) * TILE], ys[(YS ? 2 : 1) * TILE];
+    __shared__ float cs[64 * CLD];
+    int bx, by, bt;
+    if (!xcd_tile(s.Dphi / JB, a.ngroups * a.tiles_per_group, s.BH, bx, by, bt)) return;
+    const int grp = by / a.tiles_per_group, t = by % a.tiles_per_group;
+    const int row0 = grp * a.group_rows + t * 64;
+    const int rend = min((grp + 1) * a.group_rows, a.rows);
+    if (row0 >= rend) return;
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, col = lane % 32, h = lane / 32;
+    const int wr = wave / 2, wc = wave % 2;
+    const int j0 = bx * JB;
+    float* const U = a.c + (int64_t)bt * a.c_bt_stride;
+
+    int m;
+    if (a.mode == 1) {
+        m = bt * a.nmat + grp;
+    } else {
+        // earliest chunk whose linear region holds key frame grp
+        int c = 0;
+        while (c < a.nmat && ls_of(s, c) <= grp) ++c;
+        m = c < a.nmat ? bt * a.nmat + c : -1;
+    }
+    if (m < 0) {
+        // no chunk's state holds these keys: dphi = 0, so dpre = 0
+        for (int e = tid; e < 64 * JB; e += 256) {
+            const int r = e / JB, row = row0 + r;
+            if (row < rend) U[(int64_t)row * a.ldc + j0 + e % JB] = 0.f;
+        }
+        return;
+    }
+    auto yrow = [&](int c) { return feat_index(j0 + c % JB, c / JB + 1, s.Dphi, P); };
+    const TX* xb = reinterpret_cast<const TX*>(a.x) + (int64_t)bt * a.x_bt_stride;
+    const TY* yb = reinterpret_cast<const TY*>(a.y) + (int64_t)m * a.y_mat_stride;
+    f32x16 acc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+    Slice<TX, 64, 32, kLd16> sx;
+    Slice<TY, 64, 32, kLd16> sy;
+    sx.load(xb, a.ldx, row0, rend, 0, a.K);
+    sy.load_rows(yb, a.ldy, yrow, 0, a.K);
+    const int xo = (wr * 32 + col) * kLd16 + h * 8, yo = (wc * 32 + col) * kLd16 + h * 8;
+    for (int d0 = 0; d0 < a.K; d0 += 32) {
+        __syncthreads();  // the previous slice has been read
+        sx.store_split(xs, xs + TILE);
+        sy.store_split(ys, ys + TILE);
+        if (d0 + 32 < a.K) {  // the next slice is read while this one is multiplied
+            sx.load(xb, a.ldx, row0, rend, d0 + 32, a.K);
+            sy.load_rows(yb, a.ldy, yrow, d0 + 32, a.K);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const bf16x8 xh = *reinterpret_cast<const bf16x8*>(xs + xo + 16 * u);
+            const bf16x8 yh = *reinterpret_cast<const bf16x8*>(ys + yo + 16 * u);
+            if constexpr (XS) acc = mma16(*reinterpret_cast<const bf16x8*>(xs + TILE + xo + 16 * u), yh, acc);
+            if constexpr (YS) acc = mma16(xh, *reinterpret_cast<const bf16x8*>(ys + TILE + yo + 16 * u), acc);
+            acc = mma16(xh, yh, acc);
+        }
+    }
+    // dphi of the tile into LDS (with the -Y[f][sub_col] term of mode 2), then dpre
+    const int c = wc * 32 + col;
+    const float add = a.sub_col >= 0 ? -load1<TY>(yb + (int64_t)yrow(c) * a.ldy + a.sub_col) : 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) cs[(wr * 32 + crow(q, h)) * CLD + c] = acc[q] + add;
+    __syncthreads();
+    for (int e = tid; e < 64 * JB; e += 256) {
+        const int r = e / JB, jj = e % JB, row = row0 + r;
+        if (row >= rend) continue;
+        float* const up = U + (int64_t)row * a.ldc + j0 + jj;
+        const float u = *up;
+        float du = 0.f, upow = 1.f;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            du += (float)(p + 1) * upow * cs[r * CLD + p * JB + jj];
+            upow *= u;
+        }
+        *up = du * -expm1f(-u);
+    }
+}
+
+// tn_kernel's segment partials with bf16 parts.  Slices of 32 contraction rows x 64 columns
+// are staged row major (rows of kTrLd bf16), and a lane reads its 8 contraction slots of one
+// column with the transposing LDS read, in the layout of DmaTiles<64, 4>::vfrag (column
+// db * 32 + lane % 32, slot order depending only on the lane half, the same for both
+// operands, so the products pair the same rows).
+using TrTile = DmaTiles<64, 4>;
+constexpr int kTrLd = TrTile::VLD;  // 96
+
+template <class TX, class TY>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void tn16_kernel(const TnArgs a) {
+    constexpr bool XS = sizeof(TX) == 4, YS = sizeof(TY) == 4;
+    constexpr int TILE = 32 * kTrLd;
+    __shared__ __align__(16) bf16 xs[(XS ? 2 : 1) * TILE], ys[(YS ? 2 : 1) * TILE];
+    const int ntn = (a.ncols + 63) / 64;
+    int bx, by, bt;
+    if (!xcd_tile(((a.mrows + 63) / 64) * ntn, a.ngroups * a.nseg, a.BH, bx, by, bt)) return;
+    const int grp = by / a.nseg, sg = by % a.nseg;
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, col = lane % 32, h = lane / 32;
+    const int wm = wave / 2, wn = wave % 2;
+    const int m0 = (bx / ntn) * 64, n0 = (bx % ntn) * 64;
+    const int gend = min((grp + 1) * a.group_rows, a.rows);
+    const int k0 = grp * a.group_rows + sg * a.seg_rows;
+    const int k1 = min(k0 + a.seg_rows, gend);
+    const TX* xb = reinterpret_cast<const TX*>(a.x) + (int64_t)bt * a.x_bt_stride;
+    const TY* yb = reinterpret_cast<const TY*>(a.y) + (int64_t)bt * a.y_bt_stride;
+    const int vl = TrTile::vlane(lane);
+    f32x16 acc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+    Slice<TX, 32, 64, kTrLd> sx;
+    Slice<TY, 32, 64, kTrLd> sy;
+    if (k0 < k1) {
+        sx.load(xb, a.ldx, k0, k1, m0, a.mrows);
+        sy.load(yb, a.ldy, k0, k1, n0, a.ncols);
+    }
+    for (int k = k0; k < k1; k += 32) {
+        __syncthreads();
+        sx.store_split(xs, xs + TILE);
+        sy.store_split(ys, ys + TILE);
+        if (k + 32 < k1) {  // the next slice is read while this one is multiplied
+            sx.load(xb, a.ldx, k + 32, k1, m0, a.mrows);
+            sy.load(yb, a.ldy, k + 32, k1, n0, a.ncols);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const bf16x8 xh = TrTile::vfrag(xs, vl, wm, 0, u), yh = TrTile::vfrag(ys, vl, wn, 0, u);
+            if constexpr (XS) acc = mma16(TrTile::vfrag(xs + TILE, vl, wm, 0, u), yh, acc);
+            if constexpr (YS) acc = mma16(xh, TrTile::vfrag(ys + TILE, vl, wn, 0, u), acc);
+            acc = mma16(xh, yh, acc);
+        }
+    }
+    const int mm = m0 + wm * 32, nn = n0 + wn * 32;
+    if (mm >= a.mrows || nn + col >= a.ncols) return;
+    float* out = a.part + (((int64_t)bt * a.ngroups + grp) * a.nseg + sg) * a.mrows * a.ncols;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         const int r = mm + crow(q, h);
@@ -432,7 +768,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
     }
 }
 
-// Elementwise feature-map kernels: thread t of a workgroup owns element j = t % Dphi of
+// Elementwise feature-map kernel: thread t of a workgroup owns element j = t % Dphi of
 // rows t / Dphi, t / Dphi + per, ... (per = 256 / Dphi rows at a time, threads past
 // per * Dphi idle) of the workgroup's kPhiRows rows; feature (j, p) of a row sits at
 // feat(j, 1) + (p - 1) * len(part of j).
@@ -442,41 +778,6 @@ constexpr int kPhiBatch = 8;  // rows whose loads a thread issues together
 __device__ inline int part_len(int j, int Dphi, int P) {
     const int q = Dphi / P, r = Dphi % P;
     return j < r * (q + 1) ? q + 1 : q;
-}
-
-// u = softplus(pre) in place of pre, and phi[i][feat(j, p)] = u^p
-__global__ __launch_bounds__(256) void phi_fwd_kernel(const GradArgs s, float* __restrict__ U, float* __restrict__ phi) {
-    const int per = 256 / s.Dphi, t = threadIdx.x;
-    if (t >= per * s.Dphi) return;
-    const int j = t % s.Dphi, r_off = t / s.Dphi;
-    const int f1 = feat_index(j, 1, s.Dphi, s.P), step = part_len(j, s.Dphi, s.P);
-    const int64_t rows = (int64_t)s.BH * s.N;
-    const int64_t r0 = (int64_t)blockIdx.x * kPhiRows;
-    // the thread's rows r_off, r_off + per, ... in batches of kPhiBatch: every load of a
-    // batch is issued before the first result is needed
-    for (int b0 = r_off; b0 < kPhiRows; b0 += kPhiBatch * per) {
-        float x[kPhiBatch];
-#pragma unroll
-        for (int i = 0; i < kPhiBatch; ++i) {
-            const int rr = b0 + i * per;
-            const int64_t row = r0 + rr;
-            x[i] = rr < kPhiRows && row < rows ? U[row * s.Dphi + j] : 0.f;
-        }
-#pragma unroll
-        for (int i = 0; i < kPhiBatch; ++i) {
-            const int rr = b0 + i * per;
-            const int64_t row = r0 + rr;
-            if (rr >= kPhiRows || row >= rows) break;
-            const float u = fmaxf(x[i], 0.f) + log1pf(expf(-fabsf(x[i])));
-            U[row * s.Dphi + j] = u;
-            float pw = u;
-            float* out = phi + row * s.F + f1;
-            for (int p = 0; p < s.P; ++p) {
-                out[p * step] = pw;
-                pw *= u;
-            }
-        }
-    }
 }
 
 // dpre = sigmoid(pre) sum_p p u^(p-1) dphi[feat(j, p)], with sigmoid(pre) = 1 - exp(-u),
@@ -489,7 +790,8 @@ __global__ __launch_bounds__(256) void phi_bwd_kernel(const GradArgs s, float* _
     const int f1 = feat_index(j, 1, s.Dphi, s.P), step = part_len(j, s.Dphi, s.P);
     const int64_t rows = (int64_t)s.BH * s.N;
     const int64_t r0 = (int64_t)blockIdx.x * kPhiRows;
-    // batches of kPhiBatch rows as in phi_fwd_kernel; dphi of power p + 1 of every row of
+    // the thread's rows in batches of kPhiBatch (every load of a batch issued before the
+    // first result is needed); dphi of power p + 1 of every row of
     // the batch is loaded before any is used
     for (int b0 = r_off; b0 < kPhiRows; b0 += kPhiBatch * per) {
         float u[kPhiBatch], du[kPhiBatch], upow[kPhiBatch];
@@ -551,6 +853,44 @@ __global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ X
 }
 
 template <class TX, class TY>
+hipError_t launch_nt16_t(NtArgs a, const GradArgs& s, hipStream_t stream) {
+    a.tiles_per_group = (a.group_rows + 63) / 64;
+    const int64_t tiles = (int64_t)((a.ncols + 63) / 64) * a.ngroups * a.tiles_per_group * s.BH;
+    if (tiles >= ((int64_t)1 << 31) - 8) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((nt16_kernel<TX, TY>), dim3(xcd_grid(tiles)), dim3(256), 0, stream, a, s);
+    return hipGetLastError();
+}
+
+template <class TX, class TY, int P>
+hipError_t launch_ntf16_p(NtArgs a, const GradArgs& s, hipStream_t stream) {
+    a.tiles_per_group = (a.group_rows + 63) / 64;
+    const int64_t tiles = (int64_t)(s.Dphi / (64 / P)) * a.ngroups * a.tiles_per_group * s.BH;
+    if (tiles >= ((int64_t)1 << 31) - 8) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((ntf16_kernel<TX, TY, P>), dim3(xcd_grid(tiles)), dim3(256), 0, stream, a, s);
+    return hipGetLastError();
+}
+
+template <class TX, class TY>
+hipError_t launch_ntf16_t(const NtArgs& a, const GradArgs& s, hipStream_t stream) {
+    switch (s.P) {
+        case 1: return launch_ntf16_p<TX, TY, 1>(a, s, stream);
+        case 2: return launch_ntf16_p<TX, TY, 2>(a, s, stream);
+        case 4: return launch_ntf16_p<TX, TY, 4>(a, s, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <class TX, class TY>
+hipError_t launch_tn16_t(TnArgs a, int BH, hipStream_t stream) {
+    const int blocks = ((a.mrows + 63) / 64) * ((a.ncols + 63) / 64);
+    const int64_t tiles = (int64_t)blocks * a.ngroups * a.nseg * BH;
+    if (tiles >= ((int64_t)1 << 31) - 8) return hipErrorInvalidValue;
+    a.BH = BH;
+    hipLaunchKernelGGL((tn16_kernel<TX, TY>), dim3(xcd_grid(tiles)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <class TX, class TY>
 hipError_t launch_nt_t(NtArgs a, const GradArgs& s, hipStream_t stream) {
     a.tiles_per_group = (a.group_rows + 63) / 64;
     const dim3 grid((a.ncols + 63) / 64, a.ngroups * a.tiles_per_group, s.BH);
@@ -568,7 +908,13 @@ hipError_t launch_tn_t(const TnArgs& a, int BH, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_nt(const NtArgs& a, const GradArgs& s, bool x_bf16, bool y_bf16, hipStream_t stream) {
+hipError_t launch_nt(const NtArgs& a, const GradArgs& s, bool x_bf16, bool y_bf16, hipStream_t stream, bool mc16) {
+    if (mc16) {
+        if (x_bf16 && y_bf16) return launch_nt16_t<bf16, bf16>(a, s, stream);
+        if (x_bf16) return launch_nt16_t<bf16, float>(a, s, stream);
+        if (y_bf16) return launch_nt16_t<float, bf16>(a, s, stream);
+        return launch_nt16_t<float, float>(a, s, stream);
+    }
     if (x_bf16 && y_bf16) return launch_nt_t<bf16, bf16>(a, s, stream);
     if (x_bf16) return launch_nt_t<bf16, float>(a, s, stream);
     if (y_bf16) return launch_nt_t<float, bf16>(a, s, stream);
@@ -598,7 +944,15 @@ hipError_t launch_to_bf16(const float* in, void* out, int64_t n, hipStream_t str
     return hipGetLastError();
 }
 
-hipError_t launch_tn(const TnArgs& a, int BH, bool y_bf16, hipStream_t stream) {
+bool ntf16_fusable(const GradArgs& s) { return (s.P == 1 || s.P == 2 || s.P == 4) && s.Dphi % 64 == 0; }
+
+hipError_t launch_ntf16(const NtArgs& a, const GradArgs& s, bool x_bf16, hipStream_t stream) {
+    if (!ntf16_fusable(s) || (a.mode != 1 && a.mode != 2)) return hipErrorInvalidValue;
+    return x_bf16 ? launch_ntf16_t<bf16, float>(a, s, stream) : launch_ntf16_t<float, float>(a, s, stream);
+}
+
+hipError_t launch_tn(const TnArgs& a, int BH, bool y_bf16, hipStream_t stream, bool mc16) {
+    if (mc16) return y_bf16 ? launch_tn16_t<float, bf16>(a, BH, stream) : launch_tn16_t<float, float>(a, BH, stream);
     return y_bf16 ? launch_tn_t<float, bf16>(a, BH, stream) : launch_tn_t<float, float>(a, BH, stream);
 }
 
@@ -651,13 +1005,6 @@ hipError_t launch_grad_rows(const GradArgs& s, const float* o, const float* t, c
     const int per_wg = 4 * kRowsPerWave;
     hipLaunchKernelGGL(rows_kernel, dim3((unsigned)((s.N + per_wg - 1) / per_wg), s.BH), dim3(256), 0, stream, s, o, t,
                        dout, lse, z, AH, delta, lden);
-    return hipGetLastError();
-}
-
-hipError_t launch_grad_phi_fwd(const GradArgs& s, float* U, float* phi, hipStream_t stream) {
-    const int64_t rows = (int64_t)s.BH * s.N;
-    hipLaunchKernelGGL(phi_fwd_kernel, dim3((unsigned)((rows + kPhiRows - 1) / kPhiRows)), dim3(256), 0, stream, s, U,
-                       phi);
     return hipGetLastError();
 }
 

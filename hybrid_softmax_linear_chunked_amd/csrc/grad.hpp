@@ -17,6 +17,9 @@ struct GradArgs {
 // group: mode 0 the head of bt, mode 1 chunk = group, mode 2 the earliest chunk whose linear
 // region holds key frame = group (none: the rows get zeros, or are left as they are when
 // accumulating), mode 3 the slab bt itself.  accumulate: add to C instead of storing.
+// softplus (mode 0, no accumulation): C gets u = softplus(result) (the feature map's
+// activation, blog 2.2.2) and, when phi is non-null, phi[bt][i][feat(f, p)] = u^p for the
+// powers p = 1..P (row stride F, slab stride phi_bt_stride).
 struct NtArgs {
     const void* x;
     int64_t x_bt_stride;
@@ -32,6 +35,9 @@ struct NtArgs {
     int ldc;
     int rows, group_rows, ngroups, tiles_per_group;
     int accumulate;
+    int softplus;
+    float* phi;
+    int64_t phi_bt_stride;
 };
 
 // part[bt][group][seg][m][n] = sum over the rows k of segment seg of group of X[k][m] Y[k][n]
@@ -45,6 +51,7 @@ struct TnArgs {
     int mrows, ncols;
     float* part;
     int rows, group_rows, ngroups, seg_rows, nseg;
+    int BH;  // slabs (set by the bf16 launcher, which decodes its tiles from a 1-D grid)
 };
 
 // Softmax branch of the backward, flash style (bwd.hip), bf16 q, k, v and upstream gradient
@@ -66,8 +73,16 @@ struct BwdArgs {
 };
 hipError_t launch_bwd_softmax(BwdArgs a, int D, hipStream_t stream);
 
-hipError_t launch_nt(const NtArgs& a, const GradArgs& s, bool x_bf16, bool y_bf16, hipStream_t stream);
-hipError_t launch_tn(const TnArgs& a, int BH, bool y_bf16, hipStream_t stream);
+// mc16: on the bf16 matrix core, float operands as hi + lo bf16 parts (for bf16 inputs);
+// otherwise on the fp32 matrix core
+hipError_t launch_nt(const NtArgs& a, const GradArgs& s, bool x_bf16, bool y_bf16, hipStream_t stream,
+                     bool mc16 = false);
+hipError_t launch_tn(const TnArgs& a, int BH, bool y_bf16, hipStream_t stream, bool mc16 = false);
+// The feature gradient (mode 1 or 2, float Y) on the bf16 matrix core with the feature map's
+// backward fused: a.c is U [BH][N][Dphi] (ldc = Dphi), which gets dpre in place of u.
+// Only where ntf16_fusable (P = 1, 2, 4 and Dphi a multiple of 64).
+bool ntf16_fusable(const GradArgs& s);
+hipError_t launch_ntf16(const NtArgs& a, const GradArgs& s, bool x_bf16, hipStream_t stream);
 // out[i] = in[i] rounded to bf16 (ties to even), n a multiple of 4
 hipError_t launch_to_bf16(const float* in, void* out, int64_t n, hipStream_t stream);
 hipError_t launch_grad_reduce(const float* part, float* out, int nb, int no, int ns, int64_t E, hipStream_t stream,
@@ -85,7 +100,6 @@ hipError_t launch_softmax_bwd(float* S, float* dP, const float* lden, const floa
 // entries r in [rows, ldo) are set to zero.
 hipError_t launch_transpose(const void* in, bool in_bf16, int64_t in_bt_stride, int ldi, float* out,
                             int64_t out_bt_stride, int ldo, int rows, int cols, int nbt, hipStream_t stream);
-hipError_t launch_grad_phi_fwd(const GradArgs& s, float* U, float* phi, hipStream_t stream);
 hipError_t launch_grad_phi_bwd(const GradArgs& s, float* U, const float* dphi, hipStream_t stream);
 hipError_t launch_grad_colsum(const float* X, int BH, int64_t rows, int cols, int seg_rows, float* part,
                               hipStream_t stream);
