@@ -426,7 +426,10 @@ def distill_grad_leg(rh, torch, p, d, w, loss_ms, reps=3):
     gfl = grad_flops(w.B, w.H, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P)
     bw = max(gms - loss_ms, 1e-6)
     res = {"ms": round(gms, 3), "gradient_stages_ms": round(bw, 3), "gradient_flops": gfl,
-           "gradient_tflops": round(gfl / (bw * 1e-3) / 1e12, 2), "peak_fp32_matrix_tflops": 157.3,
+           "gradient_tflops": round(gfl / (bw * 1e-3) / 1e12, 2),
+           "bound": "products on the bf16 matrix core (a float operand as hi + lo bf16 parts: up to three "
+                    "products per algorithmic one; 2.5 PFLOP/s dense bf16) and HBM passes over float "
+                    "per-token rows; fp32 inputs take the fp32 matrix core (157.3 TFLOP/s)",
            "workspace_bytes": int(ws.numel())}
     del ws
     return res
@@ -468,8 +471,8 @@ def backward_leg(rh, torch, p, d, w, fwd_ms, reps=2):
     res = {"ms": round(bms, 3), "backward_stages_ms": round(st, 3), "backward_flops": fl,
            "backward_tflops": round(tf, 2), "peak_tflops": PEAK_BF16_TFLOPS,
            "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-           "bound": "mfma: softmax-branch products on the bf16 matrix core (bf16 inputs), linear branch "
-                    "on the fp32 matrix core (157.3 TFLOP/s peak)",
+           "bound": "mfma: every product on the bf16 matrix core for bf16 inputs (the linear branch's float "
+                    "operands as hi + lo bf16 parts)",
            "workspace_bytes": int(ws.numel())}
     del ws, dout
     return res
