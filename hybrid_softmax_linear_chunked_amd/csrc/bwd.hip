@@ -36,6 +36,30 @@ __device__ inline void wait_vm_lds() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
+// The same for a wave-uniform run-time N (0 .. 16; larger N waits for everything, which is
+// never wrong, only early).
+__device__ inline void wait_vm_lds_n(int n) {
+    switch (n) {
+        case 1: wait_vm_lds<1>(); break;
+        case 2: wait_vm_lds<2>(); break;
+        case 3: wait_vm_lds<3>(); break;
+        case 4: wait_vm_lds<4>(); break;
+        case 5: wait_vm_lds<5>(); break;
+        case 6: wait_vm_lds<6>(); break;
+        case 7: wait_vm_lds<7>(); break;
+        case 8: wait_vm_lds<8>(); break;
+        case 9: wait_vm_lds<9>(); break;
+        case 10: wait_vm_lds<10>(); break;
+        case 11: wait_vm_lds<11>(); break;
+        case 12: wait_vm_lds<12>(); break;
+        case 13: wait_vm_lds<13>(); break;
+        case 14: wait_vm_lds<14>(); break;
+        case 15: wait_vm_lds<15>(); break;
+        case 16: wait_vm_lds<16>(); break;
+        default: wait_vm_lds<0>(); break;
+    }
+}
+
 // One LDS-DMA instruction of 4-byte pieces: lane l copies the dword at gbase + voff to LDS
 // bytes [lds + 4 l, +4).  Same conventions as dma16_s.
 __device__ inline void dma4_s(const void* gbase, uint32_t voff, uint32_t lds) {
@@ -93,7 +117,9 @@ __device__ inline void chunk_span(const BwdArgs& a, int c, int& q0, int& q1, int
 // (ds_read_b64_tr_b16) two-way at most; one layout serves both, so each tile is copied once.
 // Tile rows of D + 16 elements: the eight rows of a transposing read fall in eight different
 // 32-byte bank groups, and the row reads of the 16x16x32 operands stay conflict-free too.
-constexpr int kDkvWaves = 4;  // waves (of 16 keys) per key-stationary workgroup
+// waves (of 16 keys) per key-stationary workgroup: one workgroup per CU, three waves per
+// SIMD, all sharing one ring of query tiles
+constexpr int kDkvWaves = 12;
 
 template <int D>
 struct BwdTiles {
@@ -291,8 +317,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdArgs a) {
         }
 }
 
-// Key-stationary pass: dK and dV of 64 keys (4 waves x 16; two workgroups per CU, which do
-// not wait for each other's barriers, so one's arithmetic overlaps the other's products), on 16x16x32
+// Key-stationary pass: dK and dV of 16 NW keys (NW waves x 16; with NW = 12 one workgroup per
+// CU and three waves per SIMD, so that one wave's arithmetic overlaps the others' products and
+// the ring of query tiles is shared by all twelve), on 16x16x32
 // products (lane l = 16 g + a holds row a and contraction slots 8 g .. 8 g + 7 of A, column a
 // and the same slots of B, and column a, rows 4 g .. 4 g + 3 of C).  Per 32-query tile and
 // wave:
@@ -302,14 +329,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdArgs a) {
 //   dV^T += G^T P, dK^T += Q^T dS: A = G or Q transposed, read with two transposing LDS
 //     reads that deliver the same queries for column 16 dc + a.
 // The accumulators of a wave are 2 D / 16 tiles of 4 registers (64 at D = 128).
-template <int D>
-__global__ __launch_bounds__(kDkvWaves * 64, 2) void bwd_dkv_kernel(const BwdArgs a) {
-    constexpr int NW = kDkvWaves, KW = 16, NK = D / 32, ND = D / 16, R = 4;
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkv_kernel(const BwdArgs a) {
+    constexpr int KW = 16, NK = D / 32, ND = D / 16, R = 4;
     constexpr int LD = BwdTiles<D>::LD16;
     using Tl = Rows32<D, LD, NW>;
     constexpr int STAT = 256;  // lden of the 32 queries, then delta
     constexpr int SLOT = 2 * Tl::BYTES + STAT;  // Q, G, statistics
-    constexpr int NMIN = 2 * Tl::NMIN;  // the statistics copy: wave 0 only
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int item = xcd_item(a.BH * a.kblocks);
@@ -392,10 +418,11 @@ __global__ __launch_bounds__(kDkvWaves * 64, 2) void bwd_dkv_kernel(const BwdArg
             dma4_s(a.stats, off, lds_addr(s0 + 2 * Tl::BYTES));
         }
     };
+    // this wave's copy instructions per tile: its share of the Q and G blocks, and the
+    // statistics (wave 0); waiting for all but `later` tiles' worth leaves those in flight
+    const int per_tile = 2 * (wave < Tl::NI ? (Tl::NI - 1 - wave) / NW + 1 : 0) + (wave == 0 ? 1 : 0);
     auto sync = [&](int later) {
-        if (later >= 2) wait_vm_lds<2 * NMIN>();
-        else if (later == 1) wait_vm_lds<NMIN>();
-        else wait_vm_lds<0>();
+        wait_vm_lds_n(per_tile * later);
         asm volatile("s_barrier" ::: "memory");
     };
     // row operand: row 16 qh + la, d = 32 s + 8 lg; transposed: rows 4 lg + la / 4 (+ 16),
@@ -502,12 +529,13 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     const size_t lds_q = 5 * (size_t)(2 * Rows32<D, BwdTiles<D>::LD16, 8>::BYTES);
     const size_t lds_k = 4 * (size_t)(2 * Rows32<D, BwdTiles<D>::LD16, kDkvWaves>::BYTES + 256);
     static size_t set_q[64] = {}, set_k[64] = {};
-    hipError_t e = lds_limit(reinterpret_cast<const void*>(bwd_dkv_kernel<D>), lds_k, set_k);
+    hipError_t e = lds_limit(reinterpret_cast<const void*>(bwd_dkv_kernel<D, kDkvWaves>), lds_k, set_k);
     if (e != hipSuccess) return e;
     e = lds_limit(reinterpret_cast<const void*>(bwd_dq_kernel<D>), lds_q, set_q);
     if (e != hipSuccess) return e;
     const int nk = a.BH * a.kblocks, nq = a.BH * a.nc * a.qtiles;
-    hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3((unsigned)((nk + 7) / 8 * 8)), dim3(kDkvWaves * 64), lds_k, stream, a);
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, kDkvWaves>), dim3((unsigned)((nk + 7) / 8 * 8)), dim3(kDkvWaves * 64), lds_k,
+                       stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)((nq + 7) / 8 * 8)), dim3(512), lds_q, stream, a);
