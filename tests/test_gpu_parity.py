@@ -133,6 +133,29 @@ def test_stream_equals_parallel_bitwise(p):
     assert slab_err(s_out.float().cpu().numpy(), ref) <= TOL[p.in_dtype]
 
 
+@pytest.mark.parametrize("T,Tc", [(3, 5), (3, 3)], ids=["T<Tc", "T=Tc"])
+def test_one_chunk_clip_same_bits_in_every_form(T, Tc):
+    """A clip that one chunk covers is plain softmax attention over all its frames.  The bf16
+    kernel splits the last query tiles of each XCD over two workgroups by a rule that looks at
+    that chunk alone (its frames and its tiles), so running the clip with Tc >= T, with
+    Tc = T (the distillation teacher's form) or streamed in one step gives the same bits; the
+    output matches the oracle.  The window spans 300 keys (five tiles), so the split engages."""
+    p = rh.Params(1, 2, 128, T, 100, Tc, 1, 128, 2, 0, BF16, BF16)
+    x = rand_inputs(p, seed=11)
+    d = to_dev(x, p)
+    par = run_parallel(p, d, aux=False)
+    teacher = p.with_(Tc=T)
+    par_t = run_parallel(teacher, d, aux=False)
+    st = rh.Stream(p, d["wq"], d["wk"])
+    s_out = st.step(d["q"].contiguous(), d["k"].contiguous(), d["v"].contiguous(), T)
+    torch.cuda.synchronize()
+    assert rh.workspace_bytes(p) > 0 and rh.workspace_bytes(teacher) == rh.workspace_bytes(p)
+    assert torch.equal(par, par_t)
+    assert torch.equal(s_out, par)
+    ref = oracle.parallel(oracle_params(p), x["q"], x["k"], x["v"], x["wq"], x["wk"])
+    assert slab_err(par.float().cpu().numpy(), ref) <= TOL[BF16]
+
+
 def test_stream_rejects_calls_after_short_chunk():
     p = CASES[0]
     x = rand_inputs(p, seed=5)
