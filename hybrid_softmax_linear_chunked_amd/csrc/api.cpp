@@ -779,7 +779,9 @@ GradLayout grad_layout(const rehyat_params* p, bool backward) {
     L.ah = take(BH * N * LD * f4);
     L.u = take(BH * N * s.Dphi * f4);
     L.phi = take(BH * N * s.F * f4);
-    L.dphi = take(BH * N * s.F * f4);
+    // dphi only where the feature map's backward is a pass of its own (the fused feature
+    // gradients of bf16 inputs write dpre over u)
+    L.dphi = take(p->in_dtype == REHYAT_BF16 && ntf16_fusable(s) ? 0 : BH * N * s.F * f4);
     L.sz = take(BH * s.nc * s.F * LD * f4);
     L.rp = take(BH * s.nc * s.Tc * s.F * LD * f4);
     L.r = take(BH * s.nc * s.F * LD * f4);

@@ -22,7 +22,9 @@
 // 32-element contraction slices of their operands through LDS with 16-byte loads along rows,
 // and each wave reads its MFMA operands from there (one 32x32 output block per wave);
 // and every sum over segments, frames, chunks or batches runs in a fixed order, so the
-// gradients are bitwise reproducible.
+// gradients are bitwise reproducible.  Fusions: the pre-activation product writes u =
+// softplus(W x + b) and its powers phi (nt_store), and for bf16 inputs with P = 1, 2, 4 the
+// feature gradients write dpre over u (ntf16_kernel), so dphi never reaches memory there.
 #include <type_traits>
 
 #include "grad.hpp"

@@ -228,7 +228,7 @@ rehyat_status rehyat_distill_loss(const rehyat_params* p, const void* q, const v
  * ignored.  Status: as rehyat_distill_loss, plus REHYAT_EINVAL when a launch grid would
  * exceed 65,535 row tiles (about 2M tokens) or B*H*chunks exceeds 65,535.  The workspace
  * holds the student and teacher outputs and float32 [B,H,N,*] gradient buffers (about
- * 1.9 GB for a 12-head, 32,760-token layer). */
+ * 1.4 GB for bf16 inputs, 1.8 GB for float32 inputs, at a 12-head, 32,760-token layer). */
 size_t rehyat_distill_grad_workspace_bytes(const rehyat_params* p);
 rehyat_status rehyat_distill_grad(const rehyat_params* p, const void* q, const void* k,
                                   const void* v, const void* wq, const void* wk,

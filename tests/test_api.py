@@ -188,6 +188,13 @@ def test_distill_grad_checks(L):
     p = WAN.c()
     need = L.rehyat_distill_grad_workspace_bytes(ctypes.byref(p))
     assert need > L.rehyat_distill_workspace_bytes(ctypes.byref(p))
+    # bf16 inputs with P = 2 fuse the feature map's backward into the feature gradients, so
+    # the float [B*H, N, F] dphi buffer (403 MB here) is not part of the workspace; fp32
+    # inputs keep it (the two layouts otherwise differ by tens of MB: image dtypes, the
+    # bf16 attention's tail-split scratch)
+    dphi = 12 * 32760 * 256 * 4
+    need32 = L.rehyat_distill_grad_workspace_bytes(ctypes.byref(WAN.with_(in_dtype=0).c()))
+    assert need32 - need > dphi // 2
     f = L.rehyat_distill_grad
     outs = [FAKE, FAKE, FAKE, None, None]            # loss, dwq, dwk, dbq, dbk
     assert f(ctypes.byref(p), *[FAKE] * 5, None, None, *outs, FAKE, need - 1, None) == EWORKSPACE
