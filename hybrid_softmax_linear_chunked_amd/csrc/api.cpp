@@ -186,59 +186,45 @@ rehyat_status rehyat_phi(const rehyat_params* p, const void* x, const void* w, c
     return hip_status(launch_phi(a, p->in_dtype, stream));
 }
 
-// Workspace of the chunk-parallel form: the per-frame partials and chunk state images, then
-// the attention stage's tail-split scratch (bf16 inputs): one arrival counter per split
-// tile, then the partials of both halves.
-struct ParallelWs {
+// Tail-split scratch of a bf16 attention launch, placed at `base` of a workspace: one arrival
+// counter per split tile, then the partials of both halves (none for float32 inputs or
+// where the plan splits nothing).
+struct SplitWs {
     int splits, split_per_xcd;
     size_t cnt, part, total;
 };
 
-static ParallelWs parallel_ws(const rehyat_params* p) {
-    ParallelWs L;
-    const int G = state_frames(p);
-    const size_t base = G > 0 ? parallel_layout(p, G).total : 0;
-    L.splits = 0;
-    L.split_per_xcd = 0;
-    if (p->in_dtype == REHYAT_BF16) {
-        AttnArgs a = attn_common(p, nullptr, nullptr);
-        a.nchunks = num_chunks(p);
-        L.splits = wide_split_plan(a);
-        L.split_per_xcd = a.split_per_xcd;
-    }
+static SplitWs split_ws(const rehyat_params* p, AttnArgs a, size_t base) {
+    SplitWs L;
+    L.splits = p->in_dtype == REHYAT_BF16 ? wide_split_plan(a) : 0;
+    L.split_per_xcd = L.splits > 0 ? a.split_per_xcd : 0;
     L.cnt = base;
     L.part = L.cnt + (L.splits > 0 ? align256((size_t)L.splits * sizeof(unsigned)) : 0);
     L.total = L.part + (size_t)L.splits * wide_split_part_bytes(p->D);
     return L;
 }
 
+// Workspace of the chunk-parallel form: the per-frame partials and chunk state images, then
+// the attention stage's tail-split scratch.
+static SplitWs parallel_ws(const rehyat_params* p) {
+    const int G = state_frames(p);
+    AttnArgs a = attn_common(p, nullptr, nullptr);
+    a.nchunks = num_chunks(p);
+    return split_ws(p, a, G > 0 ? parallel_layout(p, G).total : 0);
+}
+
 static size_t parallel_ws_bytes(const rehyat_params* p) { return parallel_ws(p).total; }
 
-// Workspace of a streaming chunk step: the per-frame partials of up to Tc frames, then for
-// bf16 inputs the tail-split scratch of the first chunk's attention launch, which splits
-// the same tiles as the chunk-parallel grid (counters zeroed by the first step).
-struct StreamWs {
-    int splits, split_per_xcd;
-    size_t cnt, part, total;
-};
-
-static StreamWs stream_ws(const rehyat_params* p) {
-    StreamWs L;
-    L.splits = 0;
-    L.split_per_xcd = 0;
-    if (p->in_dtype == REHYAT_BF16) {
-        AttnArgs a = attn_common(p, nullptr, nullptr);
-        a.stream = 1;
-        a.s_frames = p->Tc;
-        a.nchunks = 1;
-        a.split_per_xcd = 1;  // asked for; the plan decides
-        L.splits = wide_split_plan(a);
-        L.split_per_xcd = a.split_per_xcd;
-    }
-    L.cnt = partial_bytes(p, p->Tc);
-    L.part = L.cnt + (L.splits > 0 ? align256((size_t)L.splits * sizeof(unsigned)) : 0);
-    L.total = L.part + (size_t)L.splits * wide_split_part_bytes(p->D);
-    return L;
+// Workspace of a streaming chunk step: the per-frame partials of up to Tc frames, then the
+// tail-split scratch of the first chunk's attention launch, which splits the same tiles as
+// the chunk-parallel grid (sized for a whole first chunk; counters zeroed by the first step).
+static SplitWs stream_ws(const rehyat_params* p) {
+    AttnArgs a = attn_common(p, nullptr, nullptr);
+    a.stream = 1;
+    a.s_frames = p->Tc;
+    a.nchunks = 1;
+    a.split_per_xcd = 1;  // asked for; the plan decides
+    return split_ws(p, a, partial_bytes(p, p->Tc));
 }
 
 size_t rehyat_workspace_bytes(const rehyat_params* p) {
@@ -253,7 +239,7 @@ rehyat_status rehyat_parallel_states(const rehyat_params* p, const void* k, cons
     if (st != REHYAT_OK) return st;
     if (!aligned16(k) || !aligned16(v) || !aligned16(wk) || !aligned4_or_null(bk)) return REHYAT_EALIGN;
     const int G = state_frames(p);
-    const ParallelWs WL = parallel_ws(p);
+    const SplitWs WL = parallel_ws(p);
     const size_t need = WL.total;
     if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0)) return REHYAT_EWORKSPACE;
     // the attention stage's tail-split counters start at zero (each split's second arrival
@@ -317,7 +303,7 @@ rehyat_status rehyat_parallel_attend(const rehyat_params* p, const void* q, cons
             return REHYAT_EALIGN;
     }
     const int G = state_frames(p);
-    const ParallelWs WL = parallel_ws(p);
+    const SplitWs WL = parallel_ws(p);
     const size_t need = WL.total;
     if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0)) return REHYAT_EWORKSPACE;
 
@@ -430,7 +416,7 @@ rehyat_status rehyat_chunk_step(const rehyat_params* p, void* state, rehyat_stre
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(wq) || !aligned16(wk) ||
         !aligned16(out) || !aligned4_or_null(bq) || !aligned4_or_null(bk))
         return REHYAT_EALIGN;
-    const StreamWs WS = stream_ws(p);
+    const SplitWs WS = stream_ws(p);
     const size_t need = WS.total;
     if (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 256 != 0) return REHYAT_EWORKSPACE;
 

@@ -6,7 +6,8 @@ Bar: per (batch, head) slab for dq, dk, dv and per head for the parameter gradie
 max |gpu - oracle| / max |oracle| <= 1e-5 for fp32 inputs and 2e-2 for bf16 inputs (fp32
 inputs: products on the fp32 matrix core; bf16 inputs: products on the bf16 matrix core with
 fp32 accumulation, the softmax branch flash style with P and dS recomputed per tile and
-rounded to bf16 as operands).  Repeated calls give identical bits.  Shapes span several
+rounded to bf16 as operands, the linear branch's float operands as hi + lo bf16 parts).
+Repeated calls give identical bits.  Shapes span several
 64-row tiles with ragged tails, To = 0 and To > Tc, a window with no linear region (one
 chunk) and one with no softmax window (linear_only), batches and biases.
 """
@@ -35,6 +36,7 @@ SHAPES = [
     (1, 2, 64, 5, 70, 1, 0, 64, 2, 0, rh.BF16, False),     # Tc = 1, To = 0: spatial-only softmax
     (1, 2, 32, 7, 70, 3, 2, 32, 2, 0, rh.BF16, True),      # D = 32; key blocks across windows
     (1, 1, 128, 2, 33, 3, 1, 64, 2, 0, rh.BF16, False),    # T < Tc: one short chunk, ragged tiles
+    (1, 2, 64, 6, 40, 3, 1, 128, 4, 0, rh.BF16, True),     # fused feature-map backward, P = 4
 ]
 
 

@@ -4,8 +4,11 @@ through the C ABI.
 
 Bar: per head, max |gpu - oracle| / max |oracle| over the [Dphi, D] matrix (and the
 [Dphi] bias vector) <= the path's floating-point bar, 1e-5 for fp32 inputs and 2e-2 for
-bf16 inputs with fp32 accumulation (the gradient products themselves run in fp32; the
-bf16 error comes from the student's output, whose P and phi operands are bf16).  The loss
+bf16 inputs with fp32 accumulation (fp32 inputs: gradient products on the fp32 matrix core;
+bf16 inputs: on the bf16 matrix core with every float operand as hi + lo bf16 parts, about
+2^-15 relative error per product, so the bf16 error still comes mostly from the student's
+output, whose P and phi operands are bf16).  The shapes cover both the fused feature-map
+backward (P = 1, 2, 4 with Dphi a multiple of 64) and its separate pass.  The loss
 equals rehyat_distill_loss bit for bit, repeated calls give identical bits, and without a
 linear region every gradient is exactly zero.
 """
@@ -30,6 +33,8 @@ SHAPES = [
     (1, 2, 128, 6, 50, 3, 1, 128, 2, 0, rh.BF16, False),
     (2, 2, 64, 8, 29, 3, 0, 64, 1, 0, rh.BF16, True),
     (1, 3, 128, 9, 45, 2, 3, 96, 4, 0, rh.BF16, False),
+    (1, 2, 64, 6, 40, 3, 1, 128, 4, 0, rh.BF16, True),    # fused feature-map backward, P = 4
+    (1, 1, 64, 7, 30, 3, 2, 128, 3, 0, rh.BF16, False),   # P = 3 (parts 43/43/42): separate pass
 ]
 
 
