@@ -621,6 +621,50 @@ __global__ __launch_bounds__(256) void reduce4_kernel(const float* __restrict__ 
     *dst = acc;
 }
 
+// reduce4_kernel for short rows over many segments (E / 4 <= 64, E and the addresses
+// multiples of 4 floats): one workgroup per output row; thread (g, c) adds float4 column c
+// of segments [g ns / NG, (g + 1) ns / NG) of every b in order, then the NG group sums are
+// added in group order (a fixed order, so the result is reproducible).
+__global__ __launch_bounds__(256) void reduce_short_kernel(const float* __restrict__ part, float* __restrict__ out,
+                                                           int nb, int no, int ns, int64_t E, int64_t ostride,
+                                                           int accumulate) {
+    __shared__ float4 gs[256];
+    const int E4 = (int)(E / 4), NG = 256 / E4, t = threadIdx.x, c = t % E4, g = t / E4;
+    const int o = blockIdx.x;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (g < NG) {
+        const int s0 = (int)((int64_t)ns * g / NG), s1 = (int)((int64_t)ns * (g + 1) / NG);
+        for (int b = 0; b < nb; ++b)
+            for (int sg = s0; sg < s1; ++sg) {
+                const float4 x = *reinterpret_cast<const float4*>(part + (((int64_t)b * no + o) * ns + sg) * E + 4 * c);
+                acc.x += x.x;
+                acc.y += x.y;
+                acc.z += x.z;
+                acc.w += x.w;
+            }
+    }
+    gs[t] = acc;
+    __syncthreads();
+    if (t >= E4) return;
+    float4 sum = gs[t];
+    for (int k = 1; k < NG; ++k) {
+        const float4 y = gs[k * E4 + t];
+        sum.x += y.x;
+        sum.y += y.y;
+        sum.z += y.z;
+        sum.w += y.w;
+    }
+    float4* dst = reinterpret_cast<float4*>(out + (int64_t)o * ostride + 4 * t);
+    if (accumulate) {
+        const float4 y = *dst;
+        sum.x = y.x + sum.x;
+        sum.y = y.y + sum.y;
+        sum.z = y.z + sum.z;
+        sum.w = y.w + sum.w;
+    }
+    *dst = sum;
+}
+
 // R[bt][c] <- sum over c' >= c of R[bt][c'] (from the last chunk), in place
 __global__ __launch_bounds__(256) void suffix_kernel(float* __restrict__ R, int nc, int64_t E) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -963,7 +1007,10 @@ hipError_t launch_grad_reduce(const float* part, float* out, int nb, int no, int
     const int64_t os = out_stride < 0 ? E : out_stride;
     const bool v4 = E % 4 == 0 && os % 4 == 0 && reinterpret_cast<uintptr_t>(part) % 16 == 0 &&
                     reinterpret_cast<uintptr_t>(out) % 16 == 0;
-    if (v4)
+    if (v4 && E / 4 <= 64 && ns >= 8)  // short rows, many segments: split the segments too
+        hipLaunchKernelGGL(reduce_short_kernel, dim3((unsigned)no), dim3(256), 0, stream, part, out, nb, no, ns, E, os,
+                           accumulate ? 1 : 0);
+    else if (v4)
         hipLaunchKernelGGL(reduce4_kernel, dim3((unsigned)((E / 4 + 255) / 256), no), dim3(256), 0, stream, part, out,
                            nb, no, ns, E, os, accumulate ? 1 : 0);
     else
