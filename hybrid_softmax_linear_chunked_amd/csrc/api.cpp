@@ -809,7 +809,8 @@ bool grad_grid_ok(const GradArgs& s, const GradLayout& L) {
 
 // Linear branch of the backward (chunk states of blog 2.3, feature map of blog 2.2.2): with
 // AH = [a | h | 0] per query in place, the gradients of W_q, W_k (b_q, b_k when non-null)
-// and, when dq is non-null, the linear branch's share of dq, dk, dv added to them.
+// and, when dq is non-null, the linear branch's share of dq, dk, dv written to them (its
+// products are the first to reach them; the softmax branch adds to them afterwards).
 rehyat_status linear_branch(const rehyat_params* p, const GradArgs& s, const GradLayout& L, char* w,
                             const void* q, const void* k, const void* v, const void* wq, const void* wk,
                             const float* bq, const float* bk, float* dwq, float* dwk, float* dbq, float* dbk,
@@ -879,7 +880,7 @@ rehyat_status linear_branch(const rehyat_params* p, const GradArgs& s, const Gra
         }
         return e;
     };
-    // dx += dpre W (contraction over Dphi) with W transposed into L.wt
+    // dx = dpre W (contraction over Dphi) with W transposed into L.wt
     auto dx = [&](const void* wmat, float* dxout) -> hipError_t {
         hipError_t e = launch_transpose(wmat, bf, (int64_t)s.Dphi * s.D, s.D, F32(L.wt), (int64_t)s.D * s.Dphi, s.Dphi,
                                         s.Dphi, s.D, p->H, stream);
@@ -900,7 +901,6 @@ rehyat_status linear_branch(const rehyat_params* p, const GradArgs& s, const Gra
         a.ldc = s.D;
         a.group_rows = s.N;
         a.ngroups = 1;
-        a.accumulate = 1;
         return launch_nt(a, s, false, false, stream, bf);
     };
 
@@ -978,12 +978,11 @@ rehyat_status linear_branch(const rehyat_params* p, const GradArgs& s, const Gra
         a.mode = 2;
         a.K = s.F;
         a.ncols = s.D;
-        a.c = dv;
+        a.c = dv;  // rows of key frames no chunk's state holds get zeros
         a.c_bt_stride = N * s.D;
         a.ldc = s.D;
         a.group_rows = s.n;
         a.ngroups = s.T;
-        a.accumulate = 1;
         GRAD_TRY(launch_nt(a, s, false, false, stream, bf));
     }
     {
@@ -1119,15 +1118,16 @@ rehyat_status rehyat_backward(const rehyat_params* p, const void* q, const void*
     st = rehyat_forward_parallel_aux(&ps, q, k, v, wq, wk, bq, bk, w + L.stu, &aux, w + L.fwd_s, L.fwd_t - L.fwd_s,
                                      stream);
     if (st != REHYAT_OK) return st;
-    GRAD_TRY(launch_zero(dq, (int64_t)s.BH * ND, stream));
-    GRAD_TRY(launch_zero(dk, (int64_t)s.BH * ND, stream));
-    GRAD_TRY(launch_zero(dv, (int64_t)s.BH * ND, stream));
     GRAD_TRY(launch_grad_rows(s, F32(L.stu), nullptr, dout, F32(L.lse), F32(L.z), F32(L.ah), F32(L.delta),
                               F32(L.lden), stream));
     if (s.G > 0) {
+        // writes dq, dk, dv first
         st = linear_branch(p, s, L, w, q, k, v, wq, wk, bq, bk, dwq, dwk, dbq, dbk, dq, dk, dv, stream);
         if (st != REHYAT_OK) return st;
     } else {
+        GRAD_TRY(launch_zero(dq, (int64_t)s.BH * ND, stream));
+        GRAD_TRY(launch_zero(dk, (int64_t)s.BH * ND, stream));
+        GRAD_TRY(launch_zero(dv, (int64_t)s.BH * ND, stream));
         st = zero_param_grads(p, s, dwq, dwk, dbq, dbk, stream);
         if (st != REHYAT_OK) return st;
     }
