@@ -28,10 +28,12 @@
  *   - Asynchrony: all work is enqueued on the caller's stream; the return value reports
  *     validation (checked before any HIP call) and launch errors.  Device faults appear
  *     at the caller's next synchronisation.
- *   - Determinism: repeated calls on the same inputs give identical bits.  The only atomic
- *     is the arrival counter of the bf16 attention kernel's tail split (the last chunk-0
- *     query tiles of each XCD run as two workgroups over the two halves of the window; the
- *     second to finish merges both partials, in the same order whichever it is).
+ *   - Determinism: repeated calls on the same inputs give identical bits.  Atomics appear
+ *     only in the bf16 attention kernel's tail split (the last chunk-0 query tiles of each
+ *     XCD run as two workgroups over the two halves of the window): each half stores its
+ *     partial with agent-scope atomic stores and counts its arrival with one atomic add;
+ *     the second to arrive reads the other's partial with agent-scope atomic loads and
+ *     merges both in half order, so the result does not depend on which arrives first.
  *   - Thread safety: no shared mutable state beyond a per-device cache of kernel LDS limits
  *     (idempotent); one in-flight call per streaming state.
  */

@@ -21,6 +21,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
 def _regs(tok):
+    # VCC's halves are scalar registers outside the numbered range (the blocks write no VCC)
+    if tok in ("vcc_lo", "vcc_hi", "vcc"):
+        return "s", []
     m = re.fullmatch(r"([vs])\[(\d+):(\d+)\]", tok)
     if m:
         return m.group(1), list(range(int(m.group(2)), int(m.group(3)) + 1))
@@ -58,3 +61,11 @@ def test_free_operands_avoid_pinned_registers(kernel_asm):
                 assert min(regs) > vend, f"operand {name} in pinned {tok} (pinned v0-v{vend})"
             else:
                 assert not any(s0 <= r <= s1 for r in regs), f"operand {name} in pinned scalar {tok}"
+
+
+def test_blocks_leave_vcc_alone():
+    """A free scalar operand may sit in VCC, so no sweep block may write it: none of the
+    instructions that set VCC implicitly (compares, carry adds, divide scaling) appears."""
+    inc = open(os.path.join(ROOT, "hybrid_softmax_linear_chunked_amd", "csrc", "wide_substep.inc")).read()
+    assert not re.search(r"\b(v_cmp\w*|v_cmpx\w*|v_add_co\w*|v_sub_co\w*|v_subrev_co\w*|v_addc\w*|v_subb\w*|"
+                         r"v_div_scale\w*|v_cndmask\w*)\b|\bvcc", inc)
