@@ -146,6 +146,9 @@ def main():
     ap.add_argument("--legs", default="all",
                     help="comma-separated legs to run after the main step (comparator, stream, variants, "
                          "distill_loss, distill_grad, backward, wan_20s, wan14b_720p), or all")
+    ap.add_argument("--gemm-reference", action="store_true",
+                    help="only time a plain bf16 library GEMM (torch.matmul, 8192 x 8192 x 8192) and print its "
+                         "TFLOP/s: what a dense product reaches on this part under the same clock limits")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 dispatches): the reference for scaling "
                          "the FETCH_SIZE / WRITE_SIZE counters")
@@ -165,6 +168,29 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.gemm_reference:
+        n = 8192
+        g = torch.Generator(device=dev)
+        g.manual_seed(3)
+        a_ = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
+        b_ = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
+        c_ = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+        for _ in range(5):
+            torch.matmul(a_, b_, out=c_)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a_, b_, out=c_)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+        print(json.dumps({"gemm_reference": {"m": n, "n": n, "k": n, "dtype": "bf16", "ms": round(ms, 4),
+                                             "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}}),
+              flush=True)
+        return
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
         dst = torch.empty_like(src)
