@@ -575,8 +575,13 @@ def stream_leg(rh, torch, w, dev):
                 "device_free_drop_during_steps": int(free0 - low)}
 
     peak = {str(T): measure(T) for T in (21, 41, 81)}
+    # the streamed clip does the work of the chunk-parallel form on the same clip (the same
+    # windows, the same state partials)
+    fl = flop_model(w.B, w.H, w.D, w.T, w.n, w.Tc, w.To, w.Dphi, w.P)["total"]
+    tf = fl / (ms * 1e-3) / 1e12
     return {"workload": "wan_10s_stream", "frames": w.T, "tokens": w.N, "ms_per_clip": round(ms, 3),
-            "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1),
+            "tokens_per_s": round(w.B * w.N / (ms * 1e-3), 1), "flops_per_clip": fl, "tflops": round(tf, 2),
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "chunk_steps": (w.T + w.Tc - 1) // w.Tc, "peak_memory_by_frames": peak}
 
 
