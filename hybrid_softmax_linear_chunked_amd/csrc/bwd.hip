@@ -321,8 +321,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdArgs a) {
 // CU and three waves per SIMD, so that one wave's arithmetic overlaps the others' products and
 // the ring of query tiles is shared by all twelve), on 16x16x32
 // products (lane l = 16 g + a holds row a and contraction slots 8 g .. 8 g + 7 of A, column a
-// and the same slots of B, and column a, rows 4 g .. 4 g + 3 of C).  Per 32-query tile and
-// wave:
+// and the same slots of B, and column a, rows 4 g .. 4 g + 3 of C).  A ring slot holds 64
+// queries (two halves of 32, one workgroup barrier per slot).  Per 32-query half and wave:
 //   S = Q K^T, dP = G V^T: two C tiles each (queries 16 qh + 4 g + i, this lane's key a);
 //   P, dS from them; as they stand, the eight values of a lane are the B operand (queries x
 //     keys) with slot i <-> query 4 g + i and slot 4 + i <-> query 16 + 4 g + i;
@@ -335,7 +335,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkv_kernel(const
     constexpr int LD = BwdTiles<D>::LD16;
     using Tl = Rows32<D, LD, NW>;
     constexpr int STAT = 256;  // lden of the 32 queries, then delta
-    constexpr int SLOT = 2 * Tl::BYTES + STAT;  // Q, G, statistics
+    constexpr int HALF = 2 * Tl::BYTES + STAT;  // Q, G, statistics of 32 queries
+    constexpr int SLOT = 2 * HALF;              // a slot holds 64 queries: one barrier per 64
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int item = xcd_item(a.BH * a.kblocks);
@@ -362,11 +363,11 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkv_kernel(const
         }
     }
     if (c_hi < 0) return;
-    // query blocks of 32, chunk after chunk
+    // query blocks of 64 (two halves of 32), chunk after chunk
     auto nqb = [&](int c) {
         int q0, q1, k0, k1;
         chunk_span(a, c, q0, q1, k0, k1);
-        return (q1 - q0 + 31) / 32;
+        return (q1 - q0 + 63) / 64;
     };
     int ntiles = 0;
     for (int c = c_lo; c <= c_hi; ++c) ntiles += nqb(c);
@@ -379,7 +380,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkv_kernel(const
             ++c;
             nb = nqb(c);
         }
-        qb0 = c * a.Tc * a.n + 32 * i;
+        qb0 = c * a.Tc * a.n + 64 * i;
     };
 
     const int kw = key0 + wave * KW + la;  // this lane's key
@@ -408,19 +409,26 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkv_kernel(const
         int c, qb0;
         tile_at(i, c, qb0);
         const int qend = min((c * a.Tc + a.Tc), a.T) * a.n;
-        unsigned char* s0 = slot(i);
-        Tl::issue(qs, qb0, qend - 1, s0, wave, lane);
-        Tl::issue(gs, qb0, qend - 1, s0 + Tl::BYTES, wave, lane);
-        // statistics: lanes 0..31 lden, 32..63 delta (rows past the chunk are masked; each
-        // array carries 32 spare values, so reads past the last slab stay inside it)
-        if (wave == 0) {
-            const uint32_t off = (uint32_t)(((lane >= 32 ? a.stat_stride : 0) + slab + qb0 + lane % 32) * 4);
-            dma4_s(a.stats, off, lds_addr(s0 + 2 * Tl::BYTES));
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            // a half past the chunk's end copies its last rows (never used): every tile issues
+            // the same number of copies, which the waits count
+            const int qh0 = min(qb0 + 32 * hf, qend - 1);
+            unsigned char* s0 = slot(i) + hf * HALF;
+            Tl::issue(qs, qh0, qend - 1, s0, wave, lane);
+            Tl::issue(gs, qh0, qend - 1, s0 + Tl::BYTES, wave, lane);
+            // statistics: lanes 0..31 lden, 32..63 delta (rows past the chunk are masked; each
+            // array carries 32 spare values, so reads past the last slab stay inside it)
+            if (wave == 0) {
+                const uint32_t off = (uint32_t)(((lane >= 32 ? a.stat_stride : 0) + slab + qh0 + lane % 32) * 4);
+                dma4_s(a.stats, off, lds_addr(s0 + 2 * Tl::BYTES));
+            }
         }
     };
     // this wave's copy instructions per tile: its share of the Q and G blocks, and the
-    // statistics (wave 0); waiting for all but `later` tiles' worth leaves those in flight
-    const int per_tile = 2 * (wave < Tl::NI ? (Tl::NI - 1 - wave) / NW + 1 : 0) + (wave == 0 ? 1 : 0);
+    // statistics (wave 0), for both halves; waiting for all but `later` tiles' worth leaves
+    // those in flight
+    const int per_tile = 2 * (2 * (wave < Tl::NI ? (Tl::NI - 1 - wave) / NW + 1 : 0) + (wave == 0 ? 1 : 0));
     auto sync = [&](int later) {
         wait_vm_lds_n(per_tile * later);
         asm volatile("s_barrier" ::: "memory");
@@ -450,8 +458,11 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkv_kernel(const
         int q0, q1, k0, k1;
         chunk_span(a, c, q0, q1, k0, k1);
         const bool kin = kok && kw >= k0 && kw < k1;  // key inside this chunk's window
-        const int qlim = q1 - qb0;                     // queries of this block inside the chunk
-        const unsigned char* s0 = slot(i);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+        const int qlim = q1 - (qb0 + 32 * hf);  // queries of this half inside the chunk
+        if (qlim <= 0) break;
+        const unsigned char* s0 = slot(i) + hf * HALF;
         const bf16* Qt_ = reinterpret_cast<const bf16*>(s0);
         const bf16* Gt_ = reinterpret_cast<const bf16*>(s0 + Tl::BYTES);
         const float* st = reinterpret_cast<const float*>(s0 + 2 * Tl::BYTES);
@@ -485,6 +496,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkv_kernel(const
         for (int dc = 0; dc < ND; ++dc) {
             dv[dc] = mma16(tread(Gt_, dc), pf, dv[dc]);
             dk[dc] = mma16(tread(Qt_, dc), sf, dk[dc]);
+        }
         }
         sync(min(ntiles - 2 - i, 2));
     }
@@ -527,7 +539,7 @@ hipError_t lds_limit(const void* fn, size_t lds, size_t (&done)[64]) {
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     const size_t lds_q = 5 * (size_t)(2 * Rows32<D, BwdTiles<D>::LD16, 8>::BYTES);
-    const size_t lds_k = 4 * (size_t)(2 * Rows32<D, BwdTiles<D>::LD16, kDkvWaves>::BYTES + 256);
+    const size_t lds_k = 4 * 2 * (size_t)(2 * Rows32<D, BwdTiles<D>::LD16, kDkvWaves>::BYTES + 256);
     static size_t set_q[64] = {}, set_k[64] = {};
     hipError_t e = lds_limit(reinterpret_cast<const void*>(bwd_dkv_kernel<D, kDkvWaves>), lds_k, set_k);
     if (e != hipSuccess) return e;
