@@ -165,19 +165,22 @@ __device__ inline bf16x8 rd_tr(const bf16* t, int ta, int ld, int dc) {
 }
 
 // Query-stationary pass: dQ of 256 queries of one chunk (8 waves x 32, two per SIMD).  Per
-// 32-key tile and wave: S^T = K Q^T and dP^T = V G^T as 2 x 2 C tiles (keys 16 kh + 4 g + i,
+// 32-key half and wave: S^T = K Q^T and dP^T = V G^T as 2 x 2 C tiles (keys 16 kh + 4 g + i,
 // this lane's query 16 qh + a), dS^T from them, dQ += dS K (A = dS^T values, B = K
 // transposed).  Accumulators: 2 x D / 16 tiles of 4 registers.  Software-pipelined: the
-// score products of tile i + 1 are issued before the softmax arithmetic of tile i (the
-// matrix core works while the vector ALU does), so tile i + 2 must have landed before a
-// step starts and the ring holds five tiles.
+// score products of key half i + 1 are issued before the softmax arithmetic of half i (the
+// matrix core works while the vector ALU does).  A ring slot holds 64 keys (two halves of 32)
+// and the workgroup meets at one barrier per slot; slot t + 1 must have landed before slot t
+// is swept (its first half's scores are read at the end of slot t), and the ring holds four
+// slots, the copy of slot t + 3 issued as slot t starts.
 template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdArgs a) {
-    constexpr int NW = 8, NK = D / 32, ND = D / 16, R = 5;
+    constexpr int NW = 8, NK = D / 32, ND = D / 16, R = 4;
     constexpr int LD = BwdTiles<D>::LD16;
     using Tl = Rows32<D, LD, NW>;
-    constexpr int SLOT = 2 * Tl::BYTES;  // K, then V
-    constexpr int NMIN = 2 * Tl::NMIN;
+    constexpr int HALF = 2 * Tl::BYTES;  // K, then V, of 32 keys
+    constexpr int SLOT = 2 * HALF;       // a ring slot holds 64 keys: one barrier per 64
+    constexpr int NMIN = 4 * Tl::NMIN;   // copy instructions per slot of the wave with the fewest
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int blk = xcd_item(a.BH * a.nc * a.qtiles);
@@ -221,17 +224,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
         for (int dc = 0; dc < ND; ++dc) acc[qh][dc] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nkt = (Lk + 31) / 32;
-    auto slot = [&](int i) { return smem + (i % R) * SLOT; };
-    auto dma = [&](int i) {
-        unsigned char* s0 = slot(i);
-        const int r0 = k0 + 32 * i;
-        Tl::issue(ks, r0, k1 - 1, s0, wave, lane);
-        Tl::issue(vs, r0, k1 - 1, s0 + Tl::BYTES, wave, lane);
+    const int nkt = (Lk + 31) / 32;   // 32-key halves
+    const int nst = (nkt + 1) / 2;    // 64-key ring slots
+    // half i of the window: keys k0 + 32 i .. + 31, in half i % 2 of slot i / 2
+    auto slot = [&](int i) { return smem + ((i / 2) % R) * SLOT + (i % 2) * HALF; };
+    // both halves of slot tile t (a half past the window copies its last rows, never used: every
+    // slot issues the same number of copies, which the waits count)
+    auto dma = [&](int t) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            unsigned char* s0 = smem + (t % R) * SLOT + hf * HALF;
+            const int r0 = min(k0 + 64 * t + 32 * hf, k1 - 1);
+            Tl::issue(ks, r0, k1 - 1, s0, wave, lane);
+            Tl::issue(vs, r0, k1 - 1, s0 + Tl::BYTES, wave, lane);
+        }
     };
+    // wait until at most `later` slots of copies are in flight, then the workgroup barrier
     auto sync = [&](int later) {
-        if (later >= 2) wait_vm_lds<2 * NMIN>();
-        else if (later == 1) wait_vm_lds<NMIN>();
+        if (later >= 1) wait_vm_lds<NMIN>();
         else wait_vm_lds<0>();
         asm volatile("s_barrier" ::: "memory");
     };
@@ -289,19 +299,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdArgs a) {
     // the operand loads above complete before the first copy is issued: the compiler does
     // not count the copies, and a wait for those loads inside the loop would drain them
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    for (int i = 0; i < R - 1 && i < nkt; ++i) dma(i);
-    sync(min(nkt - 2, 2));  // tiles 0 and 1 landed
+    for (int t = 0; t < R - 1 && t < nst; ++t) dma(t);
+    sync(min(nst - 2, 1));  // slots 0 and 1 landed
     f32x4 SA[2][2], PA[2][2], SB[2][2], PB[2][2];
     scores(0, SA, PA);
-    auto step = [&](int i, f32x4 (&Sc)[2][2], f32x4 (&Pc)[2][2], f32x4 (&Sn)[2][2], f32x4 (&Pn)[2][2]) {
-        if (i + R - 1 < nkt) dma(i + R - 1);  // into the slot tile i - 1 used
-        if (i + 1 < nkt) scores(i + 1, Sn, Pn);
-        products(i, Sc, Pc);
-        sync(min(nkt - 3 - i, 2));  // tile i + 2 landed; every wave is done with tile i
-    };
-    for (int i = 0; i < nkt; i += 2) {
-        step(i, SA, PA, SB, PB);
-        if (i + 1 < nkt) step(i + 1, SB, PB, SA, PA);
+    // slot tile t: halves 2t and 2t + 1, each with the score products of the next half (which
+    // may lie in slot t + 1) ahead of its own dS and dQ products
+    for (int t = 0; t < nst; ++t) {
+        if (t + R - 1 < nst) dma(t + R - 1);  // into the slot tile t - 1 used
+        const int i = 2 * t;
+        if (i + 1 < nkt) scores(i + 1, SB, PB);
+        products(i, SA, PA);
+        if (i + 1 < nkt) {
+            if (i + 2 < nkt) scores(i + 2, SA, PA);
+            products(i + 1, SB, PB);
+        }
+        sync(min(nst - 3 - t, 1));  // slot t + 2 landed; every wave is done with slot t
     }
     // acc[qh][dc]: column d = 16 dc + a, rows = queries 16 qh + 4 g + {0..3} of this wave
     float* dq = a.dq + slab * D;
@@ -538,7 +551,7 @@ hipError_t lds_limit(const void* fn, size_t lds, size_t (&done)[64]) {
 
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
-    const size_t lds_q = 5 * (size_t)(2 * Rows32<D, BwdTiles<D>::LD16, 8>::BYTES);
+    const size_t lds_q = 4 * 2 * (size_t)(2 * Rows32<D, BwdTiles<D>::LD16, 8>::BYTES);
     const size_t lds_k = 4 * 2 * (size_t)(2 * Rows32<D, BwdTiles<D>::LD16, kDkvWaves>::BYTES + 256);
     static size_t set_q[64] = {}, set_k[64] = {};
     hipError_t e = lds_limit(reinterpret_cast<const void*>(bwd_dkv_kernel<D, kDkvWaves>), lds_k, set_k);
