@@ -438,8 +438,14 @@ __global__ __launch_bounds__(256) void ntf16_kernel(const NtArgs a, const GradAr
     constexpr int JB = 64 / P, CLD = 65;
     constexpr bool XS = sizeof(TX) == 4, YS = sizeof(TY) == 4;
     constexpr int TILE = 64 * kLd16;
-    __shared__ __align__(16) bf16 xs[(XS ? 2 : 1) * TILE], ys[(YS ? 2 : 1) * TILE];
-    __shared__ float cs[64 * CLD];
+    // the operand slices and, once the contraction is done, the dphi tile share one LDS area
+    // (fewer bytes per workgroup, more workgroups per CU)
+    constexpr int XB = (XS ? 2 : 1) * TILE, YB = (YS ? 2 : 1) * TILE;
+    constexpr int STAGE = (XB + YB) * (int)sizeof(bf16), CSB = 64 * CLD * (int)sizeof(float);
+    __shared__ __align__(16) unsigned char lds[STAGE > CSB ? STAGE : CSB];
+    bf16* const xs = reinterpret_cast<bf16*>(lds);
+    bf16* const ys = xs + XB;
+    float* const cs = reinterpret_cast<float*>(lds);
     int bx, by, bt;
     if (!xcd_tile(s.Dphi / JB, a.ngroups * a.tiles_per_group, s.BH, bx, by, bt)) return;
     const int grp = by / a.tiles_per_group, t = by % a.tiles_per_group;
@@ -497,9 +503,11 @@ __global__ __launch_bounds__(256) void ntf16_kernel(const NtArgs a, const GradAr
             acc = mma16(xh, yh, acc);
         }
     }
-    // dphi of the tile into LDS (with the -Y[f][sub_col] term of mode 2), then dpre
+    // dphi of the tile into LDS (with the -Y[f][sub_col] term of mode 2), then dpre; the tile
+    // overwrites the operand slices, so every wave must be done reading them
     const int c = wc * 32 + col;
     const float add = a.sub_col >= 0 ? -load1<TY>(yb + (int64_t)yrow(c) * a.ldy + a.sub_col) : 0.f;
+    __syncthreads();
 #pragma unroll
     for (int q = 0; q < 16; ++q) cs[(wr * 32 + crow(q, h)) * CLD + c] = acc[q] + add;
     __syncthreads();
