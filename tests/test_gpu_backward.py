@@ -37,6 +37,8 @@ SHAPES = [
     (1, 2, 32, 7, 70, 3, 2, 32, 2, 0, rh.BF16, True),      # D = 32; key blocks across windows
     (1, 1, 128, 2, 33, 3, 1, 64, 2, 0, rh.BF16, False),    # T < Tc: one short chunk, ragged tiles
     (1, 2, 64, 6, 40, 3, 1, 128, 4, 0, rh.BF16, True),     # fused feature-map backward, P = 4
+    (1, 2, 64, 4, 8, 2, 1, 32, 2, 0, rh.BF16, False),      # windows of 16 and 24 keys: one key half, one slot
+    (1, 1, 128, 2, 32, 2, 0, 64, 2, 0, rh.BF16, True),     # one chunk of 64 queries and keys: one full slot
 ]
 
 
