@@ -149,10 +149,13 @@ struct Slice {
 __device__ inline int part_len(int j, int Dphi, int P);
 
 // Epilogue of the nt products: lane (col, h) holds column f of rows r0 + crow(q, h).
+// FAST (bf16 inputs): the softplus of the bf16 forward (hardware exp2 / log2, softplus_fast),
+// else the float32 feature map's log1p form.
+template <bool FAST = false>
 __device__ inline void nt_store(const NtArgs& a, const GradArgs& s, int bt, float* cb, int r0, int rend, int f, int h,
                                 const f32x16& acc, float add) {
     if (a.softplus) {
-        // u = softplus(pre) (the form the feature-map kernel uses) and its powers
+        // u = softplus(pre) (the form the forward of the same input type uses) and its powers
         const int f1 = feat_index(f, 1, s.Dphi, s.P), step = part_len(f, s.Dphi, s.P);
         float* const pb = a.phi ? a.phi + (int64_t)bt * a.phi_bt_stride + f1 : nullptr;
 #pragma unroll
@@ -160,7 +163,7 @@ __device__ inline void nt_store(const NtArgs& a, const GradArgs& s, int bt, floa
             const int rr = r0 + crow(q, h);
             if (rr < rend) {
                 const float x = acc[q] + add;
-                const float u = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+                const float u = FAST ? softplus_fast<bf16>(x) : fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
                 cb[(int64_t)rr * a.ldc + f] = u;
                 if (pb) {
                     float pw = u;
@@ -421,7 +424,7 @@ __global__ __launch_bounds__(256) void nt16_kernel(const NtArgs a, const GradArg
     float add = 0.f;
     if (a.colbias) add += a.colbias[(int64_t)(bt % s.H) * a.colbias_head_stride + f];
     if (a.sub_col >= 0) add -= load1<TY>(yrow + a.sub_col);
-    nt_store(a, s, bt, cb, row0 + wr * 32, rend, f, h, acc, add);
+    nt_store<sizeof(TX) == 2 && sizeof(TY) == 2>(a, s, bt, cb, row0 + wr * 32, rend, f, h, acc, add);
 }
 
 // The feature gradients (nt modes 1 and 2) with the feature map's backward fused (blog
