@@ -51,6 +51,15 @@ __device__ inline int ls_of(const GradArgs& a, int c) {
 
 __device__ inline bf16 to_bf16(float x) { return (bf16)x; }
 
+// 1 - exp(-u) for u >= 0 (the logistic sigmoid of the pre-activation, with u its softplus): the
+// hardware exp2, and below u = 1/16, where that difference would cancel, the series
+// u - u^2/2 + u^3/6 - u^4/24 (truncation below 2^-26 relative there)
+__device__ inline float one_minus_exp_neg(float u) {
+    const float e = 1.f - __builtin_amdgcn_exp2f(-u * 1.4426950408889634f);
+    const float t = u * (1.f - u * (0.5f - u * (1.f / 6.f - u * (1.f / 24.f))));
+    return u < 0.0625f ? t : e;
+}
+
 // One thread's share of an R x C block of a row-major source (rows [r0, r0 + R), columns
 // [c0, c0 + C), zero outside rlim / clim), read as 16-byte chunks into registers and written
 // to dst[r * LD + c] as DT (bf16 or float).  Reading and writing are separate steps so that a
@@ -433,8 +442,9 @@ __global__ __launch_bounds__(256) void nt16_kernel(const NtArgs a, const GradArg
 // feature j0 + c % JB; the rows of Y are read in that order), so the epilogue holds dphi of
 // every power of its features and writes, over u in C (= U [bt][N][Dphi], in place),
 //   dpre[i][j] = sigmoid(pre) sum_p p u^(p-1) dphi[i][feat(j, p)],  sigmoid(pre) = 1 - exp(-u),
-// in the arithmetic of phi_bwd_kernel; dphi itself is never stored.  Each output column's
-// sums are those of nt16_kernel, so the result is the same.  Requires every part length to
+// with 1 - exp(-u) on the hardware exp2 (one_minus_exp_neg; phi_bwd_kernel takes expm1f);
+// dphi itself is never stored.  Each output column's
+// sums are those of nt16_kernel (the same dphi).  Requires every part length to
 // be a multiple of JB: P = 1, 2 or 4 and Dphi a multiple of 64.
 template <class TX, class TY, int P>
 __global__ __launch_bounds__(256) void ntf16_kernel(const NtArgs a, const GradArgs s) {
@@ -525,7 +535,7 @@ __global__ __launch_bounds__(256) void ntf16_kernel(const NtArgs a, const GradAr
             du += (float)(p + 1) * upow * cs[r * CLD + p * JB + jj];
             upow *= u;
         }
-        *up = du * -expm1f(-u);
+        *up = du * one_minus_exp_neg(u);
     }
 }
 
