@@ -952,7 +952,7 @@ rehyat_status linear_branch(const rehyat_params* p, const GradArgs& s, const Gra
         t.ngroups = s.nc;
         t.seg_rows = s.n;
         t.nseg = s.Tc;
-        GRAD_TRY(launch_tn(t, s.BH, false, stream, bf));
+        GRAD_TRY(launch_tn(t, s.BH, false, stream, bf, bf));  // phi in bf16 for bf16 inputs
         const int64_t E = (int64_t)s.F * LD;
         GRAD_TRY(launch_grad_reduce(F32(L.rp), F32(L.r), 1, s.BH * s.nc, s.Tc, E, stream));
         GRAD_TRY(launch_grad_suffix(F32(L.r), s.BH, s.nc, E, stream));
@@ -983,7 +983,7 @@ rehyat_status linear_branch(const rehyat_params* p, const GradArgs& s, const Gra
         a.ldc = s.D;
         a.group_rows = s.n;
         a.ngroups = s.T;
-        GRAD_TRY(launch_nt(a, s, false, false, stream, bf));
+        GRAD_TRY(launch_nt(a, s, bf, false, stream, bf));  // phi in bf16 for bf16 inputs
     }
     {
         NtArgs a = nt_base();

@@ -158,15 +158,17 @@ struct Slice {
 __device__ inline int part_len(int j, int Dphi, int P);
 
 // Epilogue of the nt products: lane (col, h) holds column f of rows r0 + crow(q, h).
-// FAST (bf16 inputs): the softplus of the bf16 forward (hardware exp2 / log2, softplus_fast),
-// else the float32 feature map's log1p form.
+// FAST (bf16 inputs): the softplus of the bf16 forward (hardware exp2 / log2, softplus_fast)
+// and phi stored in bf16, the precision in which the bf16 forward multiplies it; else the
+// float32 feature map's log1p form and phi in float.
 template <bool FAST = false>
 __device__ inline void nt_store(const NtArgs& a, const GradArgs& s, int bt, float* cb, int r0, int rend, int f, int h,
                                 const f32x16& acc, float add) {
     if (a.softplus) {
         // u = softplus(pre) (the form the forward of the same input type uses) and its powers
+        using PT = std::conditional_t<FAST, bf16, float>;
         const int f1 = feat_index(f, 1, s.Dphi, s.P), step = part_len(f, s.Dphi, s.P);
-        float* const pb = a.phi ? a.phi + (int64_t)bt * a.phi_bt_stride + f1 : nullptr;
+        PT* const pb = a.phi ? reinterpret_cast<PT*>(a.phi) + (int64_t)bt * a.phi_bt_stride + f1 : nullptr;
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             const int rr = r0 + crow(q, h);
@@ -176,9 +178,9 @@ __device__ inline void nt_store(const NtArgs& a, const GradArgs& s, int bt, floa
                 cb[(int64_t)rr * a.ldc + f] = u;
                 if (pb) {
                     float pw = u;
-                    float* out = pb + (int64_t)rr * s.F;
+                    PT* out = pb + (int64_t)rr * s.F;
                     for (int p = 0; p < s.P; ++p) {
-                        out[p * step] = pw;
+                        out[p * step] = (PT)pw;
                         pw *= u;
                     }
                 }
@@ -1018,7 +1020,9 @@ hipError_t launch_ntf16(const NtArgs& a, const GradArgs& s, bool x_bf16, hipStre
     return x_bf16 ? launch_ntf16_t<bf16, float>(a, s, stream) : launch_ntf16_t<float, float>(a, s, stream);
 }
 
-hipError_t launch_tn(const TnArgs& a, int BH, bool y_bf16, hipStream_t stream, bool mc16) {
+hipError_t launch_tn(const TnArgs& a, int BH, bool y_bf16, hipStream_t stream, bool mc16, bool x_bf16) {
+    if (mc16 && x_bf16) return y_bf16 ? hipErrorInvalidValue : launch_tn16_t<bf16, float>(a, BH, stream);
+    if (x_bf16) return hipErrorInvalidValue;
     if (mc16) return y_bf16 ? launch_tn16_t<float, bf16>(a, BH, stream) : launch_tn16_t<float, float>(a, BH, stream);
     return y_bf16 ? launch_tn_t<float, bf16>(a, BH, stream) : launch_tn_t<float, float>(a, BH, stream);
 }

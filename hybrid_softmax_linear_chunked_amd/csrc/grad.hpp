@@ -19,7 +19,8 @@ struct GradArgs {
 // accumulating), mode 3 the slab bt itself.  accumulate: add to C instead of storing.
 // softplus (mode 0, no accumulation): C gets u = softplus(result) (the feature map's
 // activation, blog 2.2.2) and, when phi is non-null, phi[bt][i][feat(f, p)] = u^p for the
-// powers p = 1..P (row stride F, slab stride phi_bt_stride).
+// powers p = 1..P (row stride F, slab stride phi_bt_stride; bf16 elements in the bf16 matrix-
+// core product nt16_kernel<bf16, bf16>, float elsewhere).
 struct NtArgs {
     const void* x;
     int64_t x_bt_stride;
@@ -77,7 +78,7 @@ hipError_t launch_bwd_softmax(BwdArgs a, int D, hipStream_t stream);
 // otherwise on the fp32 matrix core
 hipError_t launch_nt(const NtArgs& a, const GradArgs& s, bool x_bf16, bool y_bf16, hipStream_t stream,
                      bool mc16 = false);
-hipError_t launch_tn(const TnArgs& a, int BH, bool y_bf16, hipStream_t stream, bool mc16 = false);
+hipError_t launch_tn(const TnArgs& a, int BH, bool y_bf16, hipStream_t stream, bool mc16 = false, bool x_bf16 = false);
 // The feature gradient (mode 1 or 2, float Y) on the bf16 matrix core with the feature map's
 // backward fused: a.c is U [BH][N][Dphi] (ldc = Dphi), which gets dpre in place of u.
 // Only where ntf16_fusable (P = 1, 2, 4 and Dphi a multiple of 64).
