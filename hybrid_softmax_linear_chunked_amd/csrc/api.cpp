@@ -1080,7 +1080,7 @@ rehyat_status rehyat_distill_grad(const rehyat_params* p, const void* q, const v
     GRAD_TRY(launch_sqdist(F32(L.stu), F32(L.tea), len, s.BH, F32(L.sqd), loss, stream));
     if (s.G == 0) return zero_param_grads(p, s, dwq, dwk, dbq, dbk, stream);  // the loss does not depend on phi
     GRAD_TRY(launch_grad_rows(s, F32(L.stu), F32(L.tea), nullptr, F32(L.lse), F32(L.z), F32(L.ah), nullptr, nullptr,
-                              stream));
+                              nullptr, stream));
     return linear_branch(p, s, L, w, q, k, v, wq, wk, bq, bk, dwq, dwk, dbq, dbk, nullptr, nullptr, nullptr, stream);
 }
 
@@ -1118,8 +1118,9 @@ rehyat_status rehyat_backward(const rehyat_params* p, const void* q, const void*
     st = rehyat_forward_parallel_aux(&ps, q, k, v, wq, wk, bq, bk, w + L.stu, &aux, w + L.fwd_s, L.fwd_t - L.fwd_s,
                                      stream);
     if (st != REHYAT_OK) return st;
+    // bf16 inputs: the upstream gradient also rounded to bf16 once (the flash products' operand precision)
     GRAD_TRY(launch_grad_rows(s, F32(L.stu), nullptr, dout, F32(L.lse), F32(L.z), F32(L.ah), F32(L.delta),
-                              F32(L.lden), stream));
+                              F32(L.lden), bf ? (void*)(w + L.g16) : nullptr, stream));
     if (s.G > 0) {
         // writes dq, dk, dv first
         st = linear_branch(p, s, L, w, q, k, v, wq, wk, bq, bk, dwq, dwk, dbq, dbk, dq, dk, dv, stream);
@@ -1132,8 +1133,6 @@ rehyat_status rehyat_backward(const rehyat_params* p, const void* q, const void*
         if (st != REHYAT_OK) return st;
     }
 
-    // bf16 inputs: the upstream gradient rounded to bf16 once (the products' operand precision)
-    if (bf) GRAD_TRY(launch_to_bf16(dout, w + L.g16, (int64_t)s.BH * ND, stream));
     const float scale = (float)(1.0 / std::sqrt((double)s.D));
     if (bf) {
         // softmax branch, flash style (blog 2.2.1 window, scores q.k / sqrt(D)): P and dS

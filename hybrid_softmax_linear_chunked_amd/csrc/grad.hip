@@ -733,14 +733,15 @@ __global__ __launch_bounds__(256) void state_sz_kernel(const GradArgs s, const f
 
 // Per query row (kRowsPerWave rows per wave, their loads issued together): g = dout, or
 // 2 (o - t) for the distillation objective; 1/den from lse and z; AH[i] = [g / den |
-// (g . o) / den | 0 ...] (D + 32 columns), and when asked, delta_i = g . o and log den_i
+// (g . o) / den | 0 ...] (D + 32 columns), and when asked, delta_i = g . o and log den_i,
+// and g16 = dout rounded to bf16 (ties to even)
 constexpr int kRowsPerWave = 4;
 
 __global__ __launch_bounds__(256) void rows_kernel(const GradArgs s, const float* __restrict__ o,
                                                    const float* __restrict__ t, const float* __restrict__ dout,
                                                    const float* __restrict__ lse, const float* __restrict__ z,
                                                    float* __restrict__ AH, float* __restrict__ delta,
-                                                   float* __restrict__ lden) {
+                                                   float* __restrict__ lden, bf16* __restrict__ g16) {
     const int bt = blockIdx.y, wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int64_t i0 = ((int64_t)blockIdx.x * 4 + wave) * kRowsPerWave;
     const int D = s.D, LD = D + 32;
@@ -757,6 +758,7 @@ __global__ __launch_bounds__(256) void rows_kernel(const GradArgs s, const float
             if (ok && d < D) {
                 ov[k][u] = o[row * D + d];
                 gv[k][u] = dout ? dout[row * D + d] : t[row * D + d];
+                if (g16) g16[row * D + d] = to_bf16(gv[k][u]);
             }
         }
     }
@@ -990,29 +992,6 @@ hipError_t launch_nt(const NtArgs& a, const GradArgs& s, bool x_bf16, bool y_bf1
     return launch_nt_t<float, float>(a, s, stream);
 }
 
-__global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ in, bf16* __restrict__ out,
-                                                      int64_t n4) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
-        const float4 x = reinterpret_cast<const float4*>(in)[i];
-        bf16x4 v;
-        v[0] = to_bf16(x.x);
-        v[1] = to_bf16(x.y);
-        v[2] = to_bf16(x.z);
-        v[3] = to_bf16(x.w);
-        reinterpret_cast<bf16x4*>(out)[i] = v;
-    }
-}
-
-hipError_t launch_to_bf16(const float* in, void* out, int64_t n, hipStream_t stream) {
-    const int64_t n4 = n / 4;
-    int64_t blocks = (n4 + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
-    if (blocks < 1) return hipSuccess;
-    hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in, reinterpret_cast<bf16*>(out),
-                       n4);
-    return hipGetLastError();
-}
-
 bool ntf16_fusable(const GradArgs& s) { return (s.P == 1 || s.P == 2 || s.P == 4) && s.Dphi % 64 == 0; }
 
 hipError_t launch_ntf16(const NtArgs& a, const GradArgs& s, bool x_bf16, hipStream_t stream) {
@@ -1075,10 +1054,11 @@ hipError_t launch_grad_state_sz(const GradArgs& s, const float* Sp, const float*
 }
 
 hipError_t launch_grad_rows(const GradArgs& s, const float* o, const float* t, const float* dout, const float* lse,
-                            const float* z, float* AH, float* delta, float* lden, hipStream_t stream) {
+                            const float* z, float* AH, float* delta, float* lden, void* g16, hipStream_t stream) {
     const int per_wg = 4 * kRowsPerWave;
+    if (g16 && !dout) return hipErrorInvalidValue;
     hipLaunchKernelGGL(rows_kernel, dim3((unsigned)((s.N + per_wg - 1) / per_wg), s.BH), dim3(256), 0, stream, s, o, t,
-                       dout, lse, z, AH, delta, lden);
+                       dout, lse, z, AH, delta, lden, reinterpret_cast<bf16*>(g16));
     return hipGetLastError();
 }
 

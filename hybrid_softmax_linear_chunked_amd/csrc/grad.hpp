@@ -84,14 +84,13 @@ hipError_t launch_tn(const TnArgs& a, int BH, bool y_bf16, hipStream_t stream, b
 // Only where ntf16_fusable (P = 1, 2, 4 and Dphi a multiple of 64).
 bool ntf16_fusable(const GradArgs& s);
 hipError_t launch_ntf16(const NtArgs& a, const GradArgs& s, bool x_bf16, hipStream_t stream);
-// out[i] = in[i] rounded to bf16 (ties to even), n a multiple of 4
-hipError_t launch_to_bf16(const float* in, void* out, int64_t n, hipStream_t stream);
 hipError_t launch_grad_reduce(const float* part, float* out, int nb, int no, int ns, int64_t E, hipStream_t stream,
                               int64_t out_stride = -1, bool accumulate = false);
 hipError_t launch_grad_suffix(float* R, int BH, int nc, int64_t E, hipStream_t stream);
 hipError_t launch_grad_state_sz(const GradArgs& s, const float* Sp, const float* Zp, float* SZ, hipStream_t stream);
+// g16 (optional, only with dout): receives dout rounded to bf16, [BH][N][D]
 hipError_t launch_grad_rows(const GradArgs& s, const float* o, const float* t, const float* dout, const float* lse,
-                            const float* z, float* AH, float* delta, float* lden, hipStream_t stream);
+                            const float* z, float* AH, float* delta, float* lden, void* g16, hipStream_t stream);
 // Softmax branch of the backward on one chunk window (Lq queries x Lk keys, rows of ldp
 // floats, slab stride bt_stride): S (raw q.k) becomes P = exp(S / sqrt(D) - log den_i) and
 // dP (G_i . v_j) becomes dS = P (dP - delta_i) / sqrt(D); columns Lk..ldp-1 become zero.
