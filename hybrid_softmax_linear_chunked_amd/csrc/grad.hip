@@ -742,36 +742,30 @@ __global__ __launch_bounds__(256) void rows_kernel(const GradArgs s, const float
                                                    const float* __restrict__ lse, const float* __restrict__ z,
                                                    float* __restrict__ AH, float* __restrict__ delta,
                                                    float* __restrict__ lden, bf16* __restrict__ g16) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const int bt = blockIdx.y, wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int64_t i0 = ((int64_t)blockIdx.x * 4 + wave) * kRowsPerWave;
-    const int D = s.D, LD = D + 32;
-    float ov[kRowsPerWave][2], gv[kRowsPerWave][2];
+    // two adjacent columns per lane (D = 32, 64 or 128, rows 16-byte aligned): 8-byte loads
+    // and 4-byte bf16 stores
+    const int D = s.D, LD = D + 32, d = 2 * lane;
+    f32x2 ov[kRowsPerWave], gv[kRowsPerWave];
 #pragma unroll
     for (int k = 0; k < kRowsPerWave; ++k) {
         const int64_t row = (int64_t)bt * s.N + i0 + k;
-        const bool ok = i0 + k < s.N;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int d = lane + 64 * u;
-            ov[k][u] = 0.f;
-            gv[k][u] = 0.f;
-            if (ok && d < D) {
-                ov[k][u] = o[row * D + d];
-                gv[k][u] = dout ? dout[row * D + d] : t[row * D + d];
-                if (g16) g16[row * D + d] = to_bf16(gv[k][u]);
-            }
+        ov[k] = f32x2{0.f, 0.f};
+        gv[k] = f32x2{0.f, 0.f};
+        if (i0 + k < s.N && d < D) {
+            ov[k] = *reinterpret_cast<const f32x2*>(o + row * D + d);
+            gv[k] = *reinterpret_cast<const f32x2*>((dout ? dout : t) + row * D + d);
+            if (g16) *reinterpret_cast<bf16x2*>(g16 + row * D + d) = bf16x2{to_bf16(gv[k][0]), to_bf16(gv[k][1])};
         }
     }
 #pragma unroll
     for (int k = 0; k < kRowsPerWave; ++k) {
         if (i0 + k >= s.N) break;
         const int64_t row = (int64_t)bt * s.N + i0 + k;
-        float dot = 0.f;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            if (!dout) gv[k][u] = 2.f * (ov[k][u] - gv[k][u]);
-            dot += gv[k][u] * ov[k][u];
-        }
+        if (!dout) gv[k] = 2.f * (ov[k] - gv[k]);
+        float dot = gv[k][0] * ov[k][0] + gv[k][1] * ov[k][1];
 #pragma unroll
         for (int msk = 32; msk >= 1; msk >>= 1) dot += __shfl_xor(dot, msk, 64);
         const float L = lse[row], zz = z[row];
@@ -785,11 +779,7 @@ __global__ __launch_bounds__(256) void rows_kernel(const GradArgs s, const float
             inv = 1.f / (zz + expf(L));
         }
         float* ah = AH + row * LD;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int d = lane + 64 * u;
-            if (d < D) ah[d] = gv[k][u] * inv;
-        }
+        if (d < D) *reinterpret_cast<f32x2*>(ah + d) = gv[k] * inv;
         if (lane < 32) ah[D + lane] = lane == 0 ? dot * inv : 0.f;
         if (lane == 0 && delta) {
             delta[row] = dot;
