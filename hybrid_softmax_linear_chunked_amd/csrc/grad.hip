@@ -449,7 +449,7 @@ __global__ __launch_bounds__(256) void nt16_kernel(const NtArgs a, const GradArg
 // sums are those of nt16_kernel (the same dphi).  Requires every part length to
 // be a multiple of JB: P = 1, 2 or 4 and Dphi a multiple of 64.
 template <class TX, class TY, int P>
-__global__ __launch_bounds__(256) void ntf16_kernel(const NtArgs a, const GradArgs s) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void ntf16_kernel(const NtArgs a, const GradArgs s) {
     constexpr int JB = 64 / P, CLD = 65;
     constexpr bool XS = sizeof(TX) == 4, YS = sizeof(TY) == 4;
     constexpr int TILE = 64 * kLd16;
@@ -489,6 +489,16 @@ __global__ __launch_bounds__(256) void ntf16_kernel(const NtArgs a, const GradAr
         }
         return;
     }
+    // u of the workgroup's 64 x JB outputs, read before the contraction so that its latency
+    // overlaps it (each element belongs to this workgroup alone)
+    // (thread tid takes column tid % JB of rows r0 + RS * i)
+    constexpr int NE = 64 * JB / 256, RS = 256 / JB;
+    const int ur0 = row0 + tid / JB;
+    float* const ub = U + (int64_t)ur0 * a.ldc + j0 + tid % JB;
+    const int64_t ustep = (int64_t)RS * a.ldc;
+    float uv[NE];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) uv[i] = ur0 + RS * i < rend ? ub[i * ustep] : 0.f;
     auto yrow = [&](int c) { return feat_index(j0 + c % JB, c / JB + 1, s.Dphi, P); };
     const TX* xb = reinterpret_cast<const TX*>(a.x) + (int64_t)bt * a.x_bt_stride;
     const TY* yb = reinterpret_cast<const TY*>(a.y) + (int64_t)m * a.y_mat_stride;
@@ -526,18 +536,19 @@ __global__ __launch_bounds__(256) void ntf16_kernel(const NtArgs a, const GradAr
 #pragma unroll
     for (int q = 0; q < 16; ++q) cs[(wr * 32 + crow(q, h)) * CLD + c] = acc[q] + add;
     __syncthreads();
-    for (int e = tid; e < 64 * JB; e += 256) {
-        const int r = e / JB, jj = e % JB, row = row0 + r;
-        if (row >= rend) continue;
-        float* const up = U + (int64_t)row * a.ldc + j0 + jj;
-        const float u = *up;
+    const int jj = tid % JB;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        const int r = tid / JB + RS * i;
+        if (row0 + r >= rend) continue;
+        const float u = uv[i];
         float du = 0.f, upow = 1.f;
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             du += (float)(p + 1) * upow * cs[r * CLD + p * JB + jj];
             upow *= u;
         }
-        *up = du * one_minus_exp_neg(u);
+        ub[i * ustep] = du * one_minus_exp_neg(u);
     }
 }
 
