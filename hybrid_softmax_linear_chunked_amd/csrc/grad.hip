@@ -561,7 +561,7 @@ using TrTile = DmaTiles<64, 4>;
 constexpr int kTrLd = TrTile::VLD;  // 96
 
 template <class TX, class TY>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void tn16_kernel(const TnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void tn16_kernel(const TnArgs a) {
     constexpr bool XS = sizeof(TX) == 4, YS = sizeof(TY) == 4;
     constexpr int TILE = 32 * kTrLd;
     __shared__ __align__(16) bf16 xs[(XS ? 2 : 1) * TILE], ys[(YS ? 2 : 1) * TILE];
@@ -581,19 +581,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void t
     f32x16 acc;
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = 0.f;
-    Slice<TX, 32, 64, kTrLd> sx;
-    Slice<TY, 32, 64, kTrLd> sy;
+    // two slices in flight: slice i + 2 is read into the registers that slice i leaves
+    // (the loop is unrolled by two so that each register set keeps a fixed role)
+    Slice<TX, 32, 64, kTrLd> sx0, sx1;
+    Slice<TY, 32, 64, kTrLd> sy0, sy1;
     if (k0 < k1) {
-        sx.load(xb, a.ldx, k0, k1, m0, a.mrows);
-        sy.load(yb, a.ldy, k0, k1, n0, a.ncols);
+        sx0.load(xb, a.ldx, k0, k1, m0, a.mrows);
+        sy0.load(yb, a.ldy, k0, k1, n0, a.ncols);
     }
-    for (int k = k0; k < k1; k += 32) {
+    if (k0 + 32 < k1) {
+        sx1.load(xb, a.ldx, k0 + 32, k1, m0, a.mrows);
+        sy1.load(yb, a.ldy, k0 + 32, k1, n0, a.ncols);
+    }
+    auto step = [&](auto& sx, auto& sy, int k) {
         __syncthreads();
         sx.store_split(xs, xs + TILE);
         sy.store_split(ys, ys + TILE);
-        if (k + 32 < k1) {  // the next slice is read while this one is multiplied
-            sx.load(xb, a.ldx, k + 32, k1, m0, a.mrows);
-            sy.load(yb, a.ldy, k + 32, k1, n0, a.ncols);
+        if (k + 64 < k1) {
+            sx.load(xb, a.ldx, k + 64, k1, m0, a.mrows);
+            sy.load(yb, a.ldy, k + 64, k1, n0, a.ncols);
         }
         __syncthreads();
 #pragma unroll
@@ -603,6 +609,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void t
             if constexpr (YS) acc = mma16(xh, TrTile::vfrag(ys + TILE, vl, wn, 0, u), acc);
             acc = mma16(xh, yh, acc);
         }
+    };
+    for (int k = k0; k < k1; k += 64) {
+        step(sx0, sy0, k);
+        if (k + 32 < k1) step(sx1, sy1, k + 32);
     }
     const int mm = m0 + wm * 32, nn = n0 + wn * 32;
     if (mm >= a.mrows || nn + col >= a.ncols) return;
