@@ -449,7 +449,7 @@ __global__ __launch_bounds__(256) void nt16_kernel(const NtArgs a, const GradArg
 // sums are those of nt16_kernel (the same dphi).  Requires every part length to
 // be a multiple of JB: P = 1, 2 or 4 and Dphi a multiple of 64.
 template <class TX, class TY, int P>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void ntf16_kernel(const NtArgs a, const GradArgs s) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(TX) == 4 ? 5 : 6))) void ntf16_kernel(const NtArgs a, const GradArgs s) {
     constexpr int JB = 64 / P, CLD = 65;
     constexpr bool XS = sizeof(TX) == 4, YS = sizeof(TY) == 4;
     constexpr int TILE = 64 * kLd16;
